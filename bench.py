@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Paged decode attention on one MI355X: KV-read HBM GB/s (and % of peak) plus decode tokens/s.
+
+One step = one decode step of the whole batch through every layer: the plan (block tables and
+lengths -> wavefront shares, once per step since all layers share them), then per layer the
+new tokens' slot write (pa_write_kv) and the paged attention (pa_decode_attend: decode kernel
++ log-sum-exp merge).  Every layer has its own KV pool in HBM, so no layer's reads are served
+from cache.  Inputs are synthetic, seeded, already resident in HBM when timing starts.
+
+Prints one JSON line.  `value` is the KV bytes the attention reads per step (each attended
+token's K and V once, per KV head, per layer) over the measured step time, in GB/s.
+`roofline` reports the decode kernel alone, timed with HIP events around its launches (the
+library's profiling hook records them on the launch stream).  `cpu_baseline` is the fp64 CPU
+oracle timed on the host cores on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload opt13b|gqa|prefix_mixed|swa|tiny]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV-read HBM GB/s (% of peak) + decode tokens/s"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SOURCES = ["decode_impl.h", "pa_device.h", "plan.hip"]
+
+DESCRIPTIONS = {
+    "opt13b": "OPT-13B-shaped paged decode: 64 seqs, 40 q heads = 40 KV heads, d=128, fp16 KV, "
+              "16-token blocks, lengths U[64,2048], permuted blocks, 40 layers",
+    "gqa": "Qwen3-8B/Mistral-7B-shaped GQA decode: 256 seqs, 32 q / 8 KV heads, d=128, bf16 KV, "
+           "lengths log-normal(median 1024, sigma 1) clipped [16,32768], 36 layers",
+    "prefix_mixed": "shared 512-token prefix (32 blocks, refcount 128) + private suffixes U[1,512], "
+                    "128 decode seqs + 4 chunked-prefill queries of 512 causal rows over 1-4K "
+                    "contexts, 32 q / 8 KV heads, d=128, bf16, 36 layers",
+    "swa": "Gemma-3-4B-shaped sliding-window decode: 32 seqs, 8 q / 4 KV heads, d=256, fp16 KV, "
+           "window 1024, lengths U[4096,131072], 29 sliding layers",
+    "tiny": "tiny paged decode: 4 seqs, lengths {1,17,100,33}, 4 heads, d=64, fp32, 1 layer",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_144_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs, or None when
+    there is none for this workload or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def step_rows(w):
+    """Value rows of each sequence's newest q_rows tokens (this step's writes)."""
+    import numpy as np
+
+    from workloads import Append
+    last = {}
+    for op in w.script:
+        if isinstance(op, Append) and op.nv > 0:
+            last[op.seq] = (op.off, op.nv)
+    rows = []
+    for s in range(w.num_seqs):
+        off, nv = last[s]
+        n = int(w.q_rows[s])
+        rows.extend(range(off + nv - n, off + nv))
+    return np.asarray(rows, np.int64)
+
+
+def cpu_baseline(w, n_layers, seconds):
+    """The fp64 oracle on the same workload: sequences of one layer in a seeded order, eight
+    at a time, cycling until `seconds` pass.  Rates come from what was processed."""
+    import numpy as np
+
+    import oracle
+    import paged_kv_cache_144_amd as pa
+    ref = oracle.Reference(w, poison=False)
+    threads = len(os.sched_getaffinity(0))
+    order = np.random.default_rng(0).permutation(w.num_seqs)
+    done_bytes = done_rows = 0
+    passes = 0
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        chunk = order[i:i + 8]
+        ref.attention(seqs=chunk)
+        done_bytes += pa.kv_bytes_read(w.seq_lens[chunk], w.q_rows[chunk], w.window,
+                                       w.num_kv_heads, w.head_dim, w.elem_bytes)
+        done_rows += int(w.q_rows[chunk].sum())
+        i += 8
+        if i >= w.num_seqs:
+            i = 0
+            passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    frac = passes + i / w.num_seqs
+    return ref, {
+        "value": round(done_bytes / el / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 oracle on {frac:.2f} layer(s) of the same workload "
+                  f"({done_rows} query rows, {done_bytes / 1e9:.3f} GB of KV) in {el:.1f} s",
+        "tokens_per_s": round(done_rows / el / n_layers, 3),
+        "tokens_per_s_note": f"one layer's rate scaled to {n_layers} layers",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="opt13b", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--layers", type=int, default=None, help="default: the workload's")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the decode path needs no "
+              "collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_144_amd as pa
+    import workloads
+    from paged_kv_cache_144_amd.runner import DeviceWorkload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+        return
+
+    w = workloads.make(args.workload)
+    L = args.layers or w.n_layers
+    print(f"[bench] building {args.workload}: {w.num_seqs} seqs, {w.total_q_rows} rows, "
+          f"{w.num_blocks} blocks/layer, {L} layers", file=sys.stderr, flush=True)
+    dw = DeviceWorkload(w, "cuda")
+    pools = [(dw.k_cache, dw.v_cache)]
+    for _ in range(L - 1):
+        pools.append((dw.k_cache.clone(), dw.v_cache.clone()))
+    rows = torch.from_numpy(step_rows(w)).cuda()
+    k_step = dw.k_new.index_select(0, rows).contiguous()
+    v_step = dw.v_new.index_select(0, rows).contiguous()
+    slot_step = dw.slot_mapping.index_select(0, rows).contiguous()
+    out = torch.empty((w.total_q_rows, w.num_q_heads, w.head_dim), dtype=torch.float32,
+                      device="cuda")
+    kv_layer = pa.kv_bytes_read(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim,
+                                w.elem_bytes)
+    qsl = dw.qsl if dw.uses_rows else None
+    common = dict(max_seq_len=dw.max_seq_len, query_start_loc=qsl, window=w.window,
+                  workspace=dw.workspace)
+
+    def step(events=None):
+        pa.decode(dw.q, pools[0][0], pools[0][1], dw.block_tables, dw.seq_lens, float(w.scale),
+                  step="plan", **common)
+        for li, (kc, vc) in enumerate(pools):
+            pa.write_kv(k_step, v_step, slot_step, kc, vc)
+            if events is not None:
+                pa.set_decode_profile_events(*events[li])
+            pa.decode(dw.q, kc, vc, dw.block_tables, dw.seq_lens, float(w.scale), out=out,
+                      step="attend", **common)
+        if events is not None:
+            pa.set_decode_profile_events(None, None)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    # one pair of events per decode launch in the timed region
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(L)] for _ in range(args.steps)]
+    for per in evs:
+        for a, b in per:
+            a.record()
+            b.record()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(evs[k])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    dec_ms = [a.elapsed_time(b) for per in evs for a, b in per]
+    dec_avg_ms = float(np.mean(dec_ms))
+    err_bits = pa.device_error_bits(dw.workspace)
+
+    step_s = total_ms / 1e3 / args.steps
+    value = kv_layer * L / step_s / 1e9
+    tokens_per_s = w.total_q_rows / step_s
+    achieved = kv_layer / (dec_avg_ms / 1e3) / 1e9
+    traffic = measured_traffic(args.workload)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(tokens_per_s, 1),
+        "config": {
+            "workload": DESCRIPTIONS[args.workload],
+            "batch": w.num_seqs,
+            "query_rows": w.total_q_rows,
+            "layers": L,
+            "seq_len_total": int(w.seq_lens.sum()),
+            "kv_bytes_per_layer": int(kv_layer),
+            "seed": w.seed,
+        },
+        "roofline": {
+            "kernel": "decode_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "decode_kernel_avg_us": round(dec_avg_ms * 1e3, 2),
+            "launches_timed": len(dec_ms),
+        },
+        "device_error_bits": err_bits,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        ref, cb = cpu_baseline(w, L, args.cpu_seconds)
+        # the GPU output of the last layer (same values in every layer) on a few decode rows
+        dec = np.nonzero(w.q_rows == 1)[0][:16]
+        if dec.size:
+            got = out.cpu().numpy().astype(np.float64)[w.query_start_loc()[dec]]
+            cb["gpu_max_abs_err_vs_oracle"] = float(np.abs(got - ref.attention(seqs=dec)).max())
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,235 @@
+/*
+ * pa.h - paged KV-cache attention for AMD Instinct MI355X (gfx950): the C ABI.
+ *
+ * The KV cache is one pool of fixed 16-token blocks; each sequence owns a block table that
+ * maps its logical blocks to physical ones, as a page table maps pages ("PagedAttention
+ * deep dive", donmain.dev, section on splitting the KV cache into blocks; the pool is one
+ * region reserved up front and a physical block is an index into it: velog.io "Batching
+ * strategies", section 5, on why continuous batching needs PagedAttention).  This library
+ * writes new tokens' K/V into the slots the tables assign and computes decode / chunk-row
+ * attention by gathering K/V through the tables.  It also exports a host block ledger that
+ * produces the tables and slots.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) are HIP device pointers; (host) are host pointers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
+ *     enqueued on it; no call synchronizes, allocates or frees device memory, and no
+ *     pointer is kept after a call returns.  The caller owns every buffer.
+ *   - Errors are returned as pa_status; nothing is launched when a host-checkable
+ *     precondition fails.  Device-resident values the host cannot see (block ids, lengths)
+ *     are range-checked on the device: an out-of-range value is never dereferenced, it sets
+ *     a bit in the workspace's error word (see pa_decode) and the affected tokens are
+ *     treated as absent.
+ *
+ * Cache layout (the pages fix only "a pool of fixed-size blocks"; this layout is this
+ * library's choice): k_cache and v_cache are each [num_blocks][num_kv_heads][16][head_dim]
+ * in the cache dtype, row-major, so each (block, KV head) tile of 16 x head_dim is one
+ * contiguous run of bytes.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,           /* a required pointer is NULL                              */
+    PA_ERR_SHAPE = -2,          /* inconsistent or negative sizes                          */
+    PA_ERR_DTYPE = -3,          /* unknown dtype, or an unsupported dtype combination      */
+    PA_ERR_UNSUPPORTED = -4,    /* head_dim / group size / block size with no kernel       */
+    PA_ERR_WORKSPACE = -5,      /* workspace NULL, too small or not 256-byte aligned       */
+    PA_ERR_LAUNCH = -6,         /* the HIP runtime reported an error                       */
+    PA_ERR_OUT_OF_BLOCKS = -7,  /* ledger: not enough free blocks (nothing was taken)      */
+    PA_ERR_SHARED_BLOCK = -8,   /* ledger: the append would write into a shared block      */
+    PA_ERR_BAD_SEQ = -9         /* ledger: unknown sequence, or one that must be empty     */
+} pa_status;
+
+/* Describes one layer's KV pool.  block_size must be 16 for the kernels (the pages'
+ * default block size); the host ledger accepts any positive block size. */
+typedef struct pa_cache_desc {
+    int32_t num_blocks;     /* NB: physical blocks in the pool                      */
+    int32_t block_size;     /* tokens per block (16)                                 */
+    int32_t num_kv_heads;   /* Hkv                                                   */
+    int32_t head_dim;       /* d: 64, 128 or 256                                     */
+    pa_dtype dtype;         /* element type of k_cache / v_cache (and of q)          */
+} pa_cache_desc;
+
+/* Supported by the kernels: dtype F32, F16, BF16; head_dim 64, 128, 256; group size
+ * G = num_q_heads / num_kv_heads in {1, 2, 4, 8}; block_size 16. */
+
+/* ------------------------------------------------------------------ slot write
+ * pa_write_kv - scatter each new token's K and V into the slot its block table assigns.
+ * Source: "vLLM and PagedAttention" notes (ghkdgus29.github.io), section on basic
+ * decoding - new tokens' KV entries go after the existing ones in the sequence's logical
+ * block, in the physical block the manager mapped it to.
+ *
+ *   k, v          (device) [num_tokens][num_kv_heads][head_dim], cache dtype.
+ *   slot_mapping  (device) int64 [num_tokens]; slot = physical_block * 16 + offset.
+ *                 A negative slot means "skip this token" (padding, or a token outside a
+ *                 sliding window).  A slot >= num_blocks * 16 is skipped as well.
+ *   k_cache, v_cache (device) the pool, layout above; written in place.
+ *   desc          (host) pool description.
+ * The copy is bit-exact.  Two tokens mapped to the same slot leave one of them (which one
+ * is unspecified).  Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED,
+ * PA_ERR_LAUNCH. */
+pa_status pa_write_kv(const void* k, const void* v, const int64_t* slot_mapping,
+                      int32_t num_tokens, void* k_cache, void* v_cache,
+                      const pa_cache_desc* desc, void* stream);
+
+/* ------------------------------------------------------------------ attention
+ * pa_decode_workspace_size - bytes of device workspace pa_decode needs for this shape on
+ * the current device (it depends on how many wavefronts the device keeps resident).
+ * Returns 0 for unsupported arguments. */
+size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
+                                int32_t total_q_rows, int32_t num_q_heads,
+                                int32_t max_seq_len);
+
+/*
+ * pa_decode - attention of each query row over its sequence's cached K/V, gathered through
+ * the block table.  Sources: "PagedAttention deep dive" (donmain.dev), section on
+ * splitting the KV cache into blocks (the kernel follows the table and gathers the
+ * blocks); velog.io "Batching strategies", section 2.3 (KV reads are per sequence and not
+ * shared by batching: this is a bandwidth-bound read of the cache); sotaaz.com "KV cache
+ * by model", section on layer kinds (a sliding-window layer only sees the most recent W
+ * tokens); duolabs.co.kr "vLLM vs Ollama", section on paging-based KV management (chunked
+ * prefill mixes prompt chunks with decodes in one batch).
+ *
+ * For sequence s with context length L = seq_lens[s] (this step's tokens included; their
+ * K/V must already be written) and n query rows, row r sits at position p = L - n + r and
+ * attends to positions [lo, p], lo = 0, or lo = max(0, p - window + 1) when window > 0.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).  With
+ * x_t = scale * <q, K_t>:  out = sum_t softmax(x)_t V_t.  An empty range gives zeros.
+ *
+ *   out           (device) [total_q_rows][num_q_heads][head_dim] in out_dtype
+ *                 (PA_F32 recommended; F16/BF16 give the fp32 result rounded to nearest
+ *                 even).
+ *   q             (device) [total_q_rows][num_q_heads][head_dim], cache dtype.
+ *   k_cache, v_cache, desc   the pool (device) and its description (host).
+ *   block_tables  (device) int32 [num_seqs][max_blocks_per_seq]; only entries of blocks
+ *                 that hold an attended position are read (others may hold anything).
+ *   seq_lens      (device) int32 [num_seqs].
+ *   query_start_loc (device) int32 [num_seqs + 1] row offsets, or NULL for one row per
+ *                 sequence.  Sequences with one row take the decode kernel; sequences with
+ *                 more rows (chunked prefill, causal within the chunk) take the chunk-row
+ *                 kernel in the same call.
+ *   max_seq_len   host-side upper bound of seq_lens (sequences above it, or above
+ *                 16 * max_blocks_per_seq, are rejected on the device: zero output and an
+ *                 error bit).
+ *   scale         softmax scale (usually 1/sqrt(head_dim)).
+ *   window        <= 0: full attention; > 0: sliding window of that many tokens.
+ *   workspace     (device) at least pa_decode_workspace_size(...) bytes, 256-byte aligned.
+ *                 Its first 4 bytes receive the call's device error bits: 1 = a block id
+ *                 outside [0, num_blocks) was met, 2 = a sequence length or row count was
+ *                 out of range.  Concurrent calls must not share a workspace.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE,
+ * PA_ERR_LAUNCH.
+ */
+/* Tuning knob: the environment variable PA_DECODE_WAVES, when set to a positive number
+ * below the device's resident count, caps the decode wavefront workers (for sweeps and
+ * tests; a workspace sized without it is large enough). */
+pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q,
+                    const void* k_cache, const void* v_cache, const pa_cache_desc* desc,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, const int32_t* query_start_loc,
+                    int32_t num_seqs, int32_t total_q_rows, int32_t max_seq_len,
+                    int32_t num_q_heads, float scale, int32_t window,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_decode_plan + pa_decode_attend = pa_decode, split so that one plan serves every layer
+ * of a step: the plan depends only on block_tables, seq_lens, query_start_loc, the shapes
+ * and the window, which all layers of a step share (the CPU ships one set of tables per
+ * step: velog.io "Batching strategies", section 5, one step's flow).  Both take the same
+ * arguments as pa_decode; pa_decode_attend must be given the values pa_decode_plan was
+ * given on the same workspace (scale, q, caches and out may differ), and the plan stays
+ * valid until the workspace is planned again.  pa_decode_plan ignores out, q and the caches.
+ * Errors as pa_decode. */
+pa_status pa_decode_plan(const pa_cache_desc* desc, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs,
+                         int32_t total_q_rows, int32_t max_seq_len, int32_t num_q_heads,
+                         int32_t window, void* workspace, size_t workspace_bytes,
+                         void* stream);
+pa_status pa_decode_attend(void* out, pa_dtype out_dtype, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const pa_cache_desc* desc, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs,
+                           int32_t total_q_rows, int32_t max_seq_len, int32_t num_q_heads,
+                           float scale, int32_t window, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Profiling hook: when set (non-NULL), every later pa_decode / pa_decode_attend records the
+ * hipEvent_t `before` just before its decode-kernel launch and `after` just after it, on
+ * the call's stream, so a caller can time that kernel alone.  The events are the caller's;
+ * NULL, NULL switches the hook off.  Process-wide, not thread-safe. */
+void pa_set_decode_profile_events(void* before, void* after);
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_string(pa_status s);
+
+/* ------------------------------------------------------------------ host block ledger
+ * A host-only ledger of one pool's blocks (no device memory).  Sources: "PagedAttention
+ * deep dive" (donmain.dev), sections on splitting the KV cache into blocks (a block is
+ * taken only when the sequence's last block is full, from anywhere in the pool) and on
+ * waste falling under 4% (only the last block can be partly empty); "vLLM and
+ * PagedAttention" notes (ghkdgus29.github.io), sections on basic decoding (filled counts,
+ * freeing at the end), parallel sampling (reference counts of shared blocks) and
+ * scheduling (all-or-nothing per sequence).
+ *
+ * Policy where the pages are silent: free blocks leave the pool first-in first-out,
+ * starting from `free_order` (or 0..num_blocks-1); a block whose count drops to zero goes
+ * to the back of the queue, in logical-block order.  A handle is not thread-safe. */
+typedef struct pa_pool pa_pool;
+
+/* free_order (host, nullable): the order in which blocks are first handed out; a
+ * permutation of a subset of [0, num_blocks) (blocks left out are never handed out). */
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                         int32_t free_order_len, pa_pool** out);
+void pa_pool_destroy(pa_pool* p);
+
+/* Keep only the last `window` tokens of `seq` (0 = keep all).  Must precede the first
+ * append.  Later appends release blocks that fall wholly before the window (their table
+ * entries become -1) and report slot -1 for positions that are not kept. */
+pa_status pa_seq_set_window(pa_pool* p, int64_t seq, int32_t window);
+
+/* Append n_tokens to `seq` (created on first use) and write each token's slot
+ * (block * block_size + offset, or -1) to slots_out (host, n_tokens entries, nullable).
+ * All or nothing: PA_ERR_OUT_OF_BLOCKS if the free blocks do not suffice (nothing is
+ * taken), PA_ERR_SHARED_BLOCK if a token would land in a block another sequence also
+ * references (copy-on-write is not provided). */
+pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slots_out);
+
+/* `dst` (new or empty) begins with the first n_tokens of `src`, pointing at the same
+ * physical blocks (each gets one more reference).  A shared system prompt or a forked
+ * sample ("PagedAttention deep dive", section on block sharing). */
+pa_status pa_seq_share_prefix(pa_pool* p, int64_t dst, int64_t src, int32_t n_tokens);
+
+/* Drop `seq`: one reference less on each of its blocks; blocks reaching zero are free. */
+pa_status pa_seq_free(pa_pool* p, int64_t seq);
+
+/* Copy seq's block table (entries -1 for released blocks) into out (host, cap entries);
+ * *n receives its length.  PA_ERR_SHAPE if cap is too small (nothing copied). */
+pa_status pa_seq_block_table(const pa_pool* p, int64_t seq, int32_t* out, int32_t cap,
+                             int32_t* n);
+
+/* Block tables of num_seqs sequences as one row-major [num_seqs][max_blocks] int32 array
+ * (host), ready to upload; entries past a table's end and released entries get `fill`. */
+pa_status pa_pool_block_tables(const pa_pool* p, const int64_t* seqs, int32_t num_seqs,
+                               int32_t max_blocks, int32_t fill, int32_t* out);
+
+int32_t pa_seq_len(const pa_pool* p, int64_t seq);          /* -1 if unknown          */
+int32_t pa_pool_num_free(const pa_pool* p);
+int32_t pa_block_refcount(const pa_pool* p, int32_t block);  /* 0 if free or unknown   */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

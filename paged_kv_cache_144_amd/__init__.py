@@ -1,0 +1,305 @@
+"""Paged KV-cache attention for AMD MI355X (gfx950): thin Python binding over ``libpa.so``.
+
+Every step of the path runs in the HIP library; this module only marshals arguments
+(device pointers from torch tensors, the current HIP stream) and wraps the host block
+ledger.  The library must be built (``python -m paged_kv_cache_144_amd._build``); importing
+works without it, but every call then raises - there is no CPU fallback.
+
+The C ABI is declared in ``include/pa.h``; the names below mirror it:
+  write_kv  -> pa_write_kv        decode -> pa_decode (+ pa_decode_workspace_size)
+  Pool      -> pa_pool_* / pa_seq_*
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
+          -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_LAUNCH",
+          -7: "PA_ERR_OUT_OF_BLOCKS", -8: "PA_ERR_SHARED_BLOCK", -9: "PA_ERR_BAD_SEQ"}
+BLOCK_SIZE = 16
+
+# every symbol include/pa.h declares
+EXPORTS = ("pa_write_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_plan",
+           "pa_decode_attend", "pa_set_decode_profile_events", "pa_status_string",
+           "pa_pool_create", "pa_pool_destroy", "pa_seq_set_window", "pa_seq_append",
+           "pa_seq_share_prefix", "pa_seq_free", "pa_seq_block_table", "pa_pool_block_tables",
+           "pa_seq_len", "pa_pool_num_free", "pa_block_refcount")
+
+
+class PAError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__(f"{what}: {STATUS.get(code, code)}")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load():
+    """Load libpa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m paged_kv_cache_144_amd._build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    D = ctypes.POINTER(CacheDesc)
+    sig = {
+        "pa_write_kv": (i32, [P, P, P, i32, P, P, D, P]),
+        "pa_decode_workspace_size": (ctypes.c_size_t, [D, i32, i32, i32, i32]),
+        "pa_decode": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32, i32, P,
+                            ctypes.c_size_t, P]),
+        "pa_decode_plan": (i32, [D, P, i32, P, P, i32, i32, i32, i32, i32, P, ctypes.c_size_t,
+                                 P]),
+        "pa_decode_attend": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32,
+                                   i32, P, ctypes.c_size_t, P]),
+        "pa_set_decode_profile_events": (None, [P, P]),
+        "pa_status_string": (ctypes.c_char_p, [i32]),
+        "pa_pool_create": (i32, [i32, i32, P, i32, ctypes.POINTER(P)]),
+        "pa_pool_destroy": (None, [P]),
+        "pa_seq_set_window": (i32, [P, i64, i32]),
+        "pa_seq_append": (i32, [P, i64, i32, P]),
+        "pa_seq_share_prefix": (i32, [P, i64, i64, i32]),
+        "pa_seq_free": (i32, [P, i64]),
+        "pa_seq_block_table": (i32, [P, i64, P, i32, ctypes.POINTER(i32)]),
+        "pa_pool_block_tables": (i32, [P, P, i32, i32, i32, P]),
+        "pa_seq_len": (i32, [P, i64]),
+        "pa_pool_num_free": (i32, [P]),
+        "pa_block_refcount": (i32, [P, i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(code, what):
+    if code != 0:
+        raise PAError(code, what)
+
+
+# ------------------------------------------------------------------ torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    m = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def cache_desc(k_cache) -> CacheDesc:
+    nb, hkv, bs, d = k_cache.shape
+    return CacheDesc(nb, bs, hkv, d, _dtype_code(k_cache))
+
+
+def write_kv(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """pa_write_kv: k, v [T][Hkv][d]; slot_mapping int64 [T]; caches [NB][Hkv][16][d]."""
+    torch = _torch()
+    lib = load()
+    if k.shape != v.shape or k.dim() != 3 or k_cache.shape != v_cache.shape:
+        raise ValueError("shape mismatch")
+    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("k, v and the caches must share one dtype")
+    if k.shape[1:] != (k_cache.shape[1], k_cache.shape[3]) or slot_mapping.numel() != k.shape[0]:
+        raise ValueError("k/v rows do not match the cache or the slot count")
+    desc = cache_desc(k_cache)
+    rc = lib.pa_write_kv(_dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                         _dev_ptr(slot_mapping, "slot_mapping", torch.int64), k.shape[0],
+                         _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                         ctypes.byref(desc), _stream(stream))
+    _check(rc, "pa_write_kv")
+
+
+def workspace_size(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len) -> int:
+    desc = cache_desc(k_cache)
+    n = load().pa_decode_workspace_size(ctypes.byref(desc), num_seqs, total_q_rows, num_q_heads,
+                                        max_seq_len)
+    if n == 0:
+        raise PAError(-4, "pa_decode_workspace_size")
+    return int(n)
+
+
+def alloc_workspace(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len):
+    torch = _torch()
+    n = workspace_size(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len)
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(n, dtype=torch.uint8, device=k_cache.device)
+
+
+def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, *, max_seq_len,
+           query_start_loc=None, window=0, out=None, out_dtype=None, workspace=None,
+           stream=None, step="both"):
+    """pa_decode: q [R][Hq][d]; block_tables int32 [B][MB]; seq_lens int32 [B];
+    query_start_loc int32 [B+1] or None (one row per sequence).  Returns out [R][Hq][d].
+
+    step="plan" calls pa_decode_plan only, step="attend" pa_decode_attend only (reusing the
+    plan in `workspace`), step="both" pa_decode."""
+    torch = _torch()
+    lib = load()
+    R, hq, d = q.shape
+    B, mb = block_tables.shape
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens length")
+    if query_start_loc is not None and query_start_loc.numel() != B + 1:
+        raise ValueError("query_start_loc length")
+    if q.dtype != k_cache.dtype:
+        raise TypeError("q must have the cache dtype")
+    if out is None:
+        out = torch.empty((R, hq, d), dtype=out_dtype or torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(k_cache, B, R, hq, max_seq_len)
+    desc = cache_desc(k_cache)
+    bt = _dev_ptr(block_tables, "block_tables", torch.int32)
+    sl = _dev_ptr(seq_lens, "seq_lens", torch.int32)
+    qs = _dev_ptr(query_start_loc, "query_start_loc", torch.int32)
+    ws = _dev_ptr(workspace, "workspace", torch.uint8)
+    st = _stream(stream)
+    if step == "plan":
+        rc = lib.pa_decode_plan(ctypes.byref(desc), bt, mb, sl, qs, B, R, int(max_seq_len), hq,
+                                int(window), ws, workspace.numel(), st)
+        _check(rc, "pa_decode_plan")
+        return out
+    fn = lib.pa_decode if step == "both" else lib.pa_decode_attend
+    rc = fn(_dev_ptr(out, "out"), _dtype_code(out), _dev_ptr(q, "q"),
+            _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), ctypes.byref(desc), bt,
+            mb, sl, qs, B, R, int(max_seq_len), hq, float(scale), int(window), ws,
+            workspace.numel(), st)
+    _check(rc, "pa_decode" if step == "both" else "pa_decode_attend")
+    return out
+
+
+def set_decode_profile_events(before=None, after=None) -> None:
+    """pa_set_decode_profile_events with torch.cuda.Event objects (recorded once already so
+    that their handles exist), or None to switch the hook off."""
+    lib = load()
+    h = (lambda e: None if e is None else ctypes.c_void_p(e.cuda_event))
+    lib.pa_set_decode_profile_events(h(before), h(after))
+
+
+def device_error_bits(workspace) -> int:
+    """Error bits the last pa_decode on this workspace left (synchronizes)."""
+    return int(workspace[:4].cpu().view(_torch().int32)[0])
+
+
+# ------------------------------------------------------------------ host block ledger
+class Pool:
+    """pa_pool: host ledger of one pool's blocks (first-in first-out free queue)."""
+
+    def __init__(self, num_blocks, block_size=BLOCK_SIZE, free_order=None):
+        lib = load()
+        self._lib = lib
+        h = ctypes.c_void_p()
+        fo = None if free_order is None else np.ascontiguousarray(free_order, np.int32)
+        rc = lib.pa_pool_create(num_blocks, block_size,
+                                None if fo is None else fo.ctypes.data_as(ctypes.c_void_p),
+                                0 if fo is None else fo.size, ctypes.byref(h))
+        _check(rc, "pa_pool_create")
+        self._h = h
+        self.block_size = block_size
+        self.num_blocks = num_blocks
+
+    def close(self):
+        if self._h:
+            self._lib.pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover
+            pass
+
+    def set_window(self, seq, window):
+        _check(self._lib.pa_seq_set_window(self._h, seq, window), "pa_seq_set_window")
+
+    def append(self, seq, n) -> np.ndarray:
+        slots = np.empty(max(0, n), np.int64)
+        _check(self._lib.pa_seq_append(self._h, seq, n, slots.ctypes.data_as(ctypes.c_void_p)),
+               "pa_seq_append")
+        return slots
+
+    def share_prefix(self, dst, src, n_tokens):
+        _check(self._lib.pa_seq_share_prefix(self._h, dst, src, n_tokens), "pa_seq_share_prefix")
+
+    def free(self, seq):
+        _check(self._lib.pa_seq_free(self._h, seq), "pa_seq_free")
+
+    def block_table(self, seq) -> list:
+        n = ctypes.c_int32()
+        rc = self._lib.pa_seq_block_table(self._h, seq, None, 0, ctypes.byref(n))
+        if rc not in (0, -2):
+            _check(rc, "pa_seq_block_table")
+        out = np.empty(n.value, np.int32)
+        _check(self._lib.pa_seq_block_table(self._h, seq, out.ctypes.data_as(ctypes.c_void_p),
+                                            n.value, ctypes.byref(n)), "pa_seq_block_table")
+        return out.tolist()
+
+    def block_tables(self, seqs, max_blocks, fill) -> np.ndarray:
+        s = np.ascontiguousarray(seqs, np.int64)
+        out = np.empty((s.size, max_blocks), np.int32)
+        _check(self._lib.pa_pool_block_tables(self._h, s.ctypes.data_as(ctypes.c_void_p), s.size,
+                                              max_blocks, fill,
+                                              out.ctypes.data_as(ctypes.c_void_p)),
+               "pa_pool_block_tables")
+        return out
+
+    def seq_len(self, seq) -> int:
+        return int(self._lib.pa_seq_len(self._h, seq))
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_pool_num_free(self._h))
+
+    def refcount(self, block) -> int:
+        return int(self._lib.pa_block_refcount(self._h, block))
+
+
+# ------------------------------------------------------------------ byte accounting
+def kv_bytes_read(seq_lens, q_rows, window, num_kv_heads, head_dim, elem_bytes) -> int:
+    """Algorithmic KV bytes one attention layer reads: every attended position once, K and V,
+    per KV head (a sliding window caps the positions a row can see)."""
+    total = 0
+    for L, n in zip(np.asarray(seq_lens).tolist(), np.asarray(q_rows).tolist()):
+        first = L - n                       # position of the first query row
+        lo = max(0, first - window + 1) if window > 0 else 0
+        total += max(0, L - lo)
+    return 2 * num_kv_heads * head_dim * elem_bytes * total

@@ -1,0 +1,254 @@
+// The exported C ABI (declared in include/pa.h): argument validation, kernel selection,
+// workspace sizing and launches on the caller's stream.  No device memory is allocated or
+// freed here and no call synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+using pa::DecodeArgs;
+
+bool dtype_ok(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
+int dtype_bytes(int dt) { return dt == PA_F32 ? 4 : 2; }
+
+pa_status check_desc(const pa_cache_desc* d) {
+    if (!d) return PA_ERR_NULL;
+    if (!dtype_ok(d->dtype)) return PA_ERR_DTYPE;
+    if (d->num_blocks <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 || d->block_size <= 0)
+        return PA_ERR_SHAPE;
+    if (d->block_size != pa::kBlock) return PA_ERR_UNSUPPORTED;
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+// Resident decode wavefronts on the current device for one kernel instance.
+int resident_waves(const void* fn) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    auto key = std::make_pair(dev, fn);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0, groups = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&groups, fn, pa::kWavesPerGroup * pa::kWave,
+                                                     0) != hipSuccess)
+        return 0;
+    if (groups < 1) groups = 1;
+    const int waves = cus * groups * pa::kWavesPerGroup;
+    cache[key] = waves;
+    return waves;
+}
+
+struct Plan {
+    const void* fn = nullptr;
+    int group = 0;
+    int max_waves = 0;
+    pa::Layout lay{};
+};
+
+pa_status plan_shape(const pa_cache_desc* desc, int32_t num_seqs, int32_t total_q_rows,
+                     int32_t num_q_heads, Plan& p) {
+    pa_status st = check_desc(desc);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || total_q_rows < 0 || num_q_heads <= 0) return PA_ERR_SHAPE;
+    if (num_q_heads % desc->num_kv_heads) return PA_ERR_SHAPE;
+    p.group = num_q_heads / desc->num_kv_heads;
+    p.fn = pa::decode_kernel_ptr(desc->dtype, desc->head_dim, p.group);
+    if (!p.fn) return PA_ERR_UNSUPPORTED;
+    p.max_waves = resident_waves(p.fn);
+    if (p.max_waves <= 0) return PA_ERR_LAUNCH;
+    // tuning / testing knob: fewer decode wavefronts than the device keeps resident
+    if (const char* e = std::getenv("PA_DECODE_WAVES")) {
+        const int v = std::atoi(e);
+        if (v > 0 && v < p.max_waves) p.max_waves = v;
+    }
+    p.lay = pa::layout(total_q_rows, p.max_waves, p.group, desc->head_dim);
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+    switch (s) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL: return "null pointer";
+        case PA_ERR_SHAPE: return "inconsistent or negative sizes";
+        case PA_ERR_DTYPE: return "unsupported dtype";
+        case PA_ERR_UNSUPPORTED: return "no kernel for this head_dim / group / block size";
+        case PA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+        case PA_ERR_LAUNCH: return "HIP launch error";
+        case PA_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
+        case PA_ERR_SHARED_BLOCK: return "append would write into a shared block";
+        case PA_ERR_BAD_SEQ: return "unknown or non-empty sequence";
+    }
+    return "unknown status";
+}
+
+pa_status pa_write_kv(const void* k, const void* v, const int64_t* slot_mapping,
+                      int32_t num_tokens, void* k_cache, void* v_cache,
+                      const pa_cache_desc* desc, void* stream) {
+    pa_status st = check_desc(desc);
+    if (st != PA_OK) return st;
+    if (num_tokens < 0) return PA_ERR_SHAPE;
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+    hipError_t e = pa::launch_write_kv(k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                                       desc->num_blocks, desc->num_kv_heads, desc->head_dim,
+                                       dtype_bytes(desc->dtype), (hipStream_t)stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
+                                int32_t total_q_rows, int32_t num_q_heads,
+                                int32_t max_seq_len) {
+    Plan p;
+    if (max_seq_len < 0) return 0;
+    if (plan_shape(desc, num_seqs, total_q_rows, num_q_heads, p) != PA_OK) return 0;
+    return p.lay.total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Profiling hook: hipEvents recorded around the decode kernel launch (caller-owned).
+hipEvent_t g_prof_before = nullptr, g_prof_after = nullptr;
+
+pa_status build_args(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                     const void* v_cache, const pa_cache_desc* desc,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                     int32_t total_q_rows, int32_t max_seq_len, int32_t num_q_heads,
+                     float scale, int32_t window, void* workspace, size_t workspace_bytes,
+                     bool need_attend_ptrs, DecodeArgs& a, bool& nothing) {
+    Plan p;
+    nothing = false;
+    pa_status st = plan_shape(desc, num_seqs, total_q_rows, num_q_heads, p);
+    if (st != PA_OK) return st;
+    if (!dtype_ok(out_dtype)) return PA_ERR_DTYPE;
+    if (max_seq_len < 0 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
+    if (!query_start_loc && total_q_rows != num_seqs) return PA_ERR_SHAPE;
+    if (total_q_rows == 0) {
+        nothing = true;
+        return PA_OK;
+    }
+    if (num_seqs == 0) return PA_ERR_SHAPE;   // rows without sequences
+    if (!block_tables || !seq_lens) return PA_ERR_NULL;
+    if (need_attend_ptrs && (!out || !q || !k_cache || !v_cache)) return PA_ERR_NULL;
+    if (max_blocks_per_seq == 0) return PA_ERR_SHAPE;
+    // the linear block space is indexed with 32-bit offsets
+    if ((uint64_t)total_q_rows * (uint64_t)max_blocks_per_seq * (uint64_t)desc->num_kv_heads >=
+        (1ull << 32))
+        return PA_ERR_SHAPE;
+    if (!workspace || ((uintptr_t)workspace & 255u)) return PA_ERR_WORKSPACE;
+    if (workspace_bytes < p.lay.total) return PA_ERR_WORKSPACE;
+
+    a = DecodeArgs{};
+    a.out = out;
+    a.out_dtype = out_dtype;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.query_start_loc = query_start_loc;
+    a.num_blocks = desc->num_blocks;
+    a.num_kv_heads = desc->num_kv_heads;
+    a.head_dim = desc->head_dim;
+    a.num_q_heads = num_q_heads;
+    a.group = p.group;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.total_q_rows = total_q_rows;
+    a.max_seq_len = max_seq_len;
+    a.window = window > 0 ? window : 0;
+    a.scale = scale;
+    a.max_waves = p.max_waves;
+    a.ws = (char*)workspace;
+    a.lay = p.lay;
+    return PA_OK;
+}
+
+pa_status run_attend(const DecodeArgs& a, int dtype, hipStream_t s) {
+    if (g_prof_before && hipEventRecord(g_prof_before, s) != hipSuccess) return PA_ERR_LAUNCH;
+    if (pa::launch_decode(a, dtype, s) != hipSuccess) return PA_ERR_LAUNCH;
+    if (g_prof_after && hipEventRecord(g_prof_after, s) != hipSuccess) return PA_ERR_LAUNCH;
+    if (pa::launch_merge(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_plan(const pa_cache_desc* desc, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs,
+                         int32_t total_q_rows, int32_t max_seq_len, int32_t num_q_heads,
+                         int32_t window, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    DecodeArgs a;
+    bool nothing;
+    pa_status st = build_args(nullptr, PA_F32, nullptr, nullptr, nullptr, desc, block_tables,
+                              max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                              total_q_rows, max_seq_len, num_q_heads, 0.f, window, workspace,
+                              workspace_bytes, false, a, nothing);
+    if (st != PA_OK || nothing) return st;
+    return pa::launch_plan(a, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status pa_decode_attend(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                           const void* v_cache, const pa_cache_desc* desc,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, const int32_t* query_start_loc,
+                           int32_t num_seqs, int32_t total_q_rows, int32_t max_seq_len,
+                           int32_t num_q_heads, float scale, int32_t window, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    DecodeArgs a;
+    bool nothing;
+    pa_status st = build_args(out, out_dtype, q, k_cache, v_cache, desc, block_tables,
+                              max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                              total_q_rows, max_seq_len, num_q_heads, scale, window, workspace,
+                              workspace_bytes, true, a, nothing);
+    if (st != PA_OK || nothing) return st;
+    return run_attend(a, desc->dtype, (hipStream_t)stream);
+}
+
+pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                    const void* v_cache, const pa_cache_desc* desc,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                    int32_t total_q_rows, int32_t max_seq_len, int32_t num_q_heads, float scale,
+                    int32_t window, void* workspace, size_t workspace_bytes, void* stream) {
+    DecodeArgs a;
+    bool nothing;
+    pa_status st = build_args(out, out_dtype, q, k_cache, v_cache, desc, block_tables,
+                              max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                              total_q_rows, max_seq_len, num_q_heads, scale, window, workspace,
+                              workspace_bytes, true, a, nothing);
+    if (st != PA_OK || nothing) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (pa::launch_plan(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+    return run_attend(a, desc->dtype, s);
+}
+
+void pa_set_decode_profile_events(void* before, void* after) {
+    g_prof_before = (hipEvent_t)before;
+    g_prof_after = (hipEvent_t)after;
+}
+
+}  // extern "C"

@@ -1,0 +1,223 @@
+// Host block ledger: which physical block each logical block of each sequence lives in.
+//
+// Sources: "PagedAttention deep dive" (donmain.dev) - blocks are taken one at a time, only
+// when a sequence's last block is full, from anywhere in the pool (section on splitting the
+// KV cache into blocks); only the last block can be partly filled (section on waste under
+// 4%); several tables may point at one block (section on block sharing).
+// "vLLM and PagedAttention" notes (ghkdgus29.github.io) - the manager counts the entries
+// in each block and frees them when the request ends (basic decoding), counts the
+// sequences referencing a block (parallel sampling), and evicts all of a sequence or none
+// of it (scheduling).  A sliding-window layer keeps only its last W tokens (sotaaz.com,
+// section on layer kinds).
+//
+// The CPU side owns this ledger and ships block tables to the GPU each step (velog.io,
+// "Batching strategies", section 5: the scheduler and block manager run on the CPU).
+#include <cstdint>
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pa.h"
+
+namespace {
+
+struct Seq {
+    std::vector<int32_t> blocks;  // logical -> physical; -1 = released / never held
+    int64_t len = 0;              // tokens appended so far
+    int32_t window = 0;           // 0 = keep everything
+};
+
+}  // namespace
+
+struct pa_pool {
+    int32_t num_blocks = 0;
+    int32_t bs = 16;
+    std::deque<int32_t> free_q;        // first-in first-out
+    std::vector<int32_t> ref;          // per physical block
+    std::unordered_map<int64_t, Seq> seqs;
+
+    void release(int32_t b) {
+        if (--ref[b] == 0) free_q.push_back(b);
+    }
+};
+
+extern "C" {
+
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                         int32_t free_order_len, pa_pool** out) {
+    if (!out) return PA_ERR_NULL;
+    *out = nullptr;
+    if (num_blocks <= 0 || block_size <= 0) return PA_ERR_SHAPE;
+    pa_pool* p = new (std::nothrow) pa_pool();
+    if (!p) return PA_ERR_SHAPE;
+    p->num_blocks = num_blocks;
+    p->bs = block_size;
+    p->ref.assign(num_blocks, 0);
+    if (free_order) {
+        if (free_order_len < 0 || free_order_len > num_blocks) {
+            delete p;
+            return PA_ERR_SHAPE;
+        }
+        std::vector<char> seen(num_blocks, 0);
+        for (int32_t i = 0; i < free_order_len; ++i) {
+            int32_t b = free_order[i];
+            if (b < 0 || b >= num_blocks || seen[b]) {
+                delete p;
+                return PA_ERR_SHAPE;
+            }
+            seen[b] = 1;
+            p->free_q.push_back(b);
+        }
+    } else {
+        for (int32_t b = 0; b < num_blocks; ++b) p->free_q.push_back(b);
+    }
+    *out = p;
+    return PA_OK;
+}
+
+void pa_pool_destroy(pa_pool* p) { delete p; }
+
+pa_status pa_seq_set_window(pa_pool* p, int64_t seq, int32_t window) {
+    if (!p) return PA_ERR_NULL;
+    if (window < 0) return PA_ERR_SHAPE;
+    Seq& s = p->seqs[seq];
+    if (s.len != 0) return PA_ERR_BAD_SEQ;
+    s.window = window;
+    return PA_OK;
+}
+
+pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slots_out) {
+    if (!p) return PA_ERR_NULL;
+    if (n_tokens < 0) return PA_ERR_SHAPE;
+    Seq& s = p->seqs[seq];
+    const int64_t bs = p->bs;
+    const int64_t cur = s.len, end = cur + n_tokens;
+    // first position that is still kept after this append
+    const int64_t keep_from = (s.window > 0 && end - s.window > 0) ? end - s.window : 0;
+    const int64_t first_kept_blk = keep_from / bs;
+    const int64_t blocks_after = (end + bs - 1) / bs;
+    const int64_t held = (int64_t)s.blocks.size();
+
+    // a token written into the current, partly filled last block must not hit a shared one
+    if (n_tokens > 0 && cur % bs != 0) {
+        const int64_t last = cur / bs;
+        if (last >= first_kept_blk && s.blocks[last] >= 0 && p->ref[s.blocks[last]] > 1)
+            return PA_ERR_SHARED_BLOCK;
+    }
+    // blocks to open (logical ids held..blocks_after-1 that hold a kept position) versus
+    // blocks available (free now, plus held blocks this append releases for good)
+    int64_t need = 0;
+    for (int64_t i = held; i < blocks_after; ++i)
+        if (i >= first_kept_blk) ++need;
+    int64_t avail = (int64_t)p->free_q.size();
+    const int64_t rel_end = first_kept_blk < held ? first_kept_blk : held;
+    for (int64_t i = 0; i < rel_end; ++i)
+        if (s.blocks[i] >= 0 && p->ref[s.blocks[i]] == 1) ++avail;
+    if (need > avail) return PA_ERR_OUT_OF_BLOCKS;
+
+    for (int64_t i = 0; i < rel_end; ++i) {
+        if (s.blocks[i] >= 0) {
+            p->release(s.blocks[i]);
+            s.blocks[i] = -1;
+        }
+    }
+    for (int64_t i = held; i < blocks_after; ++i) {
+        if (i >= first_kept_blk) {
+            int32_t b = p->free_q.front();
+            p->free_q.pop_front();
+            p->ref[b] = 1;
+            s.blocks.push_back(b);
+        } else {
+            s.blocks.push_back(-1);
+        }
+    }
+    s.len = end;
+    if (slots_out) {
+        for (int64_t pos = cur; pos < end; ++pos) {
+            int64_t slot = -1;
+            if (pos >= keep_from) slot = (int64_t)s.blocks[pos / bs] * bs + pos % bs;
+            slots_out[pos - cur] = slot;
+        }
+    }
+    return PA_OK;
+}
+
+pa_status pa_seq_share_prefix(pa_pool* p, int64_t dst, int64_t src, int32_t n_tokens) {
+    if (!p) return PA_ERR_NULL;
+    if (n_tokens < 0) return PA_ERR_SHAPE;
+    auto it = p->seqs.find(src);
+    if (it == p->seqs.end() || dst == src) return PA_ERR_BAD_SEQ;
+    if (n_tokens > it->second.len) return PA_ERR_SHAPE;
+    auto dit = p->seqs.find(dst);
+    if (dit != p->seqs.end() && (dit->second.len != 0 || !dit->second.blocks.empty()))
+        return PA_ERR_BAD_SEQ;
+    const int64_t nblk = (n_tokens + p->bs - 1) / p->bs;
+    const std::vector<int32_t>& sb = it->second.blocks;
+    for (int64_t i = 0; i < nblk; ++i)
+        if (sb[i] < 0) return PA_ERR_BAD_SEQ;
+    std::vector<int32_t> blocks(sb.begin(), sb.begin() + nblk);
+    for (int32_t b : blocks) ++p->ref[b];
+    Seq& d = p->seqs[dst];
+    d.blocks = std::move(blocks);
+    d.len = n_tokens;
+    return PA_OK;
+}
+
+pa_status pa_seq_free(pa_pool* p, int64_t seq) {
+    if (!p) return PA_ERR_NULL;
+    auto it = p->seqs.find(seq);
+    if (it == p->seqs.end()) return PA_ERR_BAD_SEQ;
+    for (int32_t b : it->second.blocks)
+        if (b >= 0) p->release(b);
+    p->seqs.erase(it);
+    return PA_OK;
+}
+
+pa_status pa_seq_block_table(const pa_pool* p, int64_t seq, int32_t* out, int32_t cap,
+                             int32_t* n) {
+    if (!p || !n) return PA_ERR_NULL;
+    auto it = p->seqs.find(seq);
+    if (it == p->seqs.end()) return PA_ERR_BAD_SEQ;
+    const std::vector<int32_t>& b = it->second.blocks;
+    *n = (int32_t)b.size();
+    if ((int64_t)b.size() > cap) return PA_ERR_SHAPE;
+    if (!out && !b.empty()) return PA_ERR_NULL;
+    for (size_t i = 0; i < b.size(); ++i) out[i] = b[i];
+    return PA_OK;
+}
+
+pa_status pa_pool_block_tables(const pa_pool* p, const int64_t* seqs, int32_t num_seqs,
+                               int32_t max_blocks, int32_t fill, int32_t* out) {
+    if (!p || (!seqs && num_seqs) || (!out && num_seqs && max_blocks)) return PA_ERR_NULL;
+    if (num_seqs < 0 || max_blocks < 0) return PA_ERR_SHAPE;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        auto it = p->seqs.find(seqs[i]);
+        if (it == p->seqs.end()) return PA_ERR_BAD_SEQ;
+        if ((int64_t)it->second.blocks.size() > max_blocks) return PA_ERR_SHAPE;
+    }
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        const std::vector<int32_t>& b = p->seqs.find(seqs[i])->second.blocks;
+        int32_t* row = out + (size_t)i * max_blocks;
+        for (int32_t j = 0; j < max_blocks; ++j) {
+            int32_t v = j < (int32_t)b.size() ? b[j] : -1;
+            row[j] = v < 0 ? fill : v;
+        }
+    }
+    return PA_OK;
+}
+
+int32_t pa_seq_len(const pa_pool* p, int64_t seq) {
+    if (!p) return -1;
+    auto it = p->seqs.find(seq);
+    return it == p->seqs.end() ? -1 : (int32_t)it->second.len;
+}
+
+int32_t pa_pool_num_free(const pa_pool* p) { return p ? (int32_t)p->free_q.size() : 0; }
+
+int32_t pa_block_refcount(const pa_pool* p, int32_t block) {
+    if (!p || block < 0 || block >= p->num_blocks) return 0;
+    return p->ref[block];
+}
+
+}  // extern "C"

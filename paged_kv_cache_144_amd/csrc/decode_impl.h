@@ -1,0 +1,276 @@
+// Paged decode attention kernel (wavefront-64, gfx950).
+//
+// What it computes: for each (query row u, KV head g) pair, the softmax-weighted sum of the
+// V rows of the tokens the row sees, with scores scale * <q, K_t>, for the G query heads
+// g*G .. g*G+G-1 that read KV head g.  K and V are reached through the block table:
+// token t of the row's sequence sits in physical block block_tables[seq][t / 16], offset
+// t % 16 ("PagedAttention deep dive", donmain.dev, section on splitting the KV cache into
+// blocks).  A sliding window drops whole blocks before the window and masks the rest
+// (sotaaz.com, section on layer kinds).  KV reads are not shared between sequences, so
+// this is a streaming read of the cache bounded by HBM bandwidth (velog.io "Batching
+// strategies", section 2.3).
+//
+// How, on CDNA4:
+//   * one wavefront is one worker; it owns an equal share of the linear block space laid
+//     out by the plan kernel and walks the pairs that share covers;
+//   * a (block, KV head) tile is 16 x d elements, contiguous; load i of a lane reads bytes
+//     [1024 i + 16 lane, +16) of the tile, so each load instruction of the wavefront reads
+//     1 KiB of consecutive bytes.  Lane l therefore holds PE consecutive elements of token
+//     (i * TPI + l / LPT), columns (l % LPT) * PE .. +PE;
+//   * each tile is read once for all G query heads of the group;
+//   * the dot product over d is a within-row DPP reduction over LPT lanes;
+//   * the LPT-lane rows of the wavefront (TPI of them) each keep their own running max,
+//     sum and output for the tokens they hold, so the hot loop needs no cross-row traffic;
+//     rows are combined once per segment with the log-sum-exp rule;
+//   * the next block's K and V are loaded before the current block is consumed;
+//   * block ids come from one coalesced load of up to 64 table entries (one per lane),
+//     broadcast with readlane; an id outside the pool sets an error bit and masks the
+//     block instead of being dereferenced;
+//   * masked tokens are removed by selection (score -inf, V zeroed), never by a zero
+//     weight, so NaN in free or unused slots cannot reach the output.
+#pragma once
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+template <int DT, int D, int G>
+struct DecodeShape {
+    static constexpr int EB = Elem<DT>::bytes;
+    static constexpr int PE = Elem<DT>::per16;   // elements per 16-byte lane load
+    static constexpr int LPT = D / PE;           // lanes holding one token row
+    static constexpr int TPI = kWave / LPT;      // tokens per load instruction
+    static constexpr int NLD = kBlock / TPI;     // load instructions per tile
+    static constexpr int TILE = kBlock * D * EB; // bytes of one (block, head) tile
+    static_assert(LPT >= 8 && LPT <= 64 && (LPT & (LPT - 1)) == 0, "row width");
+    static_assert(NLD * 1024 == TILE, "tile covered by whole-wave loads");
+};
+
+template <int PE>
+__device__ __forceinline__ void store_row(const DecodeArgs& a, size_t idx, const float* v) {
+    if (a.out_dtype == PA_F32) {
+        float* o = (float*)a.out + idx;
+#pragma unroll
+        for (int e = 0; e < PE; e += 4) {
+            u32x4 w = {__float_as_uint(v[e]), __float_as_uint(v[e + 1]),
+                       __float_as_uint(v[e + 2]), __float_as_uint(v[e + 3])};
+            st16(o + e, w);
+        }
+    } else {
+        uint32_t w[PE / 2];
+#pragma unroll
+        for (int e = 0; e < PE; e += 2) {
+            uint32_t lo, hi;
+            if (a.out_dtype == PA_F16) {
+                lo = f32_to_f16_bits(v[e]);
+                hi = f32_to_f16_bits(v[e + 1]);
+            } else {
+                lo = f32_to_bf16_bits(v[e]);
+                hi = f32_to_bf16_bits(v[e + 1]);
+            }
+            w[e / 2] = lo | (hi << 16);
+        }
+        uint16_t* o = (uint16_t*)a.out + idx;
+        if constexpr (PE == 8) {
+            u32x4 x = {w[0], w[1], w[2], w[3]};
+            st16(o, x);
+        } else {
+            *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1]);
+        }
+    }
+}
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeArgs a) {
+    using S = DecodeShape<DT, D, G>;
+    constexpr int PE = S::PE, LPT = S::LPT, TPI = S::TPI, NLD = S::NLD;
+    constexpr float kLog2e = 1.4426950408889634f;
+    constexpr float kNegBig = -3.402823466e38f;
+
+    int32_t* hdr = (int32_t*)(a.ws + a.lay.header);
+    const uint32_t* cb = (const uint32_t*)(a.ws + a.lay.cb);
+    const UnitInfo* unit = (const UnitInfo*)(a.ws + a.lay.unit);
+    const uint32_t* wx0 = (const uint32_t*)(a.ws + a.lay.wave_x0);
+    const int32_t* wu = (const int32_t*)(a.ws + a.lay.wave_u);
+    float2* pml = (float2*)(a.ws + a.lay.part_ml);
+    float* pacc = (float*)(a.ws + a.lay.part_acc);
+
+    const int W = hdr[2];
+    const int wave = uniform(blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6));
+    if (wave >= W) return;
+
+    const int lane = lane_id();
+    const int row = lane / LPT;        // which token of each load this lane holds
+    const int col = lane % LPT;        // which PE-element column
+    const float qscale = a.scale * kLog2e;
+    const size_t head_stride = S::TILE;
+    const size_t block_stride = (size_t)a.num_kv_heads * S::TILE;
+    const char* kbase = (const char*)a.k_cache + (size_t)lane * 16;
+    const char* vbase = (const char*)a.v_cache + (size_t)lane * 16;
+
+    uint32_t x = wx0[wave];
+    const uint32_t x_end = wx0[wave + 1];
+    int u = wu[wave];
+    bool first_segment = true;
+
+    while (x < x_end) {
+        while (cb[u + 1] <= x) ++u;                       // skip finished / empty units
+        const UnitInfo ui = unit[u];
+        const uint32_t base = cb[u];
+        const int g = (int)((x - base) / (uint32_t)ui.nb);
+        const uint32_t ps = base + (uint32_t)g * ui.nb, pe = ps + ui.nb;
+        const uint32_t seg_end = x_end < pe ? x_end : pe;
+        const int j0 = ui.b_lo + (int)(x - ps), j1 = ui.b_lo + (int)(seg_end - ps);
+        const int len = ui.len;
+        const int lo_tok = (a.window > 0 && len > a.window) ? len - a.window : 0;
+
+        // this lane's slice of the G query rows, kept packed
+        uint32_t qv[G][4];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            const size_t qi = (((size_t)u * a.num_q_heads + (size_t)g * G + gi) * D + col * PE);
+            const u32x4 t = ld16((const char*)a.q + qi * S::EB);
+            qv[gi][0] = t.x; qv[gi][1] = t.y; qv[gi][2] = t.z; qv[gi][3] = t.w;
+        }
+        float m[G], l[G], acc[G][PE];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            m[gi] = kNegBig;
+            l[gi] = 0.f;
+#pragma unroll
+            for (int e = 0; e < PE; ++e) acc[gi][e] = 0.f;
+        }
+
+        const int32_t* bt = a.block_tables + (size_t)ui.seq * a.max_blocks;
+        const size_t head_off = (size_t)g * head_stride;
+
+        auto block_id = [&](int btv, int idx, bool& valid) {
+            int b = __builtin_amdgcn_readlane(btv, idx);
+            valid = (unsigned)b < (unsigned)a.num_blocks;
+            return valid ? b : 0;
+        };
+        auto load_tile = [&](int b, u32x4* kt, u32x4* vt) {
+            const size_t off = (size_t)b * block_stride + head_off;
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                kt[i] = ld16(kbase + off + i * 1024);
+                vt[i] = ld16(vbase + off + i * 1024);
+            }
+        };
+        auto consume = [&](const u32x4* kt, u32x4* vt, int j, bool valid) {
+            const int t0 = j * kBlock;
+            float sc[G][NLD];
+#pragma unroll
+            for (int i = 0; i < NLD; ++i)
+#pragma unroll
+                for (int gi = 0; gi < G; ++gi) sc[gi][i] = dot16<DT>(qv[gi], kt[i]);
+#pragma unroll
+            for (int i = 0; i < NLD; ++i)
+#pragma unroll
+                for (int gi = 0; gi < G; ++gi) sc[gi][i] = group_sum<LPT>(sc[gi][i]) * qscale;
+            if (!valid || t0 < lo_tok || t0 + kBlock > len) {   // wavefront-uniform
+#pragma unroll
+                for (int i = 0; i < NLD; ++i) {
+                    const int t = t0 + i * TPI + row;
+                    const bool ok = valid && t >= lo_tok && t < len;
+#pragma unroll
+                    for (int gi = 0; gi < G; ++gi) sc[gi][i] = ok ? sc[gi][i] : -INFINITY;
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    vt[i] = ok ? vt[i] : z;
+                }
+            }
+            float p[G][NLD];
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+                float mx = sc[gi][0];
+#pragma unroll
+                for (int i = 1; i < NLD; ++i) mx = fmaxf(mx, sc[gi][i]);
+                const float mn = fmaxf(m[gi], mx);
+                const float alpha = __builtin_amdgcn_exp2f(m[gi] - mn);
+                m[gi] = mn;
+                float sum = 0.f;
+#pragma unroll
+                for (int i = 0; i < NLD; ++i) {
+                    p[gi][i] = __builtin_amdgcn_exp2f(sc[gi][i] - mn);
+                    sum += p[gi][i];
+                }
+                l[gi] = fmaf(l[gi], alpha, sum);
+#pragma unroll
+                for (int e = 0; e < PE; ++e) acc[gi][e] *= alpha;
+            }
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                float vf[PE];
+                widen16<DT>(vt[i], vf);
+#pragma unroll
+                for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+                    for (int e = 0; e < PE; ++e) acc[gi][e] = fmaf(p[gi][i], vf[e], acc[gi][e]);
+            }
+        };
+
+        int bad = 0;
+        for (int c0 = j0; c0 < j1; c0 += kWave) {
+            const int n = (j1 - c0) < kWave ? (j1 - c0) : kWave;
+            const int btv = lane < n ? bt[c0 + lane] : 0;
+            u32x4 kA[NLD], vA[NLD], kB[NLD], vB[NLD];
+            bool okA, okB;
+            load_tile(block_id(btv, 0, okA), kA, vA);
+            for (int jj = 0; jj < n; jj += 2) {
+                // B <- block jj+1 (or jj again at the end: a cache hit, keeps waits simple)
+                load_tile(block_id(btv, jj + 1 < n ? jj + 1 : jj, okB), kB, vB);
+                bad |= !okA;
+                consume(kA, vA, c0 + jj, okA);
+                if (jj + 1 >= n) break;
+                load_tile(block_id(btv, jj + 2 < n ? jj + 2 : jj + 1, okA), kA, vA);
+                bad |= !okB;
+                consume(kB, vB, c0 + jj + 1, okB);
+            }
+        }
+        if (bad && lane == 0) atomicOr(hdr, kErrBlockId);
+
+        // combine the TPI rows of the wavefront (log-sum-exp), then write
+        const bool complete = x == ps && seg_end == pe;
+        const int slot = first_segment ? 0 : 1;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            float M = m[gi];
+#pragma unroll
+            for (int msk = LPT; msk < kWave; msk <<= 1) M = fmaxf(M, __shfl_xor(M, msk));
+            const float f = __builtin_amdgcn_exp2f(m[gi] - M);
+            float lt = l[gi] * f;
+#pragma unroll
+            for (int e = 0; e < PE; ++e) acc[gi][e] *= f;
+#pragma unroll
+            for (int msk = LPT; msk < kWave; msk <<= 1) {
+                lt += __shfl_xor(lt, msk);
+#pragma unroll
+                for (int e = 0; e < PE; ++e) acc[gi][e] += __shfl_xor(acc[gi][e], msk);
+            }
+            if (row == 0) {
+                if (complete) {
+                    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+                    float o[PE];
+#pragma unroll
+                    for (int e = 0; e < PE; ++e) o[e] = acc[gi][e] * inv;
+                    store_row<PE>(a, ((size_t)u * a.num_q_heads + (size_t)g * G + gi) * D + col * PE, o);
+                } else {
+                    const size_t pi = ((size_t)wave * 2 + slot) * G + gi;
+                    if (col == 0) pml[pi] = make_float2(M, lt);
+                    float* dst = pacc + pi * D + col * PE;
+#pragma unroll
+                    for (int e = 0; e < PE; e += 4) {
+                        u32x4 w4 = {__float_as_uint(acc[gi][e]), __float_as_uint(acc[gi][e + 1]),
+                                    __float_as_uint(acc[gi][e + 2]), __float_as_uint(acc[gi][e + 3])};
+                        st16(dst + e, w4);
+                    }
+                }
+            }
+        }
+        x = seg_end;
+        first_segment = false;
+    }
+}
+
+}  // namespace pa

@@ -1,0 +1,131 @@
+// Device helpers for the CDNA4 (gfx950) kernels: 16-byte lane loads, element conversions,
+// wavefront-64 DPP reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+template <int DT>
+struct Elem {
+    static constexpr int bytes = DT == DT_F32 ? 4 : 2;
+    static constexpr int per16 = 16 / bytes;  // elements in one 16-byte lane load
+};
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// ---- element conversion ----------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+    const f16x2 h = __builtin_bit_cast(f16x2, w);
+    return (float)h.x;
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+    const f16x2 h = __builtin_bit_cast(f16x2, w);
+    return (float)h.y;
+}
+
+// Widen the elements of one 16-byte load to fp32 (per16 values).
+template <int DT>
+__device__ __forceinline__ void widen16(u32x4 v, float* f) {
+    if constexpr (DT == DT_F32) {
+        f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+    } else if constexpr (DT == DT_F16) {
+        f[0] = f16_lo(v.x); f[1] = f16_hi(v.x); f[2] = f16_lo(v.y); f[3] = f16_hi(v.y);
+        f[4] = f16_lo(v.z); f[5] = f16_hi(v.z); f[6] = f16_lo(v.w); f[7] = f16_hi(v.w);
+    } else {
+        f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+        f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+    }
+}
+
+// fp32 -> bf16 bits, round to nearest even (quiet NaN kept).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
+    _Float16 h = (_Float16)x;  // v_cvt_f16_f32: round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// Partial dot product of the 16 bytes of q and k held by this lane.
+// For 16-bit types q is kept packed (two elements per dword) and the packed dot2
+// instructions accumulate in fp32; for fp32 it is a chain of FMAs.
+// The vector's components are copied to scalars first: a bit-cast applied directly to a
+// component of an ext_vector value is not safe with this compiler (it read component 0).
+template <int DT>
+__device__ __forceinline__ float dot16(const uint32_t* q, u32x4 k) {
+    const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+    if constexpr (DT == DT_F32) {
+        float s = __uint_as_float(q[0]) * __uint_as_float(kw[0]);
+        s = fmaf(__uint_as_float(q[1]), __uint_as_float(kw[1]), s);
+        s = fmaf(__uint_as_float(q[2]), __uint_as_float(kw[2]), s);
+        s = fmaf(__uint_as_float(q[3]), __uint_as_float(kw[3]), s);
+        return s;
+    } else if constexpr (DT == DT_F16) {
+        float s = __builtin_amdgcn_fdot2(as_f16x2(q[0]), as_f16x2(kw[0]), 0.f, false);
+        s = __builtin_amdgcn_fdot2(as_f16x2(q[1]), as_f16x2(kw[1]), s, false);
+        s = __builtin_amdgcn_fdot2(as_f16x2(q[2]), as_f16x2(kw[2]), s, false);
+        s = __builtin_amdgcn_fdot2(as_f16x2(q[3]), as_f16x2(kw[3]), s, false);
+        return s;
+    } else {
+        float s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[0]), as_bf16x2(kw[0]), 0.f, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[1]), as_bf16x2(kw[1]), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[2]), as_bf16x2(kw[2]), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[3]), as_bf16x2(kw[3]), s, false);
+        return s;
+    }
+}
+
+// ---- cross-lane --------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // reverse within each 8-lane half row
+constexpr int DPP_MIRROR = 0x140;       // reverse within each 16-lane row
+
+// Sum over each aligned group of N lanes (N = 8, 16, 32, 64); every lane gets its
+// group's sum.  Inside a 16-lane row this is DPP only.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    x += dpp<DPP_XOR1>(x);
+    x += dpp<DPP_XOR2>(x);
+    x += dpp<DPP_HALF_MIRROR>(x);
+    if constexpr (N >= 16) x += dpp<DPP_MIRROR>(x);
+    if constexpr (N >= 32)
+        x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // xor 16
+    if constexpr (N >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace pa

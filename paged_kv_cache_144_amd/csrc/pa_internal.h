@@ -1,0 +1,93 @@
+// Internal declarations shared by the host ABI (abi.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pa.h"
+
+namespace pa {
+
+constexpr int kBlock = 16;          // tokens per KV block (the kernels' fixed block size)
+constexpr int kWave = 64;           // CDNA wavefront width
+constexpr int kWavesPerGroup = 4;   // decode workgroup = 4 independent wavefront workers
+constexpr int kMinBlocksPerWave = 8;  // smallest share of KV blocks worth a wavefront
+
+// Error bits written to the first word of the workspace.
+constexpr int kErrBlockId = 1;
+constexpr int kErrSeqLen = 2;
+
+// One decode unit per query row: what the row reads, derived once per call by the plan
+// kernel.  A chunk row r of a sequence with n rows and length L is the decode row of
+// length L - n + r + 1 (causal mask), so every row is a unit of the same kind.
+struct UnitInfo {
+    int32_t b_lo;   // first logical block the row reads
+    int32_t nb;     // number of blocks it reads (0: nothing to read)
+    int32_t len;    // tokens visible to the row (positions < len)
+    int32_t seq;    // block-table row
+};
+
+// Workspace layout (all offsets 256-byte aligned); U = query rows, W = wavefront workers:
+//   header   int32[64]: [0] error bits, [1] total blocks T, [2] active waves,
+//                       [3] rows with nothing to read (their output is zeros)
+//   cb       uint32[U+1]   linear offset of pair (u, kv head 0); pair (u, g) starts at
+//                          cb[u] + g * nb(u) and spans nb(u) blocks
+//   unit     UnitInfo[U]
+//   empty    int32[U]      the rows with nothing to read
+//   wave_x0  uint32[W+1]   first linear block of each wave's share
+//   wave_u   int32[W]      unit holding that block
+//   part_ml  float2[W*2*G]       partial (max, sum) per wave, slot, head of the group
+//   part_acc float[W*2*G*d]      partial unnormalised output
+struct Layout {
+    size_t header, cb, unit, empty, wave_x0, wave_u, part_ml, part_acc, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline Layout layout(int num_rows, int max_waves, int group, int head_dim) {
+    Layout L{};
+    size_t o = 0;
+    L.header = o;   o = align256(o + 64 * sizeof(int32_t));
+    L.cb = o;       o = align256(o + (size_t)(num_rows + 1) * sizeof(uint32_t));
+    L.unit = o;     o = align256(o + (size_t)num_rows * sizeof(UnitInfo));
+    L.empty = o;    o = align256(o + (size_t)num_rows * sizeof(int32_t));
+    L.wave_x0 = o;  o = align256(o + (size_t)(max_waves + 1) * sizeof(uint32_t));
+    L.wave_u = o;   o = align256(o + (size_t)max_waves * sizeof(int32_t));
+    L.part_ml = o;  o = align256(o + (size_t)max_waves * 2 * group * 2 * sizeof(float));
+    L.part_acc = o; o = align256(o + (size_t)max_waves * 2 * group * head_dim * sizeof(float));
+    L.total = o;
+    return L;
+}
+
+// Everything one pa_decode call hands to its kernels.
+struct DecodeArgs {
+    void* out;
+    int out_dtype;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    const int32_t* query_start_loc;   // may be null
+    int32_t num_blocks, num_kv_heads, head_dim, num_q_heads, group;
+    int32_t max_blocks, num_seqs, total_q_rows, max_seq_len, window;
+    float scale;
+    int32_t max_waves;                // decode wavefront workers launched
+    char* ws;
+    Layout lay;
+};
+
+// launchers (each enqueues on `stream`, returns hipSuccess or the launch error)
+hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, int32_t n,
+                           void* kc, void* vc, int32_t nb, int32_t hkv, int32_t d,
+                           int32_t elem_bytes, hipStream_t stream);
+hipError_t launch_plan(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
+
+// The decode kernel instance for (dtype, head_dim, group), or null if none is built.
+const void* decode_kernel_ptr(int dtype, int head_dim, int group);
+
+}  // namespace pa

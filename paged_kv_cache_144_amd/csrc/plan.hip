@@ -1,0 +1,231 @@
+// Plan and merge kernels of pa_decode.
+//
+// Plan (one workgroup): validates lengths and row ranges, turns every query row into a
+// decode unit (a chunk row r of n rows at length L reads like a decode row at length
+// L - n + r + 1), lays all (unit, KV head) pairs end to end in one linear space of KV
+// blocks, and cuts that space into equal shares, one per wavefront worker.  A pair that
+// fits inside one share is finished by that wavefront; a pair cut by share boundaries
+// leaves partial (max, sum, unnormalised output) results that the merge kernel combines
+// with the log-sum-exp rule.  Equal shares keep every worker busy for the same number of
+// blocks whatever the length mix (log-normal lengths differ by three orders of magnitude).
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ void unit_range(int32_t len, int32_t window, int32_t& b_lo,
+                                           int32_t& nb) {
+    // a row at length len sees positions [lo, len); with a window only the last `window`
+    if (len <= 0) {
+        b_lo = 0;
+        nb = 0;
+        return;
+    }
+    const int32_t lo = (window > 0 && len > window) ? len - window : 0;
+    b_lo = lo / kBlock;
+    nb = (len + kBlock - 1) / kBlock - b_lo;
+}
+
+// A sequence is accepted when 0 <= L <= min(max_seq_len, 16 * max_blocks).  Rows that would
+// sit before position 0 (more rows than context) see nothing and give zeros.
+__device__ __forceinline__ bool len_ok(const DecodeArgs& a, int L) {
+    return L >= 0 && L <= a.max_seq_len && L <= a.max_blocks * kBlock;
+}
+
+// one wavefront zeroes one output row (a multiple of 16 bytes)
+__device__ void zero_row(const DecodeArgs& a, int row, int lane) {
+    const int ob = a.out_dtype == PA_F32 ? 4 : 2;
+    const size_t bytes = (size_t)a.num_q_heads * a.head_dim * ob;
+    char* p = (char*)a.out + (size_t)row * bytes;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (size_t o = (size_t)lane * 16; o < bytes; o += kWave * 16) st16(p + o, z);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
+    int32_t* hdr = (int32_t*)(a.ws + a.lay.header);
+    uint32_t* cb = (uint32_t*)(a.ws + a.lay.cb);
+    UnitInfo* unit = (UnitInfo*)(a.ws + a.lay.unit);
+    uint32_t* wx0 = (uint32_t*)(a.ws + a.lay.wave_x0);
+    int32_t* wu = (int32_t*)(a.ws + a.lay.wave_u);
+
+    int32_t* empty = (int32_t*)(a.ws + a.lay.empty);
+
+    __shared__ uint32_t s_blk[kPlanThreads];
+    __shared__ int s_err, s_bad, s_empty;
+    const int tid = threadIdx.x;
+    if (tid == 0) { s_err = 0; s_bad = 0; s_empty = 0; }
+    __syncthreads();
+
+    const int B = a.num_seqs, U = a.total_q_rows;
+    const int per = (B + kPlanThreads - 1) / kPlanThreads;
+    const int s0 = min(B, tid * per), s1 = min(B, s0 + per);
+
+    // pass 1: validate, count blocks
+    uint32_t mine = 0;
+    int err = 0, bad = 0;
+    for (int s = s0; s < s1; ++s) {
+        int r0 = s, r1 = s + 1;
+        if (a.query_start_loc) { r0 = a.query_start_loc[s]; r1 = a.query_start_loc[s + 1]; }
+        if (r0 < 0 || r1 < r0 || r1 > U || (s == 0 && r0 != 0) || (s == B - 1 && r1 != U)) {
+            bad = 1;
+            continue;
+        }
+        const int n = r1 - r0, L = a.seq_lens[s];
+        if (!len_ok(a, L)) {
+            err |= kErrSeqLen;
+            continue;
+        }
+        for (int r = 0; r < n; ++r) {
+            int32_t b_lo, nb;
+            unit_range(L - n + r + 1, a.window, b_lo, nb);
+            mine += (uint32_t)nb * (uint32_t)a.num_kv_heads;   // one pair per KV head
+        }
+    }
+    if (bad) atomicOr(&s_bad, 1);
+    if (err) atomicOr(&s_err, err);
+    s_blk[tid] = mine;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+        const uint32_t add = tid >= off ? s_blk[tid - off] : 0u;
+        __syncthreads();
+        s_blk[tid] += add;
+        __syncthreads();
+    }
+    const uint32_t T = s_blk[kPlanThreads - 1];
+    if (s_bad) {
+        // the row ranges cannot be trusted: no unit, no write
+        if (tid == 0) { hdr[0] = s_err | kErrSeqLen; hdr[1] = 0; hdr[2] = 0; hdr[3] = 0; }
+        return;
+    }
+
+    // pass 2: units and their offsets in the linear block space
+    uint32_t off = s_blk[tid] - mine;
+    for (int s = s0; s < s1; ++s) {
+        int r0 = s, r1 = s + 1;
+        if (a.query_start_loc) { r0 = a.query_start_loc[s]; r1 = a.query_start_loc[s + 1]; }
+        const int n = r1 - r0, L = a.seq_lens[s];
+        const bool ok = len_ok(a, L);
+        for (int r = 0; r < n; ++r) {
+            UnitInfo ui{0, 0, 0, s};
+            if (ok) {
+                ui.len = max(0, L - n + r + 1);
+                unit_range(ui.len, a.window, ui.b_lo, ui.nb);
+            }
+            unit[r0 + r] = ui;
+            cb[r0 + r] = off;
+            off += (uint32_t)ui.nb * (uint32_t)a.num_kv_heads;
+        }
+    }
+    if (tid == 0) cb[U] = T;
+
+    int W = 0;
+    if (T > 0) {
+        W = (int)((T + kMinBlocksPerWave - 1) / kMinBlocksPerWave);
+        W = W < 1 ? 1 : (W > a.max_waves ? a.max_waves : W);
+    }
+    __syncthreads();
+
+    // rows with nothing to read (empty context, or rejected lengths) get zeros later
+    for (int u = tid; u < U; u += kPlanThreads)
+        if (unit[u].nb == 0) empty[atomicAdd(&s_empty, 1)] = u;
+    __syncthreads();
+    if (tid == 0) { hdr[0] = s_err; hdr[1] = (int32_t)T; hdr[2] = W; hdr[3] = s_empty; }
+
+    // each wavefront's share [wx0[w], wx0[w+1]) and the unit holding its first block
+    for (int w = tid; w < W; w += kPlanThreads) {
+        const uint32_t x0 = (uint32_t)(((uint64_t)w * T) / (uint64_t)W);
+        int lo = 0, hi = U - 1;   // largest u with cb[u] <= x0 (it has nb > 0)
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cb[mid] <= x0) lo = mid; else hi = mid - 1;
+        }
+        wx0[w] = x0;
+        wu[w] = lo;
+    }
+    if (tid == 0) wx0[W] = T;
+}
+
+hipError_t launch_plan(const DecodeArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- merge
+// Every wavefront first zeroes its share of the rows with nothing to read, then wavefront
+// w merges if share boundary w cuts a pair for the first time.  Partials are
+// (m_p, l_p, acc_p) with m in log2 units: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,
+// M = max_p m_p (the usual log-sum-exp combination of softmax pieces).
+__device__ __forceinline__ void store_out1(const DecodeArgs& a, size_t idx, float v) {
+    if (a.out_dtype == PA_F32) {
+        ((float*)a.out)[idx] = v;
+    } else if (a.out_dtype == PA_F16) {
+        ((uint16_t*)a.out)[idx] = (uint16_t)f32_to_f16_bits(v);
+    } else {
+        ((uint16_t*)a.out)[idx] = (uint16_t)f32_to_bf16_bits(v);
+    }
+}
+
+__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+    const int32_t* hdr = (const int32_t*)(a.ws + a.lay.header);
+    const uint32_t* cb = (const uint32_t*)(a.ws + a.lay.cb);
+    const UnitInfo* unit = (const UnitInfo*)(a.ws + a.lay.unit);
+    const uint32_t* wx0 = (const uint32_t*)(a.ws + a.lay.wave_x0);
+    const int32_t* wu = (const int32_t*)(a.ws + a.lay.wave_u);
+    const float2* pml = (const float2*)(a.ws + a.lay.part_ml);
+    const float* pacc = (const float*)(a.ws + a.lay.part_acc);
+
+    const int32_t* empty = (const int32_t*)(a.ws + a.lay.empty);
+
+    const int W = hdr[2], n_empty = hdr[3];
+    const int mw = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int lane = lane_id();
+    for (int i = mw; i < n_empty; i += gridDim.x * kWavesPerGroup) zero_row(a, empty[i], lane);
+    const int w = mw + 1;
+    if (w >= W) return;
+    const uint32_t x = wx0[w];
+    const int u = wu[w];
+    const UnitInfo ui = unit[u];
+    const uint32_t base = cb[u];
+    const int g = (int)((x - base) / (uint32_t)ui.nb);
+    const uint32_t ps = base + (uint32_t)g * ui.nb, pe = ps + ui.nb;
+    if (x == ps) return;                 // boundary falls between pairs
+    const uint32_t prev = wx0[w - 1];
+    if (prev > ps) return;               // an earlier boundary already cuts this pair
+    const int first_slot = prev == ps ? 0 : 1;
+    int wend = w;
+    while (wend < W && wx0[wend] < pe) ++wend;
+
+    const int G = a.group, D = a.head_dim;
+    for (int gi = 0; gi < G; ++gi) {
+        float M = -3.402823466e38f;
+        for (int v = w - 1; v < wend; ++v) {
+            const int slot = v == w - 1 ? first_slot : 0;
+            M = fmaxf(M, pml[((size_t)v * 2 + slot) * G + gi].x);
+        }
+        float den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int v = w - 1; v < wend; ++v) {
+            const int slot = v == w - 1 ? first_slot : 0;
+            const size_t pi = ((size_t)v * 2 + slot) * G + gi;
+            const float2 ml = pml[pi];
+            const float f = __builtin_amdgcn_exp2f(ml.x - M);
+            den += f * ml.y;
+            for (int k = 0; k < 4; ++k)
+                if (lane + 64 * k < D) num[k] += f * pacc[pi * D + lane + 64 * k];
+        }
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        const size_t obase = ((size_t)u * a.num_q_heads + (size_t)g * G + gi) * D;
+        for (int k = 0; k < 4; ++k)
+            if (lane + 64 * k < D) store_out1(a, obase + lane + 64 * k, num[k] * inv);
+    }
+}
+
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
+    int groups = (a.max_waves - 1 + kWavesPerGroup - 1) / kWavesPerGroup;
+    if (groups < 1) groups = 1;
+    hipLaunchKernelGGL(merge_kernel, dim3(groups), dim3(kWavesPerGroup * kWave), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,96 @@
+"""Drive a synthetic workload through the library: ledger script -> block tables and slots
+(host ``Pool``), then values -> KV pool (``pa_write_kv``), then ``pa_decode``.
+
+Used by the benchmark, the smoke check and the GPU tests.  Only torch device memory and
+copies happen here; the per-token work is in the HIP kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import Pool, alloc_workspace, decode, write_kv
+
+TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+
+def to_device(a: np.ndarray, dtype: str, device):
+    """Storage array (float32 / float16 / bf16 bits as uint16) -> torch tensor on device."""
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device)
+
+
+def to_storage_np(t, dtype: str) -> np.ndarray:
+    """Device tensor -> storage numpy array (bit pattern preserved)."""
+    import torch
+    t = t.detach().cpu()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class DeviceWorkload:
+    """Device state of one layer of a workload."""
+
+    def __init__(self, w, device="cuda", poison=True, write=True):
+        import torch
+        from workloads import Append, Free, SetWindow, SharePrefix
+
+        self.w = w
+        self.device = device
+        pool = Pool(w.num_blocks, w.block_size, w.free_order)
+        slots_all = np.full(w.k.shape[0], -1, np.int64)
+        for op in w.script:
+            if isinstance(op, Append):
+                s = pool.append(op.seq, op.n)
+                if op.nv:
+                    slots_all[op.off:op.off + op.nv] = s[op.n - op.nv:]
+            elif isinstance(op, SharePrefix):
+                pool.share_prefix(op.dst, op.src, op.n_tokens)
+            elif isinstance(op, Free):
+                pool.free(op.seq)
+            elif isinstance(op, SetWindow):
+                pool.set_window(op.seq, op.window)
+            else:  # pragma: no cover
+                raise TypeError(op)
+        self.pool = pool
+        self.slots = slots_all
+        B = w.num_seqs
+        self.max_blocks = max(1, max(len(pool.block_table(s)) for s in range(B)))
+        self.block_tables_np = pool.block_tables(np.arange(B), self.max_blocks, w.reserved_block)
+        tdt = getattr(torch, TORCH_DTYPES[w.dtype])
+        shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+        fill = float("nan") if poison else 0.0
+        self.k_cache = torch.full(shape, fill, dtype=tdt, device=device)
+        self.v_cache = torch.full(shape, fill, dtype=tdt, device=device)
+        self.block_tables = torch.from_numpy(self.block_tables_np).to(device)
+        self.seq_lens = torch.from_numpy(np.ascontiguousarray(w.seq_lens, np.int32)).to(device)
+        self.qsl = torch.from_numpy(w.query_start_loc()).to(device)
+        self.q = to_device(w.q, w.dtype, device)
+        self.max_seq_len = int(w.seq_lens.max()) if B else 0
+        self.k_new = to_device(w.k, w.dtype, device)
+        self.v_new = to_device(w.v, w.dtype, device)
+        self.slot_mapping = torch.from_numpy(slots_all).to(device)
+        if write:
+            self.write()
+        self.workspace = alloc_workspace(self.k_cache, B, w.total_q_rows, w.num_q_heads,
+                                         self.max_seq_len)
+
+    @property
+    def uses_rows(self) -> bool:
+        return bool((self.w.q_rows != 1).any())
+
+    def write(self, stream=None):
+        write_kv(self.k_new, self.v_new, self.slot_mapping, self.k_cache, self.v_cache, stream)
+
+    def decode(self, out=None, out_dtype=None, k_cache=None, v_cache=None, stream=None, **kw):
+        w = self.w
+        return decode(self.q, self.k_cache if k_cache is None else k_cache,
+                      self.v_cache if v_cache is None else v_cache, self.block_tables,
+                      self.seq_lens, float(w.scale), max_seq_len=self.max_seq_len,
+                      query_start_loc=self.qsl if self.uses_rows else None, window=w.window,
+                      out=out, out_dtype=out_dtype, workspace=self.workspace, stream=stream,
+                      **kw)

@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+  * block tables, slots and the written KV pool: bit-exact;
+  * indexing through pa_decode: needle tests, bit-exact fp32 output;
+  * attention values: per element |diff| <= 2e-3 and ||diff||_2 / ||ref||_2 <= 1e-2 against
+    the fp64 oracle (fp16/bf16/fp32 inputs, fp32 accumulation and output);
+  * edge cases: NaN-poisoned free / tail / out-of-window slots, invalid block ids and
+    lengths (error bits, no fault), empty contexts, wave-count invariance, determinism.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from helpers import logical_rows
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-3, 1e-2
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def pa(torch):
+    import paged_kv_cache_144_amd as pa
+    pa.load()      # raises if the library is missing: no fallback
+    return pa
+
+
+def run(w, torch, **kw):
+    from paged_kv_cache_144_amd.runner import DeviceWorkload
+    return DeviceWorkload(w, "cuda", **kw)
+
+
+def check_close(got, ref, what):
+    got = np.asarray(got, np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    d = np.abs(got - ref)
+    rel = np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30)
+    say(f"{what}: max|d|={d.max():.3e} rel_l2={rel:.3e} max|d|/max|ref|={d.max() / np.abs(ref).max():.3e}")
+    assert d.max() <= ATOL, f"{what}: max abs {d.max()}"
+    assert rel <= RTOL, f"{what}: rel {rel}"
+
+
+SMALL = [
+    ("tiny", {}),
+    ("opt13b", dict(batch=6, lo=64, hi=700)),
+    ("gqa", dict(batch=12, median=300, lo=16, hi=3000)),
+    ("prefix_mixed", dict(batch=10, prefix=64, suffix_hi=80, chunks=2, chunk_rows=40,
+                          chunk_lo=100, chunk_hi=300)),
+    ("swa", dict(batch=5, lo=1500, hi=6000, window=1024)),
+    ("gqa", dict(batch=4, median=200, dtype="f16")),
+    ("opt13b", dict(batch=3, lo=30, hi=300, dtype="bf16")),
+    ("tiny", dict(dtype="bf16", hq=8, hkv=1, d=256)),
+    ("tiny", dict(dtype="f16", hq=4, hkv=2, d=128)),
+    ("tiny", dict(dtype="f16")),
+    ("tiny", dict(d=128)),
+    ("tiny", dict(dtype="bf16")),
+    ("opt13b", dict(batch=6, lo=64, hi=700, dtype="f32")),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
+def test_small_parity(torch, pa, orc, name, kw):
+    say("case", name, kw)
+    w = workloads.make(name, **kw)
+    dw = run(w, torch)
+    ref = orc.Reference(w)
+    # tables and slots from the library's ledger equal the oracle's
+    assert np.array_equal(dw.block_tables_np, ref.block_tables)
+    # the pool written by pa_write_kv equals the oracle's scatter, bit for bit (NaN included)
+    from paged_kv_cache_144_amd.runner import to_storage_np
+    kc = to_storage_np(dw.k_cache, w.dtype)
+    vc = to_storage_np(dw.v_cache, w.dtype)
+    assert np.array_equal(kc.view(np.uint8), ref.k_cache.view(np.uint8))
+    assert np.array_equal(vc.view(np.uint8), ref.v_cache.view(np.uint8))
+    out = dw.decode().cpu().numpy()
+    check_close(out, ref.attention(), f"{name} {kw}")
+    # device error word is clean
+    assert pa.device_error_bits(dw.workspace) == 0
+
+
+def needle_positions(L, rng, window=0, k=6):
+    lo = max(0, L - window) if window > 0 else 0
+    cands = {lo, L - 1, min(L - 1, lo + 15), min(L - 1, lo + 16), min(L - 1, lo + 17)}
+    cands.update(int(x) for x in rng.integers(lo, L, size=k))
+    return sorted(c for c in cands if lo <= c < L)
+
+
+def plant_needles(torch, dw, taus, c=800.0):
+    """Zero K of every visible token, set K[tau] = c e_0 for each sequence, q = e_0."""
+    w = dw.w
+    lr = logical_rows(w)
+    kc = dw.k_cache
+    nb_tok = w.block_size
+    for s, tau in taus.items():
+        slots = []
+        bt = dw.block_tables_np[s]
+        L = int(w.seq_lens[s])
+        lo = max(0, L - w.window) if w.window > 0 else 0
+        pos = np.arange(lo, L)
+        slots = bt[pos // nb_tok].astype(np.int64) * nb_tok + pos % nb_tok
+        sl = torch.from_numpy(slots).cuda()
+        blk, off = sl // nb_tok, sl % nb_tok
+        kc[blk, :, off, :] = 0
+        st = int(bt[tau // nb_tok]) * nb_tok + tau % nb_tok
+        kc[st // nb_tok, :, st % nb_tok, 0] = c
+    dw.q.zero_()
+    dw.q[:, :, 0] = 1.0
+    return lr
+
+
+@pytest.mark.parametrize("name,kw,runs", [
+    ("tiny", {}, None),
+    ("tiny", dict(dtype="bf16", hq=8, hkv=2, d=128), None),
+    ("opt13b", dict(batch=8, lo=64, hi=900), 6),
+    ("gqa", dict(batch=16, median=400, lo=16, hi=5000), 6),
+    ("swa", dict(batch=4, lo=3000, hi=9000, window=1024), 6),
+])
+def test_needle_bit_exact(torch, pa, orc, name, kw, runs):
+    """One token's score far above the rest makes the fp32 output equal that token's V bit
+    for bit: any wrong block id, offset, head or window edge shows up."""
+    say("needle", name, kw)
+    w = workloads.make(name, **kw)
+    dw = run(w, torch)
+    k_saved = dw.k_cache.clone()
+    lr = logical_rows(w)
+    grp = w.num_q_heads // w.num_kv_heads
+    rng = np.random.default_rng(7)
+    B = w.num_seqs
+    per_seq = [needle_positions(int(w.seq_lens[s]), rng, w.window) for s in range(B)]
+    if runs is None:
+        runs = max(int(w.seq_lens.max()), 1)
+        per_seq = [list(range(int(w.seq_lens[s]))) for s in range(B)]
+    for it in range(runs):
+        taus = {s: per_seq[s][it % len(per_seq[s])] for s in range(B)}
+        dw.k_cache.copy_(k_saved)
+        plant_needles(torch, dw, taus)
+        out = dw.decode().cpu().numpy()
+        for s, tau in taus.items():
+            v = orc.widen(w.v[lr[s][tau]], w.dtype).astype(np.float32)
+            for h in range(w.num_q_heads):
+                if not np.array_equal(out[s, h], v[h // grp]):
+                    raise AssertionError(f"needle seq {s} tau {tau} head {h}: "
+                                         f"{out[s, h][:4]} vs {v[h // grp][:4]}")
+    assert pa.device_error_bits(dw.workspace) == 0
+
+
+def test_wave_count_invariance_and_determinism(torch, pa, orc, monkeypatch):
+    """Splitting pairs across more or fewer wavefronts changes only rounding."""
+    w = workloads.make("gqa", batch=24, median=600, lo=16, hi=8000)
+    dw = run(w, torch)
+    ref = orc.Reference(w).attention()
+    base = dw.decode().cpu().numpy()
+    again = dw.decode().cpu().numpy()
+    assert np.array_equal(base, again), "run-to-run difference"
+    for waves in (1, 3, 17, 64, 257):
+        monkeypatch.setenv("PA_DECODE_WAVES", str(waves))
+        say("waves", waves)
+        out = dw.decode().cpu().numpy()
+        check_close(out, ref, f"waves={waves}")
+        assert np.abs(out - base).max() < 1e-5
+    monkeypatch.delenv("PA_DECODE_WAVES")
+
+
+def test_out_dtypes(torch, pa):
+    w = workloads.make("gqa", batch=8, median=300)
+    dw = run(w, torch)
+    f32 = dw.decode()
+    for dt in (torch.float16, torch.bfloat16):
+        o = dw.decode(out_dtype=dt)
+        r = f32.to(dt)
+        diff = (o.view(torch.int16).to(torch.int32) - r.view(torch.int16).to(torch.int32)).abs()
+        assert int(diff.max()) <= 1, dt
+
+
+def test_bad_block_id_and_lengths(torch, pa, orc):
+    """Out-of-range device values are caught on the device: error bits, no fault."""
+    w = workloads.make("tiny")
+    dw = run(w, torch)
+    ref = orc.Reference(w).attention()
+    # a block id past the pool in an attended entry of sequence 2
+    bt = dw.block_tables.clone()
+    dw.block_tables[2, 3] = w.num_blocks + 5
+    out = dw.decode().cpu().numpy()
+    assert pa.device_error_bits(dw.workspace) & 1
+    assert np.isfinite(out).all()
+    for s in (0, 1, 3):
+        check_close(out[s], ref[s], f"untouched seq {s}")
+    dw.block_tables.copy_(bt)
+    dw.block_tables[1, 0] = -3
+    out = dw.decode().cpu().numpy()
+    assert pa.device_error_bits(dw.workspace) & 1 and np.isfinite(out).all()
+    dw.block_tables.copy_(bt)
+    # a length above max_seq_len: that row is zeros, error bit 2, others intact
+    dw.seq_lens[1] = 5000
+    out = dw.decode().cpu().numpy()
+    assert pa.device_error_bits(dw.workspace) & 2
+    assert np.array_equal(out[1], np.zeros_like(out[1]))
+    for s in (0, 2, 3):
+        check_close(out[s], ref[s], f"seq {s}")
+    dw.seq_lens[1] = int(w.seq_lens[1])
+    out = dw.decode().cpu().numpy()
+    assert pa.device_error_bits(dw.workspace) == 0
+    check_close(out, ref, "restored")
+
+
+def test_bad_row_offsets_write_nothing(torch, pa):
+    w = workloads.make("prefix_mixed", batch=3, prefix=16, suffix_hi=20, chunks=1, chunk_rows=5,
+                       chunk_lo=30, chunk_hi=40)
+    dw = run(w, torch)
+    out = torch.full((w.total_q_rows, w.num_q_heads, w.head_dim), 7.0, device="cuda")
+    dw.qsl[2] = 10 ** 6                     # beyond total rows
+    dw.decode(out=out)
+    assert pa.device_error_bits(dw.workspace) & 2
+    assert bool((out == 7.0).all())
+
+
+def test_empty_context_gives_zeros(torch, pa, orc):
+    w = workloads.make("tiny")
+    dw = run(w, torch)
+    dw.seq_lens[0] = 0
+    out = dw.decode().cpu().numpy()
+    assert np.array_equal(out[0], np.zeros_like(out[0]))
+    assert pa.device_error_bits(dw.workspace) == 0
+
+
+def test_write_kv_skips(torch, pa):
+    w = workloads.make("tiny")
+    dw = run(w, torch, write=False)
+    k0 = dw.k_cache.clone()
+    n = 3
+    sm = torch.tensor([-1, w.num_blocks * 16, w.num_blocks * 16 + 999], dtype=torch.int64,
+                      device="cuda")
+    pa.write_kv(dw.k_new[:n], dw.v_new[:n], sm, dw.k_cache, dw.v_cache)
+    torch.cuda.synchronize()
+    assert torch.equal(dw.k_cache.view(torch.int32), k0.view(torch.int32))
+
+
+FULL = ["tiny", "opt13b", "gqa", "prefix_mixed", "swa"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_parity(torch, pa, orc, name):
+    """The five workloads at their full sizes, in the launch configuration the benchmark
+    times.  Decode rows are all checked; chunk rows on a sample (each sampled row is the
+    one-row decode at its causal length, which the oracle pins)."""
+    say("full", name, "generating")
+    w = workloads.make(name)
+    dw = run(w, torch)
+    say("full", name, "oracle ledger + scatter")
+    ref = orc.Reference(w, poison=False)
+    assert np.array_equal(dw.block_tables_np, ref.block_tables)
+    out = dw.decode().cpu().numpy()
+    assert pa.device_error_bits(dw.workspace) == 0
+    say("full", name, "oracle attention")
+    qsl = w.query_start_loc()
+    dec = np.nonzero(w.q_rows == 1)[0]
+    want = ref.attention(seqs=dec)
+    check_close(out[qsl[dec]], want, f"full {name} decode rows")
+    rng = np.random.default_rng(11)
+    for s in np.nonzero(w.q_rows > 1)[0]:
+        n, L = int(w.q_rows[s]), int(w.seq_lens[s])
+        rows = sorted(set([0, n - 1] + rng.integers(0, n, size=14).tolist()))
+        q = w.q[qsl[s] + np.array(rows)]
+        lens = np.array([L - n + r + 1 for r in rows], np.int32)
+        bt = np.repeat(ref.block_tables[s:s + 1], len(rows), axis=0)
+        want = orc.paged_attention(q, ref.k_cache, ref.v_cache, bt, lens, w.scale, w.dtype,
+                                   w.num_q_heads, None, w.window)
+        check_close(out[qsl[s] + np.array(rows)], want, f"full {name} chunk seq {s}")
+
+
+def test_plan_reused_across_layers(torch, pa, orc):
+    """One pa_decode_plan serves several pa_decode_attend calls on different pools and
+    output buffers (a step's layers), including the zero rows of empty contexts."""
+    w = workloads.make("gqa", batch=10, median=300)
+    dw = run(w, torch)
+    ref = orc.Reference(w).attention()
+    dw.seq_lens[3] = 0
+    ref[3] = 0
+    kc2, vc2 = dw.k_cache.clone(), dw.v_cache.clone()
+    kw = dict(max_seq_len=dw.max_seq_len, workspace=dw.workspace)
+    pa.decode(dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.seq_lens, float(w.scale),
+              step="plan", **kw)
+    for kc, vc in [(dw.k_cache, dw.v_cache), (kc2, vc2), (dw.k_cache, dw.v_cache)]:
+        out = torch.full((w.total_q_rows, w.num_q_heads, w.head_dim), 5.0, device="cuda")
+        pa.decode(dw.q, kc, vc, dw.block_tables, dw.seq_lens, float(w.scale), out=out,
+                  step="attend", **kw)
+        check_close(out.cpu().numpy(), ref, "plan reuse")
+    assert pa.device_error_bits(dw.workspace) == 0
