@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention KV-read HBM GB/s (% of peak) + decode tokens/s"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SOURCES = ["decode_impl.h", "pa_device.h", "plan.hip"]
+KERNEL_SOURCES = ["decode_impl.h", "pa_device.h", "pa_internal.h", "plan.hip"]
 
 DESCRIPTIONS = {
     "opt13b": "OPT-13B-shaped paged decode: 64 seqs, 40 q heads = 40 KV heads, d=128, fp16 KV, "
