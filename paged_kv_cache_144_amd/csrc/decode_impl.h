@@ -154,8 +154,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
             const size_t off = (size_t)b * block_stride + head_off;
 #pragma unroll
             for (int i = 0; i < NLD; ++i) {
-                kt[i] = ld16(kbase + off + i * 1024);
-                vt[i] = ld16(vbase + off + i * 1024);
+                kt[i] = ld16_stream(kbase + off + i * 1024);
+                vt[i] = ld16_stream(vbase + off + i * 1024);
             }
         };
         auto consume = [&](const u32x4* kt, u32x4* vt, int j, bool valid) {

@@ -24,6 +24,12 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Streaming load of data read once (KV tiles): marked non-temporal so it does not displace
+// reused lines in the caches.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // ---- element conversion ----------------------------------------------------------
@@ -123,6 +129,17 @@ __device__ __forceinline__ float group_sum(float x) {
     if constexpr (N >= 64) x += __shfl_xor(x, 32);
     return x;
 }
+
+// Reductions over the whole wavefront (every lane gets the result).
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp<DPP_XOR1>(x));
+    x = fmaxf(x, dpp<DPP_XOR2>(x));
+    x = fmaxf(x, dpp<DPP_HALF_MIRROR>(x));
+    x = fmaxf(x, dpp<DPP_MIRROR>(x));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 

@@ -194,26 +194,65 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     const uint32_t prev = wx0[w - 1];
     if (prev > ps) return;               // an earlier boundary already cuts this pair
     const int first_slot = prev == ps ? 0 : 1;
+
+    // contributors: wave w-1 (slot first_slot), then waves w, w+1, ... while their share
+    // starts inside the pair (slot 0).  Found 64 at a time with one load per lane.
     int wend = w;
-    while (wend < W && wx0[wend] < pe) ++wend;
+    for (;;) {
+        const int v = wend + lane;
+        const bool in = v < W && wx0[v] < pe;
+        const uint64_t m = __ballot(in);
+        const int run = m == ~0ull ? 64 : __builtin_ctzll(~m);
+        wend += run;
+        if (run < 64) break;
+    }
+    const int nc = wend - (w - 1);
 
     const int G = a.group, D = a.head_dim;
     for (int gi = 0; gi < G; ++gi) {
+        // weights 2^(m_c - M) of every contributor, held one per lane (64 at a time)
         float M = -3.402823466e38f;
-        for (int v = w - 1; v < wend; ++v) {
-            const int slot = v == w - 1 ? first_slot : 0;
-            M = fmaxf(M, pml[((size_t)v * 2 + slot) * G + gi].x);
+        for (int c0 = 0; c0 < nc; c0 += kWave) {
+            const int c = c0 + lane;
+            if (c < nc) {
+                const int v = w - 1 + c, slot = c == 0 ? first_slot : 0;
+                M = fmaxf(M, pml[((size_t)v * 2 + slot) * G + gi].x);
+            }
         }
+        M = wave_max(M);
         float den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int v = w - 1; v < wend; ++v) {
-            const int slot = v == w - 1 ? first_slot : 0;
-            const size_t pi = ((size_t)v * 2 + slot) * G + gi;
-            const float2 ml = pml[pi];
-            const float f = __builtin_amdgcn_exp2f(ml.x - M);
-            den += f * ml.y;
-            for (int k = 0; k < 4; ++k)
-                if (lane + 64 * k < D) num[k] += f * pacc[pi * D + lane + 64 * k];
+        for (int c0 = 0; c0 < nc; c0 += kWave) {
+            const int c = c0 + lane;
+            float f = 0.f;
+            if (c < nc) {
+                const int v = w - 1 + c, slot = c == 0 ? first_slot : 0;
+                const float2 ml = pml[((size_t)v * 2 + slot) * G + gi];
+                f = __builtin_amdgcn_exp2f(ml.x - M);
+                den += f * ml.y;
+            }
+            const int n = nc - c0 < kWave ? nc - c0 : kWave;
+            // four contributors per round, all loads issued before any use
+            for (int j = 0; j < n; j += 4) {
+                float fj[4], val[4][4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int jj = j + t < n ? j + t : j;        // in range; weight 0 below
+                    fj[t] = j + t < n
+                                ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), jj))
+                                : 0.f;
+                    const int v = w - 1 + c0 + jj, slot = c0 + jj == 0 ? first_slot : 0;
+                    const float* src = pacc + (((size_t)v * 2 + slot) * G + gi) * D;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        val[t][k] = lane + 64 * k < D ? src[lane + 64 * k] : 0.f;
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) num[k] += fj[t] * val[t][k];
+            }
         }
+        den = wave_sum(den);
         const float inv = den > 0.f ? 1.f / den : 0.f;
         const size_t obase = ((size_t)u * a.num_q_heads + (size_t)g * G + gi) * D;
         for (int k = 0; k < 4; ++k)
