@@ -55,11 +55,13 @@ struct Plan {
     const void* fn = nullptr;
     int group = 0;
     int max_waves = 0;
+    int chunk_rows = 0;   // query rows per chunk tile; 0 = chunk rows run as decode rows
+    int max_tiles = 0;
     pa::Layout lay{};
 };
 
 pa_status plan_shape(const pa_cache_desc* desc, int32_t num_seqs, int32_t total_q_rows,
-                     int32_t num_q_heads, Plan& p) {
+                     int32_t num_q_heads, bool one_row_per_seq, Plan& p) {
     pa_status st = check_desc(desc);
     if (st != PA_OK) return st;
     if (num_seqs < 0 || total_q_rows < 0 || num_q_heads <= 0) return PA_ERR_SHAPE;
@@ -74,7 +76,17 @@ pa_status plan_shape(const pa_cache_desc* desc, int32_t num_seqs, int32_t total_
         const int v = std::atoi(e);
         if (v > 0 && v < p.max_waves) p.max_waves = v;
     }
-    p.lay = pa::layout(total_q_rows, p.max_waves, p.group, desc->head_dim);
+    // chunk rows (sequences with several query rows) take the MFMA kernel when one exists
+    // for this shape; PA_CHUNK_KERNEL=0 sends them through the decode kernel instead
+    const char* ck = std::getenv("PA_CHUNK_KERNEL");
+    const bool chunk_off = ck && ck[0] == '0';
+    if (!one_row_per_seq && !chunk_off &&
+        pa::chunk_kernel_ptr(desc->dtype, desc->head_dim, p.group)) {
+        p.chunk_rows = pa::chunk_tile_rows(p.group);
+        // sum over sequences of ceil(n_s / QT) <= rows / QT + sequences
+        p.max_tiles = total_q_rows / p.chunk_rows + num_seqs + 1;
+    }
+    p.lay = pa::layout(total_q_rows, p.max_waves, p.max_tiles, p.group, desc->head_dim);
     return PA_OK;
 }
 
@@ -117,7 +129,8 @@ size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
                                 int32_t max_seq_len) {
     Plan p;
     if (max_seq_len < 0) return 0;
-    if (plan_shape(desc, num_seqs, total_q_rows, num_q_heads, p) != PA_OK) return 0;
+    // sized for query_start_loc != NULL (the larger case)
+    if (plan_shape(desc, num_seqs, total_q_rows, num_q_heads, false, p) != PA_OK) return 0;
     return p.lay.total;
 }
 
@@ -137,7 +150,7 @@ pa_status build_args(void* out, pa_dtype out_dtype, const void* q, const void* k
                      bool need_attend_ptrs, DecodeArgs& a, bool& nothing) {
     Plan p;
     nothing = false;
-    pa_status st = plan_shape(desc, num_seqs, total_q_rows, num_q_heads, p);
+    pa_status st = plan_shape(desc, num_seqs, total_q_rows, num_q_heads, !query_start_loc, p);
     if (st != PA_OK) return st;
     if (!dtype_ok(out_dtype)) return PA_ERR_DTYPE;
     if (max_seq_len < 0 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
@@ -178,6 +191,8 @@ pa_status build_args(void* out, pa_dtype out_dtype, const void* q, const void* k
     a.window = window > 0 ? window : 0;
     a.scale = scale;
     a.max_waves = p.max_waves;
+    a.chunk_rows = p.chunk_rows;
+    a.max_tiles = p.max_tiles;
     a.ws = (char*)workspace;
     a.lay = p.lay;
     return PA_OK;
@@ -188,6 +203,7 @@ pa_status run_attend(const DecodeArgs& a, int dtype, hipStream_t s) {
     if (pa::launch_decode(a, dtype, s) != hipSuccess) return PA_ERR_LAUNCH;
     if (g_prof_after && hipEventRecord(g_prof_after, s) != hipSuccess) return PA_ERR_LAUNCH;
     if (pa::launch_merge(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+    if (pa::launch_chunk(a, dtype, s) != hipSuccess) return PA_ERR_LAUNCH;
     return PA_OK;
 }
 

@@ -23,7 +23,7 @@ constexpr int kErrSeqLen = 2;
 // kernel.  A chunk row r of a sequence with n rows and length L is the decode row of
 // length L - n + r + 1 (causal mask), so every row is a unit of the same kind.
 struct UnitInfo {
-    int32_t b_lo;   // first logical block the row reads
+    int32_t b_lo;   // first logical block the row reads (-1: row done by the chunk kernel)
     int32_t nb;     // number of blocks it reads (0: nothing to read)
     int32_t len;    // tokens visible to the row (positions < len)
     int32_t seq;    // block-table row
@@ -31,22 +31,24 @@ struct UnitInfo {
 
 // Workspace layout (all offsets 256-byte aligned); U = query rows, W = wavefront workers:
 //   header   int32[64]: [0] error bits, [1] total blocks T, [2] active waves,
-//                       [3] rows with nothing to read (their output is zeros)
+//                       [3] rows with nothing to read (their output is zeros),
+//                       [4] chunk-row tiles
 //   cb       uint32[U+1]   linear offset of pair (u, kv head 0); pair (u, g) starts at
 //                          cb[u] + g * nb(u) and spans nb(u) blocks
 //   unit     UnitInfo[U]
 //   empty    int32[U]      the rows with nothing to read
 //   wave_x0  uint32[W+1]   first linear block of each wave's share
 //   wave_u   int32[W]      unit holding that block
+//   tiles    int2[Tmax]    chunk-row tiles (sequence, first row) for the MFMA kernel
 //   part_ml  float2[W*2*G]       partial (max, sum) per wave, slot, head of the group
 //   part_acc float[W*2*G*d]      partial unnormalised output
 struct Layout {
-    size_t header, cb, unit, empty, wave_x0, wave_u, part_ml, part_acc, total;
+    size_t header, cb, unit, empty, wave_x0, wave_u, tiles, part_ml, part_acc, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline Layout layout(int num_rows, int max_waves, int group, int head_dim) {
+inline Layout layout(int num_rows, int max_waves, int max_tiles, int group, int head_dim) {
     Layout L{};
     size_t o = 0;
     L.header = o;   o = align256(o + 64 * sizeof(int32_t));
@@ -55,6 +57,7 @@ inline Layout layout(int num_rows, int max_waves, int group, int head_dim) {
     L.empty = o;    o = align256(o + (size_t)num_rows * sizeof(int32_t));
     L.wave_x0 = o;  o = align256(o + (size_t)(max_waves + 1) * sizeof(uint32_t));
     L.wave_u = o;   o = align256(o + (size_t)max_waves * sizeof(int32_t));
+    L.tiles = o;    o = align256(o + (size_t)max_tiles * 2 * sizeof(int32_t));
     L.part_ml = o;  o = align256(o + (size_t)max_waves * 2 * group * 2 * sizeof(float));
     L.part_acc = o; o = align256(o + (size_t)max_waves * 2 * group * head_dim * sizeof(float));
     L.total = o;
@@ -75,6 +78,8 @@ struct DecodeArgs {
     int32_t max_blocks, num_seqs, total_q_rows, max_seq_len, window;
     float scale;
     int32_t max_waves;                // decode wavefront workers launched
+    int32_t chunk_rows;               // query rows per chunk tile (0: chunk rows decode)
+    int32_t max_tiles;                // chunk tiles the work list holds
     char* ws;
     Layout lay;
 };
@@ -86,8 +91,13 @@ hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, i
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream);
 
 // The decode kernel instance for (dtype, head_dim, group), or null if none is built.
 const void* decode_kernel_ptr(int dtype, int head_dim, int group);
+// The chunk-row MFMA kernel instance, or null (then chunk rows run as decode rows).
+const void* chunk_kernel_ptr(int dtype, int head_dim, int group);
+// Query rows one chunk tile covers: 4 wavefronts x 32 (row, head) pairs / group.
+inline int chunk_tile_rows(int group) { return kWavesPerGroup * 32 / group; }
 
 }  // namespace pa

@@ -43,16 +43,30 @@ __device__ void zero_row(const DecodeArgs& a, int row, int lane) {
     for (size_t o = (size_t)lane * 16; o < bytes; o += kWave * 16) st16(p + o, z);
 }
 
+// Inclusive scan of one value per thread over the workgroup (Hillis-Steele in LDS).
+__device__ uint32_t block_scan(uint32_t* buf, uint32_t v) {
+    const int tid = threadIdx.x;
+    buf[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+        const uint32_t add = tid >= off ? buf[tid - off] : 0u;
+        __syncthreads();
+        buf[tid] += add;
+        __syncthreads();
+    }
+    return buf[tid];
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     int32_t* hdr = (int32_t*)(a.ws + a.lay.header);
     uint32_t* cb = (uint32_t*)(a.ws + a.lay.cb);
     UnitInfo* unit = (UnitInfo*)(a.ws + a.lay.unit);
     uint32_t* wx0 = (uint32_t*)(a.ws + a.lay.wave_x0);
     int32_t* wu = (int32_t*)(a.ws + a.lay.wave_u);
-
     int32_t* empty = (int32_t*)(a.ws + a.lay.empty);
+    int2* tiles = (int2*)(a.ws + a.lay.tiles);
 
-    __shared__ uint32_t s_blk[kPlanThreads];
+    __shared__ uint32_t s_blk[kPlanThreads], s_til[kPlanThreads];
     __shared__ int s_err, s_bad, s_empty;
     const int tid = threadIdx.x;
     if (tid == 0) { s_err = 0; s_bad = 0; s_empty = 0; }
@@ -61,9 +75,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     const int B = a.num_seqs, U = a.total_q_rows;
     const int per = (B + kPlanThreads - 1) / kPlanThreads;
     const int s0 = min(B, tid * per), s1 = min(B, s0 + per);
+    const int QT = a.chunk_rows;
 
-    // pass 1: validate, count blocks
-    uint32_t mine = 0;
+    // pass 1: validate; count decode blocks and chunk tiles
+    uint32_t my_blk = 0, my_til = 0;
     int err = 0, bad = 0;
     for (int s = s0; s < s1; ++s) {
         int r0 = s, r1 = s + 1;
@@ -77,39 +92,44 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
             err |= kErrSeqLen;
             continue;
         }
+        if (QT > 0 && n >= 2) {          // a chunk: rows go to the MFMA kernel
+            my_til += (uint32_t)((n + QT - 1) / QT);
+            continue;
+        }
         for (int r = 0; r < n; ++r) {
             int32_t b_lo, nb;
             unit_range(L - n + r + 1, a.window, b_lo, nb);
-            mine += (uint32_t)nb * (uint32_t)a.num_kv_heads;   // one pair per KV head
+            my_blk += (uint32_t)nb * (uint32_t)a.num_kv_heads;   // one pair per KV head
         }
     }
     if (bad) atomicOr(&s_bad, 1);
     if (err) atomicOr(&s_err, err);
-    s_blk[tid] = mine;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        const uint32_t add = tid >= off ? s_blk[tid - off] : 0u;
-        __syncthreads();
-        s_blk[tid] += add;
-        __syncthreads();
-    }
+    const uint32_t blk_incl = block_scan(s_blk, my_blk);
+    const uint32_t til_incl = block_scan(s_til, my_til);
     const uint32_t T = s_blk[kPlanThreads - 1];
-    if (s_bad) {
-        // the row ranges cannot be trusted: no unit, no write
-        if (tid == 0) { hdr[0] = s_err | kErrSeqLen; hdr[1] = 0; hdr[2] = 0; hdr[3] = 0; }
+    const uint32_t NT = s_til[kPlanThreads - 1];
+    if (s_bad || NT > (uint32_t)a.max_tiles) {
+        // row ranges cannot be trusted (or would overflow the tile list): no unit, no write
+        if (tid == 0) {
+            hdr[0] = s_err | kErrSeqLen;
+            hdr[1] = 0; hdr[2] = 0; hdr[3] = 0; hdr[4] = 0;
+        }
         return;
     }
 
-    // pass 2: units and their offsets in the linear block space
-    uint32_t off = s_blk[tid] - mine;
+    // pass 2: units, their offsets in the linear block space, chunk tiles
+    uint32_t off = blk_incl - my_blk, toff = til_incl - my_til;
     for (int s = s0; s < s1; ++s) {
         int r0 = s, r1 = s + 1;
         if (a.query_start_loc) { r0 = a.query_start_loc[s]; r1 = a.query_start_loc[s + 1]; }
         const int n = r1 - r0, L = a.seq_lens[s];
         const bool ok = len_ok(a, L);
+        const bool chunk = ok && QT > 0 && n >= 2;
         for (int r = 0; r < n; ++r) {
             UnitInfo ui{0, 0, 0, s};
-            if (ok) {
+            if (chunk) {
+                ui.b_lo = -1;
+            } else if (ok) {
                 ui.len = max(0, L - n + r + 1);
                 unit_range(ui.len, a.window, ui.b_lo, ui.nb);
             }
@@ -117,6 +137,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
             cb[r0 + r] = off;
             off += (uint32_t)ui.nb * (uint32_t)a.num_kv_heads;
         }
+        if (chunk)
+            for (int q0 = 0; q0 < n; q0 += QT) tiles[toff++] = make_int2(s, q0);
     }
     if (tid == 0) cb[U] = T;
 
@@ -129,9 +151,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
 
     // rows with nothing to read (empty context, or rejected lengths) get zeros later
     for (int u = tid; u < U; u += kPlanThreads)
-        if (unit[u].nb == 0) empty[atomicAdd(&s_empty, 1)] = u;
+        if (unit[u].nb == 0 && unit[u].b_lo >= 0) empty[atomicAdd(&s_empty, 1)] = u;
     __syncthreads();
-    if (tid == 0) { hdr[0] = s_err; hdr[1] = (int32_t)T; hdr[2] = W; hdr[3] = s_empty; }
+    if (tid == 0) {
+        hdr[0] = s_err; hdr[1] = (int32_t)T; hdr[2] = W; hdr[3] = s_empty; hdr[4] = (int32_t)NT;
+    }
 
     // each wavefront's share [wx0[w], wx0[w+1]) and the unit holding its first block
     for (int w = tid; w < W; w += kPlanThreads) {

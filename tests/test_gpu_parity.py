@@ -101,8 +101,10 @@ def needle_positions(L, rng, window=0, k=6):
     return sorted(c for c in cands if lo <= c < L)
 
 
-def plant_needles(torch, dw, taus, c=800.0):
-    """Zero K of every visible token, set K[tau] = c e_0 for each sequence, q = e_0."""
+def plant_needles(torch, dw, taus, c=2048.0):
+    """Zero K of every visible token, set K[tau] = c e_0 for each sequence, q = e_0.
+    c * scale >= 110 for head_dim <= 256, so every other token's weight exp(-c * scale)
+    underflows to exactly 0 in fp32 and the output is V[tau] bit for bit."""
     w = dw.w
     lr = logical_rows(w)
     kc = dw.k_cache
@@ -303,3 +305,78 @@ def test_plan_reused_across_layers(torch, pa, orc):
                   step="attend", **kw)
         check_close(out.cpu().numpy(), ref, "plan reuse")
     assert pa.device_error_bits(dw.workspace) == 0
+
+
+CHUNK_CASES = [
+    dict(lens=[300, 64, 100, 40], rows=[37, 1, 100, 2], hq=8, hkv=2, d=128, dtype="bf16"),
+    dict(lens=[513, 90, 33], rows=[130, 1, 33], hq=4, hkv=4, d=128, dtype="f16"),
+    dict(lens=[200, 150], rows=[17, 40], hq=16, hkv=2, d=64, dtype="bf16"),
+    dict(lens=[180, 77, 20], rows=[50, 3, 30], hq=8, hkv=4, d=256, dtype="f16"),
+    dict(lens=[700, 400], rows=[64, 96], hq=8, hkv=2, d=128, dtype="bf16", window=128),
+    dict(lens=[64, 1, 40], rows=[64, 1, 5], hq=2, hkv=1, d=64, dtype="f16"),
+]
+
+
+@pytest.mark.parametrize("kw", CHUNK_CASES, ids=[f"chunk{i}" for i in range(len(CHUNK_CASES))])
+def test_chunk_rows_parity(torch, pa, orc, monkeypatch, kw):
+    """Chunk rows on the MFMA kernel: against the fp64 oracle, and against the same rows
+    run through the decode kernel (PA_CHUNK_KERNEL=0).  Covers G = 1, 2, 4, 8, d = 64,
+    128, 256, f16 and bf16, partial tiles, windows, a chunk as long as its context, and
+    more rows than context (rows before position 0 are zeros)."""
+    say("chunk case", kw)
+    w = workloads.make("rows", **kw)
+    dw = run(w, torch)
+    ref = orc.Reference(w).attention()
+    out = dw.decode().cpu().numpy()
+    assert pa.device_error_bits(dw.workspace) == 0
+    check_close(out, ref, f"chunk kernel {kw}")
+    monkeypatch.setenv("PA_CHUNK_KERNEL", "0")
+    alt = dw.decode().cpu().numpy()
+    monkeypatch.delenv("PA_CHUNK_KERNEL")
+    check_close(alt, ref, "decode path")
+    assert np.abs(out - alt).max() < 2e-3
+
+
+def test_chunk_rows_before_position_zero(torch, pa):
+    w = workloads.make("rows", lens=[5], rows=[9], hq=4, hkv=2, d=64, dtype="bf16")
+    dw = run(w, torch)
+    out = dw.decode().cpu().numpy()
+    assert np.array_equal(out[:4], np.zeros_like(out[:4]))
+    assert np.isfinite(out).all() and np.abs(out[4:]).max() > 0
+
+
+@pytest.mark.parametrize("kw", [CHUNK_CASES[0], CHUNK_CASES[3], CHUNK_CASES[4]],
+                         ids=["bf16-g4", "f16-d256", "bf16-window"])
+def test_chunk_rows_needle(torch, pa, orc, kw):
+    """A needle at position tau: every chunk row that sees tau returns V_tau bit for bit."""
+    w = workloads.make("rows", **kw)
+    dw = run(w, torch)
+    k_saved = dw.k_cache.clone()
+    lr = logical_rows(w)
+    grp = w.num_q_heads // w.num_kv_heads
+    qsl = w.query_start_loc()
+    rng = np.random.default_rng(3)
+    for _ in range(4):
+        taus = {s: int(rng.integers(max(0, int(w.seq_lens[s]) - int(w.q_rows[s]) - 5),
+                                    int(w.seq_lens[s])))
+                for s in range(w.num_seqs)}
+        dw.k_cache.copy_(k_saved)
+        plant_needles(torch, dw, taus)
+        out = dw.decode().cpu().numpy()
+        bad = []
+        for s, tau in taus.items():
+            n, L = int(w.q_rows[s]), int(w.seq_lens[s])
+            v = orc.widen(w.v[lr[s][tau]], w.dtype).astype(np.float32)
+            for r in range(n):
+                p = L - n + r
+                if p < tau or (w.window > 0 and tau <= p - w.window):
+                    continue
+                for h in range(w.num_q_heads):
+                    got = out[qsl[s] + r, h]
+                    if not np.array_equal(got, v[h // grp]):
+                        bad.append((s, tau, r, p, h, float(np.abs(got - v[h // grp]).max()),
+                                    got[:3].tolist(), v[h // grp][:3].tolist()))
+        for b in bad[:12]:
+            say("needle mismatch seq %d tau %d row %d pos %d head %d maxdiff %.3g got %s want %s"
+                % b)
+        assert not bad, f"{len(bad)} mismatches"

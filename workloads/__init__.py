@@ -340,4 +340,28 @@ def make(name: str, seed: int | None = None, **over) -> Workload:
         return Workload("swa", seed, dt, 8, 4, 256, bs, nb, lens, np.ones(B, np.int32), W,
                         np.float32(1.0 / math.sqrt(256)), 29, free_order, script, k, v, q)
 
+    if name == "rows":
+        # test-sized mixed batch with free shapes: sequence s has lens[s] context tokens and
+        # rows[s] query rows (1 = decode, more = a chunk of the last rows[s] positions)
+        seed = 6 if seed is None else seed
+        rng = np.random.default_rng(np.random.SeedSequence(entropy=seed, spawn_key=(0,)))
+        bs = 16
+        lens = np.asarray(over["lens"], np.int32)
+        rows = np.asarray(over["rows"], np.int32)
+        hq, hkv, d = over.get("hq", 8), over.get("hkv", 2), over.get("d", 128)
+        dt = over.get("dtype", "bf16")
+        need = int(sum(-(-int(L) // bs) for L in lens))
+        nb = _pool_size(need)
+        free_order = rng.permutation(nb - 1).astype(np.int32)
+        script, off = [], 0
+        for s in range(lens.size):
+            n = int(lens[s])
+            if n:
+                script.append(Append(s, n, n, off))
+                off += n
+        k, v = _values(seed, off, hkv, d, dt)
+        q = _queries(seed, int(rows.sum()), hq, d, dt)
+        return Workload("rows", seed, dt, hq, hkv, d, bs, nb, lens, rows, over.get("window", 0),
+                        np.float32(1.0 / math.sqrt(d)), 1, free_order, script, k, v, q)
+
     raise ValueError(f"unknown workload {name!r}")
