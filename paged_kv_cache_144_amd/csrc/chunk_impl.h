@@ -11,18 +11,24 @@
 //
 // Mapping.  One workgroup = (chunk tile of QT rows, KV head g); its 4 wavefronts each own 32
 // "M-rows" (query row, query head of the group), QT = 4 * 32 / G.  The context is walked in
-// steps of 32 tokens (two blocks).  Each step, the workgroup stages the steps' K and V rows
-// in LDS (16-byte coalesced loads; tokens past the sequence, before the window or in a
-// block with an invalid id are staged as zeros, so no NaN reaches a product), then every
-// wavefront computes
+// steps of 32 tokens (two blocks).  Each step, the workgroup stages the step's K and V in
+// LDS (16-byte coalesced loads; tokens past the sequence, before the window or in a block
+// with an invalid id are staged as zeros, so no NaN reaches a product): K row-major, V with
+// the two tokens of each even/odd pair interleaved per column, so that one 4-byte LDS read
+// is two consecutive tokens of one column.  Then every wavefront computes
 //     S^T[32 tokens][32 M-rows] = K . Q^T            (D/16 MFMAs, K operand from LDS)
-// applies the causal / window mask by selection, runs the online softmax per M-row (each
-// lane owns one M-row column: a running max and sum, partner lane l^32 holds the rest), and
+// applies the causal / window mask by selection (only on steps that straddle a row's edge),
+// runs the online softmax per M-row (each lane owns one M-row column; partner lane l^32
+// holds the other half of the step's tokens), and
 //     O^T[d][M-row] += V^T . P^T                     (4 * D/32 MFMAs: P = hi + lo)
 // where P^T comes straight from the S^T accumulator registers in the MFMA B-operand order
-// and V^T is gathered from LDS in the matching token order.  The next step's global loads
-// are in flight while the current step computes (LDS double buffer, one barrier per step).
+// and the V^T operand is four 4-byte LDS reads in the matching token order.  The running
+// max is raised only when a row's new maximum exceeds it by more than 2^8 (weights stay
+// <= 256), so the accumulators are rescaled on few steps.  The next step's global loads are
+// in flight while the current step computes (LDS double buffer, one barrier per step).
 #pragma once
+
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -43,15 +49,25 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> two packed 16-bit values (one v_cvt_pk_{bf16,f16}_f32, round to
+// nearest even).
 template <int DT>
-__device__ __forceinline__ uint32_t to16(float x) {
-    if constexpr (DT == DT_BF16) return f32_to_bf16_bits(x);
-    else return f32_to_f16_bits(x);
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+    const f32x2 v = {a, b};
+    if constexpr (DT == DT_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 template <int DT>
-__device__ __forceinline__ float from16(uint32_t b) {
-    if constexpr (DT == DT_BF16) return __uint_as_float(b << 16);
-    else return f16_lo(b);
+__device__ __forceinline__ float lo16(uint32_t w) {
+    if constexpr (DT == DT_BF16) return bf16_lo(w);
+    else return f16_lo(w);
+}
+template <int DT>
+__device__ __forceinline__ float hi16(uint32_t w) {
+    if constexpr (DT == DT_BF16) return bf16_hi(w);
+    else return f16_hi(w);
 }
 
 // P as the sum of two 16-bit numbers: hi = round(p), lo = round(p - hi).  Two MFMAs with
@@ -59,29 +75,34 @@ __device__ __forceinline__ float from16(uint32_t b) {
 // bf16) would put up to ~1e-2 absolute error on rows that see only a few tokens.
 template <int DT>
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
-    const uint32_t ha = to16<DT>(a), hb = to16<DT>(b);
-    hi = ha | (hb << 16);
-    lo = to16<DT>(a - from16<DT>(ha)) | (to16<DT>(b - from16<DT>(hb)) << 16);
+    hi = cvt2<DT>(a, b);
+    lo = cvt2<DT>(a - lo16<DT>(hi), b - hi16<DT>(hi));
 }
 
 template <int D>
 struct ChunkShape {
     static constexpr int MW = 32;                 // M-rows per wavefront
     static constexpr int STEP = 32;               // tokens per step
-    static constexpr int ROWB = D * 2 + 16;       // LDS bytes per staged token row (padded)
-    static constexpr int REGION = STEP * ROWB;    // one staged K or V step
-    static constexpr int CHUNKS = STEP * D * 2 / 16;            // 16-byte pieces per region
-    static constexpr int PER_THREAD = CHUNKS / (kWavesPerGroup * kWave);
-    static_assert(CHUNKS % (kWavesPerGroup * kWave) == 0, "staging split");
+    static constexpr int ROWB = D * 2 + 16;       // LDS bytes per staged K token row (padded)
+    static constexpr int ROWV = D * 4 + 16;       // LDS bytes per staged V token pair (padded)
+    static constexpr int KREG = STEP * ROWB;
+    static constexpr int VREG = STEP / 2 * ROWV;
+    static constexpr int THREADS = kWavesPerGroup * kWave;
+    static constexpr int KPIECES = STEP * D / 8;        // 16-byte pieces of K per step
+    static constexpr int VPIECES = STEP / 2 * D / 8;    // (token pair, 8 columns) pieces of V
+    static constexpr int KPT = (KPIECES + THREADS - 1) / THREADS;
+    static constexpr int VPT = (VPIECES + THREADS - 1) / THREADS;
 };
 
 template <int DT, int D, int G>
-__global__ __launch_bounds__(kWavesPerGroup * kWave) void chunk_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(DecodeArgs a) {
     using S = ChunkShape<D>;
     constexpr int KS = D / 16, DT32 = D / 32, QR = S::MW / G;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr float kNegBig = -3.402823466e38f;
-    __shared__ __attribute__((aligned(16))) char lds[2][2][S::REGION];
+    __shared__ __attribute__((aligned(16))) char lds_k[2][S::KREG];
+    __shared__ __attribute__((aligned(16))) char lds_v[2][S::VREG];
+    __shared__ int s_ids[4][2];   // block ids of the two blocks of a step, read ahead
 
     const int32_t* hdr = (const int32_t*)(a.ws + a.lay.header);
     const int2* tiles = (const int2*)(a.ws + a.lay.tiles);
@@ -114,6 +135,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void chunk_kernel(DecodeArg
     const int wr_last = min(r0 + (wave + 1) * QR, n) - 1;
     const int wp_last = L - n + wr_last;
     const int wlo_first = (a.window > 0) ? max(0, L - n + r0 + wave * QR - a.window + 1) : 0;
+    // a step needs no mask when every row of the wavefront exists and sees all its tokens
+    const bool w_rows_full = r0 + (wave + 1) * QR <= n;
+    const int wp_first = L - n + r0 + wave * QR;
+    const int wlo_last = (a.window > 0) ? max(0, wp_last - a.window + 1) : 0;
 
     // Q^T operand: 8 elements at d = 16 ks + 8 h of this lane's row and head
     u32x4 qb[KS];
@@ -121,7 +146,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void chunk_kernel(DecodeArg
         const char* qp = (const char*)a.q +
             (((size_t)(rs + qrow_c) * a.num_q_heads + (size_t)g * G + gi) * D) * 2;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qb[ks] = ld16(qp + (16 * ks + 8 * h) * 2);
+        for (int ks = 0; ks < KS; ++ks) {
+            qb[ks] = ld16(qp + (16 * ks + 8 * h) * 2);
+            // a negative scale is carried by Q's signs (exact for 16-bit values), so the
+            // softmax below always scales by a non-negative factor
+            if (a.scale < 0.f) qb[ks] ^= 0x80008000u;
+        }
     }
 
     f32x16 acc[DT32];
@@ -130,60 +160,123 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void chunk_kernel(DecodeArg
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
     float m_run = kNegBig, l_run = 0.f;
-    const float qscale = a.scale * kLog2e;
+    const float qscale = fabsf(a.scale) * kLog2e;
 
     const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks;
     const size_t tile_bytes = (size_t)kBlock * D * 2;
     const size_t block_stride = (size_t)a.num_kv_heads * tile_bytes;
-    const int nblk_seq = (L + kBlock - 1) / kBlock;
 
-    // staging: thread piece c -> token c / (D/8), 16-byte column c % (D/8)
-    u32x4 sk[S::PER_THREAD], sv[S::PER_THREAD];
+    // staging.  K piece c -> token c / (D/8), 16-byte column c % (D/8).  V piece c -> token
+    // pair c / (D/8), column group c % (D/8): tokens 2p and 2p+1, 8 columns each, written
+    // interleaved as 8 dwords (token 2p in the low half).
+    // two register sets: the loads of the next two steps are in flight during a step
+    u32x4 sk[2][S::KPT], sv[2][S::VPT][2];
     int bad = 0;
-    auto stage_load = [&](int t0) {
+    // the step's two block ids, read from the table two steps ahead into LDS
+    auto fetch_ids = [&](int t0, int& i0, int& i1) {
+        i0 = (t0 < L && t0 + kBlock > lo_first) ? bt[t0 / kBlock] : -1;
+        i1 = (t0 + kBlock < L && t0 + 2 * kBlock > lo_first) ? bt[t0 / kBlock + 1] : -1;
+    };
+    const int* ids = nullptr;
+    auto kv_off = [&](int t, int t0, bool& ok) -> size_t {
+        ok = false;
+        if (t >= L || t < lo_first) return 0;
+        const int b = ids[(t - t0) / kBlock];
+        if ((unsigned)b >= (unsigned)a.num_blocks) {
+            bad = 1;
+            return 0;
+        }
+        ok = true;
+        return (size_t)b * block_stride + (size_t)g * tile_bytes + (size_t)(t % kBlock) * D * 2;
+    };
+    auto stage_load = [&](int t0, u32x4* sk, u32x4 (*sv)[2]) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < S::PER_THREAD; ++i) {
-            const int c = tid + i * kWavesPerGroup * kWave;
-            const int tt = c / (D / 8), col = c % (D / 8);
-            const int t = t0 + tt;
-            const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int i = 0; i < S::KPT; ++i) {
+            const int c = tid + i * S::THREADS;
             sk[i] = z;
-            sv[i] = z;
-            if (t < L && t >= lo_first && t / kBlock < nblk_seq) {
-                const int b = bt[t / kBlock];
-                if ((unsigned)b < (unsigned)a.num_blocks) {
-                    const size_t off = (size_t)b * block_stride + (size_t)g * tile_bytes +
-                                       (size_t)(t % kBlock) * D * 2 + col * 16;
-                    sk[i] = ld16_stream((const char*)a.k_cache + off);
-                    sv[i] = ld16_stream((const char*)a.v_cache + off);
-                } else {
-                    bad = 1;
-                }
+            if (c < S::KPIECES) {
+                bool ok;
+                const size_t off = kv_off(t0 + c / (D / 8), t0, ok);
+                if (ok) sk[i] = ld16_stream((const char*)a.k_cache + off + (c % (D / 8)) * 16);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < S::VPT; ++i) {
+            const int c = tid + i * S::THREADS;
+            sv[i][0] = z;
+            sv[i][1] = z;
+            if (c < S::VPIECES) {
+                const int t = t0 + 2 * (c / (D / 8)), col = (c % (D / 8)) * 16;
+                bool ok0, ok1;
+                const size_t o0 = kv_off(t, t0, ok0), o1 = kv_off(t + 1, t0, ok1);
+                if (ok0) sv[i][0] = ld16_stream((const char*)a.v_cache + o0 + col);
+                if (ok1) sv[i][1] = ld16_stream((const char*)a.v_cache + o1 + col);
             }
         }
     };
-    auto stage_store = [&](int buf) {
+    auto stage_store = [&](int buf, const u32x4* sk, const u32x4 (*sv)[2]) {
 #pragma unroll
-        for (int i = 0; i < S::PER_THREAD; ++i) {
-            const int c = tid + i * kWavesPerGroup * kWave;
-            const int tt = c / (D / 8), col = c % (D / 8);
-            st16(&lds[buf][0][tt * S::ROWB + col * 16], sk[i]);
-            st16(&lds[buf][1][tt * S::ROWB + col * 16], sv[i]);
+        for (int i = 0; i < S::KPT; ++i) {
+            const int c = tid + i * S::THREADS;
+            if (c < S::KPIECES)
+                st16(&lds_k[buf][(c / (D / 8)) * S::ROWB + (c % (D / 8)) * 16], sk[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < S::VPT; ++i) {
+            const int c = tid + i * S::THREADS;
+            if (c < S::VPIECES) {
+                const uint32_t e[4] = {sv[i][0].x, sv[i][0].y, sv[i][0].z, sv[i][0].w};
+                const uint32_t o[4] = {sv[i][1].x, sv[i][1].y, sv[i][1].z, sv[i][1].w};
+                uint32_t w8[8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    w8[2 * k] = (e[k] & 0xffffu) | (o[k] << 16);
+                    w8[2 * k + 1] = (e[k] >> 16) | (o[k] & 0xffff0000u);
+                }
+                char* dst = &lds_v[buf][(c / (D / 8)) * S::ROWV + (c % (D / 8)) * 32];
+                const u32x4 w0 = {w8[0], w8[1], w8[2], w8[3]}, w1 = {w8[4], w8[5], w8[6], w8[7]};
+                st16(dst, w0);
+                st16(dst + 16, w1);
+            }
         }
     };
 
-    if (nsteps > 0) {
-        stage_load(t_first);
-        stage_store(0);
+    if (tid == 0) {
+        for (int k = 0; k < 4; ++k) {
+            int i0, i1;
+            fetch_ids(t_first + k * S::STEP, i0, i1);
+            s_ids[k][0] = i0;
+            s_ids[k][1] = i1;
+        }
     }
     __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
+    if (nsteps > 0) {
+        ids = s_ids[0];
+        stage_load(t_first, sk[0], sv[0]);
+        stage_store(0, sk[0], sv[0]);
+    }
+    if (nsteps > 1) {
+        ids = s_ids[1];
+        stage_load(t_first + S::STEP, sk[1], sv[1]);
+    }
+    if (nsteps > 2) {
+        ids = s_ids[2];
+        stage_load(t_first + 2 * S::STEP, sk[0], sv[0]);
+    }
+    __syncthreads();
+    // step st computes from LDS buffer st & 1 while steps st+1 (register set (st+1) & 1)
+    // and st+2 are loading; then st+1 goes to LDS and step st+3 starts loading into the
+    // set st+1 used.  P = (st + 1) & 1 is a compile-time constant.
+    auto body = [&](auto Pc, int st) {
+        constexpr int P = decltype(Pc)::value;
         const int buf = st & 1, t0 = t_first + st * S::STEP;
-        if (st + 1 < nsteps) stage_load(t0 + S::STEP);
+        int nid0 = -1, nid1 = -1;
+        if (tid == 0 && st + 4 < nsteps) fetch_ids(t0 + 4 * S::STEP, nid0, nid1);
         if (t0 <= wp_last && t0 + S::STEP > wlo_first) {      // wavefront-uniform
-            const char* kl = lds[buf][0];
-            const char* vl = lds[buf][1];
-            // S^T = K . Q^T
+            const char* kl = lds_k[buf];
+            const char* vl = lds_v[buf];
+            // S^T = K . Q^T (raw dot products)
             f32x16 sc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sc[r] = 0.f;
@@ -192,32 +285,53 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void chunk_kernel(DecodeArg
                 const u32x4 ka = ld16(kl + j * S::ROWB + (16 * ks + 8 * h) * 2);
                 sc = mfma32<DT>(ka, qb[ks], sc);
             }
-            // mask (selection), online softmax for this lane's M-row
-            float sv16[16];
-            float mx = kNegBig;
+            // element r of this lane is token t0 + 8 (r/4) + 4 h + r%4 of its M-row
+            const bool full = w_rows_full && t0 + S::STEP - 1 <= wp_first && t0 >= wlo_last;
+            float p16[16];
+            float mx = -INFINITY;
+            // this lane's visible token range of the step, [tlo, thi], as offsets 0..31
+            const int tlo = row_ok ? max(lo - t0, 0) : 32;
+            const int thi = row_ok ? min(pos - t0, 31) : -1;
+            auto vis = [&](int r) {
+                const int tt = 8 * (r / 4) + 4 * h + (r % 4);
+                return tt >= tlo && tt <= thi;
+            };
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = t0 + 8 * (r / 4) + 4 * h + (r % 4);
-                const bool ok = row_ok && t >= lo && t <= pos;
-                sv16[r] = ok ? sc[r] * qscale : -INFINITY;
-                mx = fmaxf(mx, sv16[r]);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, vis(r) ? sc[r] : -INFINITY);
             }
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mn = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-            m_run = mn;
-            float p16[16], psum = 0.f;
+            const float mxs = mx > -INFINITY ? mx * qscale : -INFINITY;
+            // raise the running max only when the new one exceeds it by more than 8 (log2)
+            if (__ballot(mxs > m_run + 8.f)) {                 // wavefront-uniform
+                const float mn = fmaxf(m_run, mxs);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+                m_run = mn;
+                l_run *= alpha;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p16[r] = __builtin_amdgcn_exp2f(sv16[r] - mn);
-                psum += p16[r];
+                for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+            }
+            float psum = 0.f;
+            if (full) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    p16[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], qscale, -m_run));
+                    psum += p16[r];
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    p16[r] = vis(r) ? __builtin_amdgcn_exp2f(fmaf(sc[r], qscale, -m_run)) : 0.f;
+                    psum += p16[r];
+                }
             }
             psum += __shfl_xor(psum, 32);
-            l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-            for (int dt = 0; dt < DT32; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+            l_run += psum;
             // P^T operands: K-step k2 covers tokens 16 k2 .. 16 k2 + 15; element kk of lane
             // (j, h) is token 16 k2 + (kk < 4 ? 4 h + kk : 8 + 4 h + kk - 4) = p16[8 k2 + kk]
             u32x4 pb[2], pl[2];
@@ -229,31 +343,41 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void chunk_kernel(DecodeArg
                 split2<DT>(pp[2], pp[3], h1, l1);
                 split2<DT>(pp[4], pp[5], h2, l2);
                 split2<DT>(pp[6], pp[7], h3, l3);
-                const u32x4 th = {h0, h1, h2, h3}, tl = {l0, l1, l2, l3};
+                const u32x4 th = {h0, h1, h2, h3}, tl2 = {l0, l1, l2, l3};
                 pb[k2] = th;
-                pl[k2] = tl;
+                pl[k2] = tl2;
             }
-            // O^T += V^T . P^T; the V^T operand takes the same token order
+            // O^T += V^T . P^T; the V^T operand takes the same token order: dwords of token
+            // pairs (ta, ta+1), (ta+2, ta+3), (tb, tb+1), (tb+2, tb+3)
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-                const int ta = 16 * k2 + 4 * h, tb = 16 * k2 + 8 + 4 * h;
+                const int pa_ = 8 * k2 + 2 * h, pb_ = 8 * k2 + 4 + 2 * h;   // token-pair rows
 #pragma unroll
                 for (int dt = 0; dt < DT32; ++dt) {
-                    const int dcol = (32 * dt + j) * 2;
-                    const uint16_t* v0 = (const uint16_t*)(vl + ta * S::ROWB + dcol);
-                    const uint16_t* v1 = (const uint16_t*)(vl + tb * S::ROWB + dcol);
-                    constexpr int RW = S::ROWB / 2;
-                    const u32x4 va = {(uint32_t)v0[0] | ((uint32_t)v0[RW] << 16),
-                                      (uint32_t)v0[2 * RW] | ((uint32_t)v0[3 * RW] << 16),
-                                      (uint32_t)v1[0] | ((uint32_t)v1[RW] << 16),
-                                      (uint32_t)v1[2 * RW] | ((uint32_t)v1[3 * RW] << 16)};
+                    const char* col = vl + (32 * dt + j) * 4;
+                    const u32x4 va = {*(const uint32_t*)(col + pa_ * S::ROWV),
+                                      *(const uint32_t*)(col + (pa_ + 1) * S::ROWV),
+                                      *(const uint32_t*)(col + pb_ * S::ROWV),
+                                      *(const uint32_t*)(col + (pb_ + 1) * S::ROWV)};
                     acc[dt] = mfma32<DT>(va, pb[k2], acc[dt]);
                     acc[dt] = mfma32<DT>(va, pl[k2], acc[dt]);
                 }
             }
         }
-        if (st + 1 < nsteps) stage_store(buf ^ 1);
+        if (st + 1 < nsteps) stage_store(buf ^ 1, sk[P], sv[P]);
+        if (st + 3 < nsteps) {
+            ids = s_ids[(st + 3) % 4];
+            stage_load(t0 + 3 * S::STEP, sk[P], sv[P]);
+        }
+        if (tid == 0 && st + 4 < nsteps) {
+            s_ids[(st + 4) % 4][0] = nid0;
+            s_ids[(st + 4) % 4][1] = nid1;
+        }
         __syncthreads();
+    };
+    for (int st = 0; st < nsteps; st += 2) {
+        body(std::integral_constant<int, 1>{}, st);
+        if (st + 1 < nsteps) body(std::integral_constant<int, 0>{}, st + 1);
     }
     if (bad) atomicOr((int32_t*)(a.ws + a.lay.header), kErrBlockId);
 

@@ -125,11 +125,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
         const int n = r1 - r0, L = a.seq_lens[s];
         const bool ok = len_ok(a, L);
         const bool chunk = ok && QT > 0 && n >= 2;
+        if (chunk) {
+            // the rows' unit records are written by all threads below; here the tiles and
+            // the sequence's offset (no decode blocks: every row keeps the same offset)
+            for (int q0 = 0; q0 < n; q0 += QT) tiles[toff++] = make_int2(s, q0);
+            cb[r0] = off;
+            continue;
+        }
         for (int r = 0; r < n; ++r) {
             UnitInfo ui{0, 0, 0, s};
-            if (chunk) {
-                ui.b_lo = -1;
-            } else if (ok) {
+            if (ok) {
                 ui.len = max(0, L - n + r + 1);
                 unit_range(ui.len, a.window, ui.b_lo, ui.nb);
             }
@@ -137,10 +142,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
             cb[r0 + r] = off;
             off += (uint32_t)ui.nb * (uint32_t)a.num_kv_heads;
         }
-        if (chunk)
-            for (int q0 = 0; q0 < n; q0 += QT) tiles[toff++] = make_int2(s, q0);
     }
     if (tid == 0) cb[U] = T;
+    __syncthreads();
+    // rows of chunk sequences: marked for the chunk kernel, offset of their first row
+    for (int i = tid; i < (int)NT * QT; i += kPlanThreads) {
+        const int2 tl = tiles[i / QT];
+        const int rs = a.query_start_loc[tl.x];
+        const int n = a.query_start_loc[tl.x + 1] - rs;
+        const int r = tl.y + i % QT;
+        if (r < n) {
+            const int u = rs + r;
+            unit[u] = UnitInfo{-1, 0, 0, tl.x};
+            if (u != rs) cb[u] = cb[rs];
+        }
+    }
 
     int W = 0;
     if (T > 0) {
@@ -152,23 +168,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     // rows with nothing to read (empty context, or rejected lengths) get zeros later
     for (int u = tid; u < U; u += kPlanThreads)
         if (unit[u].nb == 0 && unit[u].b_lo >= 0) empty[atomicAdd(&s_empty, 1)] = u;
+    // wavefront w's share starts at x0(w) = floor(w T / W).  It starts inside unit u exactly
+    // when ceil(cb[u] W / T) <= w < ceil(cb[u+1] W / T); these ranges tile [0, W).
+    for (int u = tid; u < U && W > 0; u += kPlanThreads) {
+        const uint64_t c0 = cb[u], c1 = cb[u + 1];
+        if (c1 == c0) continue;
+        const uint64_t w0 = (c0 * (uint64_t)W + T - 1) / T;
+        uint64_t w1 = (c1 * (uint64_t)W + T - 1) / T;
+        if (w1 > (uint64_t)W) w1 = W;
+        for (uint64_t w = w0; w < w1; ++w) {
+            wx0[w] = (uint32_t)((w * T) / (uint64_t)W);
+            wu[w] = u;
+        }
+    }
     __syncthreads();
     if (tid == 0) {
+        wx0[W] = T;
         hdr[0] = s_err; hdr[1] = (int32_t)T; hdr[2] = W; hdr[3] = s_empty; hdr[4] = (int32_t)NT;
     }
-
-    // each wavefront's share [wx0[w], wx0[w+1]) and the unit holding its first block
-    for (int w = tid; w < W; w += kPlanThreads) {
-        const uint32_t x0 = (uint32_t)(((uint64_t)w * T) / (uint64_t)W);
-        int lo = 0, hi = U - 1;   // largest u with cb[u] <= x0 (it has nb > 0)
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cb[mid] <= x0) lo = mid; else hi = mid - 1;
-        }
-        wx0[w] = x0;
-        wu[w] = lo;
-    }
-    if (tid == 0) wx0[W] = T;
 }
 
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t stream) {
