@@ -1,6 +1,5 @@
 // Dispatch of the paged decode kernel over (cache dtype, head_dim, group).
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "decode_impl.h"
 
 namespace pa {
 
@@ -39,8 +38,40 @@ hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
     const void* fn = decode_kernel_ptr(dtype, a.head_dim, a.group);
     if (!fn) return hipErrorInvalidDeviceFunction;
-    const int groups = (a.max_waves + kWavesPerGroup - 1) / kWavesPerGroup;
-    if (groups == 0) return hipSuccess;
+    int groups = (a.max_waves + kWavesPerGroup - 1) / kWavesPerGroup;
+    if (groups < 1) groups = 1;   // at least one group: it also zeroes rows with nothing to read
+    void* args[] = {(void*)&a};
+    return hipLaunchKernel(fn, dim3(groups), dim3(kWavesPerGroup * kWave), args, 0, stream);
+}
+
+// Merge kernel: wavefront w (w >= 1) finds the task of share boundary w, if any, and
+// combines that pair's partials.  Every task is cleared once done, so a plan reused by
+// later calls starts from no tasks.
+template <int D, int G>
+__global__ __launch_bounds__(kWavesPerGroup * kWave) void merge_kernel(DecodeArgs a) {
+    int4* tasks = (int4*)(a.ws + a.lay.tasks);
+    const float2* pml = (const float2*)(a.ws + a.lay.part_ml);
+    const float* pacc = (const float*)(a.ws + a.lay.part_acc);
+    const int w = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6) + 1;
+    const int W = ((const int32_t*)(a.ws + a.lay.header))[2];
+    if (w >= W) return;
+    const int4 t = tasks[w];
+    if (t.z <= 0) return;
+    merge_pair<D, G>(a, t.x, t.y, w - 1, t.z, t.w, pml, pacc, lane_id());
+    if (lane_id() == 0) tasks[w] = make_int4(0, 0, 0, 0);
+}
+
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
+    const void* fn = nullptr;
+#define PA_CASE(D, G) \
+    if (a.head_dim == D && a.group == G) fn = (const void*)&merge_kernel<D, G>;
+#define PA_CASES(D) PA_CASE(D, 1) PA_CASE(D, 2) PA_CASE(D, 4) PA_CASE(D, 8)
+    PA_CASES(64) PA_CASES(128) PA_CASES(256)
+#undef PA_CASES
+#undef PA_CASE
+    if (!fn) return hipErrorInvalidDeviceFunction;
+    if (a.max_waves <= 1) return hipSuccess;
+    const int groups = (a.max_waves - 1 + kWavesPerGroup - 1) / kWavesPerGroup;
     void* args[] = {(void*)&a};
     return hipLaunchKernel(fn, dim3(groups), dim3(kWavesPerGroup * kWave), args, 0, stream);
 }

@@ -27,7 +27,11 @@
 //     broadcast with readlane; an id outside the pool sets an error bit and masks the
 //     block instead of being dereferenced;
 //   * masked tokens are removed by selection (score -inf, V zeroed), never by a zero
-//     weight, so NaN in free or unused slots cannot reach the output.
+//     weight, so NaN in free or unused slots cannot reach the output;
+//   * a pair cut by share boundaries leaves one partial (max, sum, unnormalised output)
+//     per wavefront; the wavefront holding the pair's first block also leaves a merge task
+//     (pair, number of partials) for the merge kernel, which combines them with the
+//     log-sum-exp rule.
 #pragma once
 
 #include "pa_device.h"
@@ -81,6 +85,86 @@ __device__ __forceinline__ void store_row(const DecodeArgs& a, size_t idx, const
     }
 }
 
+// One wavefront zeroes one output row (a multiple of 16 bytes).
+__device__ inline void zero_row(const DecodeArgs& a, int row, int lane) {
+    const int ob = a.out_dtype == PA_F32 ? 4 : 2;
+    const size_t bytes = (size_t)a.num_q_heads * a.head_dim * ob;
+    char* p = (char*)a.out + (size_t)row * bytes;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (size_t o = (size_t)lane * 16; o < bytes; o += kWave * 16) st16(p + o, z);
+}
+
+__device__ __forceinline__ void store_out1(const DecodeArgs& a, size_t idx, float v) {
+    if (a.out_dtype == PA_F32) {
+        ((float*)a.out)[idx] = v;
+    } else if (a.out_dtype == PA_F16) {
+        ((uint16_t*)a.out)[idx] = (uint16_t)f32_to_f16_bits(v);
+    } else {
+        ((uint16_t*)a.out)[idx] = (uint16_t)f32_to_bf16_bits(v);
+    }
+}
+
+// Combine the partials of pair (u, g) left by wavefronts w_first .. w_first + nc - 1 (slot
+// first_slot for the first, slot 0 for the others):
+//   out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c,   M = max_c m_c   (m in log2 units)
+template <int D, int G>
+__device__ void merge_pair(const DecodeArgs& a, int u, int g, int w_first, int nc,
+                           int first_slot, const float2* pml, const float* pacc, int lane) {
+    constexpr int KD = (D + kWave - 1) / kWave;
+#pragma unroll 1
+    for (int gi = 0; gi < G; ++gi) {
+        float M = -3.402823466e38f;
+        for (int c0 = 0; c0 < nc; c0 += kWave) {
+            const int c = c0 + lane;
+            if (c < nc) {
+                const int v = w_first + c, slot = c == 0 ? first_slot : 0;
+                M = fmaxf(M, pml[((size_t)v * 2 + slot) * G + gi].x);
+            }
+        }
+        M = wave_max(M);
+        float den = 0.f, num[KD];
+#pragma unroll
+        for (int k = 0; k < KD; ++k) num[k] = 0.f;
+        for (int c0 = 0; c0 < nc; c0 += kWave) {
+            const int c = c0 + lane;
+            float f = 0.f;
+            if (c < nc) {
+                const int v = w_first + c, slot = c == 0 ? first_slot : 0;
+                const float2 ml = pml[((size_t)v * 2 + slot) * G + gi];
+                f = __builtin_amdgcn_exp2f(ml.x - M);
+                den += f * ml.y;
+            }
+            const int n = nc - c0 < kWave ? nc - c0 : kWave;
+            // four contributors per round, all loads issued before any use
+            for (int j = 0; j < n; j += 4) {
+                float fj[4], val[4][KD];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int jj = j + t < n ? j + t : j;        // in range; weight 0 below
+                    fj[t] = j + t < n
+                                ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), jj))
+                                : 0.f;
+                    const int v = w_first + c0 + jj, slot = c0 + jj == 0 ? first_slot : 0;
+                    const float* src = pacc + (((size_t)v * 2 + slot) * G + gi) * D;
+#pragma unroll
+                    for (int k = 0; k < KD; ++k)
+                        val[t][k] = lane + 64 * k < D ? src[lane + 64 * k] : 0.f;
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int k = 0; k < KD; ++k) num[k] += fj[t] * val[t][k];
+            }
+        }
+        den = wave_sum(den);
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        const size_t obase = ((size_t)u * a.num_q_heads + (size_t)g * G + gi) * D;
+#pragma unroll
+        for (int k = 0; k < KD; ++k)
+            if (lane + 64 * k < D) store_out1(a, obase + lane + 64 * k, num[k] * inv);
+    }
+}
+
 template <int DT, int D, int G>
 __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeArgs a) {
     using S = DecodeShape<DT, D, G>;
@@ -96,11 +180,17 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     float2* pml = (float2*)(a.ws + a.lay.part_ml);
     float* pacc = (float*)(a.ws + a.lay.part_acc);
 
-    const int W = hdr[2];
+    int4* tasks = (int4*)(a.ws + a.lay.tasks);
+    const int32_t* empty = (const int32_t*)(a.ws + a.lay.empty);
+
+    const int W = hdr[2], n_empty = hdr[3];
+    const uint32_t T = (uint32_t)hdr[1];
     const int wave = uniform(blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6));
+    const int lane = lane_id();
+    // rows with nothing to read are zeros (shared out among all launched wavefronts)
+    for (int i = wave; i < n_empty; i += gridDim.x * kWavesPerGroup) zero_row(a, empty[i], lane);
     if (wave >= W) return;
 
-    const int lane = lane_id();
     const int row = lane / LPT;        // which token of each load this lane holds
     const int col = lane % LPT;        // which PE-element column
     const float qscale = a.scale * kLog2e;
@@ -267,6 +357,14 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
                     }
                 }
             }
+        }
+        if (!complete && x == ps && lane == 0) {
+            // this wavefront holds the pair's first block: leave its merge task.  The
+            // wavefronts whose shares meet the pair are the one holding ps .. the one holding
+            // pe - 1; the wavefront holding block x is ceil((x + 1) W / T) - 1.
+            const uint64_t WW = (uint64_t)W, TT = T;
+            const int w_last = (int)((((uint64_t)pe) * WW + TT - 1) / TT) - 1;
+            tasks[wave + 1] = make_int4(u, g, w_last - wave + 1, first_segment ? 0 : 1);
         }
         x = seg_end;
         first_segment = false;

@@ -40,10 +40,13 @@ struct UnitInfo {
 //   wave_x0  uint32[W+1]   first linear block of each wave's share
 //   wave_u   int32[W]      unit holding that block
 //   tiles    int2[Tmax]    chunk-row tiles (sequence, first row) for the MFMA kernel
+//   tasks    int4[W+1]     merge task of the cut pair whose first share boundary is w:
+//                          (unit, KV head, contributing wavefronts, slot of the first);
+//                          written by the pair's first wavefront, cleared by the merge
 //   part_ml  float2[W*2*G]       partial (max, sum) per wave, slot, head of the group
 //   part_acc float[W*2*G*d]      partial unnormalised output
 struct Layout {
-    size_t header, cb, unit, empty, wave_x0, wave_u, tiles, part_ml, part_acc, total;
+    size_t header, cb, unit, empty, wave_x0, wave_u, tiles, tasks, part_ml, part_acc, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -58,6 +61,7 @@ inline Layout layout(int num_rows, int max_waves, int max_tiles, int group, int 
     L.wave_x0 = o;  o = align256(o + (size_t)(max_waves + 1) * sizeof(uint32_t));
     L.wave_u = o;   o = align256(o + (size_t)max_waves * sizeof(int32_t));
     L.tiles = o;    o = align256(o + (size_t)max_tiles * 2 * sizeof(int32_t));
+    L.tasks = o;    o = align256(o + (size_t)(max_waves + 1) * 4 * sizeof(int32_t));
     L.part_ml = o;  o = align256(o + (size_t)max_waves * 2 * group * 2 * sizeof(float));
     L.part_acc = o; o = align256(o + (size_t)max_waves * 2 * group * head_dim * sizeof(float));
     L.total = o;

@@ -1,13 +1,13 @@
-// Plan and merge kernels of pa_decode.
+// Plan kernel of pa_decode (one workgroup).
 //
-// Plan (one workgroup): validates lengths and row ranges, turns every query row into a
-// decode unit (a chunk row r of n rows at length L reads like a decode row at length
-// L - n + r + 1), lays all (unit, KV head) pairs end to end in one linear space of KV
-// blocks, and cuts that space into equal shares, one per wavefront worker.  A pair that
-// fits inside one share is finished by that wavefront; a pair cut by share boundaries
-// leaves partial (max, sum, unnormalised output) results that the merge kernel combines
+// Validates lengths and row ranges, turns every decode query row into a decode unit, lays
+// all (unit, KV head) pairs end to end in one linear space of KV blocks, and cuts that
+// space into equal shares, one per wavefront worker of the decode kernel.  A pair that fits
+// inside one share is finished by that wavefront; a pair cut by share boundaries leaves
+// partial (max, sum, unnormalised output) results that the last of its wavefronts combines
 // with the log-sum-exp rule.  Equal shares keep every worker busy for the same number of
 // blocks whatever the length mix (log-normal lengths differ by three orders of magnitude).
+// Rows of chunks (several query rows) go to the chunk kernel's tile list instead.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -34,14 +34,6 @@ __device__ __forceinline__ bool len_ok(const DecodeArgs& a, int L) {
     return L >= 0 && L <= a.max_seq_len && L <= a.max_blocks * kBlock;
 }
 
-// one wavefront zeroes one output row (a multiple of 16 bytes)
-__device__ void zero_row(const DecodeArgs& a, int row, int lane) {
-    const int ob = a.out_dtype == PA_F32 ? 4 : 2;
-    const size_t bytes = (size_t)a.num_q_heads * a.head_dim * ob;
-    char* p = (char*)a.out + (size_t)row * bytes;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (size_t o = (size_t)lane * 16; o < bytes; o += kWave * 16) st16(p + o, z);
-}
 
 // Inclusive scan of one value per thread over the workgroup (Hillis-Steele in LDS).
 __device__ uint32_t block_scan(uint32_t* buf, uint32_t v) {
@@ -65,6 +57,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     int32_t* wu = (int32_t*)(a.ws + a.lay.wave_u);
     int32_t* empty = (int32_t*)(a.ws + a.lay.empty);
     int2* tiles = (int2*)(a.ws + a.lay.tiles);
+    int4* tasks = (int4*)(a.ws + a.lay.tasks);
 
     __shared__ uint32_t s_blk[kPlanThreads], s_til[kPlanThreads];
     __shared__ int s_err, s_bad, s_empty;
@@ -165,6 +158,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
+    // every task slot the merge kernel may look at starts empty
+    for (int w = tid; w <= a.max_waves; w += kPlanThreads) tasks[w] = make_int4(0, 0, 0, 0);
     // rows with nothing to read (empty context, or rejected lengths) get zeros later
     for (int u = tid; u < U; u += kPlanThreads)
         if (unit[u].nb == 0 && unit[u].b_lo >= 0) empty[atomicAdd(&s_empty, 1)] = u;
@@ -190,121 +185,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
 
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------- merge
-// Every wavefront first zeroes its share of the rows with nothing to read, then wavefront
-// w merges if share boundary w cuts a pair for the first time.  Partials are
-// (m_p, l_p, acc_p) with m in log2 units: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,
-// M = max_p m_p (the usual log-sum-exp combination of softmax pieces).
-__device__ __forceinline__ void store_out1(const DecodeArgs& a, size_t idx, float v) {
-    if (a.out_dtype == PA_F32) {
-        ((float*)a.out)[idx] = v;
-    } else if (a.out_dtype == PA_F16) {
-        ((uint16_t*)a.out)[idx] = (uint16_t)f32_to_f16_bits(v);
-    } else {
-        ((uint16_t*)a.out)[idx] = (uint16_t)f32_to_bf16_bits(v);
-    }
-}
-
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
-    const int32_t* hdr = (const int32_t*)(a.ws + a.lay.header);
-    const uint32_t* cb = (const uint32_t*)(a.ws + a.lay.cb);
-    const UnitInfo* unit = (const UnitInfo*)(a.ws + a.lay.unit);
-    const uint32_t* wx0 = (const uint32_t*)(a.ws + a.lay.wave_x0);
-    const int32_t* wu = (const int32_t*)(a.ws + a.lay.wave_u);
-    const float2* pml = (const float2*)(a.ws + a.lay.part_ml);
-    const float* pacc = (const float*)(a.ws + a.lay.part_acc);
-
-    const int32_t* empty = (const int32_t*)(a.ws + a.lay.empty);
-
-    const int W = hdr[2], n_empty = hdr[3];
-    const int mw = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
-    const int lane = lane_id();
-    for (int i = mw; i < n_empty; i += gridDim.x * kWavesPerGroup) zero_row(a, empty[i], lane);
-    const int w = mw + 1;
-    if (w >= W) return;
-    const uint32_t x = wx0[w];
-    const int u = wu[w];
-    const UnitInfo ui = unit[u];
-    const uint32_t base = cb[u];
-    const int g = (int)((x - base) / (uint32_t)ui.nb);
-    const uint32_t ps = base + (uint32_t)g * ui.nb, pe = ps + ui.nb;
-    if (x == ps) return;                 // boundary falls between pairs
-    const uint32_t prev = wx0[w - 1];
-    if (prev > ps) return;               // an earlier boundary already cuts this pair
-    const int first_slot = prev == ps ? 0 : 1;
-
-    // contributors: wave w-1 (slot first_slot), then waves w, w+1, ... while their share
-    // starts inside the pair (slot 0).  Found 64 at a time with one load per lane.
-    int wend = w;
-    for (;;) {
-        const int v = wend + lane;
-        const bool in = v < W && wx0[v] < pe;
-        const uint64_t m = __ballot(in);
-        const int run = m == ~0ull ? 64 : __builtin_ctzll(~m);
-        wend += run;
-        if (run < 64) break;
-    }
-    const int nc = wend - (w - 1);
-
-    const int G = a.group, D = a.head_dim;
-    for (int gi = 0; gi < G; ++gi) {
-        // weights 2^(m_c - M) of every contributor, held one per lane (64 at a time)
-        float M = -3.402823466e38f;
-        for (int c0 = 0; c0 < nc; c0 += kWave) {
-            const int c = c0 + lane;
-            if (c < nc) {
-                const int v = w - 1 + c, slot = c == 0 ? first_slot : 0;
-                M = fmaxf(M, pml[((size_t)v * 2 + slot) * G + gi].x);
-            }
-        }
-        M = wave_max(M);
-        float den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int c0 = 0; c0 < nc; c0 += kWave) {
-            const int c = c0 + lane;
-            float f = 0.f;
-            if (c < nc) {
-                const int v = w - 1 + c, slot = c == 0 ? first_slot : 0;
-                const float2 ml = pml[((size_t)v * 2 + slot) * G + gi];
-                f = __builtin_amdgcn_exp2f(ml.x - M);
-                den += f * ml.y;
-            }
-            const int n = nc - c0 < kWave ? nc - c0 : kWave;
-            // four contributors per round, all loads issued before any use
-            for (int j = 0; j < n; j += 4) {
-                float fj[4], val[4][4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int jj = j + t < n ? j + t : j;        // in range; weight 0 below
-                    fj[t] = j + t < n
-                                ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), jj))
-                                : 0.f;
-                    const int v = w - 1 + c0 + jj, slot = c0 + jj == 0 ? first_slot : 0;
-                    const float* src = pacc + (((size_t)v * 2 + slot) * G + gi) * D;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        val[t][k] = lane + 64 * k < D ? src[lane + 64 * k] : 0.f;
-                }
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) num[k] += fj[t] * val[t][k];
-            }
-        }
-        den = wave_sum(den);
-        const float inv = den > 0.f ? 1.f / den : 0.f;
-        const size_t obase = ((size_t)u * a.num_q_heads + (size_t)g * G + gi) * D;
-        for (int k = 0; k < 4; ++k)
-            if (lane + 64 * k < D) store_out1(a, obase + lane + 64 * k, num[k] * inv);
-    }
-}
-
-hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
-    int groups = (a.max_waves - 1 + kWavesPerGroup - 1) / kWavesPerGroup;
-    if (groups < 1) groups = 1;
-    hipLaunchKernelGGL(merge_kernel, dim3(groups), dim3(kWavesPerGroup * kWave), 0, stream, a);
     return hipGetLastError();
 }
 
