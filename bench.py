@@ -9,9 +9,11 @@ from cache.  Inputs are synthetic, seeded, already resident in HBM when timing s
 
 Prints one JSON line.  `value` is the KV bytes the attention reads per step (each attended
 token's K and V once, per KV head, per layer) over the measured step time, in GB/s.
-`roofline` reports the decode kernel alone, timed with HIP events around its launches (the
-library's profiling hook records them on the launch stream).  `cpu_baseline` is the fp64 CPU
-oracle timed on the host cores on a bounded sample of the same workload.
+`roofline` reports the dominant kernel alone, timed with HIP events around its launches (the
+library's profiling hooks record them on the launch stream): the decode kernel against HBM
+bandwidth on the decode rows' KV bytes, or, when chunked-prefill rows dominate, the chunk
+kernel against the dense MFMA peak on its FLOPs.  `cpu_baseline` is the fp64 CPU oracle
+timed on the host cores on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload opt13b|gqa|prefix_mixed|swa|tiny]
 """
@@ -30,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention KV-read HBM GB/s (% of peak) + decode tokens/s"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense matrix peak, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = ["decode_impl.h", "pa_device.h", "pa_internal.h", "plan.hip"]
 
@@ -186,45 +189,89 @@ def main():
     common = dict(max_seq_len=dw.max_seq_len, query_start_loc=qsl, window=w.window,
                   workspace=dw.workspace)
 
-    def step(events=None):
+    has_chunks = bool((w.q_rows > 1).any()) and w.dtype in MFMA_PEAK_TFLOPS
+
+    def step(events=None, cevents=None):
         pa.decode(dw.q, pools[0][0], pools[0][1], dw.block_tables, dw.seq_lens, float(w.scale),
                   step="plan", **common)
         for li, (kc, vc) in enumerate(pools):
             pa.write_kv(k_step, v_step, slot_step, kc, vc)
             if events is not None:
                 pa.set_decode_profile_events(*events[li])
+            if cevents is not None:
+                pa.set_chunk_profile_events(*cevents[li])
             pa.decode(dw.q, kc, vc, dw.block_tables, dw.seq_lens, float(w.scale), out=out,
                       step="attend", **common)
         if events is not None:
             pa.set_decode_profile_events(None, None)
+        if cevents is not None:
+            pa.set_chunk_profile_events(None, None)
 
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     # one pair of events per decode launch in the timed region
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(L)] for _ in range(args.steps)]
-    for per in evs:
-        for a, b in per:
-            a.record()
-            b.record()
+    def event_pairs():
+        e = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(L)] for _ in range(args.steps)]
+        for per in e:
+            for a, b in per:
+                a.record()
+                b.record()
+        return e
+
+    evs = event_pairs()
+    cevs = event_pairs() if has_chunks else None
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for k in range(args.steps):
-        step(evs[k])
+        step(evs[k], cevs[k] if cevs else None)
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    dec_ms = [a.elapsed_time(b) for per in evs for a, b in per]
-    dec_avg_ms = float(np.mean(dec_ms))
+    dec_avg_ms = float(np.mean([a.elapsed_time(b) for per in evs for a, b in per]))
+    chunk_avg_ms = (float(np.mean([a.elapsed_time(b) for per in cevs for a, b in per]))
+                    if cevs else 0.0)
     err_bits = pa.device_error_bits(dw.workspace)
 
     step_s = total_ms / 1e3 / args.steps
     value = kv_layer * L / step_s / 1e9
     tokens_per_s = w.total_q_rows / step_s
-    achieved = kv_layer / (dec_avg_ms / 1e3) / 1e9
+    dec = w.q_rows == 1
+    kv_decode = pa.kv_bytes_read(w.seq_lens[dec], w.q_rows[dec], w.window, w.num_kv_heads,
+                                 w.head_dim, w.elem_bytes)
+    achieved = kv_decode / (dec_avg_ms / 1e3) / 1e9
     traffic = measured_traffic(args.workload)
+    decode_roof = {
+        "kernel": "decode_kernel",
+        "bound": "hbm",
+        "achieved": round(achieved, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": int(kv_decode),
+        "decode_kernel_avg_us": round(dec_avg_ms * 1e3, 2),
+        "launches_timed": args.steps * L,
+    }
+    chunk_roof = None
+    if has_chunks:
+        flops = pa.chunk_flops(w.seq_lens, w.q_rows, w.window, w.num_q_heads, w.head_dim)
+        tflops = flops / (chunk_avg_ms / 1e3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[w.dtype]
+        chunk_roof = {
+            "kernel": "chunk_kernel",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": int(flops),
+            "chunk_kernel_avg_us": round(chunk_avg_ms * 1e3, 2),
+            "launches_timed": args.steps * L,
+        }
 
     result = {
         "metric": METRIC,
@@ -250,19 +297,12 @@ def main():
             "kv_bytes_per_layer": int(kv_layer),
             "seed": w.seed,
         },
-        "roofline": {
-            "kernel": "decode_kernel",
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "decode_kernel_avg_us": round(dec_avg_ms * 1e3, 2),
-            "launches_timed": len(dec_ms),
-        },
+        "roofline": chunk_roof if chunk_roof and chunk_avg_ms > dec_avg_ms else decode_roof,
         "device_error_bits": err_bits,
     }
+    if chunk_roof:
+        result["roofline_decode"] = decode_roof
+        result["roofline_chunk"] = chunk_roof
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         ref, cb = cpu_baseline(w, L, args.cpu_seconds)

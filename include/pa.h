@@ -171,6 +171,10 @@ pa_status pa_decode_attend(void* out, pa_dtype out_dtype, const void* q,
  * NULL, NULL switches the hook off.  Process-wide, not thread-safe. */
 void pa_set_decode_profile_events(void* before, void* after);
 
+/* The same hook around the chunk-row kernel launch (calls whose sequences include chunks
+ * of several query rows and whose cache dtype is F16 or BF16). */
+void pa_set_chunk_profile_events(void* before, void* after);
+
 /* Human-readable name of a status code (static storage). */
 const char* pa_status_string(pa_status s);
 

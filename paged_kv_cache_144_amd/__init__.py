@@ -27,7 +27,8 @@ BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_write_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_plan",
-           "pa_decode_attend", "pa_set_decode_profile_events", "pa_status_string",
+           "pa_decode_attend", "pa_set_decode_profile_events", "pa_set_chunk_profile_events",
+           "pa_status_string",
            "pa_pool_create", "pa_pool_destroy", "pa_seq_set_window", "pa_seq_append",
            "pa_seq_share_prefix", "pa_seq_free", "pa_seq_block_table", "pa_pool_block_tables",
            "pa_seq_len", "pa_pool_num_free", "pa_block_refcount")
@@ -69,6 +70,7 @@ def load():
         "pa_decode_attend": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32,
                                    i32, P, ctypes.c_size_t, P]),
         "pa_set_decode_profile_events": (None, [P, P]),
+        "pa_set_chunk_profile_events": (None, [P, P]),
         "pa_status_string": (ctypes.c_char_p, [i32]),
         "pa_pool_create": (i32, [i32, i32, P, i32, ctypes.POINTER(P)]),
         "pa_pool_destroy": (None, [P]),
@@ -208,12 +210,19 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, *, max_seq_len,
     return out
 
 
+def _ev(e):
+    return None if e is None else ctypes.c_void_p(e.cuda_event)
+
+
 def set_decode_profile_events(before=None, after=None) -> None:
     """pa_set_decode_profile_events with torch.cuda.Event objects (recorded once already so
     that their handles exist), or None to switch the hook off."""
-    lib = load()
-    h = (lambda e: None if e is None else ctypes.c_void_p(e.cuda_event))
-    lib.pa_set_decode_profile_events(h(before), h(after))
+    load().pa_set_decode_profile_events(_ev(before), _ev(after))
+
+
+def set_chunk_profile_events(before=None, after=None) -> None:
+    """pa_set_chunk_profile_events (see set_decode_profile_events)."""
+    load().pa_set_chunk_profile_events(_ev(before), _ev(after))
 
 
 def device_error_bits(workspace) -> int:
@@ -293,7 +302,7 @@ class Pool:
         return int(self._lib.pa_block_refcount(self._h, block))
 
 
-# ------------------------------------------------------------------ byte accounting
+# ------------------------------------------------------------------ work accounting
 def kv_bytes_read(seq_lens, q_rows, window, num_kv_heads, head_dim, elem_bytes) -> int:
     """Algorithmic KV bytes one attention layer reads: every attended position once, K and V,
     per KV head (a sliding window caps the positions a row can see)."""
@@ -303,3 +312,17 @@ def kv_bytes_read(seq_lens, q_rows, window, num_kv_heads, head_dim, elem_bytes) 
         lo = max(0, first - window + 1) if window > 0 else 0
         total += max(0, L - lo)
     return 2 * num_kv_heads * head_dim * elem_bytes * total
+
+
+def chunk_flops(seq_lens, q_rows, window, num_q_heads, head_dim) -> int:
+    """Algorithmic FLOPs of the chunk rows (sequences with more than one query row): per row,
+    per query head, per attended token, 2 * head_dim for q.K and 2 * head_dim for p.V."""
+    total = 0
+    for L, n in zip(np.asarray(seq_lens).tolist(), np.asarray(q_rows).tolist()):
+        if n < 2:
+            continue
+        for r in range(n):
+            p = L - n + r
+            lo = max(0, p - window + 1) if window > 0 else 0
+            total += max(0, p - lo + 1)
+    return 4 * head_dim * num_q_heads * total

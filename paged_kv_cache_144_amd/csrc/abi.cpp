@@ -138,8 +138,10 @@ size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
 
 namespace {
 
-// Profiling hook: hipEvents recorded around the decode kernel launch (caller-owned).
+// Profiling hooks: hipEvents recorded around the decode / chunk kernel launches
+// (caller-owned).
 hipEvent_t g_prof_before = nullptr, g_prof_after = nullptr;
+hipEvent_t g_chunk_before = nullptr, g_chunk_after = nullptr;
 
 pa_status build_args(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
                      const void* v_cache, const pa_cache_desc* desc,
@@ -203,7 +205,11 @@ pa_status run_attend(const DecodeArgs& a, int dtype, hipStream_t s) {
     if (pa::launch_decode(a, dtype, s) != hipSuccess) return PA_ERR_LAUNCH;
     if (g_prof_after && hipEventRecord(g_prof_after, s) != hipSuccess) return PA_ERR_LAUNCH;
     if (pa::launch_merge(a, s) != hipSuccess) return PA_ERR_LAUNCH;
+    if (a.chunk_rows > 0 && g_chunk_before && hipEventRecord(g_chunk_before, s) != hipSuccess)
+        return PA_ERR_LAUNCH;
     if (pa::launch_chunk(a, dtype, s) != hipSuccess) return PA_ERR_LAUNCH;
+    if (a.chunk_rows > 0 && g_chunk_after && hipEventRecord(g_chunk_after, s) != hipSuccess)
+        return PA_ERR_LAUNCH;
     return PA_OK;
 }
 
@@ -265,6 +271,11 @@ pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_
 void pa_set_decode_profile_events(void* before, void* after) {
     g_prof_before = (hipEvent_t)before;
     g_prof_after = (hipEvent_t)after;
+}
+
+void pa_set_chunk_profile_events(void* before, void* after) {
+    g_chunk_before = (hipEvent_t)before;
+    g_chunk_after = (hipEvent_t)after;
 }
 
 }  // extern "C"
