@@ -15,7 +15,12 @@ bandwidth on the decode rows' KV bytes, or, when chunked-prefill rows dominate, 
 kernel against the dense MFMA peak on its FLOPs.  `cpu_baseline` is the fp64 CPU oracle
 timed on the host cores on a bounded sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload opt13b|gqa|prefix_mixed|swa|tiny]
+In the parallel-sampling workload each layer's step also carries out the copy-on-write
+copies of the first decode step after the fork (pa_copy_blocks) before the slot write; the
+copy kernel is reported in `roofline_copy`.
+
+  python bench.py [--steps K] [--warmup W]
+                  [--workload opt13b|gqa|prefix_mixed|swa|parallel_sampling|tiny]
 """
 from __future__ import annotations
 
@@ -47,6 +52,10 @@ DESCRIPTIONS = {
     "swa": "Gemma-3-4B-shaped sliding-window decode: 32 seqs, 8 q / 4 KV heads, d=256, fp16 KV, "
            "window 1024, lengths U[4096,131072], 29 sliding layers",
     "tiny": "tiny paged decode: 4 seqs, lengths {1,17,100,33}, 4 heads, d=64, fp32, 1 layer",
+    "parallel_sampling": "OPT-13B-shaped parallel sampling, first decode step after the fork: "
+                         "16 prompts of U[64,2048] tokens x 4 samples (64 seqs), 40 q = 40 KV "
+                         "heads, d=128, fp16 KV, 16-token blocks; 3 of the 4 samples of a "
+                         "prompt copy its partly filled last block (copy-on-write), 40 layers",
 }
 
 
@@ -190,11 +199,18 @@ def main():
                   workspace=dw.workspace)
 
     has_chunks = bool((w.q_rows > 1).any()) and w.dtype in MFMA_PEAK_TFLOPS
+    copies = dw.step_copies
 
-    def step(events=None, cevents=None):
+    def step(events=None, cevents=None, xevents=None):
         pa.decode(dw.q, pools[0][0], pools[0][1], dw.block_tables, dw.seq_lens, float(w.scale),
                   step="plan", **common)
         for li, (kc, vc) in enumerate(pools):
+            if copies is not None:
+                if xevents is not None:
+                    xevents[li][0].record()
+                pa.copy_blocks(kc, vc, copies)
+                if xevents is not None:
+                    xevents[li][1].record()
             pa.write_kv(k_step, v_step, slot_step, kc, vc)
             if events is not None:
                 pa.set_decode_profile_events(*events[li])
@@ -222,17 +238,20 @@ def main():
 
     evs = event_pairs()
     cevs = event_pairs() if has_chunks else None
+    xevs = event_pairs() if copies is not None else None
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for k in range(args.steps):
-        step(evs[k], cevs[k] if cevs else None)
+        step(evs[k], cevs[k] if cevs else None, xevs[k] if xevs else None)
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     dec_avg_ms = float(np.mean([a.elapsed_time(b) for per in evs for a, b in per]))
     chunk_avg_ms = (float(np.mean([a.elapsed_time(b) for per in cevs for a, b in per]))
                     if cevs else 0.0)
+    copy_avg_ms = (float(np.mean([a.elapsed_time(b) for per in xevs for a, b in per]))
+                   if xevs else 0.0)
     err_bits = pa.device_error_bits(dw.workspace)
 
     step_s = total_ms / 1e3 / args.steps
@@ -273,6 +292,26 @@ def main():
             "launches_timed": args.steps * L,
         }
 
+    copy_roof = None
+    if copies is not None:
+        # each copied row of K and of V, per KV head, is read once and written once
+        cbytes = (4 * int(copies[:, 2].sum().item()) * w.num_kv_heads * w.head_dim
+                  * w.elem_bytes)
+        gbs = cbytes / (copy_avg_ms / 1e3) / 1e9
+        copy_roof = {
+            "kernel": "copy_blocks_kernel",
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": int(cbytes),
+            "copies_per_launch": int(copies.shape[0]),
+            "copy_kernel_avg_us": round(copy_avg_ms * 1e3, 2),
+            "launches_timed": args.steps * L,
+        }
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -303,6 +342,8 @@ def main():
     if chunk_roof:
         result["roofline_decode"] = decode_roof
         result["roofline_chunk"] = chunk_roof
+    if copy_roof:
+        result["roofline_copy"] = copy_roof
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         ref, cb = cpu_baseline(w, L, args.cpu_seconds)

@@ -47,7 +47,8 @@ typedef enum pa_status {
     PA_ERR_WORKSPACE = -5,      /* workspace NULL, too small or not 256-byte aligned       */
     PA_ERR_LAUNCH = -6,         /* the HIP runtime reported an error                       */
     PA_ERR_OUT_OF_BLOCKS = -7,  /* ledger: not enough free blocks (nothing was taken)      */
-    PA_ERR_SHARED_BLOCK = -8,   /* ledger: the append would write into a shared block      */
+    PA_ERR_SHARED_BLOCK = -8,   /* ledger: a copy-on-write would read a block that has     *
+                                 * writes pending in the current copy batch                */
     PA_ERR_BAD_SEQ = -9         /* ledger: unknown sequence, or one that must be empty     */
 } pa_status;
 
@@ -178,6 +179,29 @@ void pa_set_chunk_profile_events(void* before, void* after);
 /* Human-readable name of a status code (static storage). */
 const char* pa_status_string(pa_status s);
 
+/* ------------------------------------------------------------------ block copy
+ * pa_copy_blocks - carry out a batch of copy-on-write copies on the device.  Source: "vLLM
+ * and PagedAttention" notes (ghkdgus29.github.io), section on parallel sampling - when
+ * samples sharing a block write different tokens into it, the block is copied.
+ *
+ *   k_cache, v_cache (device) the pool, layout above; written in place.
+ *   desc          (host) pool description (any block_size here).
+ *   copies        (device) int32 [num_copies][3]: (src_block, dst_block, entries).  For
+ *                 every KV head, rows 0 .. entries-1 of block src (K and V) are copied to the
+ *                 same rows of block dst; rows entries.. of dst are not touched.
+ *   num_copies    >= 0; 0 launches nothing.
+ *   error_word    (device, nullable) int32; a triple with a block id outside
+ *                 [0, num_blocks) or entries outside [0, block_size] is skipped and sets
+ *                 bit 0 (value 1) here.
+ * All triples are applied at once: the destinations must be distinct and no destination
+ * may be the source of another triple of the same call (pa_pool_take_copies batches obey
+ * this); otherwise the contents of the blocks concerned are unspecified, but nothing
+ * outside them is read or written.  The copy is bit-exact.  Errors: PA_ERR_NULL,
+ * PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_LAUNCH. */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc,
+                         const int32_t* copies, int32_t num_copies, int32_t* error_word,
+                         void* stream);
+
 /* ------------------------------------------------------------------ host block ledger
  * A host-only ledger of one pool's blocks (no device memory).  Sources: "PagedAttention
  * deep dive" (donmain.dev), sections on splitting the KV cache into blocks (a block is
@@ -205,14 +229,40 @@ pa_status pa_seq_set_window(pa_pool* p, int64_t seq, int32_t window);
 
 /* Append n_tokens to `seq` (created on first use) and write each token's slot
  * (block * block_size + offset, or -1) to slots_out (host, n_tokens entries, nullable).
- * All or nothing: PA_ERR_OUT_OF_BLOCKS if the free blocks do not suffice (nothing is
- * taken), PA_ERR_SHARED_BLOCK if a token would land in a block another sequence also
- * references (copy-on-write is not provided). */
+ *
+ * Copy-on-write ("vLLM and PagedAttention" notes, ghkdgus29.github.io, section on parallel
+ * sampling; "PagedAttention deep dive", section on block sharing): if the first token lands
+ * in the sequence's partly filled last block while another sequence also references that
+ * block, the append first takes a fresh block, records the copy (old block, fresh block,
+ * entries the old block holds) in the pool's copy batch, and drops one reference from the
+ * old block; the sequence's table then points at the fresh block.  The last holder of a
+ * block writes in place.  The copy is taken before any new block of the same append.
+ *
+ * Copy batches: pa_pool_take_copies ends a batch.  The caller carries out a batch's copies
+ * (pa_copy_blocks) and then its slot writes (pa_write_kv) before the next batch's.  Because
+ * a batch's copies run all at once, an append whose copy would read a block that received
+ * slots or a copy in the current batch fails with PA_ERR_SHARED_BLOCK.
+ *
+ * All or nothing: PA_ERR_OUT_OF_BLOCKS if the free blocks do not suffice for the copy and
+ * the new blocks, PA_ERR_SHARED_BLOCK as above; either way nothing changes. */
 pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slots_out);
 
+/* `dst` (new or empty) becomes a second sample of `src` (parallel sampling): the same
+ * length, window and physical blocks, each block one reference more.  Blocks released by a
+ * window stay -1 in the copy of the table. */
+pa_status pa_seq_fork(pa_pool* p, int64_t dst, int64_t src);
+
+/* End the current copy batch: write its copies, in the order they were recorded, as
+ * (src_block, dst_block, entries) int32 triples to out (host, 3 * cap entries) and start a
+ * new batch.  *n receives the number of copies.  PA_ERR_SHAPE if cap is too small (nothing
+ * is taken; *n tells how many there are). */
+pa_status pa_pool_take_copies(pa_pool* p, int32_t* out, int32_t cap, int32_t* n);
+int32_t pa_pool_num_pending_copies(const pa_pool* p);
+
 /* `dst` (new or empty) begins with the first n_tokens of `src`, pointing at the same
- * physical blocks (each gets one more reference).  A shared system prompt or a forked
- * sample ("PagedAttention deep dive", section on block sharing). */
+ * physical blocks (each gets one more reference): a shared system prompt ("PagedAttention
+ * deep dive", section on block sharing).  A prefix that ends inside a block shares that
+ * block too; the first append of either sequence into it copies it (see pa_seq_append). */
 pa_status pa_seq_share_prefix(pa_pool* p, int64_t dst, int64_t src, int32_t n_tokens);
 
 /* Drop `seq`: one reference less on each of its blocks; blocks reaching zero are free. */

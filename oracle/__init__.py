@@ -6,7 +6,8 @@ anything here, and nothing here imports the library: the two share only the seed
 generators in ``workloads``.
 
 Pieces:
-  * ``ledger``   - block ledger model (on-demand blocks, reference counts, windows);
+  * ``ledger``   - block ledger model (on-demand blocks, reference counts, copy-on-write,
+    windows); ``copy_block`` carries out one recorded copy on host caches;
   * ``pa_oracle.c`` (built into ``liboracle.so``) - fp64 slot write and attention, paged
     and contiguous;
   * ``brute``    - an independent numpy version of the attention definition for tiny
@@ -117,6 +118,15 @@ def write_kv(k, v, slots, k_cache, v_cache, block_size: int, dtype: str) -> None
         raise ValueError(f"oracle_write_kv failed ({rc})")
 
 
+def copy_block(k_cache, v_cache, src: int, dst: int, n: int) -> None:
+    """Copy-on-write of one block: the first n entries of physical block src, for every KV
+    head, of K and of V, become those of block dst ("vLLM and PagedAttention" notes,
+    ghkdgus29.github.io, section on parallel sampling).  Entries n.. of dst are left as
+    they are: the sequence that now owns dst writes them itself."""
+    k_cache[dst, :, :n] = k_cache[src, :, :n]
+    v_cache[dst, :, :n] = v_cache[src, :, :n]
+
+
 def paged_attention(q, k_cache, v_cache, block_tables, seq_lens, scale, dtype: str, num_q_heads,
                     query_start_loc=None, window: int = 0, threads: int = 0) -> np.ndarray:
     """fp64 attention through block tables. q [R][Hq][d]; returns [R][Hq][d] float64."""
@@ -190,7 +200,7 @@ class Reference:
 
         self.w = w
         led = Ledger(w.free_order, w.block_size)
-        self.slots = run_script(led, w.script)
+        self.slots, self.copies = run_script(led, w.script)
         self.ledger = led
         B = w.num_seqs
         self.max_blocks = max(1, max(len(led.block_table(s)) for s in range(B)))
@@ -206,7 +216,11 @@ class Reference:
         self.k_cache = np.full(shape, nan_bits(w.dtype) if poison else 0, st)
         self.v_cache = np.full(shape, nan_bits(w.dtype) if poison else 0, st)
         for i, op in enumerate(w.script):
-            if isinstance(op, Append) and op.nv > 0:
+            if not isinstance(op, Append):
+                continue
+            for src, dst, n in self.copies[i]:
+                copy_block(self.k_cache, self.v_cache, src, dst, n)
+            if op.nv > 0:
                 sl = np.asarray(self.slots[i][-op.nv:], np.int64)
                 write_kv(w.k[op.off:op.off + op.nv], w.v[op.off:op.off + op.nv], sl,
                          self.k_cache, self.v_cache, w.block_size, w.dtype)

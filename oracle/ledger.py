@@ -15,6 +15,10 @@ What the pages fix, and where:
     PagedAttention", section on basic decoding, block size 4 walk-through);
   * blocks shared by several sequences carry a reference count (same notes, section on
     parallel sampling: two samples share physical blocks 7 and 1, each with count 2);
+  * when samples that share a partly filled block each write a different token into it,
+    that block is copied and the count drops; fully shared earlier blocks stay shared
+    (same section; "PagedAttention deep dive", donmain.dev, section on block sharing:
+    copy-on-write at the point where sequences diverge);
   * eviction is all-or-nothing per sequence (same notes, scheduling section);
   * a sliding-window layer only keeps the most recent W tokens (sotaaz.com, section on
     layer kinds).
@@ -23,8 +27,14 @@ Readings where the pages are silent (each listed in the design notes):
   * free blocks are handed out first-in first-out, starting from a given order; a block
     whose count drops to zero goes to the back of that queue, in logical-block order;
   * an append that needs more blocks than are free fails and takes nothing;
-  * appending into a block that another sequence also references is refused (no
-    copy-on-write yet);
+  * copy-on-write: an append that writes into the partly filled last block while another
+    sequence also references it first takes a fresh block (before any new block of the
+    same append), records the copy (old block, new block, entries held) and gives the old
+    block one reference less; the last remaining holder writes in place;
+  * copies are carried out in batches, all pairs of a batch at once, copies before the
+    batch's slot writes (``take_copies`` ends a batch).  A copy therefore may not read a
+    block that received slots or a copy in the same batch: such an append is refused
+    (SharedBlock) and takes nothing;
   * with a window W, after an append of n tokens to a sequence of length c, positions
     before c+n-W are not kept: their slot is -1, a block lying wholly before that point is
     released (table entry -1) and one never allocated stays -1.
@@ -54,6 +64,8 @@ class Ledger:
         self.table: dict[int, list[int]] = {}
         self.length: dict[int, int] = {}
         self.window: dict[int, int] = {}
+        self.pending: list[tuple[int, int, int]] = []   # copies not yet taken
+        self.touched: set[int] = set()     # blocks given slots or copies since the last take
 
     # -- queries -------------------------------------------------------------------
     def num_free(self) -> int:
@@ -82,6 +94,12 @@ class Ledger:
         self.length.setdefault(seq, 0)
         self.window[seq] = int(window)
 
+    def take_copies(self) -> list[tuple[int, int, int]]:
+        """End the batch: return its copies (src block, dst block, entries) in order."""
+        out, self.pending = self.pending, []
+        self.touched.clear()
+        return out
+
     def _release(self, block: int) -> None:
         self.ref[block] -= 1
         if self.ref[block] == 0:
@@ -102,16 +120,29 @@ class Ledger:
         release = [i for i in range(min(first_kept_blk, len(tab))) if tab[i] >= 0]
         # new logical blocks to open
         new_blks = [i for i in range(len(tab), n_blk_after) if i >= first_kept_blk]
-        # appending into the current partial last block: it must not be shared
+        # appending into the current partial last block while another sequence holds it:
+        # that block is copied first
+        cow = None
         if n > 0 and cur % self.bs != 0:
             last = cur // self.bs
             if last >= first_kept_blk and tab[last] >= 0 and self.ref[tab[last]] > 1:
-                raise SharedBlock(f"seq {seq}: block {tab[last]} is shared")
-        if len(new_blks) > len(self.free) + sum(1 for i in release if self.ref[tab[i]] == 1):
-            raise OutOfBlocks(f"seq {seq}: needs {len(new_blks)} blocks, {len(self.free)} free")
+                if tab[last] in self.touched:
+                    raise SharedBlock(f"seq {seq}: shared block {tab[last]} has writes pending")
+                cow = last
+        need = len(new_blks) + (cow is not None)
+        if need > len(self.free) + sum(1 for i in release if self.ref[tab[i]] == 1):
+            raise OutOfBlocks(f"seq {seq}: needs {need} blocks, {len(self.free)} free")
         for i in release:
             self._release(tab[i])
             tab[i] = -1
+        if cow is not None:
+            old = tab[cow]
+            b = self.free.popleft()
+            self.ref[b] = 1
+            self.ref[old] -= 1
+            tab[cow] = b
+            self.pending.append((old, b, cur - cow * self.bs))
+            self.touched.add(b)
         for i in range(len(tab), n_blk_after):
             if i in new_blks:
                 b = self.free.popleft()
@@ -127,7 +158,23 @@ class Ledger:
             else:
                 b = tab[p // self.bs]
                 slots.append(b * self.bs + p % self.bs)
+                self.touched.add(b)
         return slots
+
+    def fork(self, dst: int, src: int) -> None:
+        """``dst`` (new) becomes a copy of ``src``: its length, window and physical blocks."""
+        if self.table.get(dst) or self.length.get(dst, 0):
+            raise LedgerError(f"seq {dst} is not empty")
+        if src not in self.table or src == dst:
+            raise LedgerError(f"unknown sequence {src}")
+        tab = list(self.table[src])
+        for b in tab:
+            if b >= 0:
+                self.ref[b] += 1
+        self.table[dst] = tab
+        self.length[dst] = self.length[src]
+        if src in self.window:
+            self.window[dst] = self.window[src]
 
     def share_prefix(self, dst: int, src: int, n_tokens: int) -> None:
         """``dst`` (new) begins with the first n_tokens of ``src``, sharing its blocks."""
@@ -153,13 +200,20 @@ class Ledger:
 
 
 def run_script(ledger: Ledger, script):
-    """Apply a workload's ledger script; return {Append index: slots}."""
-    from workloads import Append, Free, SetWindow, SharePrefix
+    """Apply a workload's ledger script.  Returns ({Append index: slots},
+    {Append index: copies that append recorded}); a Flush ends a batch."""
+    from workloads import Append, Flush, Fork, Free, SetWindow, SharePrefix
 
-    slots = {}
+    slots, copies = {}, {}
     for i, op in enumerate(script):
         if isinstance(op, Append):
+            before = len(ledger.pending)
             slots[i] = ledger.append(op.seq, op.n)
+            copies[i] = list(ledger.pending[before:])
+        elif isinstance(op, Flush):
+            ledger.take_copies()
+        elif isinstance(op, Fork):
+            ledger.fork(op.dst, op.src)
         elif isinstance(op, SharePrefix):
             ledger.share_prefix(op.dst, op.src, op.n_tokens)
         elif isinstance(op, Free):
@@ -168,4 +222,4 @@ def run_script(ledger: Ledger, script):
             ledger.set_window(op.seq, op.window)
         else:  # pragma: no cover
             raise TypeError(op)
-    return slots
+    return slots, copies

@@ -26,12 +26,13 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
 BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares
-EXPORTS = ("pa_write_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_plan",
+EXPORTS = ("pa_write_kv", "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode", "pa_decode_plan",
            "pa_decode_attend", "pa_set_decode_profile_events", "pa_set_chunk_profile_events",
            "pa_status_string",
            "pa_pool_create", "pa_pool_destroy", "pa_seq_set_window", "pa_seq_append",
            "pa_seq_share_prefix", "pa_seq_free", "pa_seq_block_table", "pa_pool_block_tables",
-           "pa_seq_len", "pa_pool_num_free", "pa_block_refcount")
+           "pa_seq_len", "pa_pool_num_free", "pa_block_refcount", "pa_seq_fork",
+           "pa_pool_take_copies", "pa_pool_num_pending_copies")
 
 
 class PAError(RuntimeError):
@@ -62,6 +63,7 @@ def load():
     D = ctypes.POINTER(CacheDesc)
     sig = {
         "pa_write_kv": (i32, [P, P, P, i32, P, P, D, P]),
+        "pa_copy_blocks": (i32, [P, P, D, P, i32, P, P]),
         "pa_decode_workspace_size": (ctypes.c_size_t, [D, i32, i32, i32, i32]),
         "pa_decode": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32, i32, P,
                             ctypes.c_size_t, P]),
@@ -83,6 +85,9 @@ def load():
         "pa_seq_len": (i32, [P, i64]),
         "pa_pool_num_free": (i32, [P]),
         "pa_block_refcount": (i32, [P, i32]),
+        "pa_seq_fork": (i32, [P, i64, i64]),
+        "pa_pool_take_copies": (i32, [P, P, i32, ctypes.POINTER(i32)]),
+        "pa_pool_num_pending_copies": (i32, [P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -150,6 +155,26 @@ def write_kv(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
                          _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
                          ctypes.byref(desc), _stream(stream))
     _check(rc, "pa_write_kv")
+
+
+def copy_blocks(k_cache, v_cache, copies, error_word=None, stream=None) -> None:
+    """pa_copy_blocks: copies int32 [n][3] device tensor of (src, dst, entries) triples;
+    error_word an optional int32 device tensor of one element."""
+    torch = _torch()
+    lib = load()
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or k_cache.dim() != 4:
+        raise ValueError("k_cache and v_cache must match")
+    if copies.dim() != 2 or copies.shape[1] != 3:
+        raise ValueError("copies must be [n][3]")
+    if error_word is not None and error_word.numel() < 1:
+        raise ValueError("error_word must hold one int32")
+    desc = cache_desc(k_cache)
+    n = copies.shape[0]
+    rc = lib.pa_copy_blocks(_dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                            ctypes.byref(desc),
+                            _dev_ptr(copies, "copies", torch.int32) if n else None, n,
+                            _dev_ptr(error_word, "error_word", torch.int32), _stream(stream))
+    _check(rc, "pa_copy_blocks")
 
 
 def workspace_size(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len) -> int:
@@ -269,6 +294,21 @@ class Pool:
 
     def share_prefix(self, dst, src, n_tokens):
         _check(self._lib.pa_seq_share_prefix(self._h, dst, src, n_tokens), "pa_seq_share_prefix")
+
+    def fork(self, dst, src):
+        _check(self._lib.pa_seq_fork(self._h, dst, src), "pa_seq_fork")
+
+    def num_pending_copies(self) -> int:
+        return int(self._lib.pa_pool_num_pending_copies(self._h))
+
+    def take_copies(self) -> np.ndarray:
+        """End the copy batch; its (src, dst, entries) triples as int32 [n][3]."""
+        n = ctypes.c_int32()
+        out = np.empty((max(1, self.num_pending_copies()), 3), np.int32)
+        _check(self._lib.pa_pool_take_copies(self._h, out.ctypes.data_as(ctypes.c_void_p),
+                                             out.shape[0], ctypes.byref(n)),
+               "pa_pool_take_copies")
+        return out[:n.value].copy()
 
     def free(self, seq):
         _check(self._lib.pa_seq_free(self._h, seq), "pa_seq_free")

@@ -124,6 +124,26 @@ pa_status pa_write_kv(const void* k, const void* v, const int64_t* slot_mapping,
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc,
+                         const int32_t* copies, int32_t num_copies, int32_t* error_word,
+                         void* stream) {
+    if (!desc) return PA_ERR_NULL;
+    if (!dtype_ok(desc->dtype)) return PA_ERR_DTYPE;
+    if (desc->num_blocks <= 0 || desc->num_kv_heads <= 0 || desc->num_kv_heads > 65535 ||
+        desc->head_dim <= 0 || desc->block_size <= 0 || num_copies < 0)
+        return PA_ERR_SHAPE;
+    const int64_t row_bytes = (int64_t)desc->head_dim * dtype_bytes(desc->dtype);
+    if (row_bytes % 16 || row_bytes * desc->block_size > INT32_MAX / 2)
+        return PA_ERR_UNSUPPORTED;
+    if (num_copies == 0) return PA_OK;
+    if (!k_cache || !v_cache || !copies) return PA_ERR_NULL;
+    hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, copies, num_copies,
+                                          desc->num_blocks, desc->num_kv_heads,
+                                          desc->block_size, (int32_t)row_bytes, error_word,
+                                          (hipStream_t)stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
                                 int32_t total_q_rows, int32_t num_q_heads,
                                 int32_t max_seq_len) {

@@ -6,8 +6,9 @@
 // 4%); several tables may point at one block (section on block sharing).
 // "vLLM and PagedAttention" notes (ghkdgus29.github.io) - the manager counts the entries
 // in each block and frees them when the request ends (basic decoding), counts the
-// sequences referencing a block (parallel sampling), and evicts all of a sequence or none
-// of it (scheduling).  A sliding-window layer keeps only its last W tokens (sotaaz.com,
+// sequences referencing a block and copies a shared block when samples write different
+// tokens into it, while earlier blocks stay shared (parallel sampling), and evicts all of
+// a sequence or none of it (scheduling).  A sliding-window layer keeps only its last W tokens (sotaaz.com,
 // section on layer kinds).
 //
 // The CPU side owns this ledger and ships block tables to the GPU each step (velog.io,
@@ -36,9 +37,21 @@ struct pa_pool {
     std::deque<int32_t> free_q;        // first-in first-out
     std::vector<int32_t> ref;          // per physical block
     std::unordered_map<int64_t, Seq> seqs;
+    // Copy-on-write batch: copies recorded since the last take, as (src, dst, entries)
+    // triples, and the blocks that received slots or a copy in that time.  A copy may not
+    // read such a block: the batch's copies run all at once, before the batch's writes.
+    std::vector<int32_t> pending;
+    std::vector<uint8_t> touched;
+    std::vector<int32_t> touched_list;
 
     void release(int32_t b) {
         if (--ref[b] == 0) free_q.push_back(b);
+    }
+    void touch(int32_t b) {
+        if (!touched[b]) {
+            touched[b] = 1;
+            touched_list.push_back(b);
+        }
     }
 };
 
@@ -54,6 +67,7 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* 
     p->num_blocks = num_blocks;
     p->bs = block_size;
     p->ref.assign(num_blocks, 0);
+    p->touched.assign(num_blocks, 0);
     if (free_order) {
         if (free_order_len < 0 || free_order_len > num_blocks) {
             delete p;
@@ -99,15 +113,19 @@ pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slot
     const int64_t blocks_after = (end + bs - 1) / bs;
     const int64_t held = (int64_t)s.blocks.size();
 
-    // a token written into the current, partly filled last block must not hit a shared one
+    // a token written into the current, partly filled last block while another sequence
+    // holds it: that block is copied first (copy-on-write)
+    int64_t cow = -1;
     if (n_tokens > 0 && cur % bs != 0) {
         const int64_t last = cur / bs;
-        if (last >= first_kept_blk && s.blocks[last] >= 0 && p->ref[s.blocks[last]] > 1)
-            return PA_ERR_SHARED_BLOCK;
+        if (last >= first_kept_blk && s.blocks[last] >= 0 && p->ref[s.blocks[last]] > 1) {
+            if (p->touched[s.blocks[last]]) return PA_ERR_SHARED_BLOCK;
+            cow = last;
+        }
     }
-    // blocks to open (logical ids held..blocks_after-1 that hold a kept position) versus
-    // blocks available (free now, plus held blocks this append releases for good)
-    int64_t need = 0;
+    // blocks to open (logical ids held..blocks_after-1 that hold a kept position, plus the
+    // copy) versus blocks available (free now, plus held blocks this append releases)
+    int64_t need = cow >= 0 ? 1 : 0;
     for (int64_t i = held; i < blocks_after; ++i)
         if (i >= first_kept_blk) ++need;
     int64_t avail = (int64_t)p->free_q.size();
@@ -122,6 +140,18 @@ pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slot
             s.blocks[i] = -1;
         }
     }
+    if (cow >= 0) {
+        const int32_t old = s.blocks[cow];
+        const int32_t b = p->free_q.front();
+        p->free_q.pop_front();
+        p->ref[b] = 1;
+        --p->ref[old];
+        s.blocks[cow] = b;
+        p->pending.push_back(old);
+        p->pending.push_back(b);
+        p->pending.push_back((int32_t)(cur - cow * bs));
+        p->touch(b);
+    }
     for (int64_t i = held; i < blocks_after; ++i) {
         if (i >= first_kept_blk) {
             int32_t b = p->free_q.front();
@@ -133,13 +163,46 @@ pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slot
         }
     }
     s.len = end;
-    if (slots_out) {
-        for (int64_t pos = cur; pos < end; ++pos) {
-            int64_t slot = -1;
-            if (pos >= keep_from) slot = (int64_t)s.blocks[pos / bs] * bs + pos % bs;
-            slots_out[pos - cur] = slot;
+    for (int64_t pos = cur; pos < end; ++pos) {
+        int64_t slot = -1;
+        if (pos >= keep_from) {
+            const int32_t b = s.blocks[pos / bs];
+            p->touch(b);
+            slot = (int64_t)b * bs + pos % bs;
         }
+        if (slots_out) slots_out[pos - cur] = slot;
     }
+    return PA_OK;
+}
+
+pa_status pa_seq_fork(pa_pool* p, int64_t dst, int64_t src) {
+    if (!p) return PA_ERR_NULL;
+    auto it = p->seqs.find(src);
+    if (it == p->seqs.end() || dst == src) return PA_ERR_BAD_SEQ;
+    auto dit = p->seqs.find(dst);
+    if (dit != p->seqs.end() && (dit->second.len != 0 || !dit->second.blocks.empty()))
+        return PA_ERR_BAD_SEQ;
+    Seq copy = it->second;
+    for (int32_t b : copy.blocks)
+        if (b >= 0) ++p->ref[b];
+    p->seqs[dst] = std::move(copy);
+    return PA_OK;
+}
+
+int32_t pa_pool_num_pending_copies(const pa_pool* p) {
+    return p ? (int32_t)(p->pending.size() / 3) : 0;
+}
+
+pa_status pa_pool_take_copies(pa_pool* p, int32_t* out, int32_t cap, int32_t* n) {
+    if (!p || !n) return PA_ERR_NULL;
+    const int32_t count = (int32_t)(p->pending.size() / 3);
+    *n = count;
+    if (count > cap) return PA_ERR_SHAPE;
+    if (count && !out) return PA_ERR_NULL;
+    for (size_t i = 0; i < p->pending.size(); ++i) out[i] = p->pending[i];
+    p->pending.clear();
+    for (int32_t b : p->touched_list) p->touched[b] = 0;
+    p->touched_list.clear();
     return PA_OK;
 }
 

@@ -92,6 +92,9 @@ struct DecodeArgs {
 hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, int32_t n,
                            void* kc, void* vc, int32_t nb, int32_t hkv, int32_t d,
                            int32_t elem_bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(void* kc, void* vc, const int32_t* copies, int32_t n,
+                              int32_t nb, int32_t hkv, int32_t bs, int32_t row_bytes,
+                              int32_t* err, hipStream_t stream);
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);

@@ -1,5 +1,6 @@
-"""Drive a synthetic workload through the library: ledger script -> block tables and slots
-(host ``Pool``), then values -> KV pool (``pa_write_kv``), then ``pa_decode``.
+"""Drive a synthetic workload through the library: ledger script -> block tables, slots and
+copy batches (host ``Pool``), then copies and values -> KV pool (``pa_copy_blocks``,
+``pa_write_kv``), then ``pa_decode``.
 
 Used by the benchmark, the smoke check and the GPU tests.  Only torch device memory and
 copies happen here; the per-token work is in the HIP kernels.
@@ -8,7 +9,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import Pool, alloc_workspace, decode, write_kv
+from . import Pool, alloc_workspace, copy_blocks, decode, write_kv
 
 TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
 
@@ -37,17 +38,33 @@ class DeviceWorkload:
 
     def __init__(self, w, device="cuda", poison=True, write=True):
         import torch
-        from workloads import Append, Free, SetWindow, SharePrefix
+        from workloads import Append, Flush, Fork, Free, SetWindow, SharePrefix
 
         self.w = w
         self.device = device
         pool = Pool(w.num_blocks, w.block_size, w.free_order)
         slots_all = np.full(w.k.shape[0], -1, np.int64)
+        # batches of (copies [n][3], slots of the tokens written in the batch)
+        batches = []
+        cur = np.full(w.k.shape[0], -1, np.int64)
+
+        def end_batch():
+            nonlocal cur
+            copies = pool.take_copies()
+            if copies.size or (cur >= 0).any():
+                batches.append((copies, cur))
+            cur = np.full(w.k.shape[0], -1, np.int64)
+
         for op in w.script:
             if isinstance(op, Append):
                 s = pool.append(op.seq, op.n)
                 if op.nv:
                     slots_all[op.off:op.off + op.nv] = s[op.n - op.nv:]
+                    cur[op.off:op.off + op.nv] = s[op.n - op.nv:]
+            elif isinstance(op, Flush):
+                end_batch()
+            elif isinstance(op, Fork):
+                pool.fork(op.dst, op.src)
             elif isinstance(op, SharePrefix):
                 pool.share_prefix(op.dst, op.src, op.n_tokens)
             elif isinstance(op, Free):
@@ -56,8 +73,13 @@ class DeviceWorkload:
                 pool.set_window(op.seq, op.window)
             else:  # pragma: no cover
                 raise TypeError(op)
+        end_batch()
         self.pool = pool
         self.slots = slots_all
+        self.batches = [(torch.from_numpy(c).to(device) if c.size else None,
+                         torch.from_numpy(sl).to(device)) for c, sl in batches]
+        # copies of the last batch (the step that follows a fork), or None
+        self.step_copies = self.batches[-1][0] if self.batches else None
         B = w.num_seqs
         self.max_blocks = max(1, max(len(pool.block_table(s)) for s in range(B)))
         self.block_tables_np = pool.block_tables(np.arange(B), self.max_blocks, w.reserved_block)
@@ -84,7 +106,11 @@ class DeviceWorkload:
         return bool((self.w.q_rows != 1).any())
 
     def write(self, stream=None):
-        write_kv(self.k_new, self.v_new, self.slot_mapping, self.k_cache, self.v_cache, stream)
+        """Carry out every batch in order: its copies, then its slot writes."""
+        for copies, slots in self.batches:
+            if copies is not None:
+                copy_blocks(self.k_cache, self.v_cache, copies, stream=stream)
+            write_kv(self.k_new, self.v_new, slots, self.k_cache, self.v_cache, stream)
 
     def decode(self, out=None, out_dtype=None, k_cache=None, v_cache=None, stream=None, **kw):
         w = self.w

@@ -6,7 +6,7 @@ the token was never stored, e.g. before a sliding window).
 """
 import numpy as np
 
-from workloads import Append, Free, SetWindow, SharePrefix
+from workloads import Append, Flush, Fork, Free, SetWindow, SharePrefix
 
 
 def logical_rows(w):
@@ -19,7 +19,9 @@ def logical_rows(w):
             r.extend(range(op.off, op.off + op.nv))
         elif isinstance(op, SharePrefix):
             rows[op.dst] = list(rows[op.src][:op.n_tokens])
-        elif isinstance(op, Free):
+        elif isinstance(op, Fork):
+            rows[op.dst] = list(rows[op.src])
+        elif isinstance(op, (Free, Flush)):
             pass
         elif isinstance(op, SetWindow):
             rows.setdefault(op.seq, [])

@@ -91,23 +91,92 @@ def pin_walkthrough(orc):
 
 def pin_parallel_sampling(orc):
     led = orc.Ledger([7, 1, 3, 4, 5], 4)
-    led.append("A1", 7)
-    led.share_prefix("A2", "A1", 7)
+    led.append("A1", 7)                    # "Four score and seven years ago our"
+    led.fork("A2", "A1")
     for blk, ref in _rows("parallel_sampling_bs4.txt"):
         assert led.refcount(int(blk)) == int(ref)
     assert led.block_table("A1") == led.block_table("A2") == [7, 1]
-    # both samples would now write into shared block 1: refused until copy-on-write exists
+    # the prompt's slots are written before the samples diverge
+    assert led.take_copies() == []
+    s1 = led.append("A1", 1)               # "fathers"
+    s2 = led.append("A2", 1)               # "mothers"
+    t1, t2 = led.block_table("A1"), led.block_table("A2")
+    for lb, shared, before, ref in _rows("parallel_sampling_cow_bs4.txt"):
+        lb, shared, before, ref = int(lb), int(shared), int(before), int(ref)
+        assert (t1[lb] == t2[lb]) == bool(shared)
+        assert led.refcount(before) == ref
+        if shared:
+            assert t1[lb] == t2[lb] == before
+    # readings: the first writer copies into the next free block; the last holder writes
+    # in place; the copy carries the 3 prompt entries of logical block 1
+    assert t1 == [7, 3] and t2 == [7, 1]
+    assert led.take_copies() == [(1, 3, 3)]
+    assert s1 == [3 * 4 + 3] and s2 == [1 * 4 + 3]
+    assert led.refcount(3) == 1
+    # freeing one sample drops the counts; freeing both returns every block
+    led.free_seq("A2")
+    assert led.refcount(7) == 1 and led.refcount(1) == 0 and led.num_free() == 3
+    led.free_seq("A1")
+    assert led.num_free() == 5
+
+
+def pin_cow_rules(orc):
+    # a fork at a block boundary: the next token opens a block, nothing is copied
+    led = orc.Ledger(range(8), 4)
+    led.append(0, 8)
+    led.fork(1, 0)
+    led.take_copies()
+    led.append(1, 1)
+    assert led.take_copies() == [] and led.refcount(0) == 2 and led.refcount(1) == 2
+    assert led.block_table(1) == [0, 1, 2]
+    # a copy whose source block got slots in the same batch is refused and takes nothing
+    led = orc.Ledger(range(8), 4)
+    led.append(0, 6)
+    led.fork(1, 0)
+    before = (led.num_free(), led.block_table(1), led.refcount(1))
     try:
-        led.append("A1", 1)
+        led.append(1, 1)
     except orc.SharedBlock:
         pass
     else:
-        raise AssertionError("append into a shared block was accepted")
-    # freeing one sample drops the counts; freeing both returns the blocks
-    led.free_seq("A2")
-    assert led.refcount(7) == 1 and led.refcount(1) == 1 and led.num_free() == 3
-    led.free_seq("A1")
-    assert led.num_free() == 5
+        raise AssertionError("copy from a block with pending writes accepted")
+    assert (led.num_free(), led.block_table(1), led.refcount(1)) == before
+    assert led.take_copies() == []
+    led.append(1, 3)                       # now allowed: copy, then a new block
+    assert led.block_table(1) == [0, 2, 3] and led.take_copies() == [(1, 2, 2)]
+    # all or nothing: the copy needs a free block too
+    led = orc.Ledger(range(2), 4)
+    led.append(0, 6)
+    led.fork(1, 0)
+    led.take_copies()
+    try:
+        led.append(1, 1)
+    except orc.OutOfBlocks:
+        pass
+    else:
+        raise AssertionError("copy without a free block accepted")
+    assert led.refcount(1) == 2 and led.take_copies() == [] and led.block_table(1) == [0, 1]
+
+
+def pin_cow_attention(orc):
+    # every sample attends over the prompt plus its own token, as a private sequence would;
+    # the unused slots of every block hold NaN, so a missing or short copy shows
+    w = workloads.make("parallel_sampling", plens=[7, 16, 21, 40], samples=3, hq=4, hkv=2, d=64)
+    ref = orc.Reference(w)
+    got = ref.attention()
+    k_log, v_log, off, first = contiguous_inputs(w)
+    want = orc.contiguous_attention(w.q, k_log, v_log, off, first, w.seq_lens, w.scale, w.dtype,
+                                    w.num_q_heads, w.query_start_loc(), w.window)
+    assert np.isfinite(got).all()
+    assert np.array_equal(got, want)
+    # samples of one prompt share its full blocks and no longer share the partial one
+    for p, L in enumerate([7, 16, 21, 40]):
+        tabs = [list(ref.block_tables[p * 3 + j]) for j in range(3)]
+        full = L // 16
+        assert all(t[:full] == tabs[0][:full] for t in tabs)
+        assert len({t[full] for t in tabs}) == 3
+        for b in tabs[0][:full]:
+            assert ref.ledger.refcount(b) == 3
 
 
 def pin_all_or_nothing(orc):
@@ -420,7 +489,7 @@ def pin_nan_isolation(orc):
 
 
 ALL = [pin_kv_bytes, pin_kv_totals, pin_kv_read_bytes, pin_blocks_and_waste, pin_walkthrough,
-       pin_parallel_sampling, pin_all_or_nothing, pin_window_ledger, pin_widen, pin_write_kv,
+       pin_parallel_sampling, pin_cow_rules, pin_cow_attention, pin_all_or_nothing, pin_window_ledger, pin_widen, pin_write_kv,
        pin_one_token, pin_uniform, pin_two_tokens, pin_needle, pin_contiguous, pin_permutation,
        pin_sdpa, pin_brute, pin_window, pin_chunk_rows, pin_shared_prefix, pin_gqa_mapping,
        pin_nan_isolation]

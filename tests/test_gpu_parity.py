@@ -71,6 +71,11 @@ SMALL = [
     ("tiny", dict(d=128)),
     ("tiny", dict(dtype="bf16")),
     ("opt13b", dict(batch=6, lo=64, hi=700, dtype="f32")),
+    ("parallel_sampling", dict(plens=[7, 16, 21, 40, 100, 255], samples=3, hq=4, hkv=2, d=64,
+                               dtype="f32")),
+    ("parallel_sampling", dict(prompts=4, samples=4, lo=64, hi=700)),
+    ("parallel_sampling", dict(prompts=3, samples=5, hq=8, hkv=2, d=256, dtype="bf16", lo=20,
+                               hi=300)),
 ]
 
 
@@ -253,13 +258,13 @@ def test_write_kv_skips(torch, pa):
     assert torch.equal(dw.k_cache.view(torch.int32), k0.view(torch.int32))
 
 
-FULL = ["tiny", "opt13b", "gqa", "prefix_mixed", "swa"]
+FULL = ["tiny", "opt13b", "gqa", "prefix_mixed", "swa", "parallel_sampling"]
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_parity(torch, pa, orc, name):
-    """The five workloads at their full sizes, in the launch configuration the benchmark
+    """The workloads at their full sizes, in the launch configuration the benchmark
     times.  Decode rows are all checked; chunk rows on a sample (each sampled row is the
     one-row decode at its causal length, which the oracle pins)."""
     say("full", name, "generating")
@@ -285,6 +290,39 @@ def test_full_size_parity(torch, pa, orc, name):
         want = orc.paged_attention(q, ref.k_cache, ref.v_cache, bt, lens, w.scale, w.dtype,
                                    w.num_q_heads, None, w.window)
         check_close(out[qsl[s] + np.array(rows)], want, f"full {name} chunk seq {s}")
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f16", 128), ("bf16", 256), ("f16", 64)])
+def test_copy_blocks_direct(torch, pa, orc, dtype, d):
+    """pa_copy_blocks against the oracle's block copy on a random pool: full and empty
+    copies, every row count, and triples with bad ids or row counts (skipped, error bit 1,
+    nothing else touched).  Bit-exact, NaN patterns included."""
+    say("copy_blocks", dtype, d)
+    from paged_kv_cache_144_amd.runner import to_device, to_storage_np
+    rng = np.random.default_rng(d)
+    nb, hkv, bs = 50, 3, 16
+    shape = (nb, hkv, bs, d)
+    kc = workloads.to_storage(rng.standard_normal(np.prod(shape)), dtype).reshape(shape)
+    vc = workloads.to_storage(rng.standard_normal(np.prod(shape)), dtype).reshape(shape)
+    perm = rng.permutation(nb)
+    srcs, dsts = perm[:17], perm[17:34]               # distinct; no destination is a source
+    kc[srcs[0], :, 7:] = workloads.nan_bits(dtype)
+    rows = (np.arange(17) + bs) % (bs + 1)            # 16, 0, 1, .., 15
+    good = np.stack([srcs, dsts, rows], 1).astype(np.int32)
+    bad = np.array([[-1, perm[40], 3], [perm[41], nb, 3], [perm[42], perm[43], bs + 1],
+                    [perm[44], perm[45], -1]], np.int32)
+    triples = np.concatenate([good[:9], bad, good[9:]])
+    kd, vd = to_device(kc, dtype, "cuda"), to_device(vc, dtype, "cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pa.copy_blocks(kd, vd, torch.from_numpy(triples).cuda(), err)
+    pa.copy_blocks(kd, vd, torch.zeros((0, 3), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    want_k, want_v = kc.copy(), vc.copy()
+    for src, dst, n in good:
+        orc.copy_block(want_k, want_v, int(src), int(dst), int(n))
+    assert np.array_equal(to_storage_np(kd, dtype).view(np.uint8), want_k.view(np.uint8))
+    assert np.array_equal(to_storage_np(vd, dtype).view(np.uint8), want_v.view(np.uint8))
+    assert int(err.item()) == 1
 
 
 def test_plan_reused_across_layers(torch, pa, orc):

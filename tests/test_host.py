@@ -57,6 +57,15 @@ def test_host_validation_without_gpu(pa):
     bdt = pa.CacheDesc(10, 16, 4, 128, 7)
     assert lib.pa_write_kv(None, None, None, 1, None, None, ctypes.byref(bdt), None) == -3
     assert lib.pa_write_kv(None, None, None, 1, None, None, None, None) == -1
+    # pa_copy_blocks: any block size; checks before any device work
+    assert lib.pa_copy_blocks(None, None, None, None, 1, None, None) == -1
+    assert lib.pa_copy_blocks(None, None, ctypes.byref(ok), None, -1, None, None) == -2
+    assert lib.pa_copy_blocks(None, None, ctypes.byref(ok), None, 0, None, None) == 0
+    assert lib.pa_copy_blocks(None, None, ctypes.byref(ok), None, 2, None, None) == -1
+    assert lib.pa_copy_blocks(None, None, ctypes.byref(bdt), None, 2, None, None) == -3
+    assert lib.pa_copy_blocks(None, None, ctypes.byref(bad), None, 0, None, None) == 0
+    odd8 = pa.CacheDesc(10, 16, 4, 4, pa.PA_F16)            # 8-byte rows
+    assert lib.pa_copy_blocks(None, None, ctypes.byref(odd8), None, 1, None, None) == -4
 
 
 class PoolAdapter:
@@ -84,6 +93,12 @@ class PoolAdapter:
 
     def share_prefix(self, dst, src, n):
         self._pool.share_prefix(self._id(dst), self._id(src), n)
+
+    def fork(self, dst, src):
+        self._pool.fork(self._id(dst), self._id(src))
+
+    def take_copies(self):
+        return [tuple(int(x) for x in row) for row in self._pool.take_copies()]
 
     def free_seq(self, seq):
         self._pool.free(self._id(seq))
@@ -126,7 +141,8 @@ class _PoolAsOracle:
 
 
 @pytest.mark.parametrize("pin", [pins.pin_blocks_and_waste, pins.pin_walkthrough,
-                                 pins.pin_parallel_sampling, pins.pin_all_or_nothing,
+                                 pins.pin_parallel_sampling, pins.pin_cow_rules,
+                                 pins.pin_all_or_nothing,
                                  pins.pin_window_ledger], ids=lambda f: f.__name__)
 def test_pool_pins(pa, pin):
     pin(_PoolAsOracle(pa))
@@ -135,19 +151,28 @@ def test_pool_pins(pa, pin):
 @pytest.mark.parametrize("name,kw", [
     ("tiny", {}), ("opt13b", {}), ("gqa", {}),
     ("prefix_mixed", dict(chunk_lo=1024, chunk_hi=1100)),
-    ("swa", dict(batch=6)),
+    ("swa", dict(batch=6)), ("parallel_sampling", {}),
 ])
 def test_pool_matches_oracle_ledger(pa, orc, name, kw):
-    """Same script, same free order: identical tables, slots and reference counts."""
-    from workloads import Append, Free, SetWindow, SharePrefix
+    """Same script, same free order: identical tables, slots, copies and reference counts."""
+    from workloads import Append, Flush, Fork, Free, SetWindow, SharePrefix
     w = workloads.make(name, **kw)
     led = orc.Ledger(w.free_order, w.block_size)
     pool = pa.Pool(w.num_blocks, w.block_size, w.free_order)
+    n_copies = 0
     for op in w.script:
         if isinstance(op, Append):
             a = led.append(op.seq, op.n)
             b = pool.append(op.seq, op.n)
             assert np.array_equal(np.asarray(a, np.int64), b)
+        elif isinstance(op, Flush):
+            a = led.take_copies()
+            b = pool.take_copies()
+            assert np.array_equal(np.asarray(a, np.int32).reshape(-1, 3), b)
+            n_copies += len(a)
+        elif isinstance(op, Fork):
+            led.fork(op.dst, op.src)
+            pool.fork(op.dst, op.src)
         elif isinstance(op, SharePrefix):
             led.share_prefix(op.dst, op.src, op.n_tokens)
             pool.share_prefix(op.dst, op.src, op.n_tokens)
@@ -162,6 +187,76 @@ def test_pool_matches_oracle_ledger(pa, orc, name, kw):
         assert led.seq_len(s) == pool.seq_len(s)
     assert led.num_free() == pool.num_free()
     for b in range(w.num_blocks):
+        assert led.refcount(b) == pool.refcount(b)
+    if name == "parallel_sampling":
+        # 3 of every 4 samples copy the prompt's partial last block
+        partial = int(sum(1 for op in w.script if isinstance(op, Append) and op.n > 1
+                          and op.n % w.block_size))
+        assert n_copies == partial * (w.meta["samples"] - 1) > 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pool_random_scripts_match_oracle(pa, orc, seed):
+    """Random appends, forks, shares, frees, windows and batch ends on a small pool: the C++
+    ledger and the oracle ledger agree on every result, refusal included."""
+    rng = np.random.default_rng(seed)
+    nb = 40
+    order = rng.permutation(nb).tolist()
+    led = orc.Ledger(order, 4)
+    pool = pa.Pool(nb, 4, order)
+    live = []
+    next_id = 0
+    for _ in range(400):
+        r = rng.random()
+        if r < 0.45 or not live:
+            seq = int(rng.choice(live)) if live and rng.random() < 0.8 else next_id
+            n = int(rng.integers(0, 7))
+            try:
+                a = led.append(seq, n)
+                ea = None
+            except orc.LedgerError as e:
+                a, ea = None, type(e).__name__
+            try:
+                b = pool.append(seq, n).tolist()
+                eb = None
+            except pa.PAError as e:
+                b, eb = None, {-7: "OutOfBlocks", -8: "SharedBlock"}.get(e.code, e.code)
+            assert (a, ea) == (b, eb)
+            if seq == next_id and ea is None:
+                live.append(seq)
+                next_id += 1
+        elif r < 0.6:
+            src = int(rng.choice(live))
+            led.fork(next_id, src)
+            pool.fork(next_id, src)
+            live.append(next_id)
+            next_id += 1
+        elif r < 0.68:
+            src = int(rng.choice(live))
+            n = int(rng.integers(0, led.seq_len(src) + 1))
+            ok = all(b >= 0 for b in led.block_table(src)[:-(-n // 4)])
+            if ok:
+                led.share_prefix(next_id, src, n)
+                pool.share_prefix(next_id, src, n)
+                live.append(next_id)
+                next_id += 1
+        elif r < 0.78:
+            seq = live.pop(int(rng.integers(0, len(live))))
+            led.free_seq(seq)
+            pool.free(seq)
+        elif r < 0.8:
+            led.set_window(next_id, int(rng.integers(1, 12)))
+            pool.set_window(next_id, led.window[next_id])
+            live.append(next_id)
+            next_id += 1
+        else:
+            a = led.take_copies()
+            assert np.array_equal(np.asarray(a, np.int32).reshape(-1, 3), pool.take_copies())
+        assert led.num_free() == pool.num_free()
+    for s in live:
+        assert led.block_table(s) == pool.block_table(s)
+        assert led.seq_len(s) == pool.seq_len(s)
+    for b in range(nb):
         assert led.refcount(b) == pool.refcount(b)
 
 

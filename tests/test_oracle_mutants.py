@@ -41,8 +41,15 @@ PY_MUTANTS = {
     "slot_offset": ("slots.append(b * self.bs + p % self.bs)", "slots.append(b * self.bs + (p + 1) % self.bs)"),
     "keep_off_by_one": ("keep_from = max(0, end - win) if win > 0 else 0",
                         "keep_from = max(0, end - win + 1) if win > 0 else 0"),
-    "partial_alloc": ("        if len(new_blks) > len(self.free) +", "        if len(new_blks) > 10**9 +"),
+    "partial_alloc": ("        if need > len(self.free) +", "        if need > 10**9 +"),
     "shared_write_ok": ("and self.ref[tab[last]] > 1:", "and self.ref[tab[last]] > 2:"),
+    "cow_no_copy": ("            self.pending.append((old, b, cur - cow * self.bs))\n",
+                    "            pass\n"),
+    "cow_short_copy": ("cur - cow * self.bs))", "cur - cow * self.bs - 1))"),
+    "cow_no_decref": ("            self.ref[old] -= 1\n", "            pass\n"),
+    "cow_pending_ignored": ("if tab[last] in self.touched:", "if False:"),
+    "fork_no_ref": ("                self.ref[b] += 1\n        self.table[dst] = tab",
+                    "                pass\n        self.table[dst] = tab"),
 }
 
 

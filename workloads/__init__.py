@@ -35,7 +35,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
-    "DTYPES", "Append", "SharePrefix", "Free", "SetWindow", "Workload",
+    "DTYPES", "Append", "SharePrefix", "Fork", "Flush", "Free", "SetWindow", "Workload",
     "make", "CONFIG_NAMES", "normal", "to_storage", "nan_bits",
 ]
 
@@ -135,6 +135,20 @@ class SharePrefix:
 
 
 @dataclass(frozen=True)
+class Fork:
+    """``dst`` (new, empty) becomes a second sample of ``src``: same length, same window,
+    same physical blocks (each one reference more)."""
+    dst: int
+    src: int
+
+
+@dataclass(frozen=True)
+class Flush:
+    """End of a step: the block copies and slot writes recorded since the previous Flush are
+    carried out (copies first, then writes) before anything later."""
+
+
+@dataclass(frozen=True)
 class Free:
     seq: int
 
@@ -191,7 +205,7 @@ class Workload:
         return out
 
 
-CONFIG_NAMES = ("tiny", "opt13b", "gqa", "prefix_mixed", "swa")
+CONFIG_NAMES = ("tiny", "opt13b", "gqa", "prefix_mixed", "swa", "parallel_sampling")
 
 
 def _values(seed, n_tok, hkv, d, dtype, stream_k=2, stream_v=3):
@@ -339,6 +353,46 @@ def make(name: str, seed: int | None = None, **over) -> Workload:
         q = _queries(seed, B, 8, 256, dt)
         return Workload("swa", seed, dt, 8, 4, 256, bs, nb, lens, np.ones(B, np.int32), W,
                         np.float32(1.0 / math.sqrt(256)), 29, free_order, script, k, v, q)
+
+    if name == "parallel_sampling":
+        # OPT-13B shape; every prompt is prefilled, then forked into `samples` samples that
+        # each append their own first token (the first decode step after the fork)
+        seed = 7 if seed is None else seed
+        rng = np.random.default_rng(np.random.SeedSequence(entropy=seed, spawn_key=(0,)))
+        bs = 16
+        P = over.get("prompts", 16)
+        n = over.get("samples", 4)
+        hq, hkv, d = over.get("hq", 40), over.get("hkv", 40), over.get("d", 128)
+        plen = rng.integers(over.get("lo", 64), over.get("hi", 2048) + 1, size=P)
+        if "plens" in over:
+            plen = np.asarray(over["plens"], np.int64)
+            P = plen.size
+        B = P * n
+        # every sample may take one block of its own (a copy or a new block)
+        need = int(sum(-(-int(L) // bs) for L in plen)) + B
+        nb = _pool_size(need)
+        free_order = rng.permutation(nb - 1).astype(np.int32)
+        script, off = [], 0
+        for p in range(P):
+            script.append(Append(p * n, int(plen[p]), int(plen[p]), off))
+            off += int(plen[p])
+        script.append(Flush())
+        for p in range(P):
+            for j in range(1, n):
+                script.append(Fork(p * n + j, p * n))
+        for s in range(B):
+            script.append(Append(s, 1, 1, off))
+            off += 1
+        script.append(Flush())
+        dt = over.get("dtype", "f16")
+        k, v = _values(seed, off, hkv, d, dt)
+        q = _queries(seed, B, hq, d, dt)
+        lens = (np.repeat(plen, n) + 1).astype(np.int32)
+        w = Workload("parallel_sampling", seed, dt, hq, hkv, d, bs, nb, lens,
+                     np.ones(B, np.int32), 0, np.float32(1.0 / math.sqrt(d)),
+                     over.get("layers", 40), free_order, script, k, v, q)
+        w.meta.update(prompts=P, samples=n)
+        return w
 
     if name == "rows":
         # test-sized mixed batch with free shapes: sequence s has lens[s] context tokens and
