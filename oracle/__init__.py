@@ -12,6 +12,7 @@ Pieces:
     and contiguous;
   * ``brute``    - an independent numpy version of the attention definition for tiny
     inputs;
+  * ``q8``       - the 8-bit cache: quantizer, tile layout, copies, decoding;
   * ``kv_bytes_per_token`` / ``kv_read_bytes`` - the pages' KV byte accounting.
 Every function is pinned by ``tests/test_oracle_pins.py`` to what the pages and plain
 mathematics fix.
@@ -25,6 +26,7 @@ import subprocess
 
 import numpy as np
 
+from . import q8  # noqa: F401
 from .ledger import Ledger, LedgerError, OutOfBlocks, SharedBlock, run_script  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -168,13 +170,17 @@ def contiguous_attention(q, k_log, v_log, tok_off, first_pos, seq_lens, scale, d
 
 
 # ------------------------------------------------------------------ byte accounting
-def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: int,
+                       scale_group: int = 0) -> int:
     """KV cache bytes one token takes: K and V, per KV head, per layer.
 
     The SOSP'23 notes write it as 2 x H x L x B with H the hidden size (KV-size section,
     ghkdgus29.github.io); per-model pages write 2 x KV heads x head size x bytes per layer
-    (sotaaz.com, section on layer kinds).  With H = KV heads x head size the two agree."""
-    return 2 * num_layers * num_kv_heads * head_dim * elem_bytes
+    (sotaaz.com, section on layer kinds).  With H = KV heads x head size the two agree.
+    With scale_group = g > 0 (an 8-bit cache), every g values also carry one 2-byte scale
+    (sotaaz.com, KV-cache measurements, planning notes of the full-attention section)."""
+    row = head_dim * elem_bytes + (2 * (head_dim // scale_group) if scale_group else 0)
+    return 2 * num_layers * num_kv_heads * row
 
 
 def tokens_read(seq_len: int, q_rows: int, window: int) -> int:
@@ -185,10 +191,11 @@ def tokens_read(seq_len: int, q_rows: int, window: int) -> int:
     return max(0, last - lo + 1)
 
 
-def kv_read_bytes(seq_lens, q_rows, window, num_kv_heads, head_dim, elem_bytes) -> int:
+def kv_read_bytes(seq_lens, q_rows, window, num_kv_heads, head_dim, elem_bytes,
+                  scale_group: int = 0) -> int:
     """Algorithmic KV bytes one layer of attention reads (each attended token once)."""
     n = sum(tokens_read(int(L), int(r), window) for L, r in zip(seq_lens, q_rows))
-    return 2 * num_kv_heads * head_dim * elem_bytes * n
+    return kv_bytes_per_token(1, num_kv_heads, head_dim, elem_bytes, scale_group) * n
 
 
 # ------------------------------------------------------------------ whole workload
@@ -196,7 +203,7 @@ class Reference:
     """The oracle's view of a workload: its tables, slots, caches and outputs."""
 
     def __init__(self, w, threads: int = 0, poison: bool = True):
-        from workloads import DTYPES, Append, nan_bits
+        from workloads import ACT, DTYPES, Append, nan_bits
 
         self.w = w
         led = Ledger(w.free_order, w.block_size)
@@ -211,20 +218,43 @@ class Reference:
             row = np.array(t, np.int32)
             row[row < 0] = fill
             self.block_tables[s, :len(t)] = row
-        st, _ = DTYPES[w.dtype]
+        self.q8 = w.dtype in ACT
         shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
-        self.k_cache = np.full(shape, nan_bits(w.dtype) if poison else 0, st)
-        self.v_cache = np.full(shape, nan_bits(w.dtype) if poison else 0, st)
+        if self.q8:
+            # tile pools of codes and scales; poison 0xFF decodes to NaN
+            self.k_cache = q8.empty_cache(*shape[:2], w.head_dim, w.block_size,
+                                          0xFF if poison else 0)
+            self.v_cache = q8.empty_cache(*shape[:2], w.head_dim, w.block_size,
+                                          0xFF if poison else 0)
+        else:
+            st, _ = DTYPES[w.dtype]
+            self.k_cache = np.full(shape, nan_bits(w.dtype) if poison else 0, st)
+            self.v_cache = np.full(shape, nan_bits(w.dtype) if poison else 0, st)
         for i, op in enumerate(w.script):
             if not isinstance(op, Append):
                 continue
             for src, dst, n in self.copies[i]:
-                copy_block(self.k_cache, self.v_cache, src, dst, n)
+                (q8.copy_block if self.q8 else copy_block)(self.k_cache, self.v_cache, src, dst, n)
             if op.nv > 0:
                 sl = np.asarray(self.slots[i][-op.nv:], np.int64)
-                write_kv(w.k[op.off:op.off + op.nv], w.v[op.off:op.off + op.nv], sl,
-                         self.k_cache, self.v_cache, w.block_size, w.dtype)
+                kr, vr = w.k[op.off:op.off + op.nv], w.v[op.off:op.off + op.nv]
+                if self.q8:
+                    q8.write_kv(widen(kr, w.act).astype(np.float32),
+                                widen(vr, w.act).astype(np.float32), sl, self.k_cache,
+                                self.v_cache)
+                else:
+                    write_kv(kr, vr, sl, self.k_cache, self.v_cache, w.block_size, w.dtype)
         self.threads = threads
+        self._decoded = None
+
+    def _attention_inputs(self, q):
+        """(q, k_cache, v_cache, dtype) for the attention definition.  An 8-bit cache is
+        decoded to float32 (exactly) and q widened to float32 (exactly)."""
+        if not self.q8:
+            return q, self.k_cache, self.v_cache, self.w.dtype
+        if self._decoded is None:
+            self._decoded = (q8.dequantize_cache(self.k_cache), q8.dequantize_cache(self.v_cache))
+        return (widen(q, self.w.act).astype(np.float32), *self._decoded, "f32")
 
     def write_batches(self):
         """(slots, k, v) triples in script order, exactly what the GPU side must write."""
@@ -239,13 +269,13 @@ class Reference:
         w = self.w
         qsl = w.query_start_loc()
         if seqs is None:
-            return paged_attention(w.q, self.k_cache, self.v_cache, self.block_tables,
-                                   w.seq_lens, w.scale, w.dtype, w.num_q_heads, qsl, w.window,
-                                   self.threads)
+            q, kc, vc, dt = self._attention_inputs(w.q)
+            return paged_attention(q, kc, vc, self.block_tables, w.seq_lens, w.scale, dt,
+                                   w.num_q_heads, qsl, w.window, self.threads)
         seqs = np.asarray(seqs)
         rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs])
         sub_qsl = np.zeros(seqs.size + 1, np.int32)
         np.cumsum(w.q_rows[seqs], out=sub_qsl[1:])
-        return paged_attention(w.q[rows], self.k_cache, self.v_cache, self.block_tables[seqs],
-                               w.seq_lens[seqs], w.scale, w.dtype, w.num_q_heads, sub_qsl,
-                               w.window, self.threads)
+        q, kc, vc, dt = self._attention_inputs(w.q[rows])
+        return paged_attention(q, kc, vc, self.block_tables[seqs], w.seq_lens[seqs], w.scale,
+                               dt, w.num_q_heads, sub_qsl, w.window, self.threads)

@@ -345,13 +345,15 @@ class Pool:
 # ------------------------------------------------------------------ work accounting
 def kv_bytes_read(seq_lens, q_rows, window, num_kv_heads, head_dim, elem_bytes) -> int:
     """Algorithmic KV bytes one attention layer reads: every attended position once, K and V,
-    per KV head (a sliding window caps the positions a row can see)."""
+    per KV head (a sliding window caps the positions a row can see).  elem_bytes is the
+    cache's bytes per element: 4, 2, or 17/16 for an 8-bit cache (a 2-byte scale per 32
+    one-byte codes)."""
     total = 0
     for L, n in zip(np.asarray(seq_lens).tolist(), np.asarray(q_rows).tolist()):
         first = L - n                       # position of the first query row
         lo = max(0, first - window + 1) if window > 0 else 0
         total += max(0, L - lo)
-    return 2 * num_kv_heads * head_dim * elem_bytes * total
+    return int(round(2 * num_kv_heads * head_dim * elem_bytes * total))
 
 
 def chunk_flops(seq_lens, q_rows, window, num_q_heads, head_dim) -> int:

@@ -47,6 +47,22 @@ def pin_kv_totals(orc):
         assert total == int(mib) * 2**20, (model, ctx, total / 2**20, mib)
 
 
+def pin_kv_q8_bytes(orc):
+    # 32 one-byte codes plus one 2-byte scale per 32 values: 34/64 of a 16-bit cache
+    for case, m16, m8, exact in _rows("kv_q8_mib.txt"):
+        if int(exact):
+            # Qwen3-8B: 36 layers, 8 KV heads, head_dim 128, 32K tokens
+            b16 = orc.kv_bytes_per_token(36, 8, 128, 2) * 32768
+            b8 = orc.kv_bytes_per_token(36, 8, 128, 1, scale_group=32) * 32768
+            assert (b16, b8) == (int(m16) * 2**20, int(m8) * 2**20), case
+            assert round(100 * b8 / b16, 1) == 53.1
+        else:
+            for d in (128, 256, 576):
+                ratio = orc.kv_bytes_per_token(1, 1, d, 1, 32) / orc.kv_bytes_per_token(1, 1, d, 2)
+                assert round(int(m16) * ratio) == int(m8), (case, d)
+    assert orc.kv_read_bytes([100, 4096], [1, 1], 1024, 4, 256, 1, 32) == 2 * 4 * 272 * 1124
+
+
 def pin_kv_read_bytes(orc):
     # one decode row reads every context token once; a window caps it at W
     assert orc.tokens_read(100, 1, 0) == 100
@@ -55,6 +71,76 @@ def pin_kv_read_bytes(orc):
     # chunk rows: the union of their ranges is the whole context
     assert orc.tokens_read(3000, 512, 0) == 3000
     assert orc.kv_read_bytes([100, 4096], [1, 1], 1024, 4, 256, 2) == 4096 * (100 + 1024)
+
+
+# ------------------------------------------------------------------ the 8-bit cache
+def pin_q8_grid(orc):
+    # values already on a group's grid (scale a power of two, largest |code| 127) come back
+    # exactly, with that scale; each group has its own scale
+    rng = np.random.default_rng(5)
+    codes = rng.integers(-127, 128, size=(6, 128)).astype(np.int8)
+    codes[:, ::32] = np.where(rng.random((6, 4)) < 0.5, 127, -127)
+    exps = rng.integers(-12, 6, size=(6, 4))
+    scales = np.ldexp(1.0, exps).astype(np.float16)
+    x = (codes.reshape(6, 4, 32) * scales[..., None].astype(np.float32)).reshape(6, 128)
+    c, s = orc.q8.quantize(x.astype(np.float32))
+    assert np.array_equal(c, codes) and np.array_equal(s, scales)
+    assert np.array_equal(orc.q8.dequantize(c, s), x.astype(np.float64))
+
+
+def pin_q8_rounding(orc):
+    rng = np.random.default_rng(6)
+    # magnitudes whose scales are normal fp16 numbers (>= 2^-14)
+    x = (rng.standard_normal((200, 64)) * np.exp(rng.uniform(-4, 6, (200, 1)))).astype(np.float32)
+    c, s = orc.q8.quantize(x)
+    sf = s.astype(np.float64)
+    err = np.abs(orc.q8.dequantize(c, s) - x).reshape(200, 2, 32)
+    # nearest code: at most half a step away (plus the fp32 rounding of x / s)
+    assert np.all(err <= sf[..., None] * (0.5 + 1e-5))
+    # the scale is the group's largest |x| / 127 rounded to fp16, so the largest code is 127
+    assert np.all(np.abs(c.reshape(200, 2, 32)).max(-1) == 127)
+    amax = np.abs(x.reshape(200, 2, 32)).max(-1)
+    assert np.all(np.abs(sf - amax / 127) <= amax / 127 * 2.0**-11)
+    # symmetric, half-way cases to even, zero groups, saturation
+    c2, s2 = orc.q8.quantize(-x)
+    assert np.array_equal(c2, -c) and np.array_equal(s2, s)
+    half = np.zeros((1, 32), np.float32)
+    half[0, :4] = [127.0, 2.5, -3.5, 0.5]
+    assert orc.q8.quantize(half)[0][0, :4].tolist() == [127, 2, -4, 0]
+    z = orc.q8.quantize(np.zeros((2, 32), np.float32))
+    assert not z[0].any() and not z[1].astype(np.float32).any()
+    # subnormal scales are coarser (codes may saturate), but stay close to the value
+    tiny = (rng.standard_normal((20, 32)) * 1e-4).astype(np.float32)
+    ct, st = orc.q8.quantize(tiny)
+    amx = np.abs(tiny).max(-1, keepdims=True)
+    assert float(st.max()) < 2.0**-14
+    assert np.all(np.abs(orc.q8.dequantize(ct, st) - tiny) <= 0.25 * amx)
+    big = np.full((1, 32), 1e9, np.float32)
+    cb, sb = orc.q8.quantize(big)
+    assert float(sb[0, 0]) == 65504.0 and np.all(cb == 127)
+
+
+def pin_q8_paged(orc):
+    # paged attention over the 8-bit pool equals plain attention over each token's own
+    # quantized-then-decoded rows (no table, no tile): the tile layout, the scatter and the
+    # copy-on-write of codes and scales; free and unused slots decode to NaN
+    cases = [("tiny", dict(dtype="q8_f16", d=64)), ("tiny", dict(dtype="q8_bf16", d=128)),
+             ("swa", dict(batch=3, lo=50, hi=120, window=40, dtype="q8_f16")),
+             ("parallel_sampling", dict(plens=[7, 16, 21, 40], samples=3, hq=4, hkv=2, d=64,
+                                        dtype="q8_bf16"))]
+    for name, kw in cases:
+        w = workloads.make(name, **kw)
+        got = orc.Reference(w).attention()
+        k, v, off, first = contiguous_inputs(w)
+        kd = np.stack([orc.q8.dequantize(*orc.q8.quantize(orc.widen(r, w.act).astype(np.float32)))
+                       for r in k]).astype(np.float32) if len(k) else k
+        vd = np.stack([orc.q8.dequantize(*orc.q8.quantize(orc.widen(r, w.act).astype(np.float32)))
+                       for r in v]).astype(np.float32) if len(v) else v
+        q = orc.widen(w.q, w.act).astype(np.float32)
+        want = orc.contiguous_attention(q, kd, vd, off, first, w.seq_lens, w.scale, "f32",
+                                        w.num_q_heads, w.query_start_loc(), w.window)
+        assert np.isfinite(got).all(), name
+        assert np.array_equal(got, want), name
 
 
 # ------------------------------------------------------------------ the block ledger
@@ -488,7 +574,8 @@ def pin_nan_isolation(orc):
         assert np.array_equal(out, out0)
 
 
-ALL = [pin_kv_bytes, pin_kv_totals, pin_kv_read_bytes, pin_blocks_and_waste, pin_walkthrough,
+ALL = [pin_kv_bytes, pin_kv_totals, pin_kv_q8_bytes, pin_kv_read_bytes, pin_q8_grid,
+       pin_q8_rounding, pin_q8_paged, pin_blocks_and_waste, pin_walkthrough,
        pin_parallel_sampling, pin_cow_rules, pin_cow_attention, pin_all_or_nothing, pin_window_ledger, pin_widen, pin_write_kv,
        pin_one_token, pin_uniform, pin_two_tokens, pin_needle, pin_contiguous, pin_permutation,
        pin_sdpa, pin_brute, pin_window, pin_chunk_rows, pin_shared_prefix, pin_gqa_mapping,

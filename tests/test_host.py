@@ -280,11 +280,16 @@ def test_pool_errors(pa):
 
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("opt13b", dict(batch=5)),
                                      ("prefix_mixed", dict(batch=4, chunks=2, chunk_rows=7)),
-                                     ("swa", dict(batch=4))])
+                                     ("swa", dict(batch=4)), ("opt13b", dict(dtype="q8_f16")),
+                                     ("swa", dict(batch=4, dtype="q8_f16"))])
 def test_kv_bytes_matches_oracle(pa, orc, name, kw):
     w = workloads.make(name, **kw)
     a = pa.kv_bytes_read(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim,
                          w.elem_bytes)
-    b = orc.kv_read_bytes(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim,
-                          w.elem_bytes)
+    if w.dtype in workloads.ACT:
+        b = orc.kv_read_bytes(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim, 1,
+                              scale_group=32)
+    else:
+        b = orc.kv_read_bytes(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim,
+                              w.elem_bytes)
     assert a == b

@@ -1,6 +1,7 @@
 """Planted mistakes in copies of the oracle must each fail at least one pin (CPU only).
 
-Each mutant is a textual change to a copy of ``oracle/pa_oracle.c`` or ``oracle/ledger.py``:
+Each mutant is a textual change to a copy of ``oracle/pa_oracle.c``, ``oracle/ledger.py`` or
+``oracle/q8.py``:
 a dropped term, a wrong sign or index, a transposed operand.  The real oracle is untouched.
 """
 import importlib.util
@@ -53,6 +54,18 @@ PY_MUTANTS = {
 }
 
 
+Q8_MUTANTS = {
+    "q8_qmax": ("QMAX = 127\n", "QMAX = 126\n"),
+    "q8_truncate": ("np.rint(r.astype(np.float32))", "np.trunc(r.astype(np.float32))"),
+    "q8_signed_max": ("amax = np.abs(g).max(axis=-1)", "amax = g.max(axis=-1)"),
+    "q8_scale_slot": ("cache[blk, :, bs, off * w:(off + 1) * w] = sb",
+                      "cache[blk, :, bs, (bs - 1 - off) * w:(bs - off) * w] = sb"),
+    "q8_copy_no_scales": ("        cache[dst, :, bs, :n * w] = cache[src, :, bs, :n * w]\n", ""),
+    "q8_group_order": ("c.reshape(*c.shape[:-1], d // GROUP, GROUP) * s[..., None]",
+                       "c.reshape(*c.shape[:-1], GROUP, d // GROUP) * s[..., None, :]"),
+}
+
+
 def _fails_some_pin(orc):
     failed = []
     for pin in pins.ALL:
@@ -90,5 +103,20 @@ def test_ledger_mutant_caught(orc, tmp_path, monkeypatch, name):
     spec.loader.exec_module(mod)
     for attr in ("Ledger", "SharedBlock", "OutOfBlocks", "LedgerError", "run_script"):
         monkeypatch.setattr(orc, attr, getattr(mod, attr))
+    failed = _fails_some_pin(orc)
+    assert failed, f"planted mistake {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(Q8_MUTANTS))
+def test_q8_mutant_caught(orc, tmp_path, monkeypatch, name):
+    old, new = Q8_MUTANTS[name]
+    src = open(os.path.join(ORACLE_DIR, "q8.py")).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    path = tmp_path / "q8_mut.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location("q8_mut", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    monkeypatch.setattr(orc, "q8", mod)
     failed = _fails_some_pin(orc)
     assert failed, f"planted mistake {name} passed every pin"

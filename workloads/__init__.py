@@ -36,11 +36,19 @@ import numpy as np
 
 __all__ = [
     "DTYPES", "Append", "SharePrefix", "Fork", "Flush", "Free", "SetWindow", "Workload",
-    "make", "CONFIG_NAMES", "normal", "to_storage", "nan_bits",
+    "make", "CONFIG_NAMES", "normal", "to_storage", "nan_bits", "ACT", "act_dtype",
 ]
 
 # storage dtype per cache dtype name: (numpy storage type, bytes per element)
 DTYPES = {"f32": (np.float32, 4), "f16": (np.float16, 2), "bf16": (np.uint16, 2)}
+# 8-bit caches (one 16-bit scale per 32 values): the activations (q, new k / v) keep a
+# 16-bit type; these names give that type
+ACT = {"q8_f16": "f16", "q8_bf16": "bf16"}
+
+
+def act_dtype(dtype: str) -> str:
+    """Type of q and of the new k / v rows for a cache dtype name."""
+    return ACT.get(dtype, dtype)
 
 _CHUNK = 1 << 22
 
@@ -79,6 +87,7 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     bf16 is returned as its uint16 bit pattern (numpy has no bf16 type).  Inputs are finite.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
+    dtype = act_dtype(dtype)
     if dtype == "f32":
         return x
     if dtype == "f16":
@@ -110,7 +119,8 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def nan_bits(dtype: str):
     """A quiet-NaN storage value for the dtype (used to poison bytes nobody may read)."""
-    return {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0)}[dtype]
+    return {"f32": np.float32(np.nan), "f16": np.float16(np.nan),
+            "bf16": np.uint16(0x7FC0)}[act_dtype(dtype)]
 
 
 # ---------------------------------------------------------------- ledger script entries
@@ -195,8 +205,16 @@ class Workload:
         return int(self.q_rows.sum())
 
     @property
-    def elem_bytes(self) -> int:
+    def elem_bytes(self) -> float:
+        """Cache bytes per stored K (or V) element, scales included (17/16 for 8-bit)."""
+        if self.dtype in ACT:
+            return 1.0 + 2.0 / 32
         return DTYPES[self.dtype][1]
+
+    @property
+    def act(self) -> str:
+        """Type of q and of the new k / v rows."""
+        return act_dtype(self.dtype)
 
     def query_start_loc(self) -> np.ndarray:
         """Row offsets [B+1] (a plain running sum over ``q_rows``)."""
