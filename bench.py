@@ -21,6 +21,7 @@ copy kernel is reported in `roofline_copy`.
 
   python bench.py [--steps K] [--warmup W]
                   [--workload opt13b|gqa|prefix_mixed|swa|parallel_sampling|tiny]
+                  [--kv native|q8]
 """
 from __future__ import annotations
 
@@ -36,6 +37,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention KV-read HBM GB/s (% of peak) + decode tokens/s"
+# 8-bit variants keep each workload's 16-bit activation type
+Q8_DTYPE = {"opt13b": "q8_f16", "gqa": "q8_bf16", "swa": "q8_f16", "prefix_mixed": "q8_bf16",
+            "parallel_sampling": "q8_f16"}
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense matrix peak, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
@@ -145,6 +149,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="opt13b", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--layers", type=int, default=None, help="default: the workload's")
+    ap.add_argument("--kv", choices=["native", "q8"], default="native",
+                    help="q8: 8-bit KV cache (one fp16 scale per 32 values), same workload")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
@@ -178,7 +184,13 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
         return
 
-    w = workloads.make(args.workload)
+    if args.kv == "q8":
+        if args.workload not in Q8_DTYPE:
+            print(f"bench.py: no 8-bit variant of {args.workload}", file=sys.stderr)
+            sys.exit(2)
+        w = workloads.make(args.workload, dtype=Q8_DTYPE[args.workload])
+    else:
+        w = workloads.make(args.workload)
     L = args.layers or w.n_layers
     print(f"[bench] building {args.workload}: {w.num_seqs} seqs, {w.total_q_rows} rows, "
           f"{w.num_blocks} blocks/layer, {L} layers", file=sys.stderr, flush=True)
@@ -261,7 +273,7 @@ def main():
     kv_decode = pa.kv_bytes_read(w.seq_lens[dec], w.q_rows[dec], w.window, w.num_kv_heads,
                                  w.head_dim, w.elem_bytes)
     achieved = kv_decode / (dec_avg_ms / 1e3) / 1e9
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload + ("_q8" if args.kv == "q8" else ""))
     decode_roof = {
         "kernel": "decode_kernel",
         "bound": "hbm",
@@ -328,7 +340,8 @@ def main():
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(tokens_per_s, 1),
         "config": {
-            "workload": DESCRIPTIONS[args.workload],
+            "workload": DESCRIPTIONS[args.workload] + (
+                "; 8-bit KV cache, one fp16 scale per 32 values" if args.kv == "q8" else ""),
             "batch": w.num_seqs,
             "query_rows": w.total_q_rows,
             "layers": L,

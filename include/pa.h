@@ -24,7 +24,7 @@
  * Cache layout (the pages fix only "a pool of fixed-size blocks"; this layout is this
  * library's choice): k_cache and v_cache are each [num_blocks][num_kv_heads][16][head_dim]
  * in the cache dtype, row-major, so each (block, KV head) tile of 16 x head_dim is one
- * contiguous run of bytes.
+ * contiguous run of bytes.  8-bit caches add a row of scales to each tile (see pa_dtype).
  */
 #ifndef PA_H
 #define PA_H
@@ -36,7 +36,27 @@
 extern "C" {
 #endif
 
-typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* Element types.  PA_Q8_F16 and PA_Q8_BF16 are cache types only: an 8-bit cache with one
+ * fp16 scale per 32 values, whose queries and new K / V rows are fp16 (PA_Q8_F16) or bf16
+ * (PA_Q8_BF16).  Source: "KV cache by model" (sotaaz.com), planning notes of the
+ * full-attention section - an 8-bit cache keeps a scale for every 32 values and takes
+ * 53.1% of a 16-bit one.
+ *
+ * 8-bit cache layout: k_cache and v_cache are each [num_blocks][num_kv_heads][17][head_dim]
+ * bytes.  Rows 0-15 of a (block, head) tile hold the int8 codes of the block's 16 tokens;
+ * row 16 holds their scales, [16][head_dim / 32] fp16.  A value decodes as scale * code.
+ * pa_write_kv quantizes each group of 32 consecutive values of a new row: scale = the
+ * group's largest |x| / 127 in fp32, rounded to fp16 (held at 65504 if it would overflow);
+ * code = round-half-to-even(x / scale) in fp32, clamped to [-127, 127]; an all-zero group
+ * gets scale 0 and codes 0.  (The pages give the group size and the scale's 2 bytes; the
+ * rest is this library's choice.) */
+typedef enum pa_dtype {
+    PA_F32 = 0,
+    PA_F16 = 1,
+    PA_BF16 = 2,
+    PA_Q8_F16 = 3,
+    PA_Q8_BF16 = 4
+} pa_dtype;
 
 typedef enum pa_status {
     PA_OK = 0,
@@ -62,8 +82,10 @@ typedef struct pa_cache_desc {
     pa_dtype dtype;         /* element type of k_cache / v_cache (and of q)          */
 } pa_cache_desc;
 
-/* Supported by the kernels: dtype F32, F16, BF16; head_dim 64, 128, 256; group size
- * G = num_q_heads / num_kv_heads in {1, 2, 4, 8}; block_size 16. */
+/* Supported by the kernels: dtype F32, F16, BF16, Q8_F16, Q8_BF16; head_dim 64, 128, 256;
+ * group size G = num_q_heads / num_kv_heads in {1, 2, 4, 8}; block_size 16.  Where an
+ * entry point says "cache dtype" for q, k or v, an 8-bit cache means its fp16 / bf16
+ * activation type. */
 
 /* ------------------------------------------------------------------ slot write
  * pa_write_kv - scatter each new token's K and V into the slot its block table assigns.

@@ -247,7 +247,7 @@ class Reference:
         self.threads = threads
         self._decoded = None
 
-    def _attention_inputs(self, q):
+    def attention_inputs(self, q):
         """(q, k_cache, v_cache, dtype) for the attention definition.  An 8-bit cache is
         decoded to float32 (exactly) and q widened to float32 (exactly)."""
         if not self.q8:
@@ -269,13 +269,13 @@ class Reference:
         w = self.w
         qsl = w.query_start_loc()
         if seqs is None:
-            q, kc, vc, dt = self._attention_inputs(w.q)
+            q, kc, vc, dt = self.attention_inputs(w.q)
             return paged_attention(q, kc, vc, self.block_tables, w.seq_lens, w.scale, dt,
                                    w.num_q_heads, qsl, w.window, self.threads)
         seqs = np.asarray(seqs)
         rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs])
         sub_qsl = np.zeros(seqs.size + 1, np.int32)
         np.cumsum(w.q_rows[seqs], out=sub_qsl[1:])
-        q, kc, vc, dt = self._attention_inputs(w.q[rows])
+        q, kc, vc, dt = self.attention_inputs(w.q[rows])
         return paged_attention(q, kc, vc, self.block_tables[seqs], w.seq_lens[seqs], w.scale,
                                dt, w.num_q_heads, sub_qsl, w.window, self.threads)

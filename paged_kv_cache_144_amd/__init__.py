@@ -7,7 +7,11 @@ works without it, but every call then raises - there is no CPU fallback.
 
 The C ABI is declared in ``include/pa.h``; the names below mirror it:
   write_kv  -> pa_write_kv        decode -> pa_decode (+ pa_decode_workspace_size)
-  Pool      -> pa_pool_* / pa_seq_*
+  copy_blocks -> pa_copy_blocks    Pool   -> pa_pool_* / pa_seq_*
+
+An 8-bit cache (one fp16 scale per 32 values) is a uint8 tensor [NB][Hkv][17][d]
+(``q8_cache``); its queries and new rows are fp16 or bf16, which selects PA_Q8_F16 or
+PA_Q8_BF16.
 """
 from __future__ import annotations
 
@@ -19,7 +23,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_Q8_F16, PA_Q8_BF16 = 0, 1, 2, 3, 4
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_LAUNCH",
           -7: "PA_ERR_OUT_OF_BLOCKS", -8: "PA_ERR_SHARED_BLOCK", -9: "PA_ERR_BAD_SEQ"}
@@ -134,9 +138,33 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def cache_desc(k_cache) -> CacheDesc:
-    nb, hkv, bs, d = k_cache.shape
-    return CacheDesc(nb, bs, hkv, d, _dtype_code(k_cache))
+def cache_desc(k_cache, act=None) -> CacheDesc:
+    """Pool description.  For an 8-bit (uint8) cache, `act` is the torch dtype of its
+    queries and new rows (fp16 unless given)."""
+    torch = _torch()
+    nb, hkv, rows, d = k_cache.shape
+    if k_cache.dtype == torch.uint8:
+        if rows != BLOCK_SIZE + 1:
+            raise ValueError("an 8-bit cache is [NB][Hkv][17][d]")
+        code = PA_Q8_BF16 if act == torch.bfloat16 else PA_Q8_F16
+        return CacheDesc(nb, BLOCK_SIZE, hkv, d, code)
+    return CacheDesc(nb, rows, hkv, d, _dtype_code(k_cache))
+
+
+def q8_cache(num_blocks, num_kv_heads, head_dim, device="cuda", fill=0xFF):
+    """An empty 8-bit cache tensor (every byte `fill`; 0xFF decodes to NaN)."""
+    torch = _torch()
+    return torch.full((num_blocks, num_kv_heads, BLOCK_SIZE + 1, head_dim), fill,
+                      dtype=torch.uint8, device=device)
+
+
+def _check_act(t, k_cache, what):
+    torch = _torch()
+    if k_cache.dtype == torch.uint8:
+        if t.dtype not in (torch.float16, torch.bfloat16):
+            raise TypeError(f"{what} must be fp16 or bf16 for an 8-bit cache")
+    elif t.dtype != k_cache.dtype:
+        raise TypeError(f"{what} must have the cache dtype")
 
 
 def write_kv(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
@@ -145,11 +173,12 @@ def write_kv(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
     lib = load()
     if k.shape != v.shape or k.dim() != 3 or k_cache.shape != v_cache.shape:
         raise ValueError("shape mismatch")
-    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
-        raise TypeError("k, v and the caches must share one dtype")
+    _check_act(k, k_cache, "k")
+    if v.dtype != k.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("k and v, and the two caches, must share their dtypes")
     if k.shape[1:] != (k_cache.shape[1], k_cache.shape[3]) or slot_mapping.numel() != k.shape[0]:
         raise ValueError("k/v rows do not match the cache or the slot count")
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, k.dtype)
     rc = lib.pa_write_kv(_dev_ptr(k, "k"), _dev_ptr(v, "v"),
                          _dev_ptr(slot_mapping, "slot_mapping", torch.int64), k.shape[0],
                          _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
@@ -177,8 +206,9 @@ def copy_blocks(k_cache, v_cache, copies, error_word=None, stream=None) -> None:
     _check(rc, "pa_copy_blocks")
 
 
-def workspace_size(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len) -> int:
-    desc = cache_desc(k_cache)
+def workspace_size(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len,
+                   q_dtype=None) -> int:
+    desc = cache_desc(k_cache, q_dtype)
     n = load().pa_decode_workspace_size(ctypes.byref(desc), num_seqs, total_q_rows, num_q_heads,
                                         max_seq_len)
     if n == 0:
@@ -186,9 +216,9 @@ def workspace_size(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len) ->
     return int(n)
 
 
-def alloc_workspace(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len):
+def alloc_workspace(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len, q_dtype=None):
     torch = _torch()
-    n = workspace_size(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len)
+    n = workspace_size(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len, q_dtype)
     # torch's caching allocator returns 512-byte aligned blocks
     return torch.empty(n, dtype=torch.uint8, device=k_cache.device)
 
@@ -209,13 +239,12 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, *, max_seq_len,
         raise ValueError("seq_lens length")
     if query_start_loc is not None and query_start_loc.numel() != B + 1:
         raise ValueError("query_start_loc length")
-    if q.dtype != k_cache.dtype:
-        raise TypeError("q must have the cache dtype")
+    _check_act(q, k_cache, "q")
     if out is None:
         out = torch.empty((R, hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if workspace is None:
-        workspace = alloc_workspace(k_cache, B, R, hq, max_seq_len)
-    desc = cache_desc(k_cache)
+        workspace = alloc_workspace(k_cache, B, R, hq, max_seq_len, q.dtype)
+    desc = cache_desc(k_cache, q.dtype)
     bt = _dev_ptr(block_tables, "block_tables", torch.int32)
     sl = _dev_ptr(seq_lens, "seq_lens", torch.int32)
     qs = _dev_ptr(query_start_loc, "query_start_loc", torch.int32)

@@ -16,12 +16,25 @@ namespace {
 
 using pa::DecodeArgs;
 
+// element types of q, new rows and outputs
 bool dtype_ok(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
 int dtype_bytes(int dt) { return dt == PA_F32 ? 4 : 2; }
+// cache types: the element types, or 8-bit codes with a scale per 32 values
+bool is_q8(int dt) { return dt == PA_Q8_F16 || dt == PA_Q8_BF16; }
+bool cache_dtype_ok(int dt) { return dtype_ok(dt) || is_q8(dt); }
+// the type of q and of new K / V rows for a cache type
+int act_dtype(int dt) { return dt == PA_Q8_F16 ? PA_F16 : dt == PA_Q8_BF16 ? PA_BF16 : dt; }
+// bytes of one token's row of one (block, head) tile, and of its scales (8-bit tiles)
+int64_t row_bytes(const pa_cache_desc* d) {
+    return is_q8(d->dtype) ? d->head_dim : (int64_t)d->head_dim * dtype_bytes(d->dtype);
+}
+int64_t scale_bytes(const pa_cache_desc* d) {
+    return is_q8(d->dtype) ? 2 * (d->head_dim / pa::kQ8Group) : 0;
+}
 
 pa_status check_desc(const pa_cache_desc* d) {
     if (!d) return PA_ERR_NULL;
-    if (!dtype_ok(d->dtype)) return PA_ERR_DTYPE;
+    if (!cache_dtype_ok(d->dtype)) return PA_ERR_DTYPE;
     if (d->num_blocks <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 || d->block_size <= 0)
         return PA_ERR_SHAPE;
     if (d->block_size != pa::kBlock) return PA_ERR_UNSUPPORTED;
@@ -104,7 +117,7 @@ const char* pa_status_string(pa_status s) {
         case PA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
         case PA_ERR_LAUNCH: return "HIP launch error";
         case PA_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
-        case PA_ERR_SHARED_BLOCK: return "append would write into a shared block";
+        case PA_ERR_SHARED_BLOCK: return "copy-on-write would read a block with pending writes";
         case PA_ERR_BAD_SEQ: return "unknown or non-empty sequence";
     }
     return "unknown status";
@@ -118,9 +131,14 @@ pa_status pa_write_kv(const void* k, const void* v, const int64_t* slot_mapping,
     if (num_tokens < 0) return PA_ERR_SHAPE;
     if (num_tokens == 0) return PA_OK;
     if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
-    hipError_t e = pa::launch_write_kv(k, v, slot_mapping, num_tokens, k_cache, v_cache,
-                                       desc->num_blocks, desc->num_kv_heads, desc->head_dim,
-                                       dtype_bytes(desc->dtype), (hipStream_t)stream);
+    hipError_t e =
+        is_q8(desc->dtype)
+            ? pa::launch_write_kv_q8(k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                                     desc->num_blocks, desc->num_kv_heads, desc->head_dim,
+                                     act_dtype(desc->dtype), (hipStream_t)stream)
+            : pa::launch_write_kv(k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                                  desc->num_blocks, desc->num_kv_heads, desc->head_dim,
+                                  dtype_bytes(desc->dtype), (hipStream_t)stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -128,19 +146,20 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc
                          const int32_t* copies, int32_t num_copies, int32_t* error_word,
                          void* stream) {
     if (!desc) return PA_ERR_NULL;
-    if (!dtype_ok(desc->dtype)) return PA_ERR_DTYPE;
+    if (!cache_dtype_ok(desc->dtype)) return PA_ERR_DTYPE;
     if (desc->num_blocks <= 0 || desc->num_kv_heads <= 0 || desc->num_kv_heads > 65535 ||
         desc->head_dim <= 0 || desc->block_size <= 0 || num_copies < 0)
         return PA_ERR_SHAPE;
-    const int64_t row_bytes = (int64_t)desc->head_dim * dtype_bytes(desc->dtype);
-    if (row_bytes % 16 || row_bytes * desc->block_size > INT32_MAX / 2)
+    const int64_t rb = row_bytes(desc), sb = scale_bytes(desc);
+    if (rb % 16 || sb % 4 || (rb + sb) * desc->block_size > INT32_MAX / 2 ||
+        (is_q8(desc->dtype) && (desc->head_dim % pa::kQ8Group || desc->block_size != pa::kBlock)))
         return PA_ERR_UNSUPPORTED;
     if (num_copies == 0) return PA_OK;
     if (!k_cache || !v_cache || !copies) return PA_ERR_NULL;
     hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, copies, num_copies,
                                           desc->num_blocks, desc->num_kv_heads,
-                                          desc->block_size, (int32_t)row_bytes, error_word,
-                                          (hipStream_t)stream);
+                                          desc->block_size, (int32_t)rb, (int32_t)sb,
+                                          error_word, (hipStream_t)stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

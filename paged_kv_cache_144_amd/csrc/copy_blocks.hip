@@ -3,11 +3,12 @@
 // write different tokens into it, the block is copied and each sample keeps its own.
 //
 // One workgroup per (copy, KV head).  The rows a copy moves, rows 0 .. entries-1 of one
-// (block, head) tile, are one contiguous run of entries * head_dim * elem_bytes bytes in
-// both blocks, so the workgroup moves 16-byte pieces of K and then of V with consecutive
-// threads on consecutive addresses.  A triple with an id outside the pool, or a row count
-// outside [0, block_size], is skipped and reported; nothing outside the two tiles is
-// touched.
+// (block, head) tile, are one contiguous run of entries * row_bytes bytes in both blocks, so
+// the workgroup moves 16-byte pieces of K and then of V with consecutive threads on
+// consecutive addresses.  An 8-bit tile also carries a row of scales after its 16 code
+// rows; the entries' scales (scale_bytes each, a multiple of 4) are copied in 4-byte
+// pieces.  A triple with an id outside the pool, or a row count outside [0, block_size], is
+// skipped and reported; nothing outside the two tiles is touched.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -17,30 +18,42 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kc,
                                                           char* __restrict__ vc,
                                                           const int32_t* __restrict__ copies,
                                                           int nb, int hkv, int bs,
-                                                          int row_chunks, int32_t* err) {
+                                                          int row_bytes, int scale_bytes,
+                                                          int32_t* err) {
     const int c = blockIdx.x, h = blockIdx.y;
     const int src = copies[3 * c], dst = copies[3 * c + 1], rows = copies[3 * c + 2];
     if (src < 0 || src >= nb || dst < 0 || dst >= nb || rows < 0 || rows > bs) {
         if (err && h == 0 && threadIdx.x == 0) atomicOr(err, kErrBlockId);
         return;
     }
-    const int64_t tile = (int64_t)bs * row_chunks;   // 16-byte pieces per (block, head)
+    const int64_t tile = (int64_t)bs * (row_bytes + scale_bytes);
     const int64_t from = ((int64_t)src * hkv + h) * tile;
     const int64_t to = ((int64_t)dst * hkv + h) * tile;
-    const int n = rows * row_chunks;
+    const int n = rows * (row_bytes / 16);
     for (int i = threadIdx.x; i < 2 * n; i += blockDim.x) {
         char* base = i < n ? kc : vc;
         const int j = i < n ? i : i - n;
-        st16(base + (to + j) * 16, ld16(base + (from + j) * 16));
+        st16(base + to + (int64_t)j * 16, ld16(base + from + (int64_t)j * 16));
+    }
+    if (scale_bytes) {
+        const int64_t so = (int64_t)bs * row_bytes;
+        const int m = rows * (scale_bytes / 4);
+        for (int i = threadIdx.x; i < 2 * m; i += blockDim.x) {
+            char* base = i < m ? kc : vc;
+            const int j = i < m ? i : i - m;
+            *reinterpret_cast<uint32_t*>(base + to + so + (int64_t)j * 4) =
+                *reinterpret_cast<const uint32_t*>(base + from + so + (int64_t)j * 4);
+        }
     }
 }
 
 hipError_t launch_copy_blocks(void* kc, void* vc, const int32_t* copies, int32_t n,
                               int32_t nb, int32_t hkv, int32_t bs, int32_t row_bytes,
-                              int32_t* err, hipStream_t stream) {
+                              int32_t scale_bytes, int32_t* err, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)n, (unsigned)hkv), dim3(256), 0,
-                       stream, (char*)kc, (char*)vc, copies, nb, hkv, bs, row_bytes / 16, err);
+                       stream, (char*)kc, (char*)vc, copies, nb, hkv, bs, row_bytes,
+                       scale_bytes, err);
     return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@ namespace pa {
 const void* decode_kernel_ptr_f32(int head_dim, int group);
 const void* decode_kernel_ptr_f16(int head_dim, int group);
 const void* decode_kernel_ptr_bf16(int head_dim, int group);
+const void* decode_kernel_ptr_q8(int dtype, int head_dim, int group);
 const void* chunk_kernel_ptr_f16(int head_dim, int group);
 const void* chunk_kernel_ptr_bf16(int head_dim, int group);
 
@@ -14,6 +15,8 @@ const void* decode_kernel_ptr(int dtype, int head_dim, int group) {
         case DT_F32: return decode_kernel_ptr_f32(head_dim, group);
         case DT_F16: return decode_kernel_ptr_f16(head_dim, group);
         case DT_BF16: return decode_kernel_ptr_bf16(head_dim, group);
+        case DT_Q8F16:
+        case DT_Q8BF16: return decode_kernel_ptr_q8(dtype, head_dim, group);
         default: return nullptr;
     }
 }
@@ -22,7 +25,7 @@ const void* chunk_kernel_ptr(int dtype, int head_dim, int group) {
     switch (dtype) {
         case DT_F16: return chunk_kernel_ptr_f16(head_dim, group);
         case DT_BF16: return chunk_kernel_ptr_bf16(head_dim, group);
-        default: return nullptr;   // fp32 caches: chunk rows take the decode kernel
+        default: return nullptr;   // fp32 and 8-bit caches: chunk rows take the decode kernel
     }
 }
 

@@ -28,6 +28,12 @@
 //     block instead of being dereferenced;
 //   * masked tokens are removed by selection (score -inf, V zeroed), never by a zero
 //     weight, so NaN in free or unused slots cannot reach the output;
+//   * 8-bit caches ("KV cache by model", sotaaz.com: one scale per 32 values) are decoded
+//     in registers: codes become fp16 values 1152 + code by placing the flipped code byte
+//     under the exponent bits of 1024 (exact), the score is a packed fp16 dot product with
+//     q (held in fp16 after a per-lane power-of-two scaling, exact), minus 1152 * sum(q),
+//     times the group's scale; V codes are converted byte by byte to fp32 (code + 128) and
+//     the 128 * sum of weights is taken off once per segment;
 //   * a pair cut by share boundaries leaves one partial (max, sum, unnormalised output)
 //     per wavefront; the wavefront holding the pair's first block also leaves a merge task
 //     (pair, number of partials) for the merge kernel, which combines them with the
@@ -39,9 +45,16 @@
 
 namespace pa {
 
+// How a cache dtype's tiles are loaded and consumed.  Lane l of a load holds PE elements
+// of token (i * TPI + l / LPT), columns (l % LPT) * PE .. +PE.
+template <int DT, int D, int G, bool Q8 = (DT == DT_Q8F16 || DT == DT_Q8BF16)>
+struct KvOps;
+
+// fp32 / fp16 / bf16 caches: 16-byte lane loads, 1 KiB per load instruction.
 template <int DT, int D, int G>
-struct DecodeShape {
+struct KvOps<DT, D, G, false> {
     static constexpr int EB = Elem<DT>::bytes;
+    static constexpr int QB = EB;                // bytes per query element
     static constexpr int PE = Elem<DT>::per16;   // elements per 16-byte lane load
     static constexpr int LPT = D / PE;           // lanes holding one token row
     static constexpr int TPI = kWave / LPT;      // tokens per load instruction
@@ -49,6 +62,167 @@ struct DecodeShape {
     static constexpr int TILE = kBlock * D * EB; // bytes of one (block, head) tile
     static_assert(LPT >= 8 && LPT <= 64 && (LPT & (LPT - 1)) == 0, "row width");
     static_assert(NLD * 1024 == TILE, "tile covered by whole-wave loads");
+
+    struct Tile { u32x4 k[NLD], v[NLD]; };
+    struct Q { uint32_t v[G][4]; };
+    struct Extra {};
+
+    __device__ static size_t lane_off(int lane) { return (size_t)lane * 16; }
+    // this lane's slice of query row q_row (element index of its first element)
+    __device__ static void load_q(const char* q, size_t elem, int gi, Q& r) {
+        const u32x4 t = ld16(q + elem * QB);
+        r.v[gi][0] = t.x; r.v[gi][1] = t.y; r.v[gi][2] = t.z; r.v[gi][3] = t.w;
+    }
+    __device__ static void load(const char* kb, const char* vb, size_t off, Tile& t) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            t.k[i] = ld16_stream(kb + off + i * 1024);
+            t.v[i] = ld16_stream(vb + off + i * 1024);
+        }
+    }
+    // this lane's share of q . k for each load and head (summed over the row afterwards)
+    __device__ static void partial_scores(const Q& q, const Tile& t, float sc[G][NLD]) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) sc[gi][i] = dot16<DT>(q.v[gi], t.k[i]);
+    }
+    __device__ static void mask_v(Tile& t, int i, bool ok) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        t.v[i] = ok ? t.v[i] : z;
+    }
+    __device__ static void init(Extra&) {}
+    __device__ static void rescale(Extra&, int, float) {}
+    __device__ static void accumulate(float (&acc)[G][PE], const float (&p)[G][NLD],
+                                      const Tile& t, Extra&) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            float vf[PE];
+            widen16<DT>(t.v[i], vf);
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+                for (int e = 0; e < PE; ++e) acc[gi][e] = fmaf(p[gi][i], vf[e], acc[gi][e]);
+        }
+    }
+    __device__ static void finish(float (&)[G][PE], const Extra&) {}
+};
+
+// 8-bit caches: each (block, head) tile is 16 rows of D one-byte codes followed by one row
+// holding the 16 tokens' fp16 scales ([16][D / 32]); 8-byte lane loads of codes (512 bytes
+// per load instruction) and one 2-byte scale load per lane and load.
+template <int DT, int D, int G>
+struct KvOps<DT, D, G, true> {
+    static constexpr int ADT = DT == DT_Q8F16 ? DT_F16 : DT_BF16;   // query / new-row type
+    static constexpr int QB = 2;
+    static constexpr int PE = 8;
+    static constexpr int LPT = D / PE;
+    static constexpr int TPI = kWave / LPT;
+    static constexpr int NLD = kBlock / TPI;
+    static constexpr int GROUPS = D / kQ8Group;
+    static constexpr int SCALES = kBlock * D;          // offset of the scale row
+    static constexpr int TILE = SCALES + D;            // 17 * D bytes
+    static_assert(LPT >= 8 && LPT <= 32 && (LPT & (LPT - 1)) == 0, "row width");
+    static_assert(NLD * kWave * PE == SCALES, "codes covered by whole-wave loads");
+
+    struct Tile { u32x2 k[NLD], v[NLD]; uint32_t ks[NLD], vs[NLD]; };
+    // q in fp16 scaled by 2^e per lane and head, 1152 * sum of those values, 2^-e
+    struct Q { uint32_t v[G][4]; float off[G]; float inv[G]; };
+    struct Extra { float corr[G]; };   // sum of weight * scale, per head
+
+    __device__ static size_t lane_off(int lane) { return (size_t)lane * PE; }
+    __device__ static size_t scale_off(int lane) {
+        const int row = lane / LPT, col = lane % LPT;
+        return SCALES + (size_t)(row * GROUPS + col * PE / kQ8Group) * 2 - (size_t)lane * PE;
+    }
+    __device__ static void load_q(const char* q, size_t elem, int gi, Q& r) {
+        const u32x4 t = ld16(q + elem * QB);
+        float f[8];
+        widen16<ADT>(t, f);
+        float mx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
+        // 2^(15 - e) with mx < 2^e: the scaled values lie below 2^15 and convert to fp16
+        // exactly (fp16 and bf16 values both fit in fp16's 11-bit significand)
+        const int ex = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float a = ldexpf(f[e], 15 - ex), b = ldexpf(f[e + 1], 15 - ex);
+            r.v[gi][e / 2] = f32_to_f16_bits(a) | (f32_to_f16_bits(b) << 16);
+            sum += a + b;
+        }
+        r.off[gi] = 1152.f * sum;
+        r.inv[gi] = ldexpf(1.f, ex - 15);
+    }
+    __device__ static void load(const char* kb, const char* vb, size_t off, Tile& t) {
+        const int lane = lane_id();
+        const size_t so = off + scale_off(lane);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            t.k[i] = ld8_stream(kb + off + i * (kWave * PE));
+            t.v[i] = ld8_stream(vb + off + i * (kWave * PE));
+            t.ks[i] = ld2_stream(kb + so + (size_t)i * TPI * GROUPS * 2);
+            t.vs[i] = ld2_stream(vb + so + (size_t)i * TPI * GROUPS * 2);
+        }
+    }
+    // fp16 pair (1152 + c0, 1152 + c1) from two code bytes of w (already flipped by 0x80)
+    __device__ static uint32_t pair_lo(uint32_t w) {
+        return (w & 0xffu) | ((w & 0xff00u) << 8) | 0x64006400u;
+    }
+    __device__ static uint32_t pair_hi(uint32_t w) {
+        return ((w >> 16) & 0xffu) | ((w >> 8) & 0xff0000u) | 0x64006400u;
+    }
+    __device__ static void partial_scores(const Q& q, const Tile& t, float sc[G][NLD]) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const uint32_t w0 = t.k[i].x ^ 0x80808080u, w1 = t.k[i].y ^ 0x80808080u;
+            const uint32_t h[4] = {pair_lo(w0), pair_hi(w0), pair_lo(w1), pair_hi(w1)};
+            const float ks = f16_lo(t.ks[i]);
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+                float s = __builtin_amdgcn_fdot2(as_f16x2(q.v[gi][0]), as_f16x2(h[0]), 0.f, false);
+                s = __builtin_amdgcn_fdot2(as_f16x2(q.v[gi][1]), as_f16x2(h[1]), s, false);
+                s = __builtin_amdgcn_fdot2(as_f16x2(q.v[gi][2]), as_f16x2(h[2]), s, false);
+                s = __builtin_amdgcn_fdot2(as_f16x2(q.v[gi][3]), as_f16x2(h[3]), s, false);
+                sc[gi][i] = (s - q.off[gi]) * (q.inv[gi] * ks);
+            }
+        }
+    }
+    __device__ static void mask_v(Tile& t, int i, bool ok) { t.vs[i] = ok ? t.vs[i] : 0u; }
+    __device__ static void init(Extra& x) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) x.corr[gi] = 0.f;
+    }
+    __device__ static void rescale(Extra& x, int gi, float alpha) { x.corr[gi] *= alpha; }
+    __device__ static void accumulate(float (&acc)[G][PE], const float (&p)[G][NLD],
+                                      const Tile& t, Extra& x) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const uint32_t w0 = t.v[i].x ^ 0x80808080u, w1 = t.v[i].y ^ 0x80808080u;
+            float u[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                u[e] = (float)((w0 >> (8 * e)) & 0xffu);
+                u[e + 4] = (float)((w1 >> (8 * e)) & 0xffu);
+            }
+            const float vs = f16_lo(t.vs[i]);
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+                const float wv = p[gi][i] * vs;
+                x.corr[gi] += wv;
+#pragma unroll
+                for (int e = 0; e < PE; ++e) acc[gi][e] = fmaf(wv, u[e], acc[gi][e]);
+            }
+        }
+    }
+    // sum_t w_t (c_t + 128) - 128 sum_t w_t = sum_t w_t c_t
+    __device__ static void finish(float (&acc)[G][PE], const Extra& x) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int e = 0; e < PE; ++e) acc[gi][e] = fmaf(-128.f, x.corr[gi], acc[gi][e]);
+    }
 };
 
 template <int PE>
@@ -167,7 +341,7 @@ __device__ void merge_pair(const DecodeArgs& a, int u, int g, int w_first, int n
 
 template <int DT, int D, int G>
 __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeArgs a) {
-    using S = DecodeShape<DT, D, G>;
+    using S = KvOps<DT, D, G>;
     constexpr int PE = S::PE, LPT = S::LPT, TPI = S::TPI, NLD = S::NLD;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr float kNegBig = -3.402823466e38f;
@@ -196,8 +370,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     const float qscale = a.scale * kLog2e;
     const size_t head_stride = S::TILE;
     const size_t block_stride = (size_t)a.num_kv_heads * S::TILE;
-    const char* kbase = (const char*)a.k_cache + (size_t)lane * 16;
-    const char* vbase = (const char*)a.v_cache + (size_t)lane * 16;
+    const char* kbase = (const char*)a.k_cache + S::lane_off(lane);
+    const char* vbase = (const char*)a.v_cache + S::lane_off(lane);
 
     uint32_t x = wx0[wave];
     const uint32_t x_end = wx0[wave + 1];
@@ -216,13 +390,14 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
         const int lo_tok = (a.window > 0 && len > a.window) ? len - a.window : 0;
 
         // this lane's slice of the G query rows, kept packed
-        uint32_t qv[G][4];
+        typename S::Q qv;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             const size_t qi = (((size_t)u * a.num_q_heads + (size_t)g * G + gi) * D + col * PE);
-            const u32x4 t = ld16((const char*)a.q + qi * S::EB);
-            qv[gi][0] = t.x; qv[gi][1] = t.y; qv[gi][2] = t.z; qv[gi][3] = t.w;
+            S::load_q((const char*)a.q, qi, gi, qv);
         }
+        typename S::Extra ex;
+        S::init(ex);
         float m[G], l[G], acc[G][PE];
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
@@ -240,21 +415,13 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
             valid = (unsigned)b < (unsigned)a.num_blocks;
             return valid ? b : 0;
         };
-        auto load_tile = [&](int b, u32x4* kt, u32x4* vt) {
-            const size_t off = (size_t)b * block_stride + head_off;
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                kt[i] = ld16_stream(kbase + off + i * 1024);
-                vt[i] = ld16_stream(vbase + off + i * 1024);
-            }
+        auto load_tile = [&](int b, typename S::Tile& t) {
+            S::load(kbase, vbase, (size_t)b * block_stride + head_off, t);
         };
-        auto consume = [&](const u32x4* kt, u32x4* vt, int j, bool valid) {
+        auto consume = [&](typename S::Tile& tl, int j, bool valid) {
             const int t0 = j * kBlock;
             float sc[G][NLD];
-#pragma unroll
-            for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                for (int gi = 0; gi < G; ++gi) sc[gi][i] = dot16<DT>(qv[gi], kt[i]);
+            S::partial_scores(qv, tl, sc);
 #pragma unroll
             for (int i = 0; i < NLD; ++i)
 #pragma unroll
@@ -266,8 +433,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
                     const bool ok = valid && t >= lo_tok && t < len;
 #pragma unroll
                     for (int gi = 0; gi < G; ++gi) sc[gi][i] = ok ? sc[gi][i] : -INFINITY;
-                    const u32x4 z = {0u, 0u, 0u, 0u};
-                    vt[i] = ok ? vt[i] : z;
+                    S::mask_v(tl, i, ok);
                 }
             }
             float p[G][NLD];
@@ -288,37 +454,31 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
                 l[gi] = fmaf(l[gi], alpha, sum);
 #pragma unroll
                 for (int e = 0; e < PE; ++e) acc[gi][e] *= alpha;
+                S::rescale(ex, gi, alpha);
             }
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                float vf[PE];
-                widen16<DT>(vt[i], vf);
-#pragma unroll
-                for (int gi = 0; gi < G; ++gi)
-#pragma unroll
-                    for (int e = 0; e < PE; ++e) acc[gi][e] = fmaf(p[gi][i], vf[e], acc[gi][e]);
-            }
+            S::accumulate(acc, p, tl, ex);
         };
 
         int bad = 0;
         for (int c0 = j0; c0 < j1; c0 += kWave) {
             const int n = (j1 - c0) < kWave ? (j1 - c0) : kWave;
             const int btv = lane < n ? bt[c0 + lane] : 0;
-            u32x4 kA[NLD], vA[NLD], kB[NLD], vB[NLD];
+            typename S::Tile A, B;
             bool okA, okB;
-            load_tile(block_id(btv, 0, okA), kA, vA);
+            load_tile(block_id(btv, 0, okA), A);
             for (int jj = 0; jj < n; jj += 2) {
                 // B <- block jj+1 (or jj again at the end: a cache hit, keeps waits simple)
-                load_tile(block_id(btv, jj + 1 < n ? jj + 1 : jj, okB), kB, vB);
+                load_tile(block_id(btv, jj + 1 < n ? jj + 1 : jj, okB), B);
                 bad |= !okA;
-                consume(kA, vA, c0 + jj, okA);
+                consume(A, c0 + jj, okA);
                 if (jj + 1 >= n) break;
-                load_tile(block_id(btv, jj + 2 < n ? jj + 2 : jj + 1, okA), kA, vA);
+                load_tile(block_id(btv, jj + 2 < n ? jj + 2 : jj + 1, okA), A);
                 bad |= !okB;
-                consume(kB, vB, c0 + jj + 1, okB);
+                consume(B, c0 + jj + 1, okB);
             }
         }
         if (bad && lane == 0) atomicOr(hdr, kErrBlockId);
+        S::finish(acc, ex);
 
         // combine the TPI rows of the wavefront (log-sum-exp), then write
         const bool complete = x == ps && seg_end == pe;

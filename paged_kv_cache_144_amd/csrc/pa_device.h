@@ -9,10 +9,13 @@
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+// Cache dtypes (the values of pa_dtype).  DT_Q8F16 / DT_Q8BF16: one-byte codes with one
+// fp16 scale per 32 values; queries and new rows in fp16 / bf16.
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_Q8F16 = 3, DT_Q8BF16 = 4 };
 
 template <int DT>
 struct Elem {
@@ -28,6 +31,14 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 // reused lines in the caches.
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Narrower streaming loads for 8-bit tiles: 8 bytes of codes, one 2-byte scale.
+__device__ __forceinline__ u32x2 ld8_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ uint32_t ld2_stream(const void* p) {
+    return (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
 }
 
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

@@ -14,6 +14,7 @@ constexpr int kBlock = 16;          // tokens per KV block (the kernels' fixed b
 constexpr int kWave = 64;           // CDNA wavefront width
 constexpr int kWavesPerGroup = 4;   // decode workgroup = 4 independent wavefront workers
 constexpr int kMinBlocksPerWave = 8;  // smallest share of KV blocks worth a wavefront
+constexpr int kQ8Group = 32;        // values per scale in 8-bit caches
 
 // Error bits written to the first word of the workspace.
 constexpr int kErrBlockId = 1;
@@ -92,9 +93,12 @@ struct DecodeArgs {
 hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, int32_t n,
                            void* kc, void* vc, int32_t nb, int32_t hkv, int32_t d,
                            int32_t elem_bytes, hipStream_t stream);
+hipError_t launch_write_kv_q8(const void* k, const void* v, const int64_t* slots, int32_t n,
+                              void* kc, void* vc, int32_t nb, int32_t hkv, int32_t d,
+                              int act_dtype, hipStream_t stream);
 hipError_t launch_copy_blocks(void* kc, void* vc, const int32_t* copies, int32_t n,
                               int32_t nb, int32_t hkv, int32_t bs, int32_t row_bytes,
-                              int32_t* err, hipStream_t stream);
+                              int32_t scale_bytes, int32_t* err, hipStream_t stream);
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);

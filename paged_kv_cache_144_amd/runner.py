@@ -9,15 +9,20 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import Pool, alloc_workspace, copy_blocks, decode, write_kv
+from . import Pool, alloc_workspace, copy_blocks, decode, q8_cache, write_kv
 
 TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+
+def _act(dtype: str) -> str:
+    # 8-bit caches keep their queries and new rows in a 16-bit type
+    return {"q8_f16": "f16", "q8_bf16": "bf16"}.get(dtype, dtype)
 
 
 def to_device(a: np.ndarray, dtype: str, device):
     """Storage array (float32 / float16 / bf16 bits as uint16) -> torch tensor on device."""
     import torch
-    if dtype == "bf16":
+    if _act(dtype) == "bf16":
         t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
     else:
         t = torch.from_numpy(np.ascontiguousarray(a))
@@ -28,7 +33,9 @@ def to_storage_np(t, dtype: str) -> np.ndarray:
     """Device tensor -> storage numpy array (bit pattern preserved)."""
     import torch
     t = t.detach().cpu()
-    if dtype == "bf16":
+    if t.dtype == torch.uint8:
+        return t.numpy()
+    if _act(dtype) == "bf16":
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
 
@@ -83,11 +90,17 @@ class DeviceWorkload:
         B = w.num_seqs
         self.max_blocks = max(1, max(len(pool.block_table(s)) for s in range(B)))
         self.block_tables_np = pool.block_tables(np.arange(B), self.max_blocks, w.reserved_block)
-        tdt = getattr(torch, TORCH_DTYPES[w.dtype])
         shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
-        fill = float("nan") if poison else 0.0
-        self.k_cache = torch.full(shape, fill, dtype=tdt, device=device)
-        self.v_cache = torch.full(shape, fill, dtype=tdt, device=device)
+        if w.dtype in ("q8_f16", "q8_bf16"):
+            # every byte 0xFF: codes -1 with NaN scales
+            fill8 = 0xFF if poison else 0
+            self.k_cache = q8_cache(w.num_blocks, w.num_kv_heads, w.head_dim, device, fill8)
+            self.v_cache = q8_cache(w.num_blocks, w.num_kv_heads, w.head_dim, device, fill8)
+        else:
+            tdt = getattr(torch, TORCH_DTYPES[w.dtype])
+            fill = float("nan") if poison else 0.0
+            self.k_cache = torch.full(shape, fill, dtype=tdt, device=device)
+            self.v_cache = torch.full(shape, fill, dtype=tdt, device=device)
         self.block_tables = torch.from_numpy(self.block_tables_np).to(device)
         self.seq_lens = torch.from_numpy(np.ascontiguousarray(w.seq_lens, np.int32)).to(device)
         self.qsl = torch.from_numpy(w.query_start_loc()).to(device)
@@ -99,7 +112,7 @@ class DeviceWorkload:
         if write:
             self.write()
         self.workspace = alloc_workspace(self.k_cache, B, w.total_q_rows, w.num_q_heads,
-                                         self.max_seq_len)
+                                         self.max_seq_len, self.q.dtype)
 
     @property
     def uses_rows(self) -> bool:

@@ -76,6 +76,16 @@ SMALL = [
     ("parallel_sampling", dict(prompts=4, samples=4, lo=64, hi=700)),
     ("parallel_sampling", dict(prompts=3, samples=5, hq=8, hkv=2, d=256, dtype="bf16", lo=20,
                                hi=300)),
+    # 8-bit caches: codes and scales bit-exact, attention against the decoded values
+    ("opt13b", dict(batch=6, lo=64, hi=700, dtype="q8_f16")),
+    ("gqa", dict(batch=12, median=300, lo=16, hi=3000, dtype="q8_bf16")),
+    ("swa", dict(batch=5, lo=1500, hi=6000, window=1024, dtype="q8_f16")),
+    ("tiny", dict(dtype="q8_bf16", hq=8, hkv=1, d=256)),
+    ("tiny", dict(dtype="q8_f16", d=64)),
+    ("gqa", dict(batch=6, median=200, dtype="q8_f16")),
+    ("parallel_sampling", dict(prompts=3, samples=3, lo=20, hi=300, dtype="q8_f16")),
+    ("prefix_mixed", dict(batch=10, prefix=64, suffix_hi=80, chunks=2, chunk_rows=40,
+                          chunk_lo=100, chunk_hi=300, dtype="q8_bf16")),
 ]
 
 
@@ -258,17 +268,20 @@ def test_write_kv_skips(torch, pa):
     assert torch.equal(dw.k_cache.view(torch.int32), k0.view(torch.int32))
 
 
-FULL = ["tiny", "opt13b", "gqa", "prefix_mixed", "swa", "parallel_sampling"]
+FULL = [("tiny", {}), ("opt13b", {}), ("gqa", {}), ("prefix_mixed", {}), ("swa", {}),
+        ("parallel_sampling", {}), ("opt13b", dict(dtype="q8_f16")),
+        ("gqa", dict(dtype="q8_bf16"))]
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_parity(torch, pa, orc, name):
+@pytest.mark.parametrize("name,kw", FULL,
+                         ids=[n + ("-" + k["dtype"] if k else "") for n, k in FULL])
+def test_full_size_parity(torch, pa, orc, name, kw):
     """The workloads at their full sizes, in the launch configuration the benchmark
     times.  Decode rows are all checked; chunk rows on a sample (each sampled row is the
     one-row decode at its causal length, which the oracle pins)."""
-    say("full", name, "generating")
-    w = workloads.make(name)
+    say("full", name, kw, "generating")
+    w = workloads.make(name, **kw)
     dw = run(w, torch)
     say("full", name, "oracle ledger + scatter")
     ref = orc.Reference(w, poison=False)
@@ -287,8 +300,9 @@ def test_full_size_parity(torch, pa, orc, name):
         q = w.q[qsl[s] + np.array(rows)]
         lens = np.array([L - n + r + 1 for r in rows], np.int32)
         bt = np.repeat(ref.block_tables[s:s + 1], len(rows), axis=0)
-        want = orc.paged_attention(q, ref.k_cache, ref.v_cache, bt, lens, w.scale, w.dtype,
-                                   w.num_q_heads, None, w.window)
+        qa, kc, vc, dt = ref.attention_inputs(q)
+        want = orc.paged_attention(qa, kc, vc, bt, lens, w.scale, dt, w.num_q_heads, None,
+                                   w.window)
         check_close(out[qsl[s] + np.array(rows)], want, f"full {name} chunk seq {s}")
 
 

@@ -57,6 +57,13 @@ def test_host_validation_without_gpu(pa):
     bdt = pa.CacheDesc(10, 16, 4, 128, 7)
     assert lib.pa_write_kv(None, None, None, 1, None, None, ctypes.byref(bdt), None) == -3
     assert lib.pa_write_kv(None, None, None, 1, None, None, None, None) == -1
+    # 8-bit cache types are accepted; unknown codes are not
+    q8 = pa.CacheDesc(10, 16, 4, 128, pa.PA_Q8_F16)
+    assert lib.pa_write_kv(None, None, None, 1, None, None, ctypes.byref(q8), None) == -1
+    q8b = pa.CacheDesc(10, 16, 4, 128, pa.PA_Q8_BF16)
+    assert lib.pa_write_kv(None, None, None, 0, None, None, ctypes.byref(q8b), None) == 0
+    unk = pa.CacheDesc(10, 16, 4, 128, 5)
+    assert lib.pa_write_kv(None, None, None, 1, None, None, ctypes.byref(unk), None) == -3
     # pa_copy_blocks: any block size; checks before any device work
     assert lib.pa_copy_blocks(None, None, None, None, 1, None, None) == -1
     assert lib.pa_copy_blocks(None, None, ctypes.byref(ok), None, -1, None, None) == -2
