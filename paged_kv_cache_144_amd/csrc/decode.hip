@@ -47,21 +47,22 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
     return hipLaunchKernel(fn, dim3(groups), dim3(kWavesPerGroup * kWave), args, 0, stream);
 }
 
-// Merge kernel: wavefront w (w >= 1) finds the task of share boundary w, if any, and
-// combines that pair's partials.  Every task is cleared once done, so a plan reused by
-// later calls starts from no tasks.
+// Merge kernel: one wavefront per (share boundary w >= 1, head of the group).  It reads
+// the task of boundary w, if any, and combines that pair's partials for its head.  The
+// decode kernel rewrites the same tasks on every call with the same plan and the plan
+// zeroes every task slot, so tasks are read-only here.
 template <int D, int G>
 __global__ __launch_bounds__(kWavesPerGroup * kWave) void merge_kernel(DecodeArgs a) {
-    int4* tasks = (int4*)(a.ws + a.lay.tasks);
+    const int4* tasks = (const int4*)(a.ws + a.lay.tasks);
     const float2* pml = (const float2*)(a.ws + a.lay.part_ml);
     const float* pacc = (const float*)(a.ws + a.lay.part_acc);
-    const int w = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6) + 1;
+    const int q = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int w = q / G + 1, gi = q % G;
     const int W = ((const int32_t*)(a.ws + a.lay.header))[2];
     if (w >= W) return;
     const int4 t = tasks[w];
     if (t.z <= 0) return;
-    merge_pair<D, G>(a, t.x, t.y, w - 1, t.z, t.w, pml, pacc, lane_id());
-    if (lane_id() == 0) tasks[w] = make_int4(0, 0, 0, 0);
+    merge_pair<D, G>(a, t.x, t.y, w - 1, t.z, t.w, gi, pml, pacc, lane_id());
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
@@ -74,7 +75,7 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
 #undef PA_CASE
     if (!fn) return hipErrorInvalidDeviceFunction;
     if (a.max_waves <= 1) return hipSuccess;
-    const int groups = (a.max_waves - 1 + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int groups = ((a.max_waves - 1) * a.group + kWavesPerGroup - 1) / kWavesPerGroup;
     void* args[] = {(void*)&a};
     return hipLaunchKernel(fn, dim3(groups), dim3(kWavesPerGroup * kWave), args, 0, stream);
 }

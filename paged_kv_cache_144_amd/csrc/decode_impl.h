@@ -109,25 +109,28 @@ struct KvOps<DT, D, G, false> {
 };
 
 // 8-bit caches: each (block, head) tile is 16 rows of D one-byte codes followed by one row
-// holding the 16 tokens' fp16 scales ([16][D / 32]); 8-byte lane loads of codes (512 bytes
-// per load instruction) and one 2-byte scale load per lane and load.
+// holding the 16 tokens' fp16 scales ([16][D / 32]).  A lane loads PE codes of a token row
+// (16 bytes for G <= 4, 8 bytes for G = 8, whose accumulators would not fit twice as many
+// columns) and the 2-byte scale of their group.
 template <int DT, int D, int G>
 struct KvOps<DT, D, G, true> {
     static constexpr int ADT = DT == DT_Q8F16 ? DT_F16 : DT_BF16;   // query / new-row type
     static constexpr int QB = 2;
-    static constexpr int PE = 8;
+    static constexpr int PE = G <= 4 ? 16 : 8;
+    static constexpr int NW = PE / 4;                  // code dwords per lane and load
     static constexpr int LPT = D / PE;
     static constexpr int TPI = kWave / LPT;
     static constexpr int NLD = kBlock / TPI;
     static constexpr int GROUPS = D / kQ8Group;
     static constexpr int SCALES = kBlock * D;          // offset of the scale row
     static constexpr int TILE = SCALES + D;            // 17 * D bytes
-    static_assert(LPT >= 8 && LPT <= 32 && (LPT & (LPT - 1)) == 0, "row width");
+    static_assert(LPT >= 4 && LPT <= 32 && (LPT & (LPT - 1)) == 0, "row width");
     static_assert(NLD * kWave * PE == SCALES, "codes covered by whole-wave loads");
 
-    struct Tile { u32x2 k[NLD], v[NLD]; uint32_t ks[NLD], vs[NLD]; };
+    typedef uint32_t CodeVec __attribute__((ext_vector_type(NW)));
+    struct Tile { CodeVec k[NLD], v[NLD]; uint32_t ks[NLD], vs[NLD]; };
     // q in fp16 scaled by 2^e per lane and head, 1152 * sum of those values, 2^-e
-    struct Q { uint32_t v[G][4]; float off[G]; float inv[G]; };
+    struct Q { uint32_t v[G][PE / 2]; float off[G]; float inv[G]; };
     struct Extra { float corr[G]; };   // sum of weight * scale, per head
 
     __device__ static size_t lane_off(int lane) { return (size_t)lane * PE; }
@@ -135,19 +138,22 @@ struct KvOps<DT, D, G, true> {
         const int row = lane / LPT, col = lane % LPT;
         return SCALES + (size_t)(row * GROUPS + col * PE / kQ8Group) * 2 - (size_t)lane * PE;
     }
+    __device__ static CodeVec ld_codes(const char* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const CodeVec*>(p));
+    }
     __device__ static void load_q(const char* q, size_t elem, int gi, Q& r) {
-        const u32x4 t = ld16(q + elem * QB);
-        float f[8];
-        widen16<ADT>(t, f);
+        float f[PE];
+#pragma unroll
+        for (int j = 0; j < PE / 8; ++j) widen16<ADT>(ld16(q + (elem + 8 * j) * QB), f + 8 * j);
         float mx = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
+        for (int e = 0; e < PE; ++e) mx = fmaxf(mx, fabsf(f[e]));
         // 2^(15 - e) with mx < 2^e: the scaled values lie below 2^15 and convert to fp16
         // exactly (fp16 and bf16 values both fit in fp16's 11-bit significand)
         const int ex = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
         float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
+        for (int e = 0; e < PE; e += 2) {
             const float a = ldexpf(f[e], 15 - ex), b = ldexpf(f[e + 1], 15 - ex);
             r.v[gi][e / 2] = f32_to_f16_bits(a) | (f32_to_f16_bits(b) << 16);
             sum += a + b;
@@ -160,8 +166,8 @@ struct KvOps<DT, D, G, true> {
         const size_t so = off + scale_off(lane);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            t.k[i] = ld8_stream(kb + off + i * (kWave * PE));
-            t.v[i] = ld8_stream(vb + off + i * (kWave * PE));
+            t.k[i] = ld_codes(kb + off + i * (kWave * PE));
+            t.v[i] = ld_codes(vb + off + i * (kWave * PE));
             t.ks[i] = ld2_stream(kb + so + (size_t)i * TPI * GROUPS * 2);
             t.vs[i] = ld2_stream(vb + so + (size_t)i * TPI * GROUPS * 2);
         }
@@ -173,18 +179,32 @@ struct KvOps<DT, D, G, true> {
     __device__ static uint32_t pair_hi(uint32_t w) {
         return ((w >> 16) & 0xffu) | ((w >> 8) & 0xff0000u) | 0x64006400u;
     }
+    __device__ static void words(const CodeVec& c, uint32_t (&w)[NW]) {
+        if constexpr (NW == 2) {
+            w[0] = c.x; w[1] = c.y;
+        } else {
+            w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
+        }
+    }
     __device__ static void partial_scores(const Q& q, const Tile& t, float sc[G][NLD]) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            const uint32_t w0 = t.k[i].x ^ 0x80808080u, w1 = t.k[i].y ^ 0x80808080u;
-            const uint32_t h[4] = {pair_lo(w0), pair_hi(w0), pair_lo(w1), pair_hi(w1)};
+            uint32_t w[NW];
+            words(t.k[i], w);
+            uint32_t h[PE / 2];
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                const uint32_t x = w[j] ^ 0x80808080u;
+                h[2 * j] = pair_lo(x);
+                h[2 * j + 1] = pair_hi(x);
+            }
             const float ks = f16_lo(t.ks[i]);
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) {
-                float s = __builtin_amdgcn_fdot2(as_f16x2(q.v[gi][0]), as_f16x2(h[0]), 0.f, false);
-                s = __builtin_amdgcn_fdot2(as_f16x2(q.v[gi][1]), as_f16x2(h[1]), s, false);
-                s = __builtin_amdgcn_fdot2(as_f16x2(q.v[gi][2]), as_f16x2(h[2]), s, false);
-                s = __builtin_amdgcn_fdot2(as_f16x2(q.v[gi][3]), as_f16x2(h[3]), s, false);
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < PE / 2; ++j)
+                    s = __builtin_amdgcn_fdot2(as_f16x2(q.v[gi][j]), as_f16x2(h[j]), s, false);
                 sc[gi][i] = (s - q.off[gi]) * (q.inv[gi] * ks);
             }
         }
@@ -199,12 +219,14 @@ struct KvOps<DT, D, G, true> {
                                       const Tile& t, Extra& x) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            const uint32_t w0 = t.v[i].x ^ 0x80808080u, w1 = t.v[i].y ^ 0x80808080u;
-            float u[8];
+            uint32_t w[NW];
+            words(t.v[i], w);
+            float u[PE];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                u[e] = (float)((w0 >> (8 * e)) & 0xffu);
-                u[e + 4] = (float)((w1 >> (8 * e)) & 0xffu);
+            for (int j = 0; j < NW; ++j) {
+                const uint32_t y = w[j] ^ 0x80808080u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u[4 * j + e] = (float)((y >> (8 * e)) & 0xffu);
             }
             const float vs = f16_lo(t.vs[i]);
 #pragma unroll
@@ -250,9 +272,12 @@ __device__ __forceinline__ void store_row(const DecodeArgs& a, size_t idx, const
             w[e / 2] = lo | (hi << 16);
         }
         uint16_t* o = (uint16_t*)a.out + idx;
-        if constexpr (PE == 8) {
-            u32x4 x = {w[0], w[1], w[2], w[3]};
-            st16(o, x);
+        if constexpr (PE % 8 == 0) {
+#pragma unroll
+            for (int j = 0; j < PE / 8; ++j) {
+                u32x4 x = {w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+                st16(o + 8 * j, x);
+            }
         } else {
             *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1]);
         }
@@ -278,15 +303,15 @@ __device__ __forceinline__ void store_out1(const DecodeArgs& a, size_t idx, floa
     }
 }
 
-// Combine the partials of pair (u, g) left by wavefronts w_first .. w_first + nc - 1 (slot
-// first_slot for the first, slot 0 for the others):
+// Combine the partials of head gi of pair (u, g) left by wavefronts w_first ..
+// w_first + nc - 1 (slot first_slot for the first, slot 0 for the others):
 //   out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c,   M = max_c m_c   (m in log2 units)
 template <int D, int G>
 __device__ void merge_pair(const DecodeArgs& a, int u, int g, int w_first, int nc,
-                           int first_slot, const float2* pml, const float* pacc, int lane) {
+                           int first_slot, int gi, const float2* pml, const float* pacc,
+                           int lane) {
     constexpr int KD = (D + kWave - 1) / kWave;
-#pragma unroll 1
-    for (int gi = 0; gi < G; ++gi) {
+    {
         float M = -3.402823466e38f;
         for (int c0 = 0; c0 < nc; c0 += kWave) {
             const int c = c0 + lane;
@@ -345,6 +370,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     constexpr int PE = S::PE, LPT = S::LPT, TPI = S::TPI, NLD = S::NLD;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr float kNegBig = -3.402823466e38f;
+    constexpr float kLazy = 8.f;
 
     int32_t* hdr = (int32_t*)(a.ws + a.lay.header);
     const uint32_t* cb = (const uint32_t*)(a.ws + a.lay.cb);
@@ -436,25 +462,40 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
                     S::mask_v(tl, i, ok);
                 }
             }
+            // Lazy rescaling: the running max m only moves when a score exceeds it by more
+            // than kLazy (weights then stay below 2^kLazy); the sum and the output use the
+            // same m, so the result is unchanged.  The test is wavefront-uniform.
+            float mx[G];
+            bool grow = false;
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+                mx[gi] = sc[gi][0];
+#pragma unroll
+                for (int i = 1; i < NLD; ++i) mx[gi] = fmaxf(mx[gi], sc[gi][i]);
+                grow |= mx[gi] > m[gi] + kLazy;
+            }
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+                for (int gi = 0; gi < G; ++gi) {
+                    const float mn = fmaxf(m[gi], mx[gi]);
+                    const float alpha = __builtin_amdgcn_exp2f(m[gi] - mn);
+                    m[gi] = mn;
+                    l[gi] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < PE; ++e) acc[gi][e] *= alpha;
+                    S::rescale(ex, gi, alpha);
+                }
+            }
             float p[G][NLD];
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) {
-                float mx = sc[gi][0];
-#pragma unroll
-                for (int i = 1; i < NLD; ++i) mx = fmaxf(mx, sc[gi][i]);
-                const float mn = fmaxf(m[gi], mx);
-                const float alpha = __builtin_amdgcn_exp2f(m[gi] - mn);
-                m[gi] = mn;
                 float sum = 0.f;
 #pragma unroll
                 for (int i = 0; i < NLD; ++i) {
-                    p[gi][i] = __builtin_amdgcn_exp2f(sc[gi][i] - mn);
+                    p[gi][i] = __builtin_amdgcn_exp2f(sc[gi][i] - m[gi]);
                     sum += p[gi][i];
                 }
-                l[gi] = fmaf(l[gi], alpha, sum);
-#pragma unroll
-                for (int e = 0; e < PE; ++e) acc[gi][e] *= alpha;
-                S::rescale(ex, gi, alpha);
+                l[gi] += sum;
             }
             S::accumulate(acc, p, tl, ex);
         };

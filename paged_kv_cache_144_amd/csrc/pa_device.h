@@ -126,14 +126,14 @@ constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;  // reverse within each 8-lane half row
 constexpr int DPP_MIRROR = 0x140;       // reverse within each 16-lane row
 
-// Sum over each aligned group of N lanes (N = 8, 16, 32, 64); every lane gets its
+// Sum over each aligned group of N lanes (N = 4, 8, 16, 32, 64); every lane gets its
 // group's sum.  Inside a 16-lane row this is DPP only.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-    static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
     x += dpp<DPP_XOR1>(x);
     x += dpp<DPP_XOR2>(x);
-    x += dpp<DPP_HALF_MIRROR>(x);
+    if constexpr (N >= 8) x += dpp<DPP_HALF_MIRROR>(x);
     if constexpr (N >= 16) x += dpp<DPP_MIRROR>(x);
     if constexpr (N >= 32)
         x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // xor 16

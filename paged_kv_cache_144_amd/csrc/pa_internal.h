@@ -43,7 +43,7 @@ struct UnitInfo {
 //   tiles    int2[Tmax]    chunk-row tiles (sequence, first row) for the MFMA kernel
 //   tasks    int4[W+1]     merge task of the cut pair whose first share boundary is w:
 //                          (unit, KV head, contributing wavefronts, slot of the first);
-//                          written by the pair's first wavefront, cleared by the merge
+//                          zeroed by the plan, written by the pair's first wavefront
 //   part_ml  float2[W*2*G]       partial (max, sum) per wave, slot, head of the group
 //   part_acc float[W*2*G*d]      partial unnormalised output
 struct Layout {
