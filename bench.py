@@ -142,6 +142,87 @@ def cpu_baseline(w, n_layers, seconds):
     }
 
 
+HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction, published
+
+
+def time_swap(pa, dw, pools, n_seqs):
+    """Evict the n_seqs sequences that arrived last (all of their blocks, every layer) to
+    pinned host memory, then bring them back into free blocks; GB/s of each direction over
+    the host link, next to a plain contiguous hipMemcpy of the same bytes."""
+    import numpy as np
+    import torch
+    pool = dw.pool
+    pool.take_copies()
+    victims, outs = [], []
+    blocks = sum(1 for s in range(dw.w.num_seqs) for b in pool.block_table(s) if b >= 0)
+    pool.set_host_blocks(blocks)
+    for _ in range(n_seqs):
+        v = pool.latest_resident()
+        if v is None:
+            break
+        victims.append(v)
+        outs.append(pool.swap_out(v))
+    pool.take_copies()
+    ins = [pool.swap_in(v) for v in victims]
+    pool.take_copies()
+    out_p = torch.from_numpy(np.concatenate(outs)).cuda()
+    in_p = torch.from_numpy(np.concatenate(ins)).cuda()
+    kc = pools[0][0]
+    nh = int(out_p.shape[0])
+    host = [(torch.empty((nh,) + tuple(kc.shape[1:]), dtype=kc.dtype, pin_memory=True),
+             torch.empty((nh,) + tuple(kc.shape[1:]), dtype=kc.dtype, pin_memory=True))
+            for _ in pools]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tile_bytes = kc[0].numel() * kc.element_size()          # all heads of one block
+    moved = 2 * nh * tile_bytes * len(pools)                 # K and V, every layer
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3
+
+    def out_all():
+        for (k, v), (hk, hv) in zip(pools, host):
+            pa.swap_blocks(k, v, hk, hv, out_p, err)
+
+    def in_all():
+        for (k, v), (hk, hv) in zip(pools, host):
+            pa.swap_blocks(hk, hv, k, v, in_p, err)
+
+    out_all()
+    in_all()                                                  # warm-up
+    t_out = timed(out_all)
+    t_in = timed(in_all)
+    # the same bytes as one contiguous copy each way
+    hbuf = torch.empty(moved // len(pools), dtype=torch.uint8, pin_memory=True)
+    dbuf = torch.empty_like(hbuf, device="cuda")
+    dbuf.fill_(1)
+    t_d2h = timed(lambda: [hbuf.copy_(dbuf, non_blocking=True) for _ in pools])
+    t_h2d = timed(lambda: [dbuf.copy_(hbuf, non_blocking=True) for _ in pools])
+    return {
+        "seqs": len(victims),
+        "blocks": nh,
+        "layers": len(pools),
+        "bytes_each_way": moved,
+        "out_GBps": round(moved / t_out / 1e9, 2),
+        "in_GBps": round(moved / t_in / 1e9, 2),
+        "out_ms": round(t_out * 1e3, 3),
+        "in_ms": round(t_in * 1e3, 3),
+        "memcpy_d2h_GBps": round(moved / t_d2h / 1e9, 2),
+        "memcpy_h2d_GBps": round(moved / t_h2d / 1e9, 2),
+        "bound": "host link",
+        "peak": HOST_LINK_PEAK_GBS,
+        "unit": "GB/s",
+        "frac_out": round(moved / t_out / 1e9 / HOST_LINK_PEAK_GBS, 4),
+        "frac_in": round(moved / t_in / 1e9 / HOST_LINK_PEAK_GBS, 4),
+        "error_bits": int(err.item()),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +234,9 @@ def main():
                     help="q8: 8-bit KV cache (one fp16 scale per 32 values), same workload")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--swap-seqs", type=int, default=0, metavar="N",
+                    help="after the timed steps, also time evicting the N sequences that "
+                         "arrived last to pinned host memory and bringing them back")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -357,6 +441,8 @@ def main():
         result["roofline_chunk"] = chunk_roof
     if copy_roof:
         result["roofline_copy"] = copy_roof
+    if args.swap_seqs > 0:
+        result["swap"] = time_swap(pa, dw, pools, args.swap_seqs)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         ref, cb = cpu_baseline(w, L, args.cpu_seconds)

@@ -67,8 +67,8 @@ typedef enum pa_status {
     PA_ERR_WORKSPACE = -5,      /* workspace NULL, too small or not 256-byte aligned       */
     PA_ERR_LAUNCH = -6,         /* the HIP runtime reported an error                       */
     PA_ERR_OUT_OF_BLOCKS = -7,  /* ledger: not enough free blocks (nothing was taken)      */
-    PA_ERR_SHARED_BLOCK = -8,   /* ledger: a copy-on-write would read a block that has     *
-                                 * writes pending in the current copy batch                */
+    PA_ERR_SHARED_BLOCK = -8,   /* ledger: a copy-on-write or swap-out would read a block  *
+                                 * that has writes pending in the current batch            */
     PA_ERR_BAD_SEQ = -9         /* ledger: unknown sequence, or one that must be empty     */
 } pa_status;
 
@@ -224,6 +224,29 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc
                          const int32_t* copies, int32_t num_copies, int32_t* error_word,
                          void* stream);
 
+/* ------------------------------------------------------------------ block swap
+ * pa_swap_blocks - copy whole blocks between two pools with the same tile shape, for
+ * swapping ("vLLM and PagedAttention" notes, scheduling section: evicted KV blocks go to
+ * CPU memory and come back when there is room).  Either pool may be pinned host memory
+ * (allocated with hipHostMalloc, e.g. a torch tensor with pin_memory=True): the kernel
+ * reads or writes it directly over the host link.
+ *
+ *   src_k, src_v  the pool read: src_blocks blocks of num_kv_heads tiles (device or pinned
+ *                 host).
+ *   dst_k, dst_v  the pool written: dst_blocks blocks (device or pinned host).
+ *   desc          (host) tile shape (block_size, num_kv_heads, head_dim, dtype; its
+ *                 num_blocks is not used).
+ *   pairs         (device) int32 [n][2]: (src block, dst block).
+ *   error_word    (device, nullable) int32; a pair with an id out of range is skipped and
+ *                 sets bit 0 (value 1).
+ * All pairs are applied at once: destinations must be distinct and no pool may be both
+ * read and written by one call.  The copy is bit-exact.  Errors: PA_ERR_NULL,
+ * PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED (a pointer that is neither device memory
+ * nor pinned host memory), PA_ERR_LAUNCH. */
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                         const pa_cache_desc* desc, int32_t src_blocks, int32_t dst_blocks,
+                         const int32_t* pairs, int32_t n, int32_t* error_word, void* stream);
+
 /* ------------------------------------------------------------------ host block ledger
  * A host-only ledger of one pool's blocks (no device memory).  Sources: "PagedAttention
  * deep dive" (donmain.dev), sections on splitting the KV cache into blocks (a block is
@@ -260,19 +283,53 @@ pa_status pa_seq_set_window(pa_pool* p, int64_t seq, int32_t window);
  * old block; the sequence's table then points at the fresh block.  The last holder of a
  * block writes in place.  The copy is taken before any new block of the same append.
  *
- * Copy batches: pa_pool_take_copies ends a batch.  The caller carries out a batch's copies
- * (pa_copy_blocks) and then its slot writes (pa_write_kv) before the next batch's.  Because
- * a batch's copies run all at once, an append whose copy would read a block that received
- * slots or a copy in the current batch fails with PA_ERR_SHARED_BLOCK.
+ * Batches: pa_pool_take_copies ends a batch.  The caller carries out a batch's swap-outs
+ * (pa_swap_blocks), copies (pa_copy_blocks), swap-ins and slot writes (pa_write_kv), in
+ * that order, before the next batch's.  Because each kind runs all at once, an append
+ * whose copy would read a block with writes pending in the current batch (slots, a copy
+ * or a swap-in into it) fails with PA_ERR_SHARED_BLOCK, and blocks released while work on
+ * them is pending are not handed out again before the batch ends.
  *
  * All or nothing: PA_ERR_OUT_OF_BLOCKS if the free blocks do not suffice for the copy and
- * the new blocks, PA_ERR_SHARED_BLOCK as above; either way nothing changes. */
+ * the new blocks, PA_ERR_SHARED_BLOCK as above, PA_ERR_BAD_SEQ for a swapped-out
+ * sequence; nothing changes on error. */
 pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slots_out);
 
 /* `dst` (new or empty) becomes a second sample of `src` (parallel sampling): the same
  * length, window and physical blocks, each block one reference more.  Blocks released by a
  * window stay -1 in the copy of the table. */
 pa_status pa_seq_fork(pa_pool* p, int64_t dst, int64_t src);
+
+/* ---- swapping (ghkdgus29.github.io, "vLLM and PagedAttention" notes, scheduling section:
+ * eviction takes all of a sequence's blocks or none, the victim is the sequence that
+ * arrived last, and swapping moves the evicted blocks to CPU memory until GPU memory frees
+ * up).  The host swap space is a pool of host blocks, ids 0 .. num_host_blocks-1, handed
+ * out first-in first-out; the caller owns its memory (pinned host tiles laid out like the
+ * device pool's) and moves the data with pa_swap_blocks.
+ *
+ * Batch order: a batch's swap-outs run first, then its copies (pa_copy_blocks), then its
+ * swap-ins, then its slot writes; pa_pool_take_copies ends the batch.  A block or host
+ * block freed while work on it is pending in the batch joins its free queue only when the
+ * batch ends.
+ *
+ * pa_pool_set_host_blocks: size the host swap space (PA_ERR_BAD_SEQ while host blocks are
+ * in use).
+ * pa_pool_latest_resident: the victim - the resident sequence holding device blocks that
+ * arrived last (a sequence arrives when it is first created); PA_ERR_BAD_SEQ if none.
+ * pa_seq_swap_out: move the blocks `seq` holds alone (reference count 1) to host blocks;
+ * blocks it shares stay on the device, still referenced.  Writes (device, host) int32
+ * pairs to pairs (host, 2 * cap entries), *n their number.  All or nothing:
+ * PA_ERR_OUT_OF_BLOCKS if host blocks are short, PA_ERR_SHARED_BLOCK if one of the blocks
+ * has writes pending in the batch, PA_ERR_SHAPE if cap < *n; nothing changes on error.
+ * The sequence's table entries for moved blocks become -1; until its swap-in it cannot
+ * append, fork or share.  pa_seq_free releases its host blocks too.
+ * pa_seq_swap_in: bring it back; writes (host, device) pairs; all or nothing
+ * (PA_ERR_OUT_OF_BLOCKS if free device blocks are short). */
+pa_status pa_pool_set_host_blocks(pa_pool* p, int32_t num_host_blocks);
+int32_t pa_pool_num_host_free(const pa_pool* p);
+pa_status pa_pool_latest_resident(const pa_pool* p, int64_t* seq);
+pa_status pa_seq_swap_out(pa_pool* p, int64_t seq, int32_t* pairs, int32_t cap, int32_t* n);
+pa_status pa_seq_swap_in(pa_pool* p, int64_t seq, int32_t* pairs, int32_t cap, int32_t* n);
 
 /* End the current copy batch: write its copies, in the order they were recorded, as
  * (src_block, dst_block, entries) int32 triples to out (host, 3 * cap entries) and start a

@@ -203,11 +203,11 @@ class Reference:
     """The oracle's view of a workload: its tables, slots, caches and outputs."""
 
     def __init__(self, w, threads: int = 0, poison: bool = True):
-        from workloads import ACT, DTYPES, Append, nan_bits
+        from workloads import ACT, DTYPES, Append, SwapIn, SwapOut, nan_bits
 
         self.w = w
-        led = Ledger(w.free_order, w.block_size)
-        self.slots, self.copies = run_script(led, w.script)
+        led = Ledger(w.free_order, w.block_size, w.meta.get("host_blocks", 0))
+        self.slots, self.copies, self.swaps = run_script(led, w.script)
         self.ledger = led
         B = w.num_seqs
         self.max_blocks = max(1, max(len(led.block_table(s)) for s in range(B)))
@@ -230,7 +230,19 @@ class Reference:
             st, _ = DTYPES[w.dtype]
             self.k_cache = np.full(shape, nan_bits(w.dtype) if poison else 0, st)
             self.v_cache = np.full(shape, nan_bits(w.dtype) if poison else 0, st)
+        # host swap space: tiles laid out like the device pool's
+        nh = w.meta.get("host_blocks", 0)
+        self.host_k = np.zeros((nh,) + self.k_cache.shape[1:], self.k_cache.dtype)
+        self.host_v = np.zeros((nh,) + self.v_cache.shape[1:], self.v_cache.dtype)
         for i, op in enumerate(w.script):
+            if isinstance(op, SwapOut):
+                for b, h in self.swaps[i][1]:
+                    self.host_k[h], self.host_v[h] = self.k_cache[b], self.v_cache[b]
+                continue
+            if isinstance(op, SwapIn):
+                for h, b in self.swaps[i][1]:
+                    self.k_cache[b], self.v_cache[b] = self.host_k[h], self.host_v[h]
+                continue
             if not isinstance(op, Append):
                 continue
             for src, dst, n in self.copies[i]:

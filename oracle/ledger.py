@@ -19,7 +19,9 @@ What the pages fix, and where:
     that block is copied and the count drops; fully shared earlier blocks stay shared
     (same section; "PagedAttention deep dive", donmain.dev, section on block sharing:
     copy-on-write at the point where sequences diverge);
-  * eviction is all-or-nothing per sequence (same notes, scheduling section);
+  * eviction is all-or-nothing per sequence, the victim is the sequence that arrived last,
+    and swapping moves an evicted sequence's blocks to CPU memory until GPU memory frees
+    up (same notes, scheduling section);
   * a sliding-window layer only keeps the most recent W tokens (sotaaz.com, section on
     layer kinds).
 
@@ -31,10 +33,19 @@ Readings where the pages are silent (each listed in the design notes):
     sequence also references it first takes a fresh block (before any new block of the
     same append), records the copy (old block, new block, entries held) and gives the old
     block one reference less; the last remaining holder writes in place;
-  * copies are carried out in batches, all pairs of a batch at once, copies before the
-    batch's slot writes (``take_copies`` ends a batch).  A copy therefore may not read a
-    block that received slots or a copy in the same batch: such an append is refused
-    (SharedBlock) and takes nothing;
+  * batches: the device carries out a batch's work in the order swap-outs, copies,
+    swap-ins, slot writes, the pairs of each kind all at once; ``take_copies`` ends a
+    batch.  Hence (a) a copy or a swap-out may not read a block that has writes pending in
+    the batch (slots, a copy or a swap-in into it): such a call is refused (SharedBlock)
+    and takes nothing; (b) a block, or a host block, freed while work on it is pending in
+    the batch joins its free queue only when the batch ends;
+  * swapping: the host swap space is a pool of host blocks handed out first-in first-out;
+    a swap-out moves only the blocks the sequence holds alone (a block it shares stays on
+    the device, still referenced); it needs a host block for each, all or nothing, and
+    leaves the sequence unusable (no append, fork or share) until its swap-in, which needs
+    a free device block for each host block, all or nothing;
+  * arrival: a sequence arrives when it is first created (append, fork, share or window);
+    the victim is the resident sequence holding device blocks that arrived last;
   * with a window W, after an append of n tokens to a sequence of length c, positions
     before c+n-W are not kept: their slot is -1, a block lying wholly before that point is
     released (table entry -1) and one never allocated stays -1.
@@ -57,24 +68,37 @@ class SharedBlock(LedgerError):
 
 
 class Ledger:
-    def __init__(self, free_order, block_size: int = 16):
+    def __init__(self, free_order, block_size: int = 16, host_blocks: int = 0):
         self.bs = int(block_size)
         self.free = deque(int(b) for b in free_order)
         self.ref: dict[int, int] = {}
         self.table: dict[int, list[int]] = {}
         self.length: dict[int, int] = {}
         self.window: dict[int, int] = {}
+        self.arrival: dict[int, int] = {}
+        self._clock = 0
+        # the current batch
         self.pending: list[tuple[int, int, int]] = []   # copies not yet taken
-        self.touched: set[int] = set()     # blocks given slots or copies since the last take
+        self.touched: set[int] = set()     # blocks with writes pending (slots, copy, swap-in)
+        self.copy_src: set[int] = set()    # blocks a pending copy reads
+        self.quarantine: list[int] = []    # freed with work pending: free at the batch end
+        # host swap space
+        self.host_free = deque(range(int(host_blocks)))
+        self.host_quarantine: list[int] = []
+        self.swapped: dict[int, list[int]] = {}   # seq -> host block per logical block, or -1
 
     # -- queries -------------------------------------------------------------------
     def num_free(self) -> int:
         return len(self.free)
 
+    def num_host_free(self) -> int:
+        return len(self.host_free)
+
     def refcount(self, block: int) -> int:
         return self.ref.get(int(block), 0)
 
     def block_table(self, seq: int) -> list[int]:
+        """Device block per logical block; -1 where released or swapped out."""
         return list(self.table.get(seq, []))
 
     def seq_len(self, seq: int) -> int:
@@ -88,28 +112,58 @@ class Ledger:
             out.append(max(0, min(self.bs, n - i * self.bs)))
         return out
 
+    def latest_resident(self):
+        """The victim: the resident sequence holding device blocks that arrived last."""
+        best = None
+        for s, tab in self.table.items():
+            if s in self.swapped or not any(b >= 0 for b in tab):
+                continue
+            if best is None or self.arrival[s] > self.arrival[best]:
+                best = s
+        return best
+
     # -- operations ----------------------------------------------------------------
+    def _create(self, seq: int) -> None:
+        if seq not in self.table:
+            self.table[seq] = []
+            self.length[seq] = 0
+            self._clock += 1
+            self.arrival[seq] = self._clock
+
+    def _resident(self, seq: int) -> None:
+        if seq in self.swapped:
+            raise LedgerError(f"seq {seq} is swapped out")
+
     def set_window(self, seq: int, window: int) -> None:
-        self.table.setdefault(seq, [])
-        self.length.setdefault(seq, 0)
+        self._create(seq)
         self.window[seq] = int(window)
 
     def take_copies(self) -> list[tuple[int, int, int]]:
         """End the batch: return its copies (src block, dst block, entries) in order."""
         out, self.pending = self.pending, []
         self.touched.clear()
+        self.copy_src.clear()
+        self.free.extend(self.quarantine)
+        self.quarantine = []
+        self.host_free.extend(self.host_quarantine)
+        self.host_quarantine = []
         return out
+
+    def _busy(self, block: int) -> bool:
+        return block in self.touched or block in self.copy_src
 
     def _release(self, block: int) -> None:
         self.ref[block] -= 1
         if self.ref[block] == 0:
             del self.ref[block]
-            self.free.append(block)
+            (self.quarantine if self._busy(block) else self.free).append(block)
 
     def append(self, seq: int, n: int) -> list[int]:
         """Append n tokens; return the slot of each (block * bs + offset, or -1)."""
-        tab = self.table.setdefault(seq, [])
-        cur = self.length.setdefault(seq, 0)
+        self._resident(seq)
+        self._create(seq)
+        tab = self.table[seq]
+        cur = self.length[seq]
         end = cur + n
         win = self.window.get(seq, 0)
         keep_from = max(0, end - win) if win > 0 else 0
@@ -130,7 +184,8 @@ class Ledger:
                     raise SharedBlock(f"seq {seq}: shared block {tab[last]} has writes pending")
                 cow = last
         need = len(new_blks) + (cow is not None)
-        if need > len(self.free) + sum(1 for i in release if self.ref[tab[i]] == 1):
+        freed_now = sum(1 for i in release if self.ref[tab[i]] == 1 and not self._busy(tab[i]))
+        if need > len(self.free) + freed_now:
             raise OutOfBlocks(f"seq {seq}: needs {need} blocks, {len(self.free)} free")
         for i in release:
             self._release(tab[i])
@@ -143,6 +198,7 @@ class Ledger:
             tab[cow] = b
             self.pending.append((old, b, cur - cow * self.bs))
             self.touched.add(b)
+            self.copy_src.add(old)
         for i in range(len(tab), n_blk_after):
             if i in new_blks:
                 b = self.free.popleft()
@@ -161,24 +217,10 @@ class Ledger:
                 self.touched.add(b)
         return slots
 
-    def fork(self, dst: int, src: int) -> None:
-        """``dst`` (new) becomes a copy of ``src``: its length, window and physical blocks."""
-        if self.table.get(dst) or self.length.get(dst, 0):
-            raise LedgerError(f"seq {dst} is not empty")
-        if src not in self.table or src == dst:
-            raise LedgerError(f"unknown sequence {src}")
-        tab = list(self.table[src])
-        for b in tab:
-            if b >= 0:
-                self.ref[b] += 1
-        self.table[dst] = tab
-        self.length[dst] = self.length[src]
-        if src in self.window:
-            self.window[dst] = self.window[src]
-
     def share_prefix(self, dst: int, src: int, n_tokens: int) -> None:
         """``dst`` (new) begins with the first n_tokens of ``src``, sharing its blocks."""
-        if self.table.get(dst):
+        self._resident(src)
+        if self.table.get(dst) or dst in self.swapped:
             raise LedgerError(f"seq {dst} is not empty")
         if n_tokens > self.length.get(src, 0):
             raise LedgerError("prefix longer than source")
@@ -188,23 +230,89 @@ class Ledger:
             raise LedgerError("prefix holds released blocks")
         for b in blocks:
             self.ref[b] += 1
+        self._create(dst)
         self.table[dst] = list(blocks)
         self.length[dst] = n_tokens
+
+    def fork(self, dst: int, src: int) -> None:
+        """``dst`` (new) becomes a copy of ``src``: its length, window and physical blocks."""
+        if self.table.get(dst) or self.length.get(dst, 0) or dst in self.swapped:
+            raise LedgerError(f"seq {dst} is not empty")
+        if src not in self.table or src == dst:
+            raise LedgerError(f"unknown sequence {src}")
+        self._resident(src)
+        tab = list(self.table[src])
+        for b in tab:
+            if b >= 0:
+                self.ref[b] += 1
+        self._create(dst)
+        self.table[dst] = tab
+        self.length[dst] = self.length[src]
+        if src in self.window:
+            self.window[dst] = self.window[src]
+
+    def swap_out(self, seq: int) -> list[tuple[int, int]]:
+        """Move the blocks ``seq`` holds alone to host blocks; (device, host) pairs."""
+        if seq not in self.table:
+            raise LedgerError(f"unknown sequence {seq}")
+        self._resident(seq)
+        tab = self.table[seq]
+        alone = [i for i, b in enumerate(tab) if b >= 0 and self.ref[b] == 1]
+        if any(tab[i] in self.touched for i in alone):
+            raise SharedBlock(f"seq {seq}: a block has writes pending")
+        if len(alone) > len(self.host_free):
+            raise OutOfBlocks(f"seq {seq}: needs {len(alone)} host blocks")
+        where = [-1] * len(tab)
+        pairs = []
+        for i in alone:
+            h = self.host_free.popleft()
+            pairs.append((tab[i], h))
+            where[i] = h
+            self._release(tab[i])
+            tab[i] = -1
+        self.swapped[seq] = where
+        return pairs
+
+    def swap_in(self, seq: int) -> list[tuple[int, int]]:
+        """Bring a swapped sequence back into free device blocks; (host, device) pairs."""
+        if seq not in self.swapped:
+            raise LedgerError(f"seq {seq} is not swapped out")
+        where = self.swapped[seq]
+        need = sum(1 for h in where if h >= 0)
+        if need > len(self.free):
+            raise OutOfBlocks(f"seq {seq}: needs {need} blocks, {len(self.free)} free")
+        tab = self.table[seq]
+        pairs = []
+        for i, h in enumerate(where):
+            if h >= 0:
+                b = self.free.popleft()
+                self.ref[b] = 1
+                tab[i] = b
+                pairs.append((h, b))
+                self.touched.add(b)
+                self.host_quarantine.append(h)
+        del self.swapped[seq]
+        return pairs
 
     def free_seq(self, seq: int) -> None:
         for b in self.table.pop(seq, []):
             if b >= 0:
                 self._release(b)
+        for h in self.swapped.pop(seq, []):
+            if h >= 0:
+                self.host_quarantine.append(h)
         self.length.pop(seq, None)
         self.window.pop(seq, None)
+        self.arrival.pop(seq, None)
 
 
 def run_script(ledger: Ledger, script):
     """Apply a workload's ledger script.  Returns ({Append index: slots},
-    {Append index: copies that append recorded}); a Flush ends a batch."""
-    from workloads import Append, Flush, Fork, Free, SetWindow, SharePrefix
+    {Append index: copies that append recorded}, {SwapOut / SwapIn index: block pairs});
+    a Flush ends a batch."""
+    from workloads import Append, Flush, Fork, Free, SetWindow, SharePrefix, SwapIn, SwapOut
 
-    slots, copies = {}, {}
+    slots, copies, swaps = {}, {}, {}
     for i, op in enumerate(script):
         if isinstance(op, Append):
             before = len(ledger.pending)
@@ -220,6 +328,11 @@ def run_script(ledger: Ledger, script):
             ledger.free_seq(op.seq)
         elif isinstance(op, SetWindow):
             ledger.set_window(op.seq, op.window)
+        elif isinstance(op, SwapOut):
+            seq = ledger.latest_resident() if op.seq is None else op.seq
+            swaps[i] = (seq, ledger.swap_out(seq))
+        elif isinstance(op, SwapIn):
+            swaps[i] = (op.seq, ledger.swap_in(op.seq))
         else:  # pragma: no cover
             raise TypeError(op)
-    return slots, copies
+    return slots, copies, swaps

@@ -30,13 +30,15 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
 BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares
-EXPORTS = ("pa_write_kv", "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode", "pa_decode_plan",
+EXPORTS = ("pa_write_kv", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode", "pa_decode_plan",
            "pa_decode_attend", "pa_set_decode_profile_events", "pa_set_chunk_profile_events",
            "pa_status_string",
            "pa_pool_create", "pa_pool_destroy", "pa_seq_set_window", "pa_seq_append",
            "pa_seq_share_prefix", "pa_seq_free", "pa_seq_block_table", "pa_pool_block_tables",
            "pa_seq_len", "pa_pool_num_free", "pa_block_refcount", "pa_seq_fork",
-           "pa_pool_take_copies", "pa_pool_num_pending_copies")
+           "pa_pool_take_copies", "pa_pool_num_pending_copies", "pa_pool_set_host_blocks",
+           "pa_pool_num_host_free", "pa_pool_latest_resident", "pa_seq_swap_out",
+           "pa_seq_swap_in")
 
 
 class PAError(RuntimeError):
@@ -68,6 +70,7 @@ def load():
     sig = {
         "pa_write_kv": (i32, [P, P, P, i32, P, P, D, P]),
         "pa_copy_blocks": (i32, [P, P, D, P, i32, P, P]),
+        "pa_swap_blocks": (i32, [P, P, P, P, D, i32, i32, P, i32, P, P]),
         "pa_decode_workspace_size": (ctypes.c_size_t, [D, i32, i32, i32, i32]),
         "pa_decode": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32, i32, P,
                             ctypes.c_size_t, P]),
@@ -92,6 +95,11 @@ def load():
         "pa_seq_fork": (i32, [P, i64, i64]),
         "pa_pool_take_copies": (i32, [P, P, i32, ctypes.POINTER(i32)]),
         "pa_pool_num_pending_copies": (i32, [P]),
+        "pa_pool_set_host_blocks": (i32, [P, i32]),
+        "pa_pool_num_host_free": (i32, [P]),
+        "pa_pool_latest_resident": (i32, [P, ctypes.POINTER(i64)]),
+        "pa_seq_swap_out": (i32, [P, i64, P, i32, ctypes.POINTER(i32)]),
+        "pa_seq_swap_in": (i32, [P, i64, P, i32, ctypes.POINTER(i32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -204,6 +212,29 @@ def copy_blocks(k_cache, v_cache, copies, error_word=None, stream=None) -> None:
                             _dev_ptr(copies, "copies", torch.int32) if n else None, n,
                             _dev_ptr(error_word, "error_word", torch.int32), _stream(stream))
     _check(rc, "pa_copy_blocks")
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, error_word=None, stream=None) -> None:
+    """pa_swap_blocks: whole blocks src -> dst for int32 [n][2] (src, dst) device pairs.
+    Either pool may be a pinned host tensor (pin_memory=True) of the same tile shape."""
+    torch = _torch()
+    lib = load()
+    if (src_k.shape[1:] != dst_k.shape[1:] or src_k.shape != src_v.shape
+            or dst_k.shape != dst_v.shape or src_k.dtype != dst_k.dtype):
+        raise ValueError("the two pools must have one tile shape and dtype")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n][2]")
+    for t, name in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
+        if not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a contiguous device or pinned host tensor")
+    desc = cache_desc(src_k)
+    n = pairs.shape[0]
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    rc = lib.pa_swap_blocks(p(src_k), p(src_v), p(dst_k), p(dst_v), ctypes.byref(desc),
+                            src_k.shape[0], dst_k.shape[0],
+                            _dev_ptr(pairs, "pairs", torch.int32) if n else None, n,
+                            _dev_ptr(error_word, "error_word", torch.int32), _stream(stream))
+    _check(rc, "pa_swap_blocks")
 
 
 def workspace_size(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len,
@@ -341,6 +372,39 @@ class Pool:
 
     def free(self, seq):
         _check(self._lib.pa_seq_free(self._h, seq), "pa_seq_free")
+
+    def set_host_blocks(self, n):
+        _check(self._lib.pa_pool_set_host_blocks(self._h, n), "pa_pool_set_host_blocks")
+
+    def num_host_free(self) -> int:
+        return int(self._lib.pa_pool_num_host_free(self._h))
+
+    def latest_resident(self):
+        s = ctypes.c_int64()
+        rc = self._lib.pa_pool_latest_resident(self._h, ctypes.byref(s))
+        if rc == -9:
+            return None
+        _check(rc, "pa_pool_latest_resident")
+        return int(s.value)
+
+    def _swap(self, fn, seq, what):
+        n = ctypes.c_int32()
+        rc = fn(self._h, seq, None, 0, ctypes.byref(n))
+        if rc not in (0, -2):
+            _check(rc, what)
+        out = np.empty((max(1, n.value), 2), np.int32)
+        if rc == -2:
+            _check(fn(self._h, seq, out.ctypes.data_as(ctypes.c_void_p), out.shape[0],
+                      ctypes.byref(n)), what)
+        return out[:n.value].copy()
+
+    def swap_out(self, seq) -> np.ndarray:
+        """Evict seq: its (device block, host block) pairs, int32 [n][2]."""
+        return self._swap(self._lib.pa_seq_swap_out, seq, "pa_seq_swap_out")
+
+    def swap_in(self, seq) -> np.ndarray:
+        """Bring seq back: its (host block, device block) pairs, int32 [n][2]."""
+        return self._swap(self._lib.pa_seq_swap_in, seq, "pa_seq_swap_in")
 
     def block_table(self, seq) -> list:
         n = ctypes.c_int32()

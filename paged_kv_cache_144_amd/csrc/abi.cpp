@@ -163,6 +163,59 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The address a kernel uses for p: device memory as is, pinned host memory through its
+// device mapping.  Anything else (pageable host memory) is refused.
+pa_status kernel_address(const void* p, const void** out) {
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();   // do not leave the failed query as the last error
+        return PA_ERR_UNSUPPORTED;
+    }
+    if (attr.type == hipMemoryTypeDevice) {
+        *out = p;
+        return PA_OK;
+    }
+    if (attr.type == hipMemoryTypeHost && attr.devicePointer) {
+        // the same offset into the allocation, through its device mapping
+        *out = (const char*)attr.devicePointer + ((const char*)p - (const char*)attr.hostPointer);
+        return PA_OK;
+    }
+    return PA_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                         const pa_cache_desc* desc, int32_t src_blocks, int32_t dst_blocks,
+                         const int32_t* pairs, int32_t n, int32_t* error_word, void* stream) {
+    if (!desc) return PA_ERR_NULL;
+    if (!cache_dtype_ok(desc->dtype)) return PA_ERR_DTYPE;
+    if (desc->num_kv_heads <= 0 || desc->num_kv_heads > 65535 || desc->head_dim <= 0 ||
+        desc->block_size <= 0 || src_blocks < 0 || dst_blocks < 0 || n < 0)
+        return PA_ERR_SHAPE;
+    const int64_t tile = desc->block_size * (row_bytes(desc) + scale_bytes(desc));
+    if (tile % 16 || tile > INT32_MAX / 2 ||
+        (is_q8(desc->dtype) && (desc->head_dim % pa::kQ8Group || desc->block_size != pa::kBlock)))
+        return PA_ERR_UNSUPPORTED;
+    if (n == 0) return PA_OK;
+    if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return PA_ERR_NULL;
+    const void *sk, *sv, *dk, *dv;
+    pa_status st;
+    if ((st = kernel_address(src_k, &sk)) != PA_OK || (st = kernel_address(src_v, &sv)) != PA_OK ||
+        (st = kernel_address(dst_k, &dk)) != PA_OK || (st = kernel_address(dst_v, &dv)) != PA_OK)
+        return st;
+    hipError_t e = pa::launch_swap_blocks(sk, sv, (void*)dk, (void*)dv, pairs, n, src_blocks,
+                                          dst_blocks, desc->num_kv_heads, (int32_t)tile,
+                                          error_word, (hipStream_t)stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
                                 int32_t total_q_rows, int32_t num_q_heads,
                                 int32_t max_seq_len) {

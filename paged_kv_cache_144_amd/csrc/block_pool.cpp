@@ -8,8 +8,15 @@
 // in each block and frees them when the request ends (basic decoding), counts the
 // sequences referencing a block and copies a shared block when samples write different
 // tokens into it, while earlier blocks stay shared (parallel sampling), and evicts all of
-// a sequence or none of it (scheduling).  A sliding-window layer keeps only its last W tokens (sotaaz.com,
-// section on layer kinds).
+// a sequence or none of it, the latest arrival first, moving its blocks to CPU memory until
+// there is room again (scheduling).  A sliding-window layer keeps only its last W tokens
+// (sotaaz.com, section on layer kinds).
+//
+// Batches: the caller carries out one batch's work in the order swap-outs, copies,
+// swap-ins, slot writes (each kind all at once) and ends the batch with
+// pa_pool_take_copies.  So a copy or a swap-out may not read a block with writes pending
+// in the batch, and a block (or host block) freed while work on it is pending joins its
+// free queue only when the batch ends.
 //
 // The CPU side owns this ledger and ships block tables to the GPU each step (velog.io,
 // "Batching strategies", section 5: the scheduler and block manager run on the CPU).
@@ -24,9 +31,12 @@
 namespace {
 
 struct Seq {
-    std::vector<int32_t> blocks;  // logical -> physical; -1 = released / never held
+    std::vector<int32_t> blocks;  // logical -> physical; -1 = released / never held / on host
+    std::vector<int32_t> host;    // while swapped out: host block per logical block, or -1
     int64_t len = 0;              // tokens appended so far
     int32_t window = 0;           // 0 = keep everything
+    int64_t arrival = 0;          // creation order
+    bool swapped = false;
 };
 
 }  // namespace
@@ -43,15 +53,56 @@ struct pa_pool {
     std::vector<int32_t> pending;
     std::vector<uint8_t> touched;
     std::vector<int32_t> touched_list;
+    // Blocks a pending copy reads, and blocks freed while work on them is pending: those
+    // join the free queue when the batch ends, so no batch reads and writes one block in
+    // two roles.
+    std::vector<uint8_t> copy_src;
+    std::vector<int32_t> copy_src_list;
+    std::vector<int32_t> quarantine;
+    // host swap space
+    int32_t num_host = 0;
+    std::deque<int32_t> host_free;
+    std::vector<int32_t> host_quarantine;
+    int64_t clock = 0;
 
+    bool busy(int32_t b) const { return touched[b] || copy_src[b]; }
     void release(int32_t b) {
-        if (--ref[b] == 0) free_q.push_back(b);
+        if (--ref[b] != 0) return;
+        if (busy(b))
+            quarantine.push_back(b);
+        else
+            free_q.push_back(b);
     }
     void touch(int32_t b) {
         if (!touched[b]) {
             touched[b] = 1;
             touched_list.push_back(b);
         }
+    }
+    void mark_copy_src(int32_t b) {
+        if (!copy_src[b]) {
+            copy_src[b] = 1;
+            copy_src_list.push_back(b);
+        }
+    }
+    // the sequence, created (with the next arrival stamp) if it does not exist
+    Seq& create(int64_t seq) {
+        auto it = seqs.find(seq);
+        if (it != seqs.end()) return it->second;
+        Seq& s = seqs[seq];
+        s.arrival = ++clock;
+        return s;
+    }
+    void end_batch() {
+        pending.clear();
+        for (int32_t b : touched_list) touched[b] = 0;
+        touched_list.clear();
+        for (int32_t b : copy_src_list) copy_src[b] = 0;
+        copy_src_list.clear();
+        for (int32_t b : quarantine) free_q.push_back(b);
+        quarantine.clear();
+        for (int32_t h : host_quarantine) host_free.push_back(h);
+        host_quarantine.clear();
     }
 };
 
@@ -68,6 +119,7 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* 
     p->bs = block_size;
     p->ref.assign(num_blocks, 0);
     p->touched.assign(num_blocks, 0);
+    p->copy_src.assign(num_blocks, 0);
     if (free_order) {
         if (free_order_len < 0 || free_order_len > num_blocks) {
             delete p;
@@ -95,8 +147,8 @@ void pa_pool_destroy(pa_pool* p) { delete p; }
 pa_status pa_seq_set_window(pa_pool* p, int64_t seq, int32_t window) {
     if (!p) return PA_ERR_NULL;
     if (window < 0) return PA_ERR_SHAPE;
-    Seq& s = p->seqs[seq];
-    if (s.len != 0) return PA_ERR_BAD_SEQ;
+    Seq& s = p->create(seq);
+    if (s.len != 0 || s.swapped) return PA_ERR_BAD_SEQ;
     s.window = window;
     return PA_OK;
 }
@@ -104,7 +156,11 @@ pa_status pa_seq_set_window(pa_pool* p, int64_t seq, int32_t window) {
 pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slots_out) {
     if (!p) return PA_ERR_NULL;
     if (n_tokens < 0) return PA_ERR_SHAPE;
-    Seq& s = p->seqs[seq];
+    {
+        auto it = p->seqs.find(seq);
+        if (it != p->seqs.end() && it->second.swapped) return PA_ERR_BAD_SEQ;
+    }
+    Seq& s = p->create(seq);
     const int64_t bs = p->bs;
     const int64_t cur = s.len, end = cur + n_tokens;
     // first position that is still kept after this append
@@ -131,7 +187,7 @@ pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slot
     int64_t avail = (int64_t)p->free_q.size();
     const int64_t rel_end = first_kept_blk < held ? first_kept_blk : held;
     for (int64_t i = 0; i < rel_end; ++i)
-        if (s.blocks[i] >= 0 && p->ref[s.blocks[i]] == 1) ++avail;
+        if (s.blocks[i] >= 0 && p->ref[s.blocks[i]] == 1 && !p->busy(s.blocks[i])) ++avail;
     if (need > avail) return PA_ERR_OUT_OF_BLOCKS;
 
     for (int64_t i = 0; i < rel_end; ++i) {
@@ -146,6 +202,7 @@ pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slot
         p->free_q.pop_front();
         p->ref[b] = 1;
         --p->ref[old];
+        p->mark_copy_src(old);
         s.blocks[cow] = b;
         p->pending.push_back(old);
         p->pending.push_back(b);
@@ -177,15 +234,22 @@ pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slot
 
 pa_status pa_seq_fork(pa_pool* p, int64_t dst, int64_t src) {
     if (!p) return PA_ERR_NULL;
-    auto it = p->seqs.find(src);
-    if (it == p->seqs.end() || dst == src) return PA_ERR_BAD_SEQ;
     auto dit = p->seqs.find(dst);
-    if (dit != p->seqs.end() && (dit->second.len != 0 || !dit->second.blocks.empty()))
+    if (dit != p->seqs.end() &&
+        (dit->second.len != 0 || !dit->second.blocks.empty() || dit->second.swapped))
         return PA_ERR_BAD_SEQ;
-    Seq copy = it->second;
-    for (int32_t b : copy.blocks)
+    auto it = p->seqs.find(src);
+    if (it == p->seqs.end() || dst == src || it->second.swapped) return PA_ERR_BAD_SEQ;
+    for (int32_t b : it->second.blocks)
         if (b >= 0) ++p->ref[b];
-    p->seqs[dst] = std::move(copy);
+    const Seq& from = it->second;
+    std::vector<int32_t> blocks = from.blocks;
+    const int64_t len = from.len;
+    const int32_t window = from.window;
+    Seq& d = p->create(dst);
+    d.blocks = std::move(blocks);
+    d.len = len;
+    d.window = window;
     return PA_OK;
 }
 
@@ -200,9 +264,106 @@ pa_status pa_pool_take_copies(pa_pool* p, int32_t* out, int32_t cap, int32_t* n)
     if (count > cap) return PA_ERR_SHAPE;
     if (count && !out) return PA_ERR_NULL;
     for (size_t i = 0; i < p->pending.size(); ++i) out[i] = p->pending[i];
-    p->pending.clear();
-    for (int32_t b : p->touched_list) p->touched[b] = 0;
-    p->touched_list.clear();
+    p->end_batch();
+    return PA_OK;
+}
+
+pa_status pa_pool_set_host_blocks(pa_pool* p, int32_t num_host_blocks) {
+    if (!p) return PA_ERR_NULL;
+    if (num_host_blocks < 0) return PA_ERR_SHAPE;
+    if ((int32_t)p->host_free.size() != p->num_host || !p->host_quarantine.empty())
+        return PA_ERR_BAD_SEQ;   // host blocks in use
+    p->num_host = num_host_blocks;
+    p->host_free.clear();
+    for (int32_t h = 0; h < num_host_blocks; ++h) p->host_free.push_back(h);
+    return PA_OK;
+}
+
+int32_t pa_pool_num_host_free(const pa_pool* p) { return p ? (int32_t)p->host_free.size() : 0; }
+
+pa_status pa_pool_latest_resident(const pa_pool* p, int64_t* seq) {
+    if (!p || !seq) return PA_ERR_NULL;
+    const Seq* best = nullptr;
+    int64_t best_id = 0;
+    for (const auto& kv : p->seqs) {
+        const Seq& s = kv.second;
+        if (s.swapped) continue;
+        bool any = false;
+        for (int32_t b : s.blocks) any = any || b >= 0;
+        if (!any) continue;
+        if (!best || s.arrival > best->arrival) {
+            best = &s;
+            best_id = kv.first;
+        }
+    }
+    if (!best) return PA_ERR_BAD_SEQ;
+    *seq = best_id;
+    return PA_OK;
+}
+
+pa_status pa_seq_swap_out(pa_pool* p, int64_t seq, int32_t* pairs, int32_t cap, int32_t* n) {
+    if (!p || !n) return PA_ERR_NULL;
+    *n = 0;
+    auto it = p->seqs.find(seq);
+    if (it == p->seqs.end() || it->second.swapped) return PA_ERR_BAD_SEQ;
+    Seq& s = it->second;
+    int32_t count = 0;
+    for (int32_t b : s.blocks) {
+        if (b >= 0 && p->ref[b] == 1) {
+            if (p->touched[b]) return PA_ERR_SHARED_BLOCK;   // writes pending
+            ++count;
+        }
+    }
+    if (count > (int32_t)p->host_free.size()) return PA_ERR_OUT_OF_BLOCKS;
+    *n = count;
+    if (count > cap) return PA_ERR_SHAPE;
+    if (count && !pairs) return PA_ERR_NULL;
+    s.host.assign(s.blocks.size(), -1);
+    int32_t k = 0;
+    for (size_t i = 0; i < s.blocks.size(); ++i) {
+        const int32_t b = s.blocks[i];
+        if (b < 0 || p->ref[b] != 1) continue;
+        const int32_t h = p->host_free.front();
+        p->host_free.pop_front();
+        pairs[2 * k] = b;
+        pairs[2 * k + 1] = h;
+        ++k;
+        s.host[i] = h;
+        p->release(b);
+        s.blocks[i] = -1;
+    }
+    s.swapped = true;
+    return PA_OK;
+}
+
+pa_status pa_seq_swap_in(pa_pool* p, int64_t seq, int32_t* pairs, int32_t cap, int32_t* n) {
+    if (!p || !n) return PA_ERR_NULL;
+    *n = 0;
+    auto it = p->seqs.find(seq);
+    if (it == p->seqs.end() || !it->second.swapped) return PA_ERR_BAD_SEQ;
+    Seq& s = it->second;
+    int32_t count = 0;
+    for (int32_t h : s.host) count += h >= 0;
+    if (count > (int32_t)p->free_q.size()) return PA_ERR_OUT_OF_BLOCKS;
+    *n = count;
+    if (count > cap) return PA_ERR_SHAPE;
+    if (count && !pairs) return PA_ERR_NULL;
+    int32_t k = 0;
+    for (size_t i = 0; i < s.host.size(); ++i) {
+        const int32_t h = s.host[i];
+        if (h < 0) continue;
+        const int32_t b = p->free_q.front();
+        p->free_q.pop_front();
+        p->ref[b] = 1;
+        s.blocks[i] = b;
+        pairs[2 * k] = h;
+        pairs[2 * k + 1] = b;
+        ++k;
+        p->touch(b);
+        p->host_quarantine.push_back(h);
+    }
+    s.host.clear();
+    s.swapped = false;
     return PA_OK;
 }
 
@@ -210,10 +371,11 @@ pa_status pa_seq_share_prefix(pa_pool* p, int64_t dst, int64_t src, int32_t n_to
     if (!p) return PA_ERR_NULL;
     if (n_tokens < 0) return PA_ERR_SHAPE;
     auto it = p->seqs.find(src);
-    if (it == p->seqs.end() || dst == src) return PA_ERR_BAD_SEQ;
+    if (it == p->seqs.end() || dst == src || it->second.swapped) return PA_ERR_BAD_SEQ;
     if (n_tokens > it->second.len) return PA_ERR_SHAPE;
     auto dit = p->seqs.find(dst);
-    if (dit != p->seqs.end() && (dit->second.len != 0 || !dit->second.blocks.empty()))
+    if (dit != p->seqs.end() &&
+        (dit->second.len != 0 || !dit->second.blocks.empty() || dit->second.swapped))
         return PA_ERR_BAD_SEQ;
     const int64_t nblk = (n_tokens + p->bs - 1) / p->bs;
     const std::vector<int32_t>& sb = it->second.blocks;
@@ -221,7 +383,7 @@ pa_status pa_seq_share_prefix(pa_pool* p, int64_t dst, int64_t src, int32_t n_to
         if (sb[i] < 0) return PA_ERR_BAD_SEQ;
     std::vector<int32_t> blocks(sb.begin(), sb.begin() + nblk);
     for (int32_t b : blocks) ++p->ref[b];
-    Seq& d = p->seqs[dst];
+    Seq& d = p->create(dst);
     d.blocks = std::move(blocks);
     d.len = n_tokens;
     return PA_OK;
@@ -233,6 +395,8 @@ pa_status pa_seq_free(pa_pool* p, int64_t seq) {
     if (it == p->seqs.end()) return PA_ERR_BAD_SEQ;
     for (int32_t b : it->second.blocks)
         if (b >= 0) p->release(b);
+    for (int32_t h : it->second.host)
+        if (h >= 0) p->host_quarantine.push_back(h);
     p->seqs.erase(it);
     return PA_OK;
 }

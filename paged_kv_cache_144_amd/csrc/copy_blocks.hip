@@ -47,6 +47,43 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kc,
     }
 }
 
+// Swapping: one workgroup per (pair, KV head) moves the whole tile (16-byte pieces of K,
+// then of V) from one pool to another; either may be pinned host memory, reached over the
+// host link.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(const char* __restrict__ sk,
+                                                          const char* __restrict__ sv,
+                                                          char* __restrict__ dk,
+                                                          char* __restrict__ dv,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int src_nb, int dst_nb, int hkv,
+                                                          int tile_bytes, int32_t* err) {
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int src = pairs[2 * c], dst = pairs[2 * c + 1];
+    if (src < 0 || src >= src_nb || dst < 0 || dst >= dst_nb) {
+        if (err && h == 0 && threadIdx.x == 0) atomicOr(err, kErrBlockId);
+        return;
+    }
+    const int64_t from = ((int64_t)src * hkv + h) * tile_bytes;
+    const int64_t to = ((int64_t)dst * hkv + h) * tile_bytes;
+    const int n = tile_bytes / 16;
+    for (int i = threadIdx.x; i < 2 * n; i += blockDim.x) {
+        const bool k = i < n;
+        const int64_t j = (int64_t)(k ? i : i - n) * 16;
+        st16((k ? dk : dv) + to + j, ld16((k ? sk : sv) + from + j));
+    }
+}
+
+hipError_t launch_swap_blocks(const void* sk, const void* sv, void* dk, void* dv,
+                              const int32_t* pairs, int32_t n, int32_t src_nb, int32_t dst_nb,
+                              int32_t hkv, int32_t tile_bytes, int32_t* err,
+                              hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(swap_blocks_kernel, dim3((unsigned)n, (unsigned)hkv), dim3(256), 0,
+                       stream, (const char*)sk, (const char*)sv, (char*)dk, (char*)dv, pairs,
+                       src_nb, dst_nb, hkv, tile_bytes, err);
+    return hipGetLastError();
+}
+
 hipError_t launch_copy_blocks(void* kc, void* vc, const int32_t* copies, int32_t n,
                               int32_t nb, int32_t hkv, int32_t bs, int32_t row_bytes,
                               int32_t scale_bytes, int32_t* err, hipStream_t stream) {

@@ -99,6 +99,10 @@ hipError_t launch_write_kv_q8(const void* k, const void* v, const int64_t* slots
 hipError_t launch_copy_blocks(void* kc, void* vc, const int32_t* copies, int32_t n,
                               int32_t nb, int32_t hkv, int32_t bs, int32_t row_bytes,
                               int32_t scale_bytes, int32_t* err, hipStream_t stream);
+hipError_t launch_swap_blocks(const void* sk, const void* sv, void* dk, void* dv,
+                              const int32_t* pairs, int32_t n, int32_t src_nb, int32_t dst_nb,
+                              int32_t hkv, int32_t tile_bytes, int32_t* err,
+                              hipStream_t stream);
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import Pool, alloc_workspace, copy_blocks, decode, q8_cache, write_kv
+from . import Pool, alloc_workspace, copy_blocks, decode, q8_cache, swap_blocks, write_kv
 
 TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
 
@@ -45,22 +45,30 @@ class DeviceWorkload:
 
     def __init__(self, w, device="cuda", poison=True, write=True):
         import torch
-        from workloads import Append, Flush, Fork, Free, SetWindow, SharePrefix
+        from workloads import Append, Flush, Fork, Free, SetWindow, SharePrefix, SwapIn, SwapOut
 
         self.w = w
         self.device = device
         pool = Pool(w.num_blocks, w.block_size, w.free_order)
+        nh = int(w.meta.get("host_blocks", 0))
+        if nh:
+            pool.set_host_blocks(nh)
         slots_all = np.full(w.k.shape[0], -1, np.int64)
-        # batches of (copies [n][3], slots of the tokens written in the batch)
+        # batches of (swap-out pairs, copies, swap-in pairs, slots of the tokens written);
+        # the device carries out each batch in that order
         batches = []
         cur = np.full(w.k.shape[0], -1, np.int64)
+        outs, ins = [], []
 
         def end_batch():
-            nonlocal cur
+            nonlocal cur, outs, ins
             copies = pool.take_copies()
-            if copies.size or (cur >= 0).any():
-                batches.append((copies, cur))
+            o = np.concatenate(outs) if outs else np.zeros((0, 2), np.int32)
+            i = np.concatenate(ins) if ins else np.zeros((0, 2), np.int32)
+            if copies.size or o.size or i.size or (cur >= 0).any():
+                batches.append((o, copies, i, cur))
             cur = np.full(w.k.shape[0], -1, np.int64)
+            outs, ins = [], []
 
         for op in w.script:
             if isinstance(op, Append):
@@ -70,6 +78,11 @@ class DeviceWorkload:
                     cur[op.off:op.off + op.nv] = s[op.n - op.nv:]
             elif isinstance(op, Flush):
                 end_batch()
+            elif isinstance(op, SwapOut):
+                seq = pool.latest_resident() if op.seq is None else op.seq
+                outs.append(pool.swap_out(seq))
+            elif isinstance(op, SwapIn):
+                ins.append(pool.swap_in(op.seq))
             elif isinstance(op, Fork):
                 pool.fork(op.dst, op.src)
             elif isinstance(op, SharePrefix):
@@ -83,10 +96,11 @@ class DeviceWorkload:
         end_batch()
         self.pool = pool
         self.slots = slots_all
-        self.batches = [(torch.from_numpy(c).to(device) if c.size else None,
-                         torch.from_numpy(sl).to(device)) for c, sl in batches]
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device) if a.size else None
+        self.batches = [(dev(o), dev(c), dev(i), torch.from_numpy(sl).to(device))
+                        for o, c, i, sl in batches]
         # copies of the last batch (the step that follows a fork), or None
-        self.step_copies = self.batches[-1][0] if self.batches else None
+        self.step_copies = self.batches[-1][1] if self.batches else None
         B = w.num_seqs
         self.max_blocks = max(1, max(len(pool.block_table(s)) for s in range(B)))
         self.block_tables_np = pool.block_tables(np.arange(B), self.max_blocks, w.reserved_block)
@@ -106,6 +120,10 @@ class DeviceWorkload:
         self.qsl = torch.from_numpy(w.query_start_loc()).to(device)
         self.q = to_device(w.q, w.dtype, device)
         self.max_seq_len = int(w.seq_lens.max()) if B else 0
+        # host swap space: pinned tiles shaped like the device pool's
+        hshape = (nh,) + tuple(self.k_cache.shape[1:])
+        self.host_k = torch.zeros(hshape, dtype=self.k_cache.dtype, pin_memory=nh > 0)
+        self.host_v = torch.zeros(hshape, dtype=self.k_cache.dtype, pin_memory=nh > 0)
         self.k_new = to_device(w.k, w.dtype, device)
         self.v_new = to_device(w.v, w.dtype, device)
         self.slot_mapping = torch.from_numpy(slots_all).to(device)
@@ -119,10 +137,16 @@ class DeviceWorkload:
         return bool((self.w.q_rows != 1).any())
 
     def write(self, stream=None):
-        """Carry out every batch in order: its copies, then its slot writes."""
-        for copies, slots in self.batches:
+        """Carry out every batch in order: swap-outs, copies, swap-ins, slot writes."""
+        for outs, copies, ins, slots in self.batches:
+            if outs is not None:
+                swap_blocks(self.k_cache, self.v_cache, self.host_k, self.host_v, outs,
+                            stream=stream)
             if copies is not None:
                 copy_blocks(self.k_cache, self.v_cache, copies, stream=stream)
+            if ins is not None:
+                swap_blocks(self.host_k, self.host_v, self.k_cache, self.v_cache, ins,
+                            stream=stream)
             write_kv(self.k_new, self.v_new, slots, self.k_cache, self.v_cache, stream)
 
     def decode(self, out=None, out_dtype=None, k_cache=None, v_cache=None, stream=None, **kw):

@@ -170,6 +170,7 @@ def pin_walkthrough(orc):
         if op == "append":
             led.append(0, int(n))
             assert led.filled(0) == [int(x) for x in filled.split(",")], led.filled(0)
+            led.take_copies()               # each step's writes are done before the next
         else:
             led.free_seq(0)
             assert led.num_free() == 16 and led.block_table(0) == []
@@ -265,6 +266,106 @@ def pin_cow_attention(orc):
             assert ref.ledger.refcount(b) == 3
 
 
+def pin_swap_ledger(orc):
+    # eviction: all of a sequence or none of it, the latest arrival first, to host blocks
+    led = orc.Ledger(range(12), 4, host_blocks=3)
+    led.append("a", 9)                     # 3 blocks
+    led.append("b", 5)                     # 2 blocks
+    led.append("c", 4)                     # 1 block
+    led.take_copies()
+    assert led.latest_resident() == "c"
+    assert led.swap_out("c") == [(5, 0)]
+    assert led.latest_resident() == "b" and led.block_table("c") == [-1]
+    assert led.num_free() == 7 and led.num_host_free() == 2
+    # not enough host blocks: refused, nothing moves
+    before = (led.block_table("a"), led.num_free(), led.num_host_free())
+    try:
+        led.swap_out("a")
+    except orc.OutOfBlocks:
+        pass
+    else:
+        raise AssertionError("partial eviction accepted")
+    assert (led.block_table("a"), led.num_free(), led.num_host_free()) == before
+    # a swapped sequence can do nothing until it is back
+    for call in (lambda: led.append("c", 1), lambda: led.fork("d", "c")):
+        try:
+            call()
+        except orc.LedgerError:
+            pass
+        else:
+            raise AssertionError("swapped sequence used")
+    # back into the first free blocks; its host block waits for the batch end
+    assert led.swap_in("c") == [(0, 6)] and led.block_table("c") == [6]
+    assert led.num_host_free() == 2
+    led.take_copies()
+    assert led.num_host_free() == 3
+    # writes pending in the batch block an eviction
+    led.append("b", 1)
+    try:
+        led.swap_out("b")
+    except orc.SharedBlock:
+        pass
+    else:
+        raise AssertionError("eviction with pending writes accepted")
+    led.take_copies()
+    # a block shared with another sequence stays on the device, still referenced
+    led.fork("d", "a")
+    led.take_copies()
+    assert led.latest_resident() == "d" and led.swap_out("d") == []
+    assert all(led.refcount(x) == 2 for x in led.block_table("a"))
+    assert led.swap_in("d") == []
+    # swap-in needs a free device block per host block, all or nothing
+    led.swap_out("b")
+    led.take_copies()
+    led.append("e", 4 * led.num_free())
+    try:
+        led.swap_in("b")
+    except orc.OutOfBlocks:
+        pass
+    else:
+        raise AssertionError("swap-in without free blocks accepted")
+    led.free_seq("e")
+    led.take_copies()
+    assert len(led.swap_in("b")) == 2
+
+
+def pin_batch_reuse(orc):
+    # a block freed while a copy still has to read it is not handed out in the same batch
+    led = orc.Ledger([0, 1, 2, 3], 4)
+    led.append("x", 6)                     # blocks 0, 1
+    led.fork("y", "x")
+    led.take_copies()
+    led.append("x", 1)                     # copies block 1 -> 2
+    led.free_seq("y")                      # block 1 has no holder left
+    assert led.num_free() == 1             # block 3 only; block 1 waits
+    led.append("z", 4)
+    assert led.block_table("z") == [3]
+    try:
+        led.append("w", 1)
+    except orc.OutOfBlocks:
+        pass
+    else:
+        raise AssertionError("a block with a pending copy was handed out")
+    assert led.take_copies() == [(1, 2, 2)]
+    led.append("w", 1)
+    assert led.block_table("w") == [1]
+
+
+def pin_swap_attention(orc):
+    # after evictions, newcomers in the freed blocks and swap-ins, every sequence attends
+    # over exactly its own tokens (unwritten and free slots hold NaN)
+    w = workloads.make("swap", batch=10, victims=3, lo=5, hi=70, hq=4, hkv=2, d=64)
+    ref = orc.Reference(w)
+    got = ref.attention()
+    k, v, off, first = contiguous_inputs(w)
+    want = orc.contiguous_attention(w.q, k, v, off, first, w.seq_lens, w.scale, w.dtype,
+                                    w.num_q_heads, w.query_start_loc(), w.window)
+    assert np.isfinite(got).all() and np.array_equal(got, want)
+    # the victims were the three last arrivals and came back to other blocks
+    outs = [ref.swaps[i] for i in sorted(ref.swaps) if isinstance(w.script[i], workloads.SwapOut)]
+    assert [s for s, _ in outs] == [9, 8, 7]
+
+
 def pin_all_or_nothing(orc):
     led = orc.Ledger(range(4), 16)
     led.append(0, 40)                       # 3 blocks
@@ -288,9 +389,18 @@ def pin_window_ledger(orc):
     assert len(tab) == 7 and tab[:4] == [-1] * 4 and all(b >= 0 for b in tab[4:])
     assert slots[:68] == [-1] * 68 and all(s >= 0 for s in slots[68:])
     assert led.num_free() == 97
+    led.take_copies()                       # the step's writes are done
     led.append(0, 30)                       # now 130: keeps 98..129 -> blocks 6, 7, 8
     tab = led.block_table(0)
     assert tab[:6] == [-1] * 6 and all(b >= 0 for b in tab[6:]) and led.num_free() == 97
+    # within one batch, released blocks that still have writes pending wait for its end
+    led = orc.Ledger(range(100), 16)
+    led.set_window(0, 32)
+    led.append(0, 100)
+    led.append(0, 30)
+    assert led.num_free() == 95
+    led.take_copies()
+    assert led.num_free() == 97
 
 
 # ------------------------------------------------------------------ element widening
@@ -576,7 +686,8 @@ def pin_nan_isolation(orc):
 
 ALL = [pin_kv_bytes, pin_kv_totals, pin_kv_q8_bytes, pin_kv_read_bytes, pin_q8_grid,
        pin_q8_rounding, pin_q8_paged, pin_blocks_and_waste, pin_walkthrough,
-       pin_parallel_sampling, pin_cow_rules, pin_cow_attention, pin_all_or_nothing, pin_window_ledger, pin_widen, pin_write_kv,
+       pin_parallel_sampling, pin_cow_rules, pin_cow_attention, pin_swap_ledger,
+       pin_batch_reuse, pin_swap_attention, pin_all_or_nothing, pin_window_ledger, pin_widen, pin_write_kv,
        pin_one_token, pin_uniform, pin_two_tokens, pin_needle, pin_contiguous, pin_permutation,
        pin_sdpa, pin_brute, pin_window, pin_chunk_rows, pin_shared_prefix, pin_gqa_mapping,
        pin_nan_isolation]

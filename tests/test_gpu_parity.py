@@ -86,6 +86,10 @@ SMALL = [
     ("parallel_sampling", dict(prompts=3, samples=3, lo=20, hi=300, dtype="q8_f16")),
     ("prefix_mixed", dict(batch=10, prefix=64, suffix_hi=80, chunks=2, chunk_rows=40,
                           chunk_lo=100, chunk_hi=300, dtype="q8_bf16")),
+    # swapping: evictions to pinned host memory, newcomers in the freed blocks, swap-ins
+    ("swap", dict(batch=10, victims=3, lo=5, hi=70, hq=4, hkv=2, d=64, dtype="f32")),
+    ("swap", dict(batch=12, victims=4, lo=64, hi=700)),
+    ("swap", dict(batch=8, victims=3, lo=20, hi=300, hq=8, hkv=2, dtype="q8_bf16")),
 ]
 
 
@@ -103,6 +107,11 @@ def test_small_parity(torch, pa, orc, name, kw):
     vc = to_storage_np(dw.v_cache, w.dtype)
     assert np.array_equal(kc.view(np.uint8), ref.k_cache.view(np.uint8))
     assert np.array_equal(vc.view(np.uint8), ref.v_cache.view(np.uint8))
+    if ref.host_k.size:     # the host swap space, bit for bit
+        assert np.array_equal(to_storage_np(dw.host_k, w.dtype).view(np.uint8),
+                              ref.host_k.view(np.uint8))
+        assert np.array_equal(to_storage_np(dw.host_v, w.dtype).view(np.uint8),
+                              ref.host_v.view(np.uint8))
     out = dw.decode().cpu().numpy()
     check_close(out, ref.attention(), f"{name} {kw}")
     # device error word is clean
@@ -269,7 +278,7 @@ def test_write_kv_skips(torch, pa):
 
 
 FULL = [("tiny", {}), ("opt13b", {}), ("gqa", {}), ("prefix_mixed", {}), ("swa", {}),
-        ("parallel_sampling", {}), ("opt13b", dict(dtype="q8_f16")),
+        ("parallel_sampling", {}), ("swap", {}), ("opt13b", dict(dtype="q8_f16")),
         ("gqa", dict(dtype="q8_bf16"))]
 
 
@@ -337,6 +346,55 @@ def test_copy_blocks_direct(torch, pa, orc, dtype, d):
     assert np.array_equal(to_storage_np(kd, dtype).view(np.uint8), want_k.view(np.uint8))
     assert np.array_equal(to_storage_np(vd, dtype).view(np.uint8), want_v.view(np.uint8))
     assert int(err.item()) == 1
+
+
+@pytest.mark.parametrize("dtype,d", [("f16", 128), ("q8_bf16", 128), ("f32", 64)])
+def test_swap_blocks_direct(torch, pa, orc, dtype, d):
+    """pa_swap_blocks device -> pinned host -> device: whole tiles (8-bit scale rows
+    included) bit for bit, NaN patterns too; pairs out of range are skipped with error bit
+    1 and nothing else is touched."""
+    say("swap_blocks", dtype, d)
+    from paged_kv_cache_144_amd.runner import to_device, to_storage_np
+    rng = np.random.default_rng(7 + d)
+    nb, nh, hkv = 40, 12, 3
+    if dtype.startswith("q8"):
+        shape = (nb, hkv, 17, d)
+        dev = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        dk = torch.from_numpy(dev).cuda()
+        dv = torch.from_numpy(dev[::-1].copy()).cuda()
+        hk = torch.zeros((nh, hkv, 17, d), dtype=torch.uint8, pin_memory=True)
+    else:
+        shape = (nb, hkv, 16, d)
+        dev = workloads.to_storage(rng.standard_normal(int(np.prod(shape))), dtype).reshape(shape)
+        dev[3, 1, 5:] = workloads.nan_bits(dtype)
+        dk = to_device(dev, dtype, "cuda")
+        dv = to_device(dev[::-1].copy(), dtype, "cuda")
+        hk = torch.zeros((nh,) + shape[1:], dtype=dk.dtype, pin_memory=True)
+    hv = torch.zeros_like(hk).pin_memory()
+    out_pairs = np.array([[3, 0], [7, 5], [11, 2], [0, 11], [39, 7]], np.int32)
+    bad = np.array([[-1, 1], [40, 3], [2, 12], [5, -3]], np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pa.swap_blocks(dk, dv, hk, hv, torch.from_numpy(np.concatenate([out_pairs, bad])).cuda(), err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    hk_np = to_storage_np(hk, dtype)
+    hv_np = to_storage_np(hv, dtype)
+    kd_np, vd_np = to_storage_np(dk, dtype), to_storage_np(dv, dtype)
+    for b, h in out_pairs:
+        assert np.array_equal(hk_np[h].view(np.uint8), kd_np[b].view(np.uint8))
+        assert np.array_equal(hv_np[h].view(np.uint8), vd_np[b].view(np.uint8))
+    for h in set(range(nh)) - set(out_pairs[:, 1].tolist()):
+        assert not hk_np[h].view(np.uint8).any() and not hv_np[h].view(np.uint8).any()
+    # back into other device blocks
+    in_pairs = np.array([[0, 20], [5, 21], [2, 30], [11, 31], [7, 1]], np.int32)
+    k2, v2 = dk.clone(), dv.clone()
+    pa.swap_blocks(hk, hv, k2, v2, torch.from_numpy(in_pairs).cuda())
+    torch.cuda.synchronize()
+    want_k, want_v = kd_np.copy(), vd_np.copy()
+    for h, b in in_pairs:
+        want_k[b], want_v[b] = hk_np[h], hv_np[h]
+    assert np.array_equal(to_storage_np(k2, dtype).view(np.uint8), want_k.view(np.uint8))
+    assert np.array_equal(to_storage_np(v2, dtype).view(np.uint8), want_v.view(np.uint8))
 
 
 def test_plan_reused_across_layers(torch, pa, orc):

@@ -71,6 +71,14 @@ def test_host_validation_without_gpu(pa):
     assert lib.pa_copy_blocks(None, None, ctypes.byref(ok), None, 2, None, None) == -1
     assert lib.pa_copy_blocks(None, None, ctypes.byref(bdt), None, 2, None, None) == -3
     assert lib.pa_copy_blocks(None, None, ctypes.byref(bad), None, 0, None, None) == 0
+    # pa_swap_blocks: nothing to do, missing pointers, pageable host memory
+    assert lib.pa_swap_blocks(None, None, None, None, ctypes.byref(ok), 4, 4, None, 0, None,
+                              None) == 0
+    assert lib.pa_swap_blocks(None, None, None, None, ctypes.byref(ok), 4, 4, None, 1, None,
+                              None) == -1
+    assert lib.pa_swap_blocks(None, None, None, None, None, 4, 4, None, 1, None, None) == -1
+    assert lib.pa_swap_blocks(None, None, None, None, ctypes.byref(ok), -1, 4, None, 1, None,
+                              None) == -2
     odd8 = pa.CacheDesc(10, 16, 4, 4, pa.PA_F16)            # 8-byte rows
     assert lib.pa_copy_blocks(None, None, ctypes.byref(odd8), None, 1, None, None) == -4
 
@@ -78,31 +86,51 @@ def test_host_validation_without_gpu(pa):
 class PoolAdapter:
     """The C++ ledger behind the oracle ledger's method names, so the same pins run on it."""
 
-    def __init__(self, pa, free_order, block_size):
+    def __init__(self, pa, free_order, block_size, host_blocks=0):
         fo = list(free_order)
         self._names = {}
         self._pool = pa.Pool(max(fo) + 1 if fo else 1, block_size, fo)
+        if host_blocks:
+            self._pool.set_host_blocks(host_blocks)
         self.bs = block_size
         self._pa = pa
 
     def _id(self, seq):
         return self._names.setdefault(seq, len(self._names) + 1)
 
-    def append(self, seq, n):
+    def _call(self, fn, *a):
         try:
-            return self._pool.append(self._id(seq), n).tolist()
+            return fn(*a)
         except self._pa.PAError as e:
             if e.code == -7:
                 raise OutOfBlocks() from None
             if e.code == -8:
                 raise SharedBlock() from None
+            if e.code == -9:
+                raise LedgerError() from None
             raise
+
+    def append(self, seq, n):
+        return self._call(self._pool.append, self._id(seq), n).tolist()
+
+    def swap_out(self, seq):
+        return [tuple(int(x) for x in r) for r in self._call(self._pool.swap_out, self._id(seq))]
+
+    def swap_in(self, seq):
+        return [tuple(int(x) for x in r) for r in self._call(self._pool.swap_in, self._id(seq))]
+
+    def latest_resident(self):
+        s = self._pool.latest_resident()
+        return None if s is None else {v: k for k, v in self._names.items()}[s]
+
+    def num_host_free(self):
+        return self._pool.num_host_free()
 
     def share_prefix(self, dst, src, n):
         self._pool.share_prefix(self._id(dst), self._id(src), n)
 
     def fork(self, dst, src):
-        self._pool.fork(self._id(dst), self._id(src))
+        self._call(self._pool.fork, self._id(dst), self._id(src))
 
     def take_copies(self):
         return [tuple(int(x) for x in row) for row in self._pool.take_copies()]
@@ -132,23 +160,30 @@ class PoolAdapter:
         return [max(0, min(self.bs, n - i * self.bs)) for i in range(len(self.block_table(seq)))]
 
 
-class OutOfBlocks(Exception):
+class LedgerError(Exception):
     pass
 
 
-class SharedBlock(Exception):
+class OutOfBlocks(LedgerError):
+    pass
+
+
+class SharedBlock(LedgerError):
     pass
 
 
 class _PoolAsOracle:
     def __init__(self, pa):
-        self.Ledger = lambda free_order, block_size=16: PoolAdapter(pa, free_order, block_size)
+        self.Ledger = lambda free_order, block_size=16, host_blocks=0: PoolAdapter(
+            pa, free_order, block_size, host_blocks)
         self.OutOfBlocks = OutOfBlocks
         self.SharedBlock = SharedBlock
+        self.LedgerError = LedgerError
 
 
 @pytest.mark.parametrize("pin", [pins.pin_blocks_and_waste, pins.pin_walkthrough,
                                  pins.pin_parallel_sampling, pins.pin_cow_rules,
+                                 pins.pin_swap_ledger, pins.pin_batch_reuse,
                                  pins.pin_all_or_nothing,
                                  pins.pin_window_ledger], ids=lambda f: f.__name__)
 def test_pool_pins(pa, pin):
@@ -158,14 +193,17 @@ def test_pool_pins(pa, pin):
 @pytest.mark.parametrize("name,kw", [
     ("tiny", {}), ("opt13b", {}), ("gqa", {}),
     ("prefix_mixed", dict(chunk_lo=1024, chunk_hi=1100)),
-    ("swa", dict(batch=6)), ("parallel_sampling", {}),
+    ("swa", dict(batch=6)), ("parallel_sampling", {}), ("swap", {}),
 ])
 def test_pool_matches_oracle_ledger(pa, orc, name, kw):
     """Same script, same free order: identical tables, slots, copies and reference counts."""
-    from workloads import Append, Flush, Fork, Free, SetWindow, SharePrefix
+    from workloads import Append, Flush, Fork, Free, SetWindow, SharePrefix, SwapIn, SwapOut
     w = workloads.make(name, **kw)
-    led = orc.Ledger(w.free_order, w.block_size)
+    nh = w.meta.get("host_blocks", 0)
+    led = orc.Ledger(w.free_order, w.block_size, nh)
     pool = pa.Pool(w.num_blocks, w.block_size, w.free_order)
+    if nh:
+        pool.set_host_blocks(nh)
     n_copies = 0
     for op in w.script:
         if isinstance(op, Append):
@@ -180,6 +218,14 @@ def test_pool_matches_oracle_ledger(pa, orc, name, kw):
         elif isinstance(op, Fork):
             led.fork(op.dst, op.src)
             pool.fork(op.dst, op.src)
+        elif isinstance(op, SwapOut):
+            seq = led.latest_resident() if op.seq is None else op.seq
+            assert pool.latest_resident() == led.latest_resident()
+            assert np.array_equal(np.asarray(led.swap_out(seq), np.int32).reshape(-1, 2),
+                                  pool.swap_out(seq))
+        elif isinstance(op, SwapIn):
+            assert np.array_equal(np.asarray(led.swap_in(op.seq), np.int32).reshape(-1, 2),
+                                  pool.swap_in(op.seq))
         elif isinstance(op, SharePrefix):
             led.share_prefix(op.dst, op.src, op.n_tokens)
             pool.share_prefix(op.dst, op.src, op.n_tokens)
@@ -202,65 +248,86 @@ def test_pool_matches_oracle_ledger(pa, orc, name, kw):
         assert n_copies == partial * (w.meta["samples"] - 1) > 0
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(8))
 def test_pool_random_scripts_match_oracle(pa, orc, seed):
-    """Random appends, forks, shares, frees, windows and batch ends on a small pool: the C++
-    ledger and the oracle ledger agree on every result, refusal included."""
+    """Random appends, forks, shares, frees, windows, swap-outs, swap-ins and batch ends on
+    a small pool: the C++ ledger and the oracle ledger agree on every result, refusals
+    included (same error kind, nothing changed)."""
     rng = np.random.default_rng(seed)
-    nb = 40
+    nb, nh = 40, 12
     order = rng.permutation(nb).tolist()
-    led = orc.Ledger(order, 4)
+    led = orc.Ledger(order, 4, nh)
     pool = pa.Pool(nb, 4, order)
-    live = []
+    pool.set_host_blocks(nh)
+    codes = {-7: "OutOfBlocks", -8: "SharedBlock", -9: "LedgerError"}
+
+    def both(f_led, f_pool, conv=lambda x: x):
+        try:
+            a, ea = f_led(), None
+        except orc.LedgerError as e:
+            a, ea = None, type(e).__name__
+        try:
+            b, eb = conv(f_pool()), None
+        except pa.PAError as e:
+            b, eb = None, codes.get(e.code, e.code)
+        assert (ea, a) == (eb, b)
+        return ea is None
+
+    pairs = lambda x: [tuple(int(v) for v in r) for r in x]
+    live, swapped = [], []
     next_id = 0
-    for _ in range(400):
+    for _ in range(600):
         r = rng.random()
-        if r < 0.45 or not live:
-            seq = int(rng.choice(live)) if live and rng.random() < 0.8 else next_id
+        if r < 0.4 or not live:
+            seq = int(rng.choice(live + swapped)) if live and rng.random() < 0.8 else next_id
             n = int(rng.integers(0, 7))
-            try:
-                a = led.append(seq, n)
-                ea = None
-            except orc.LedgerError as e:
-                a, ea = None, type(e).__name__
-            try:
-                b = pool.append(seq, n).tolist()
-                eb = None
-            except pa.PAError as e:
-                b, eb = None, {-7: "OutOfBlocks", -8: "SharedBlock"}.get(e.code, e.code)
-            assert (a, ea) == (b, eb)
-            if seq == next_id and ea is None:
+            ok = both(lambda: led.append(seq, n), lambda: pool.append(seq, n).tolist())
+            if seq == next_id and ok:
                 live.append(seq)
                 next_id += 1
-        elif r < 0.6:
-            src = int(rng.choice(live))
-            led.fork(next_id, src)
-            pool.fork(next_id, src)
-            live.append(next_id)
-            next_id += 1
-        elif r < 0.68:
+        elif r < 0.5:
+            src = int(rng.choice(live + swapped))
+            if both(lambda: led.fork(next_id, src), lambda: pool.fork(next_id, src)):
+                live.append(next_id)
+                next_id += 1
+        elif r < 0.55:
             src = int(rng.choice(live))
             n = int(rng.integers(0, led.seq_len(src) + 1))
-            ok = all(b >= 0 for b in led.block_table(src)[:-(-n // 4)])
-            if ok:
+            if all(b >= 0 for b in led.block_table(src)[:-(-n // 4)]):
                 led.share_prefix(next_id, src, n)
                 pool.share_prefix(next_id, src, n)
                 live.append(next_id)
                 next_id += 1
-        elif r < 0.78:
-            seq = live.pop(int(rng.integers(0, len(live))))
+        elif r < 0.63:
+            pick = live + swapped
+            seq = pick[int(rng.integers(0, len(pick)))]
+            (live if seq in live else swapped).remove(seq)
             led.free_seq(seq)
             pool.free(seq)
-        elif r < 0.8:
+        elif r < 0.65:
             led.set_window(next_id, int(rng.integers(1, 12)))
             pool.set_window(next_id, led.window[next_id])
             live.append(next_id)
             next_id += 1
+        elif r < 0.73:
+            assert pool.latest_resident() == led.latest_resident()
+            seq = led.latest_resident() if rng.random() < 0.5 else int(rng.choice(live))
+            if seq is not None and both(lambda: led.swap_out(seq),
+                                        lambda: pool.swap_out(seq), pairs):
+                live.remove(seq)
+                swapped.append(seq)
+        elif r < 0.8:
+            if swapped:
+                seq = swapped[int(rng.integers(0, len(swapped)))]
+                if both(lambda: led.swap_in(seq), lambda: pool.swap_in(seq), pairs):
+                    swapped.remove(seq)
+                    live.append(seq)
         else:
             a = led.take_copies()
             assert np.array_equal(np.asarray(a, np.int32).reshape(-1, 3), pool.take_copies())
         assert led.num_free() == pool.num_free()
-    for s in live:
+        assert led.num_host_free() == pool.num_host_free()
+    for s in live + swapped:
         assert led.block_table(s) == pool.block_table(s)
         assert led.seq_len(s) == pool.seq_len(s)
     for b in range(nb):

@@ -38,7 +38,7 @@ C_MUTANTS = {
 PY_MUTANTS = {
     "ceil_to_floor": ("n_blk_after = -(-end // self.bs)", "n_blk_after = end // self.bs + (1 if end % self.bs > 1 else 0)"),
     "share_no_ref": ("            self.ref[b] += 1\n", "            pass\n"),
-    "free_lost": ("            self.free.append(block)\n", "            pass\n"),
+    "free_lost": ("(self.quarantine if self._busy(block) else self.free).append(block)", "pass"),
     "slot_offset": ("slots.append(b * self.bs + p % self.bs)", "slots.append(b * self.bs + (p + 1) % self.bs)"),
     "keep_off_by_one": ("keep_from = max(0, end - win) if win > 0 else 0",
                         "keep_from = max(0, end - win + 1) if win > 0 else 0"),
@@ -49,8 +49,17 @@ PY_MUTANTS = {
     "cow_short_copy": ("cur - cow * self.bs))", "cur - cow * self.bs - 1))"),
     "cow_no_decref": ("            self.ref[old] -= 1\n", "            pass\n"),
     "cow_pending_ignored": ("if tab[last] in self.touched:", "if False:"),
-    "fork_no_ref": ("                self.ref[b] += 1\n        self.table[dst] = tab",
-                    "                pass\n        self.table[dst] = tab"),
+    "victim_first_arrival": ("self.arrival[s] > self.arrival[best]", "self.arrival[s] < self.arrival[best]"),
+    "swap_shared_too": ("alone = [i for i, b in enumerate(tab) if b >= 0 and self.ref[b] == 1]",
+                        "alone = [i for i, b in enumerate(tab) if b >= 0]"),
+    "swap_in_unchecked": ("        if need > len(self.free):\n            raise OutOfBlocks(f\"seq {seq}: needs {need} blocks, {len(self.free)} free\")\n        tab = self.table[seq]",
+                          "        tab = self.table[seq]"),
+    "swap_pending_ok": ("        if any(tab[i] in self.touched for i in alone):\n", "        if False:\n"),
+    "no_quarantine": ("(self.quarantine if self._busy(block) else self.free)", "self.free"),
+    "host_reuse_now": ("                self.host_quarantine.append(h)\n        del self.swapped[seq]",
+                       "                self.host_free.append(h)\n        del self.swapped[seq]"),
+    "fork_no_ref": ("                self.ref[b] += 1\n        self._create(dst)\n        self.table[dst] = tab",
+                    "                pass\n        self._create(dst)\n        self.table[dst] = tab"),
 }
 
 

@@ -35,7 +35,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
-    "DTYPES", "Append", "SharePrefix", "Fork", "Flush", "Free", "SetWindow", "Workload",
+    "DTYPES", "Append", "SharePrefix", "Fork", "Flush", "SwapOut", "SwapIn", "Free",
+    "SetWindow", "Workload",
     "make", "CONFIG_NAMES", "normal", "to_storage", "nan_bits", "ACT", "act_dtype",
 ]
 
@@ -159,6 +160,18 @@ class Flush:
 
 
 @dataclass(frozen=True)
+class SwapOut:
+    """Evict ``seq`` (None: the resident sequence that arrived last) to host blocks."""
+    seq: int | None = None
+
+
+@dataclass(frozen=True)
+class SwapIn:
+    """Bring swapped-out ``seq`` back into device blocks."""
+    seq: int
+
+
+@dataclass(frozen=True)
 class Free:
     seq: int
 
@@ -223,7 +236,7 @@ class Workload:
         return out
 
 
-CONFIG_NAMES = ("tiny", "opt13b", "gqa", "prefix_mixed", "swa", "parallel_sampling")
+CONFIG_NAMES = ("tiny", "opt13b", "gqa", "prefix_mixed", "swa", "parallel_sampling", "swap")
 
 
 def _values(seed, n_tok, hkv, d, dtype, stream_k=2, stream_v=3):
@@ -273,11 +286,12 @@ def _plain(name, seed, dtype, hq, hkv, d, lens, n_layers, rng, last_token_apart=
 
 
 def make(name: str, seed: int | None = None, **over) -> Workload:
-    """Build one of the five named workloads.
+    """Build one of the named workloads (CONFIG_NAMES, plus "rows" for free-shape tests).
 
     Keyword overrides shrink a workload for fast parity runs while keeping its structure:
       batch=, lo=, hi= (length range), median= / sigma= (log-normal), prefix=, chunks=,
-      chunk_rows=, chunk_lo=, chunk_hi=, window=.
+      chunk_rows=, chunk_lo=, chunk_hi=, window=, prompts= / samples= / plens=, victims=,
+      dtype= (including the 8-bit cache names "q8_f16" and "q8_bf16").
     """
     if name == "tiny":
         seed = 1 if seed is None else seed
@@ -410,6 +424,54 @@ def make(name: str, seed: int | None = None, **over) -> Workload:
                      np.ones(B, np.int32), 0, np.float32(1.0 / math.sqrt(d)),
                      over.get("layers", 40), free_order, script, k, v, q)
         w.meta.update(prompts=P, samples=n)
+        return w
+
+    if name == "swap":
+        # OPT-13B shape under memory pressure: every sequence is prefilled; the `victims`
+        # that arrived last are swapped out, the same number of newcomers run in the freed
+        # blocks and leave, the victims are swapped back in (earliest arrival first) and
+        # every sequence appends its next token
+        seed = 8 if seed is None else seed
+        rng = np.random.default_rng(np.random.SeedSequence(entropy=seed, spawn_key=(0,)))
+        bs = 16
+        B = over.get("batch", 64)
+        V = over.get("victims", 8)
+        hq, hkv, d = over.get("hq", 40), over.get("hkv", 40), over.get("d", 128)
+        lens = rng.integers(over.get("lo", 64), over.get("hi", 2048) + 1, size=B)
+        need = int(sum(-(-int(L) // bs) for L in lens)) + B
+        nb = _pool_size(need)
+        free_order = rng.permutation(nb - 1).astype(np.int32)
+        script, off = [], 0
+        for s_ in range(B):
+            script.append(Append(s_, int(lens[s_]), int(lens[s_]), off))
+            off += int(lens[s_])
+        script.append(Flush())
+        for _ in range(V):
+            script.append(SwapOut(None))
+        script.append(Flush())
+        for k in range(V):                     # newcomers as long as the victims
+            n = int(lens[B - 1 - k])
+            script.append(Append(B + k, n, n, off))
+            off += n
+        script.append(Flush())
+        for k in range(V):
+            script.append(Free(B + k))
+        script.append(Flush())
+        for k in range(V):
+            script.append(SwapIn(B - V + k))
+        script.append(Flush())
+        for s_ in range(B):
+            script.append(Append(s_, 1, 1, off))
+            off += 1
+        script.append(Flush())
+        dt = over.get("dtype", "f16")
+        k_, v_ = _values(seed, off, hkv, d, dt)
+        q = _queries(seed, B, hq, d, dt)
+        host = int(sum(-(-int(L) // bs) for L in lens[B - V:]))
+        w = Workload("swap", seed, dt, hq, hkv, d, bs, nb, (lens + 1).astype(np.int32),
+                     np.ones(B, np.int32), 0, np.float32(1.0 / math.sqrt(d)),
+                     over.get("layers", 40), free_order, script, k_, v_, q)
+        w.meta.update(host_blocks=host, victims=V)
         return w
 
     if name == "rows":
