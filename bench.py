@@ -230,6 +230,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="opt13b", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--layers", type=int, default=None, help="default: the workload's")
+    ap.add_argument("--block-size", type=int, choices=[8, 16, 32], default=16,
+                    help="tokens per KV block (8 and 32: OPT-13B and GQA shapes, 16-bit KV)")
     ap.add_argument("--kv", choices=["native", "q8"], default="native",
                     help="q8: 8-bit KV cache (one fp16 scale per 32 values), same workload")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -268,13 +270,19 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
         return
 
+    over = {}
+    if args.block_size != 16:
+        if args.workload not in ("opt13b", "gqa") or args.kv == "q8":
+            print("bench.py: 8- and 32-token blocks are built for the OPT-13B and GQA "
+                  "shapes with 16-bit KV", file=sys.stderr)
+            sys.exit(2)
+        over["block_size"] = args.block_size
     if args.kv == "q8":
         if args.workload not in Q8_DTYPE:
             print(f"bench.py: no 8-bit variant of {args.workload}", file=sys.stderr)
             sys.exit(2)
-        w = workloads.make(args.workload, dtype=Q8_DTYPE[args.workload])
-    else:
-        w = workloads.make(args.workload)
+        over["dtype"] = Q8_DTYPE[args.workload]
+    w = workloads.make(args.workload, **over)
     L = args.layers or w.n_layers
     print(f"[bench] building {args.workload}: {w.num_seqs} seqs, {w.total_q_rows} rows, "
           f"{w.num_blocks} blocks/layer, {L} layers", file=sys.stderr, flush=True)
@@ -290,6 +298,8 @@ def main():
                       device="cuda")
     kv_layer = pa.kv_bytes_read(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim,
                                 w.elem_bytes)
+    held = sum(len([b for b in dw.pool.block_table(s) if b >= 0]) for s in range(w.num_seqs))
+    waste = 1.0 - min(int(w.seq_lens.sum()), held * w.block_size) / max(1, held * w.block_size)
     qsl = dw.qsl if dw.uses_rows else None
     common = dict(max_seq_len=dw.max_seq_len, query_start_loc=qsl, window=w.window,
                   workspace=dw.workspace)
@@ -357,7 +367,8 @@ def main():
     kv_decode = pa.kv_bytes_read(w.seq_lens[dec], w.q_rows[dec], w.window, w.num_kv_heads,
                                  w.head_dim, w.elem_bytes)
     achieved = kv_decode / (dec_avg_ms / 1e3) / 1e9
-    traffic = measured_traffic(args.workload + ("_q8" if args.kv == "q8" else ""))
+    traffic = (measured_traffic(args.workload + ("_q8" if args.kv == "q8" else ""))
+               if args.block_size == 16 else None)
     decode_roof = {
         "kernel": "decode_kernel",
         "bound": "hbm",
@@ -425,7 +436,11 @@ def main():
         "decode_tokens_per_s": round(tokens_per_s, 1),
         "config": {
             "workload": DESCRIPTIONS[args.workload] + (
-                "; 8-bit KV cache, one fp16 scale per 32 values" if args.kv == "q8" else ""),
+                "; 8-bit KV cache, one fp16 scale per 32 values" if args.kv == "q8" else "") + (
+                f"; {args.block_size}-token blocks" if args.block_size != 16 else ""),
+            "block_size": w.block_size,
+            # slots allocated but empty (last blocks) over slots allocated
+            "internal_waste": round(float(waste), 5),
             "batch": w.num_seqs,
             "query_rows": w.total_q_rows,
             "layers": L,

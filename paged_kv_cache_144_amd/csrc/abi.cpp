@@ -37,7 +37,10 @@ pa_status check_desc(const pa_cache_desc* d) {
     if (!cache_dtype_ok(d->dtype)) return PA_ERR_DTYPE;
     if (d->num_blocks <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 || d->block_size <= 0)
         return PA_ERR_SHAPE;
-    if (d->block_size != pa::kBlock) return PA_ERR_UNSUPPORTED;
+    // 16-token blocks for every type; 8 and 32 for the 16-bit types
+    const bool bs16 = d->dtype == PA_F16 || d->dtype == PA_BF16;
+    if (d->block_size != pa::kBlock && !(bs16 && (d->block_size == 8 || d->block_size == 32)))
+        return PA_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
@@ -80,7 +83,7 @@ pa_status plan_shape(const pa_cache_desc* desc, int32_t num_seqs, int32_t total_
     if (num_seqs < 0 || total_q_rows < 0 || num_q_heads <= 0) return PA_ERR_SHAPE;
     if (num_q_heads % desc->num_kv_heads) return PA_ERR_SHAPE;
     p.group = num_q_heads / desc->num_kv_heads;
-    p.fn = pa::decode_kernel_ptr(desc->dtype, desc->head_dim, p.group);
+    p.fn = pa::decode_kernel_ptr(desc->dtype, desc->head_dim, p.group, desc->block_size);
     if (!p.fn) return PA_ERR_UNSUPPORTED;
     p.max_waves = resident_waves(p.fn);
     if (p.max_waves <= 0) return PA_ERR_LAUNCH;
@@ -94,7 +97,7 @@ pa_status plan_shape(const pa_cache_desc* desc, int32_t num_seqs, int32_t total_
     const char* ck = std::getenv("PA_CHUNK_KERNEL");
     const bool chunk_off = ck && ck[0] == '0';
     if (!one_row_per_seq && !chunk_off &&
-        pa::chunk_kernel_ptr(desc->dtype, desc->head_dim, p.group)) {
+        pa::chunk_kernel_ptr(desc->dtype, desc->head_dim, p.group, desc->block_size)) {
         p.chunk_rows = pa::chunk_tile_rows(p.group);
         // sum over sequences of ceil(n_s / QT) <= rows / QT + sequences
         p.max_tiles = total_q_rows / p.chunk_rows + num_seqs + 1;
@@ -137,8 +140,8 @@ pa_status pa_write_kv(const void* k, const void* v, const int64_t* slot_mapping,
                                      desc->num_blocks, desc->num_kv_heads, desc->head_dim,
                                      act_dtype(desc->dtype), (hipStream_t)stream)
             : pa::launch_write_kv(k, v, slot_mapping, num_tokens, k_cache, v_cache,
-                                  desc->num_blocks, desc->num_kv_heads, desc->head_dim,
-                                  dtype_bytes(desc->dtype), (hipStream_t)stream);
+                                  desc->num_blocks, desc->block_size, desc->num_kv_heads,
+                                  desc->head_dim, dtype_bytes(desc->dtype), (hipStream_t)stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -276,6 +279,7 @@ pa_status build_args(void* out, pa_dtype out_dtype, const void* q, const void* k
     a.num_blocks = desc->num_blocks;
     a.num_kv_heads = desc->num_kv_heads;
     a.head_dim = desc->head_dim;
+    a.block_size = desc->block_size;
     a.num_q_heads = num_q_heads;
     a.group = p.group;
     a.max_blocks = max_blocks_per_seq;

@@ -7,10 +7,19 @@ const void* decode_kernel_ptr_f32(int head_dim, int group);
 const void* decode_kernel_ptr_f16(int head_dim, int group);
 const void* decode_kernel_ptr_bf16(int head_dim, int group);
 const void* decode_kernel_ptr_q8(int dtype, int head_dim, int group);
+const void* decode_kernel_ptr_f16_bs(int head_dim, int group, int block_size);
+const void* decode_kernel_ptr_bf16_bs(int head_dim, int group, int block_size);
 const void* chunk_kernel_ptr_f16(int head_dim, int group);
 const void* chunk_kernel_ptr_bf16(int head_dim, int group);
 
-const void* decode_kernel_ptr(int dtype, int head_dim, int group) {
+const void* decode_kernel_ptr(int dtype, int head_dim, int group, int block_size) {
+    if (block_size != kBlock) {
+        switch (dtype) {
+            case DT_F16: return decode_kernel_ptr_f16_bs(head_dim, group, block_size);
+            case DT_BF16: return decode_kernel_ptr_bf16_bs(head_dim, group, block_size);
+            default: return nullptr;   // fp32 and 8-bit caches: 16-token blocks only
+        }
+    }
     switch (dtype) {
         case DT_F32: return decode_kernel_ptr_f32(head_dim, group);
         case DT_F16: return decode_kernel_ptr_f16(head_dim, group);
@@ -21,7 +30,8 @@ const void* decode_kernel_ptr(int dtype, int head_dim, int group) {
     }
 }
 
-const void* chunk_kernel_ptr(int dtype, int head_dim, int group) {
+const void* chunk_kernel_ptr(int dtype, int head_dim, int group, int block_size) {
+    if (block_size != kBlock) return nullptr;   // other block sizes: chunk rows decode
     switch (dtype) {
         case DT_F16: return chunk_kernel_ptr_f16(head_dim, group);
         case DT_BF16: return chunk_kernel_ptr_bf16(head_dim, group);
@@ -31,7 +41,7 @@ const void* chunk_kernel_ptr(int dtype, int head_dim, int group) {
 
 hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream) {
     if (a.chunk_rows <= 0 || a.max_tiles <= 0) return hipSuccess;
-    const void* fn = chunk_kernel_ptr(dtype, a.head_dim, a.group);
+    const void* fn = chunk_kernel_ptr(dtype, a.head_dim, a.group, a.block_size);
     if (!fn) return hipErrorInvalidDeviceFunction;
     void* args[] = {(void*)&a};
     return hipLaunchKernel(fn, dim3(a.max_tiles, a.num_kv_heads), dim3(kWavesPerGroup * kWave),
@@ -39,7 +49,7 @@ hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
-    const void* fn = decode_kernel_ptr(dtype, a.head_dim, a.group);
+    const void* fn = decode_kernel_ptr(dtype, a.head_dim, a.group, a.block_size);
     if (!fn) return hipErrorInvalidDeviceFunction;
     int groups = (a.max_waves + kWavesPerGroup - 1) / kWavesPerGroup;
     if (groups < 1) groups = 1;   // at least one group: it also zeroes rows with nothing to read

@@ -47,21 +47,22 @@ namespace pa {
 
 // How a cache dtype's tiles are loaded and consumed.  Lane l of a load holds PE elements
 // of token (i * TPI + l / LPT), columns (l % LPT) * PE .. +PE.
-template <int DT, int D, int G, bool Q8 = (DT == DT_Q8F16 || DT == DT_Q8BF16)>
+template <int DT, int D, int G, int BS, bool Q8 = (DT == DT_Q8F16 || DT == DT_Q8BF16)>
 struct KvOps;
 
-// fp32 / fp16 / bf16 caches: 16-byte lane loads, 1 KiB per load instruction.
-template <int DT, int D, int G>
-struct KvOps<DT, D, G, false> {
+// fp32 / fp16 / bf16 caches: 16-byte lane loads, 1 KiB per load instruction; a tile is
+// BS tokens (the block size).
+template <int DT, int D, int G, int BS>
+struct KvOps<DT, D, G, BS, false> {
     static constexpr int EB = Elem<DT>::bytes;
     static constexpr int QB = EB;                // bytes per query element
     static constexpr int PE = Elem<DT>::per16;   // elements per 16-byte lane load
     static constexpr int LPT = D / PE;           // lanes holding one token row
     static constexpr int TPI = kWave / LPT;      // tokens per load instruction
-    static constexpr int NLD = kBlock / TPI;     // load instructions per tile
-    static constexpr int TILE = kBlock * D * EB; // bytes of one (block, head) tile
+    static constexpr int NLD = BS / TPI;         // load instructions per tile
+    static constexpr int TILE = BS * D * EB;     // bytes of one (block, head) tile
     static_assert(LPT >= 8 && LPT <= 64 && (LPT & (LPT - 1)) == 0, "row width");
-    static_assert(NLD * 1024 == TILE, "tile covered by whole-wave loads");
+    static_assert(NLD >= 1 && NLD * 1024 == TILE, "tile covered by whole-wave loads");
 
     struct Tile { u32x4 k[NLD], v[NLD]; };
     struct Q { uint32_t v[G][4]; };
@@ -112,8 +113,9 @@ struct KvOps<DT, D, G, false> {
 // holding the 16 tokens' fp16 scales ([16][D / 32]).  A lane loads PE codes of a token row
 // (16 bytes for G <= 4, 8 bytes for G = 8, whose accumulators would not fit twice as many
 // columns) and the 2-byte scale of their group.
-template <int DT, int D, int G>
-struct KvOps<DT, D, G, true> {
+template <int DT, int D, int G, int BS>
+struct KvOps<DT, D, G, BS, true> {
+    static_assert(BS == kBlock, "8-bit tiles hold 16 tokens");
     static constexpr int ADT = DT == DT_Q8F16 ? DT_F16 : DT_BF16;   // query / new-row type
     static constexpr int QB = 2;
     static constexpr int PE = G <= 4 ? 16 : 8;
@@ -364,9 +366,9 @@ __device__ void merge_pair(const DecodeArgs& a, int u, int g, int w_first, int n
     }
 }
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, int BS = kBlock>
 __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeArgs a) {
-    using S = KvOps<DT, D, G>;
+    using S = KvOps<DT, D, G, BS>;
     constexpr int PE = S::PE, LPT = S::LPT, TPI = S::TPI, NLD = S::NLD;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr float kNegBig = -3.402823466e38f;
@@ -445,14 +447,14 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
             S::load(kbase, vbase, (size_t)b * block_stride + head_off, t);
         };
         auto consume = [&](typename S::Tile& tl, int j, bool valid) {
-            const int t0 = j * kBlock;
+            const int t0 = j * BS;
             float sc[G][NLD];
             S::partial_scores(qv, tl, sc);
 #pragma unroll
             for (int i = 0; i < NLD; ++i)
 #pragma unroll
                 for (int gi = 0; gi < G; ++gi) sc[gi][i] = group_sum<LPT>(sc[gi][i]) * qscale;
-            if (!valid || t0 < lo_tok || t0 + kBlock > len) {   // wavefront-uniform
+            if (!valid || t0 < lo_tok || t0 + BS > len) {   // wavefront-uniform
 #pragma unroll
                 for (int i = 0; i < NLD; ++i) {
                     const int t = t0 + i * TPI + row;

@@ -10,7 +10,8 @@
 
 namespace pa {
 
-constexpr int kBlock = 16;          // tokens per KV block (the kernels' fixed block size)
+constexpr int kBlock = 16;          // default tokens per KV block (8 and 32 also have
+                                    // decode kernels for 16-bit caches)
 constexpr int kWave = 64;           // CDNA wavefront width
 constexpr int kWavesPerGroup = 4;   // decode workgroup = 4 independent wavefront workers
 constexpr int kMinBlocksPerWave = 8;  // smallest share of KV blocks worth a wavefront
@@ -79,7 +80,7 @@ struct DecodeArgs {
     const int32_t* block_tables;
     const int32_t* seq_lens;
     const int32_t* query_start_loc;   // may be null
-    int32_t num_blocks, num_kv_heads, head_dim, num_q_heads, group;
+    int32_t num_blocks, block_size, num_kv_heads, head_dim, num_q_heads, group;
     int32_t max_blocks, num_seqs, total_q_rows, max_seq_len, window;
     float scale;
     int32_t max_waves;                // decode wavefront workers launched
@@ -91,7 +92,7 @@ struct DecodeArgs {
 
 // launchers (each enqueues on `stream`, returns hipSuccess or the launch error)
 hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, int32_t n,
-                           void* kc, void* vc, int32_t nb, int32_t hkv, int32_t d,
+                           void* kc, void* vc, int32_t nb, int32_t bs, int32_t hkv, int32_t d,
                            int32_t elem_bytes, hipStream_t stream);
 hipError_t launch_write_kv_q8(const void* k, const void* v, const int64_t* slots, int32_t n,
                               void* kc, void* vc, int32_t nb, int32_t hkv, int32_t d,
@@ -109,9 +110,9 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream);
 
 // The decode kernel instance for (dtype, head_dim, group), or null if none is built.
-const void* decode_kernel_ptr(int dtype, int head_dim, int group);
+const void* decode_kernel_ptr(int dtype, int head_dim, int group, int block_size);
 // The chunk-row MFMA kernel instance, or null (then chunk rows run as decode rows).
-const void* chunk_kernel_ptr(int dtype, int head_dim, int group);
+const void* chunk_kernel_ptr(int dtype, int head_dim, int group, int block_size);
 // Query rows one chunk tile covers: 4 wavefronts x 32 (row, head) pairs / group.
 inline int chunk_tile_rows(int group) { return kWavesPerGroup * 32 / group; }
 

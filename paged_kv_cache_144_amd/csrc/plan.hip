@@ -15,8 +15,8 @@ namespace pa {
 
 constexpr int kPlanThreads = 1024;
 
-__device__ __forceinline__ void unit_range(int32_t len, int32_t window, int32_t& b_lo,
-                                           int32_t& nb) {
+__device__ __forceinline__ void unit_range(int32_t len, int32_t window, int32_t bs,
+                                           int32_t& b_lo, int32_t& nb) {
     // a row at length len sees positions [lo, len); with a window only the last `window`
     if (len <= 0) {
         b_lo = 0;
@@ -24,14 +24,14 @@ __device__ __forceinline__ void unit_range(int32_t len, int32_t window, int32_t&
         return;
     }
     const int32_t lo = (window > 0 && len > window) ? len - window : 0;
-    b_lo = lo / kBlock;
-    nb = (len + kBlock - 1) / kBlock - b_lo;
+    b_lo = lo / bs;
+    nb = (len + bs - 1) / bs - b_lo;
 }
 
-// A sequence is accepted when 0 <= L <= min(max_seq_len, 16 * max_blocks).  Rows that would
+// A sequence is accepted when 0 <= L <= min(max_seq_len, block_size * max_blocks).  Rows that would
 // sit before position 0 (more rows than context) see nothing and give zeros.
 __device__ __forceinline__ bool len_ok(const DecodeArgs& a, int L) {
-    return L >= 0 && L <= a.max_seq_len && L <= a.max_blocks * kBlock;
+    return L >= 0 && L <= a.max_seq_len && (int64_t)L <= (int64_t)a.max_blocks * a.block_size;
 }
 
 
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
         }
         for (int r = 0; r < n; ++r) {
             int32_t b_lo, nb;
-            unit_range(L - n + r + 1, a.window, b_lo, nb);
+            unit_range(L - n + r + 1, a.window, a.block_size, b_lo, nb);
             my_blk += (uint32_t)nb * (uint32_t)a.num_kv_heads;   // one pair per KV head
         }
     }
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
             UnitInfo ui{0, 0, 0, s};
             if (ok) {
                 ui.len = max(0, L - n + r + 1);
-                unit_range(ui.len, a.window, ui.b_lo, ui.nb);
+                unit_range(ui.len, a.window, a.block_size, ui.b_lo, ui.nb);
             }
             unit[r0 + r] = ui;
             cb[r0 + r] = off;

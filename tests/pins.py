@@ -366,6 +366,27 @@ def pin_swap_attention(orc):
     assert [s for s, _ in outs] == [9, 8, 7]
 
 
+def pin_block_sizes(orc):
+    # the block size changes where tokens sit, never what a row attends to; internal waste
+    # stays below one block per sequence ("vLLM and PagedAttention" notes, section on the
+    # block size; "PagedAttention deep dive", section on waste under 4%)
+    for name, kw in [("opt13b", dict(batch=4, lo=20, hi=150)),
+                     ("gqa", dict(batch=5, median=60, lo=16, hi=300))]:
+        outs = []
+        for bs in (4, 8, 16, 32):
+            w = workloads.make(name, block_size=bs, **kw)
+            ref = orc.Reference(w)
+            outs.append(ref.attention())
+            for s, L in enumerate(w.seq_lens):
+                held = len(ref.ledger.block_table(s))
+                assert held == -(-int(L) // bs) and 0 <= held * bs - int(L) < bs
+        k, v, off, first = contiguous_inputs(w)
+        want = orc.contiguous_attention(w.q, k, v, off, first, w.seq_lens, w.scale, w.dtype,
+                                        w.num_q_heads, w.query_start_loc(), w.window)
+        for o in outs:
+            assert np.array_equal(o, want), name
+
+
 def pin_all_or_nothing(orc):
     led = orc.Ledger(range(4), 16)
     led.append(0, 40)                       # 3 blocks
@@ -687,7 +708,7 @@ def pin_nan_isolation(orc):
 ALL = [pin_kv_bytes, pin_kv_totals, pin_kv_q8_bytes, pin_kv_read_bytes, pin_q8_grid,
        pin_q8_rounding, pin_q8_paged, pin_blocks_and_waste, pin_walkthrough,
        pin_parallel_sampling, pin_cow_rules, pin_cow_attention, pin_swap_ledger,
-       pin_batch_reuse, pin_swap_attention, pin_all_or_nothing, pin_window_ledger, pin_widen, pin_write_kv,
+       pin_batch_reuse, pin_swap_attention, pin_block_sizes, pin_all_or_nothing, pin_window_ledger, pin_widen, pin_write_kv,
        pin_one_token, pin_uniform, pin_two_tokens, pin_needle, pin_contiguous, pin_permutation,
        pin_sdpa, pin_brute, pin_window, pin_chunk_rows, pin_shared_prefix, pin_gqa_mapping,
        pin_nan_isolation]

@@ -86,6 +86,12 @@ SMALL = [
     ("parallel_sampling", dict(prompts=3, samples=3, lo=20, hi=300, dtype="q8_f16")),
     ("prefix_mixed", dict(batch=10, prefix=64, suffix_hi=80, chunks=2, chunk_rows=40,
                           chunk_lo=100, chunk_hi=300, dtype="q8_bf16")),
+    # 8- and 32-token blocks (16-bit caches)
+    ("opt13b", dict(batch=6, lo=64, hi=700, block_size=8)),
+    ("opt13b", dict(batch=6, lo=64, hi=700, block_size=32)),
+    ("gqa", dict(batch=12, median=300, lo=16, hi=3000, block_size=8)),
+    ("gqa", dict(batch=12, median=300, lo=16, hi=3000, block_size=32)),
+    ("gqa", dict(batch=5, median=200, dtype="f16", block_size=32)),
     # swapping: evictions to pinned host memory, newcomers in the freed blocks, swap-ins
     ("swap", dict(batch=10, victims=3, lo=5, hi=70, hq=4, hkv=2, d=64, dtype="f32")),
     ("swap", dict(batch=12, victims=4, lo=64, hi=700)),
@@ -278,13 +284,14 @@ def test_write_kv_skips(torch, pa):
 
 
 FULL = [("tiny", {}), ("opt13b", {}), ("gqa", {}), ("prefix_mixed", {}), ("swa", {}),
-        ("parallel_sampling", {}), ("swap", {}), ("opt13b", dict(dtype="q8_f16")),
+        ("parallel_sampling", {}), ("swap", {}), ("opt13b", dict(block_size=32)),
+        ("gqa", dict(block_size=8)), ("opt13b", dict(dtype="q8_f16")),
         ("gqa", dict(dtype="q8_bf16"))]
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name,kw", FULL,
-                         ids=[n + ("-" + k["dtype"] if k else "") for n, k in FULL])
+                         ids=[n + "".join(f"-{k}{v}" for k, v in kw.items()) for n, kw in FULL])
 def test_full_size_parity(torch, pa, orc, name, kw):
     """The workloads at their full sizes, in the launch configuration the benchmark
     times.  Decode rows are all checked; chunk rows on a sample (each sampled row is the

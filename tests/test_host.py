@@ -47,8 +47,12 @@ def test_status_strings(pa):
 def test_host_validation_without_gpu(pa):
     """Argument errors are reported before any device work is attempted."""
     lib = pa.load()
-    bad = pa.CacheDesc(10, 8, 4, 128, pa.PA_F16)            # block size 8: no kernel
+    bad = pa.CacheDesc(10, 4, 4, 128, pa.PA_F16)            # block size 4: no kernel
     assert lib.pa_write_kv(None, None, None, 1, None, None, ctypes.byref(bad), None) == -4
+    bad32 = pa.CacheDesc(10, 8, 4, 128, pa.PA_F32)          # 8-token blocks: 16-bit only
+    assert lib.pa_write_kv(None, None, None, 1, None, None, ctypes.byref(bad32), None) == -4
+    ok8 = pa.CacheDesc(10, 8, 4, 128, pa.PA_BF16)
+    assert lib.pa_write_kv(None, None, None, 1, None, None, ctypes.byref(ok8), None) == -1
     odd = pa.CacheDesc(10, 16, 4, 96, pa.PA_F16)            # head_dim 96: no kernel
     assert lib.pa_write_kv(None, None, None, 1, None, None, ctypes.byref(odd), None) == -4
     ok = pa.CacheDesc(10, 16, 4, 128, pa.PA_F16)

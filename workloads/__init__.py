@@ -254,10 +254,9 @@ def _pool_size(blocks_needed: int) -> int:
     return int(math.ceil(1.1 * blocks_needed)) + 1
 
 
-def _plain(name, seed, dtype, hq, hkv, d, lens, n_layers, rng, last_token_apart=False):
+def _plain(name, seed, dtype, hq, hkv, d, lens, n_layers, rng, last_token_apart=False, bs=16):
     """Decode batch: each sequence appends its context; with ``last_token_apart`` the
     context minus one token first, then the new token of every sequence."""
-    bs = 16
     lens = np.asarray(lens, np.int32)
     B = lens.size
     need = int(sum(-(-int(L) // bs) for L in lens))
@@ -310,7 +309,8 @@ def make(name: str, seed: int | None = None, **over) -> Workload:
         rng = np.random.default_rng(np.random.SeedSequence(entropy=seed, spawn_key=(0,)))
         B = over.get("batch", 64)
         lens = rng.integers(over.get("lo", 64), over.get("hi", 2048) + 1, size=B)
-        return _plain("opt13b", seed, over.get("dtype", "f16"), 40, 40, 128, lens, 40, rng)
+        return _plain("opt13b", seed, over.get("dtype", "f16"), 40, 40, 128, lens, 40, rng,
+                      bs=over.get("block_size", 16))
 
     if name == "gqa":
         seed = 3 if seed is None else seed
@@ -320,7 +320,8 @@ def make(name: str, seed: int | None = None, **over) -> Workload:
         sig = over.get("sigma", 1.0)
         x = rng.lognormal(math.log(med), sig, size=B)
         lens = np.clip(np.rint(x), over.get("lo", 16), over.get("hi", 32768)).astype(np.int32)
-        return _plain("gqa", seed, over.get("dtype", "bf16"), 32, 8, 128, lens, 36, rng)
+        return _plain("gqa", seed, over.get("dtype", "bf16"), 32, 8, 128, lens, 36, rng,
+                      bs=over.get("block_size", 16))
 
     if name == "prefix_mixed":
         seed = 4 if seed is None else seed
