@@ -73,6 +73,7 @@ struct Plan {
     int max_waves = 0;
     int chunk_rows = 0;   // query rows per chunk tile; 0 = chunk rows run as decode rows
     int max_tiles = 0;
+    int pair_cost = pa::kPairCost;
     pa::Layout lay{};
 };
 
@@ -91,6 +92,11 @@ pa_status plan_shape(const pa_cache_desc* desc, int32_t num_seqs, int32_t total_
     if (const char* e = std::getenv("PA_DECODE_WAVES")) {
         const int v = std::atoi(e);
         if (v > 0 && v < p.max_waves) p.max_waves = v;
+    }
+    // tuning knob: the fixed cost of a pair in the wave split, in quarter blocks
+    if (const char* e = std::getenv("PA_PAIR_COST")) {
+        const int v = std::atoi(e);
+        if (v >= 0 && v <= pa::kMaxPairCost) p.pair_cost = v;
     }
     // chunk rows (sequences with several query rows) take the MFMA kernel when one exists
     // for this shape; PA_CHUNK_KERNEL=0 sends them through the decode kernel instead
@@ -260,9 +266,10 @@ pa_status build_args(void* out, pa_dtype out_dtype, const void* q, const void* k
     if (!block_tables || !seq_lens) return PA_ERR_NULL;
     if (need_attend_ptrs && (!out || !q || !k_cache || !v_cache)) return PA_ERR_NULL;
     if (max_blocks_per_seq == 0) return PA_ERR_SHAPE;
-    // the linear block space is indexed with 32-bit offsets
-    if ((uint64_t)total_q_rows * (uint64_t)max_blocks_per_seq * (uint64_t)desc->num_kv_heads >=
-        (1ull << 32))
+    // the linear block space and its weighted copy (4 per block plus the pair cost) are
+    // indexed with 32-bit offsets
+    if ((uint64_t)total_q_rows * (uint64_t)desc->num_kv_heads *
+            (4ull * (uint64_t)max_blocks_per_seq + pa::kMaxPairCost) >= (1ull << 32))
         return PA_ERR_SHAPE;
     if (!workspace || ((uintptr_t)workspace & 255u)) return PA_ERR_WORKSPACE;
     if (workspace_bytes < p.lay.total) return PA_ERR_WORKSPACE;
@@ -291,6 +298,7 @@ pa_status build_args(void* out, pa_dtype out_dtype, const void* q, const void* k
     a.max_waves = p.max_waves;
     a.chunk_rows = p.chunk_rows;
     a.max_tiles = p.max_tiles;
+    a.pair_cost = p.pair_cost;
     a.ws = (char*)workspace;
     a.lay = p.lay;
     return PA_OK;

@@ -36,8 +36,6 @@
 namespace pa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -47,36 +45,6 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Two fp32 values -> two packed 16-bit values (one v_cvt_pk_{bf16,f16}_f32, round to
-// nearest even).
-template <int DT>
-__device__ __forceinline__ uint32_t cvt2(float a, float b) {
-    const f32x2 v = {a, b};
-    if constexpr (DT == DT_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-}
-template <int DT>
-__device__ __forceinline__ float lo16(uint32_t w) {
-    if constexpr (DT == DT_BF16) return bf16_lo(w);
-    else return f16_lo(w);
-}
-template <int DT>
-__device__ __forceinline__ float hi16(uint32_t w) {
-    if constexpr (DT == DT_BF16) return bf16_hi(w);
-    else return f16_hi(w);
-}
-
-// P as the sum of two 16-bit numbers: hi = round(p), lo = round(p - hi).  Two MFMAs with
-// hi and lo carry P to about 16 significant bits; one 16-bit P alone (2^-9 relative for
-// bf16) would put up to ~1e-2 absolute error on rows that see only a few tokens.
-template <int DT>
-__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
-    hi = cvt2<DT>(a, b);
-    lo = cvt2<DT>(a - lo16<DT>(hi), b - hi16<DT>(hi));
 }
 
 template <int D>

@@ -249,6 +249,24 @@ struct KvOps<DT, D, G, BS, true> {
     }
 };
 
+// The wavefronts whose shares hold blocks of a pair cut by share boundaries: `wave` holds
+// its first block; the shares are consecutive and non-empty, so the others are the waves
+// after it whose shares start before the pair's end pe.  `next` is wx0[wave + 1 + lane]
+// (or pe where that index is past W), loaded early by the caller.
+__device__ inline int pair_waves(const uint32_t* wx0, int W, int wave, uint32_t pe,
+                                 uint32_t next, int lane) {
+    int n = 1;
+    uint64_t m = __builtin_amdgcn_ballot_w64(next < pe);
+    for (int base = wave + 1;;) {
+        n += __builtin_popcountll(m);
+        if (m != ~0ull) break;
+        base += kWave;
+        const int w = base + lane;
+        m = __builtin_amdgcn_ballot_w64(w < W && wx0[w] < pe);
+    }
+    return n;
+}
+
 template <int PE>
 __device__ __forceinline__ void store_row(const DecodeArgs& a, size_t idx, const float* v) {
     if (a.out_dtype == PA_F32) {
@@ -386,7 +404,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     const int32_t* empty = (const int32_t*)(a.ws + a.lay.empty);
 
     const int W = hdr[2], n_empty = hdr[3];
-    const uint32_t T = (uint32_t)hdr[1];
     const int wave = uniform(blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6));
     const int lane = lane_id();
     // rows with nothing to read are zeros (shared out among all launched wavefronts)
@@ -416,6 +433,11 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
         const int j0 = ui.b_lo + (int)(x - ps), j1 = ui.b_lo + (int)(seg_end - ps);
         const int len = ui.len;
         const int lo_tok = (a.window > 0 && len > a.window) ? len - a.window : 0;
+        // a pair cut after this segment and starting in it: its later shares' starts,
+        // loaded now and used when the merge record is written
+        const bool opens_cut = x == ps && seg_end < pe;
+        uint32_t next = pe;
+        if (opens_cut && wave + 1 + lane < W) next = wx0[wave + 1 + lane];
 
         // this lane's slice of the G query rows, kept packed
         typename S::Q qv;
@@ -561,13 +583,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
                 }
             }
         }
-        if (!complete && x == ps && lane == 0) {
-            // this wavefront holds the pair's first block: leave its merge task.  The
-            // wavefronts whose shares meet the pair are the one holding ps .. the one holding
-            // pe - 1; the wavefront holding block x is ceil((x + 1) W / T) - 1.
-            const uint64_t WW = (uint64_t)W, TT = T;
-            const int w_last = (int)((((uint64_t)pe) * WW + TT - 1) / TT) - 1;
-            tasks[wave + 1] = make_int4(u, g, w_last - wave + 1, first_segment ? 0 : 1);
+        if (opens_cut) {
+            // this wavefront holds the pair's first block: leave its merge task
+            const int nc = pair_waves(wx0, W, wave, pe, next, lane);
+            if (lane == 0) tasks[wave + 1] = make_int4(u, g, nc, first_segment ? 0 : 1);
         }
         x = seg_end;
         first_segment = false;

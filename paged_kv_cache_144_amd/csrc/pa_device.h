@@ -12,6 +12,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // Cache dtypes (the values of pa_dtype).  DT_Q8F16 / DT_Q8BF16: one-byte codes with one
 // fp16 scale per 32 values; queries and new rows in fp16 / bf16.
@@ -81,6 +83,37 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
     _Float16 h = (_Float16)x;  // v_cvt_f16_f32: round to nearest even
     return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> two packed 16-bit values of type DT (one v_cvt_pk_{bf16,f16}_f32,
+// round to nearest even).
+template <int DT>
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+    const f32x2 v = {a, b};
+    if constexpr (DT == DT_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+template <int DT>
+__device__ __forceinline__ float lo16(uint32_t w) {
+    if constexpr (DT == DT_BF16) return bf16_lo(w);
+    else return f16_lo(w);
+}
+template <int DT>
+__device__ __forceinline__ float hi16(uint32_t w) {
+    if constexpr (DT == DT_BF16) return bf16_hi(w);
+    else return f16_hi(w);
+}
+
+// A probability as the sum of two 16-bit numbers: hi = round(p), lo = round(p - hi).  Two
+// matrix products with hi and lo carry p to about 16 significant bits; one 16-bit p alone
+// (2^-9 relative for bf16) would put up to ~1e-2 absolute error on rows that see only a
+// few tokens.
+template <int DT>
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = cvt2<DT>(a, b);
+    lo = cvt2<DT>(a - lo16<DT>(hi), b - hi16<DT>(hi));
 }
 
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }

@@ -14,7 +14,12 @@ constexpr int kBlock = 16;          // default tokens per KV block (8 and 32 als
                                     // decode kernels for 16-bit caches)
 constexpr int kWave = 64;           // CDNA wavefront width
 constexpr int kWavesPerGroup = 4;   // decode workgroup = 4 independent wavefront workers
-constexpr int kMinBlocksPerWave = 8;  // smallest share of KV blocks worth a wavefront
+constexpr int kMinBlocksPerWave = 16;  // smallest share of KV blocks worth a wavefront
+constexpr int kPairCost = 14;       // default fixed cost per pair in quarter blocks: the
+                                    // dependent loads that start a segment
+// Consecutive share starts are at least 31 quarter blocks apart (4 T / ceil(T / 16) - 1
+// with T >= 16 blocks); a pair cost C with C + 4 <= 31 keeps every share non-empty.
+constexpr int kMaxPairCost = 27;
 constexpr int kQ8Group = 32;        // values per scale in 8-bit caches
 
 // Error bits written to the first word of the workspace.
@@ -37,6 +42,8 @@ struct UnitInfo {
 //                       [4] chunk-row tiles
 //   cb       uint32[U+1]   linear offset of pair (u, kv head 0); pair (u, g) starts at
 //                          cb[u] + g * nb(u) and spans nb(u) blocks
+//   cw       uint32[U+1]   the same in the weighted space the wave shares cut evenly: a
+//                          pair weighs 4 nb(u) + pair_cost (quarter blocks)
 //   unit     UnitInfo[U]
 //   empty    int32[U]      the rows with nothing to read
 //   wave_x0  uint32[W+1]   first linear block of each wave's share
@@ -48,7 +55,7 @@ struct UnitInfo {
 //   part_ml  float2[W*2*G]       partial (max, sum) per wave, slot, head of the group
 //   part_acc float[W*2*G*d]      partial unnormalised output
 struct Layout {
-    size_t header, cb, unit, empty, wave_x0, wave_u, tiles, tasks, part_ml, part_acc, total;
+    size_t header, cb, cw, unit, empty, wave_x0, wave_u, tiles, tasks, part_ml, part_acc, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -58,6 +65,7 @@ inline Layout layout(int num_rows, int max_waves, int max_tiles, int group, int 
     size_t o = 0;
     L.header = o;   o = align256(o + 64 * sizeof(int32_t));
     L.cb = o;       o = align256(o + (size_t)(num_rows + 1) * sizeof(uint32_t));
+    L.cw = o;       o = align256(o + (size_t)(num_rows + 1) * sizeof(uint32_t));
     L.unit = o;     o = align256(o + (size_t)num_rows * sizeof(UnitInfo));
     L.empty = o;    o = align256(o + (size_t)num_rows * sizeof(int32_t));
     L.wave_x0 = o;  o = align256(o + (size_t)(max_waves + 1) * sizeof(uint32_t));
@@ -86,6 +94,7 @@ struct DecodeArgs {
     int32_t max_waves;                // decode wavefront workers launched
     int32_t chunk_rows;               // query rows per chunk tile (0: chunk rows decode)
     int32_t max_tiles;                // chunk tiles the work list holds
+    int32_t pair_cost;                // fixed cost of a (row, KV head) pair, quarter blocks
     char* ws;
     Layout lay;
 };

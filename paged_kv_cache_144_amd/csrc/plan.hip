@@ -52,6 +52,7 @@ __device__ uint32_t block_scan(uint32_t* buf, uint32_t v) {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     int32_t* hdr = (int32_t*)(a.ws + a.lay.header);
     uint32_t* cb = (uint32_t*)(a.ws + a.lay.cb);
+    uint32_t* cw = (uint32_t*)(a.ws + a.lay.cw);
     UnitInfo* unit = (UnitInfo*)(a.ws + a.lay.unit);
     uint32_t* wx0 = (uint32_t*)(a.ws + a.lay.wave_x0);
     int32_t* wu = (int32_t*)(a.ws + a.lay.wave_u);
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     int2* tiles = (int2*)(a.ws + a.lay.tiles);
     int4* tasks = (int4*)(a.ws + a.lay.tasks);
 
-    __shared__ uint32_t s_blk[kPlanThreads], s_til[kPlanThreads];
+    __shared__ uint32_t s_blk[kPlanThreads], s_til[kPlanThreads], s_wt[kPlanThreads];
     __shared__ int s_err, s_bad, s_empty;
     const int tid = threadIdx.x;
     if (tid == 0) { s_err = 0; s_bad = 0; s_empty = 0; }
@@ -69,9 +70,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     const int per = (B + kPlanThreads - 1) / kPlanThreads;
     const int s0 = min(B, tid * per), s1 = min(B, s0 + per);
     const int QT = a.chunk_rows;
+    const uint32_t C = (uint32_t)a.pair_cost, H = (uint32_t)a.num_kv_heads;
 
-    // pass 1: validate; count decode blocks and chunk tiles
-    uint32_t my_blk = 0, my_til = 0;
+    // pass 1: validate; count decode blocks (and their weight) and chunk tiles
+    uint32_t my_blk = 0, my_til = 0, my_wt = 0;
     int err = 0, bad = 0;
     for (int s = s0; s < s1; ++s) {
         int r0 = s, r1 = s + 1;
@@ -92,13 +94,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
         for (int r = 0; r < n; ++r) {
             int32_t b_lo, nb;
             unit_range(L - n + r + 1, a.window, a.block_size, b_lo, nb);
-            my_blk += (uint32_t)nb * (uint32_t)a.num_kv_heads;   // one pair per KV head
+            my_blk += (uint32_t)nb * H;                          // one pair per KV head
+            if (nb > 0) my_wt += (4u * (uint32_t)nb + C) * H;
         }
     }
     if (bad) atomicOr(&s_bad, 1);
     if (err) atomicOr(&s_err, err);
     const uint32_t blk_incl = block_scan(s_blk, my_blk);
     const uint32_t til_incl = block_scan(s_til, my_til);
+    const uint32_t wt_incl = block_scan(s_wt, my_wt);
+    const uint32_t TW = s_wt[kPlanThreads - 1];
     const uint32_t T = s_blk[kPlanThreads - 1];
     const uint32_t NT = s_til[kPlanThreads - 1];
     if (s_bad || NT > (uint32_t)a.max_tiles) {
@@ -111,7 +116,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     }
 
     // pass 2: units, their offsets in the linear block space, chunk tiles
-    uint32_t off = blk_incl - my_blk, toff = til_incl - my_til;
+    uint32_t off = blk_incl - my_blk, toff = til_incl - my_til, woff = wt_incl - my_wt;
     for (int s = s0; s < s1; ++s) {
         int r0 = s, r1 = s + 1;
         if (a.query_start_loc) { r0 = a.query_start_loc[s]; r1 = a.query_start_loc[s + 1]; }
@@ -123,6 +128,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
             // the sequence's offset (no decode blocks: every row keeps the same offset)
             for (int q0 = 0; q0 < n; q0 += QT) tiles[toff++] = make_int2(s, q0);
             cb[r0] = off;
+            cw[r0] = woff;
             continue;
         }
         for (int r = 0; r < n; ++r) {
@@ -133,10 +139,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
             }
             unit[r0 + r] = ui;
             cb[r0 + r] = off;
-            off += (uint32_t)ui.nb * (uint32_t)a.num_kv_heads;
+            cw[r0 + r] = woff;
+            off += (uint32_t)ui.nb * H;
+            if (ui.nb > 0) woff += (4u * (uint32_t)ui.nb + C) * H;
         }
     }
-    if (tid == 0) cb[U] = T;
+    if (tid == 0) {
+        cb[U] = T;
+        cw[U] = TW;
+    }
     __syncthreads();
     // rows of chunk sequences: marked for the chunk kernel, offset of their first row
     for (int i = tid; i < (int)NT * QT; i += kPlanThreads) {
@@ -147,7 +158,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
         if (r < n) {
             const int u = rs + r;
             unit[u] = UnitInfo{-1, 0, 0, tl.x};
-            if (u != rs) cb[u] = cb[rs];
+            if (u != rs) {
+                cb[u] = cb[rs];
+                cw[u] = cw[rs];
+            }
         }
     }
 
@@ -163,16 +177,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     // rows with nothing to read (empty context, or rejected lengths) get zeros later
     for (int u = tid; u < U; u += kPlanThreads)
         if (unit[u].nb == 0 && unit[u].b_lo >= 0) empty[atomicAdd(&s_empty, 1)] = u;
-    // wavefront w's share starts at x0(w) = floor(w T / W).  It starts inside unit u exactly
-    // when ceil(cb[u] W / T) <= w < ceil(cb[u+1] W / T); these ranges tile [0, W).
+    // The shares cut the weighted space evenly: wavefront w's share starts at weighted
+    // position y(w) = floor(w TW / W), where a pair weighs 4 nb + C quarter blocks (its
+    // blocks plus the fixed cost of starting a segment).  y(w) falls inside unit u exactly
+    // when ceil(cw[u] W / TW) <= w < ceil(cw[u+1] W / TW); these ranges tile [0, W).  A
+    // position in a pair's first C quarters maps to the pair's first block, one further on
+    // to the next whole block.  Consecutive y differ by at least 31 >= C + 4, so every share
+    // holds at least one block and the shares are consecutive.
     for (int u = tid; u < U && W > 0; u += kPlanThreads) {
-        const uint64_t c0 = cb[u], c1 = cb[u + 1];
+        const uint64_t c0 = cw[u], c1 = cw[u + 1];
         if (c1 == c0) continue;
-        const uint64_t w0 = (c0 * (uint64_t)W + T - 1) / T;
-        uint64_t w1 = (c1 * (uint64_t)W + T - 1) / T;
+        const uint64_t w0 = (c0 * (uint64_t)W + TW - 1) / TW;
+        uint64_t w1 = (c1 * (uint64_t)W + TW - 1) / TW;
         if (w1 > (uint64_t)W) w1 = W;
+        const uint32_t nb = (uint32_t)unit[u].nb, pw = 4u * nb + C;
         for (uint64_t w = w0; w < w1; ++w) {
-            wx0[w] = (uint32_t)((w * T) / (uint64_t)W);
+            const uint32_t y = (uint32_t)((w * TW) / (uint64_t)W) - (uint32_t)c0;
+            const uint32_t g = y / pw, o = y - g * pw;
+            uint32_t k = o <= C ? 0u : (o - C + 3) / 4;
+            k = k < nb ? k : nb;
+            wx0[w] = cb[u] + g * nb + k;
             wu[w] = u;
         }
     }

@@ -86,6 +86,10 @@ SMALL = [
     ("parallel_sampling", dict(prompts=3, samples=3, lo=20, hi=300, dtype="q8_f16")),
     ("prefix_mixed", dict(batch=10, prefix=64, suffix_hi=80, chunks=2, chunk_rows=40,
                           chunk_lo=100, chunk_hi=300, dtype="q8_bf16")),
+    # matrix-core decode: groups of 4 and 8, head_dim 64 / 128 / 256
+    ("tiny", dict(dtype="f16", hq=16, hkv=4, d=64)),
+    ("tiny", dict(dtype="bf16", hq=16, hkv=2, d=128)),
+    ("gqa", dict(batch=9, median=400, lo=16, hi=5000, dtype="f16")),
     # 8- and 32-token blocks (16-bit caches)
     ("opt13b", dict(batch=6, lo=64, hi=700, block_size=8)),
     ("opt13b", dict(batch=6, lo=64, hi=700, block_size=32)),
