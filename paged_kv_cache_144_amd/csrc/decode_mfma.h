@@ -92,56 +92,96 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
     // V: coalesced; load i of lane l reads bytes 1024 i + 16 l of the tile
     const char* vbase = (const char*)a.v_cache + (size_t)lane * 16;
 
-    uint32_t x = wx0[wave];
+    const uint32_t x_start = wx0[wave];
     const uint32_t x_end = wx0[wave + 1];
-    int u = wu[wave];
-    bool first_segment = true;
+    int uh = wu[wave];
 
-    while (x < x_end) {
-        while (cb[u + 1] <= x) ++u;
-        const UnitInfo ui = unit[u];
-        const uint32_t base = cb[u];
-        const int g = (int)((x - base) / (uint32_t)ui.nb);
-        const uint32_t ps = base + (uint32_t)g * ui.nb, pe = ps + ui.nb;
-        const uint32_t seg_end = x_end < pe ? x_end : pe;
-        const int j0 = ui.b_lo + (int)(x - ps), j1 = ui.b_lo + (int)(seg_end - ps);
-        const int len = ui.len;
-        const int lo_tok = (a.window > 0 && len > a.window) ? len - a.window : 0;
-        const bool opens_cut = x == ps && seg_end < pe;
-        uint32_t next = pe;
+    // A segment: the part of pair (u, g) inside this wavefront's share; blocks j0 .. j1-1
+    // of the sequence's table row.
+    struct Seg {
+        int u, g, seq, len, lo_tok, j0, j1;
+        uint32_t ps, pe, end;
+        bool starts;     // the segment starts at the pair's first block
+    };
+    auto describe = [&](uint32_t xs) {
+        while (cb[uh + 1] <= xs) ++uh;
+        const UnitInfo ui = unit[uh];
+        const uint32_t base = cb[uh];
+        Seg sg;
+        sg.u = uh;
+        sg.g = (int)((xs - base) / (uint32_t)ui.nb);
+        sg.ps = base + (uint32_t)sg.g * ui.nb;
+        sg.pe = sg.ps + ui.nb;
+        sg.end = x_end < sg.pe ? x_end : sg.pe;
+        sg.starts = xs == sg.ps;
+        sg.j0 = ui.b_lo + (int)(xs - sg.ps);
+        sg.j1 = ui.b_lo + (int)(sg.end - sg.ps);
+        sg.seq = ui.seq;
+        sg.len = ui.len;
+        sg.lo_tok = (a.window > 0 && ui.len > a.window) ? ui.len - a.window : 0;
+        return sg;
+    };
+    // block ids c0 .. c0+63 of the segment, one per lane
+    auto load_ids = [&](const Seg& sg, int c0) {
+        const int n = sg.j1 - c0;
+        return lane < n ? a.block_tables[(size_t)sg.seq * a.max_blocks + c0 + lane] : 0;
+    };
+    // B operand of S^T: query head c16 of the group (zero for c16 >= G), columns
+    // 32 c + 8 q4 .. +8
+    auto load_q = [&](const Seg& sg, u32x4 (&qb)[KC]) {
+        const size_t qrow = ((size_t)sg.u * a.num_q_heads + (size_t)sg.g * G + c16) * D;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            qb[c] = c16 < G ? ld16((const char*)a.q + (qrow + 32 * c + 8 * q4) * 2) : z;
+    };
+    struct Tile { u32x4 k[KC], v[NLD]; };
+    auto block_id = [&](int ids, int idx, bool& valid) {
+        int b = __builtin_amdgcn_readlane(ids, idx);
+        valid = (unsigned)b < (unsigned)a.num_blocks;
+        return valid ? b : 0;
+    };
+    auto load_tile = [&](const Seg& sg, int b, Tile& t) {
+        const size_t off = (size_t)b * block_stride + (size_t)sg.g * tile;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) t.k[c] = ld16_stream(kbase + off + c * 64);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) t.v[i] = ld16_stream(vbase + off + i * 1024);
+    };
+
+    if (x_start >= x_end) return;
+    Seg cur = describe(x_start);
+    u32x4 qb[KC];
+    load_q(cur, qb);
+    int ids = load_ids(cur, cur.j0);
+    Tile A, B;
+    bool okA, okB;
+    load_tile(cur, block_id(ids, 0, okA), A);
+    bool first_segment = true;
+    int bad = 0;
+
+    for (;;) {
+        // the next segment's record, queries and first block ids load while this one runs
+        const bool more = cur.end < x_end;
+        Seg nxt = cur;
+        u32x4 qn[KC];
+        int nids = 0;
+        if (more) {
+            nxt = describe(cur.end);
+            load_q(nxt, qn);
+            nids = load_ids(nxt, nxt.j0);
+        }
+        // a pair that starts here and continues past the share: the later shares' starts
+        const bool opens_cut = cur.starts && cur.end < cur.pe;
+        uint32_t next = cur.pe;
         if (opens_cut && wave + 1 + lane < W) next = wx0[wave + 1 + lane];
 
-        // B operand of S^T: query head c16 of the group (zero for c16 >= G), columns
-        // 32 c + 8 q4 .. +8
-        u32x4 qb[KC];
-        {
-            const size_t qrow = ((size_t)u * a.num_q_heads + (size_t)g * G + c16) * D;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int c = 0; c < KC; ++c)
-                qb[c] = c16 < G ? ld16((const char*)a.q + (qrow + 32 * c + 8 * q4) * 2) : z;
-        }
         f32x4 acc[VB];     // O: lane holds column 16 b + c16 of heads 4 q4 .. 4 q4 + 3
 #pragma unroll
         for (int b = 0; b < VB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m = kNegBig, lsum = 0.f;   // head c16, this lane's tokens
+        const int len = cur.len, lo_tok = cur.lo_tok;
 
-        const int32_t* bt = a.block_tables + (size_t)ui.seq * a.max_blocks;
-        const size_t head_off = (size_t)g * tile;
-        struct Tile { u32x4 k[KC], v[NLD]; };
-
-        auto block_id = [&](int btv, int idx, bool& valid) {
-            int b = __builtin_amdgcn_readlane(btv, idx);
-            valid = (unsigned)b < (unsigned)a.num_blocks;
-            return valid ? b : 0;
-        };
-        auto load_tile = [&](int b, Tile& t) {
-            const size_t off = (size_t)b * block_stride + head_off;
-#pragma unroll
-            for (int c = 0; c < KC; ++c) t.k[c] = ld16_stream(kbase + off + c * 64);
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) t.v[i] = ld16_stream(vbase + off + i * 1024);
-        };
         auto consume = [&](Tile& tl, int j, bool valid) {
             const int t0 = j * kBlock;
             const bool edge = !valid || t0 < lo_tok || t0 + kBlock > len;   // uniform
@@ -162,13 +202,13 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
                 *reinterpret_cast<u32x2*>(dst + 8) = u32x2{v.z, v.w};
             }
             // S^T: lane holds head c16, tokens 4 q4 .. +3
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < KC; ++c) s = mfma_16x16x32<DT>(tl.k[c], qb[c], s);
+            for (int c = 0; c < KC; ++c) sacc = mfma_16x16x32<DT>(tl.k[c], qb[c], sacc);
             float sc[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                sc[r] = c16 < G ? s[r] * qscale : -INFINITY;
+                sc[r] = c16 < G ? sacc[r] * qscale : -INFINITY;
                 if (edge) {
                     const int t = t0 + 4 * q4 + r;
                     const bool ok = valid && t >= lo_tok && t < len;
@@ -214,29 +254,51 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
             }
         };
 
-        int bad = 0;
-        for (int c0 = j0; c0 < j1; c0 += kWave) {
-            const int n = (j1 - c0) < kWave ? (j1 - c0) : kWave;
-            const int btv = lane < n ? bt[c0 + lane] : 0;
-            Tile A, B;
-            bool okA, okB;
-            load_tile(block_id(btv, 0, okA), A);
-            for (int jj = 0; jj < n; jj += 2) {
-                load_tile(block_id(btv, jj + 1 < n ? jj + 1 : jj, okB), B);
+        // blocks of the segment, in chunks of 64 ids; A holds the segment's first block.
+        // The load after each block's is the next block of the stream: in this chunk, the
+        // next chunk, the next segment, or (at the very end) the last block again.
+        int cids = ids;
+        for (int c0 = cur.j0;; c0 += kWave) {
+            const int n = (cur.j1 - c0) < kWave ? (cur.j1 - c0) : kWave;
+            const bool last_chunk = c0 + kWave >= cur.j1;
+            const int nc_ids = last_chunk ? 0 : load_ids(cur, c0 + kWave);
+            auto next_block = [&](int k, bool& ok, const Seg*& sg) {
+                sg = &cur;
+                if (k < n) return block_id(cids, k, ok);
+                if (!last_chunk) return block_id(nc_ids, 0, ok);
+                if (more) {
+                    sg = &nxt;
+                    return block_id(nids, 0, ok);
+                }
+                return block_id(cids, n - 1, ok);
+            };
+            const Seg* sgB;
+            const Seg* sgA;
+            int jj = 0;
+            for (;; jj += 2) {
+                const int bB = next_block(jj + 1, okB, sgB);
+                load_tile(*sgB, bB, B);
                 bad |= !okA;
                 consume(A, c0 + jj, okA);
-                if (jj + 1 >= n) break;
-                load_tile(block_id(btv, jj + 2 < n ? jj + 2 : jj + 1, okA), A);
+                if (jj + 1 >= n) {
+                    A = B;
+                    okA = okB;
+                    break;
+                }
+                const int bA = next_block(jj + 2, okA, sgA);
+                load_tile(*sgA, bA, A);
                 bad |= !okB;
                 consume(B, c0 + jj + 1, okB);
+                if (jj + 2 >= n) break;
             }
+            if (last_chunk) break;
+            cids = nc_ids;
         }
-        if (bad && lane == 0) atomicOr(hdr, kErrBlockId);
 
         // the head's sum over its 4 lanes; O-layout lanes fetch (m, l) of their heads
         float lt = lsum + __shfl_xor(lsum, 16);
         lt += __shfl_xor(lt, 32);
-        const bool complete = x == ps && seg_end == pe;
+        const bool complete = cur.starts && cur.end == cur.pe;
         const int slot = first_segment ? 0 : 1;
         if (!complete && q4 == 0 && c16 < G) {
             const size_t pi = ((size_t)wave * 2 + slot) * G + c16;
@@ -249,7 +311,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
             if (h < G) {
                 if (complete) {
                     const float inv = lh > 0.f ? 1.f / lh : 0.f;
-                    const size_t ob = ((size_t)u * a.num_q_heads + (size_t)g * G + h) * D + c16;
+                    const size_t ob = ((size_t)cur.u * a.num_q_heads + (size_t)cur.g * G + h) * D + c16;
 #pragma unroll
                     for (int b = 0; b < VB; ++b) store_out1(a, ob + 16 * b, acc[b][r] * inv);
                 } else {
@@ -260,12 +322,17 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
             }
         }
         if (opens_cut) {
-            const int nc = pair_waves(wx0, W, wave, pe, next, lane);
-            if (lane == 0) tasks[wave + 1] = make_int4(u, g, nc, first_segment ? 0 : 1);
+            const int nc = pair_waves(wx0, W, wave, cur.pe, next, lane);
+            if (lane == 0) tasks[wave + 1] = make_int4(cur.u, cur.g, nc, first_segment ? 0 : 1);
         }
-        x = seg_end;
+        if (!more) break;
+        cur = nxt;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) qb[c] = qn[c];
+        ids = nids;
         first_segment = false;
     }
+    if (bad && lane == 0) atomicOr(hdr, kErrBlockId);
 }
 
 }  // namespace pa
