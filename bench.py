@@ -43,7 +43,7 @@ Q8_DTYPE = {"opt13b": "q8_f16", "gqa": "q8_bf16", "swa": "q8_f16", "prefix_mixed
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense matrix peak, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SOURCES = ["decode_impl.h", "pa_device.h", "pa_internal.h", "plan.hip"]
+KERNEL_SOURCES = ["decode_impl.h", "decode_mfma.h", "pa_device.h", "pa_internal.h", "plan.hip"]
 
 DESCRIPTIONS = {
     "opt13b": "OPT-13B-shaped paged decode: 64 seqs, 40 q heads = 40 KV heads, d=128, fp16 KV, "
