@@ -10,18 +10,22 @@ const void* decode_kernel_ptr_f16(int head_dim, int group);
 const void* decode_kernel_ptr_bf16(int head_dim, int group);
 const void* decode_kernel_ptr_q8(int dtype, int head_dim, int group);
 const void* decode_kernel_ptr_mfma(int dtype, int head_dim, int group);
+const void* decode_kernel_ptr_mfma_q8(int dtype, int head_dim, int group);
 const void* decode_kernel_ptr_f16_bs(int head_dim, int group, int block_size);
 const void* decode_kernel_ptr_bf16_bs(int head_dim, int group, int block_size);
 const void* chunk_kernel_ptr_f16(int head_dim, int group);
 const void* chunk_kernel_ptr_bf16(int head_dim, int group);
 
 const void* decode_kernel_ptr(int dtype, int head_dim, int group, int block_size) {
-    // groups of 4 or 8 query heads with 16-bit caches: the matrix-core kernel
+    // groups of 4 or 8 query heads with 16-token blocks: the matrix-core kernel
     // (PA_DECODE_MFMA=0 selects the per-lane kernel instead)
-    if (block_size == kBlock && (dtype == DT_F16 || dtype == DT_BF16) &&
-        (group == 4 || group == 8)) {
+    if (block_size == kBlock && dtype != DT_F32 && (group == 4 || group == 8)) {
         const char* e = std::getenv("PA_DECODE_MFMA");
-        if (!(e && e[0] == '0')) return decode_kernel_ptr_mfma(dtype, head_dim, group);
+        if (!(e && e[0] == '0')) {
+            if (dtype == DT_Q8F16 || dtype == DT_Q8BF16)
+                return decode_kernel_ptr_mfma_q8(dtype, head_dim, group);
+            return decode_kernel_ptr_mfma(dtype, head_dim, group);
+        }
     }
     if (block_size != kBlock) {
         switch (dtype) {

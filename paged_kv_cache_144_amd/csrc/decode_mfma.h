@@ -1,10 +1,14 @@
 // Paged decode attention on the matrix cores, for groups of G = 4 or 8 query heads per KV
-// head (grouped-query attention) with fp16 / bf16 caches and 16-token blocks.
+// head (grouped-query attention) with 16-token blocks: fp16 / bf16 caches, and 8-bit caches
+// with one fp16 scale per 32 values.
 //
 // It computes what decode_kernel computes (same work split, partials and merge records;
 // "PagedAttention deep dive", donmain.dev, section on splitting the KV cache into blocks,
 // for how tokens are found through the block table), but the two products of a block run
-// as MFMAs instead of per-lane dot products:
+// as MFMAs instead of per-lane dot products.  The control flow (segments, prefetch,
+// softmax, partials) is shared; how a tile becomes MFMA operands is a policy:
+//
+// 16-bit caches (MfmaKv16):
 //   * S^T = K Q^T with v_mfma_f32_16x16x32: the A operand is read straight from the tile
 //     (lane l holds 8 consecutive elements of token row l % 16), the B operand is the G
 //     query rows of the group, zero-padded to 16 and kept in registers for the segment;
@@ -13,9 +17,25 @@
 //     their lanes; each lane does the softmax work of its 4 tokens of one head only;
 //   * V's B operand needs 4 consecutive tokens of one column per lane, so each V tile is
 //     staged in the wavefront's own LDS rows and read back transposed;
-//   * P is carried as hi + lo 16-bit parts (two MFMAs), as in the chunk-row kernel;
-//   * masked tokens are removed by selection: their scores become -inf and their V rows
-//     are zeroed before staging, so NaN in free or unused slots cannot reach the output.
+//   * P is carried as hi + lo 16-bit parts (two MFMAs), as in the chunk-row kernel.
+//
+// 8-bit caches (MfmaKvQ8; the format of "KV cache by model", sotaaz.com):
+//   * K codes become exact fp16 integers (the flipped code byte under the exponent of 1024
+//     gives 1152 + code; a packed subtract of 1152 leaves the code); the query is held in
+//     fp16 after a power-of-two scaling per head (exact for fp16 and bf16 values), whose
+//     inverse joins the softmax scale;
+//   * each 16x16x32 step of S^T covers exactly one 32-column scale group, so every step
+//     keeps its own accumulator and the per-(token, group) scales are applied to the four
+//     partial scores of each lane before they are summed;
+//   * O = P V runs on v_mfma_f32_16x16x4_f32: its A operand for step s is the probability
+//     each lane already holds for token 4 (l / 16) + s, and its B operand is code x scale
+//     in fp32 (exact: 8 x 11 significant bits) of that token and one of the lane's D / 16
+//     consecutive columns.  The lane loads those columns straight from the tile (one
+//     scale group per lane), so nothing is staged in LDS and P needs no hi/lo split.
+//
+// Masked tokens are removed by selection in both: their scores become -inf and their V
+// values zero (16-bit: rows zeroed before staging; 8-bit: scale zeroed), so NaN in free or
+// unused slots cannot reach the output.
 #pragma once
 
 #include "decode_impl.h"
@@ -46,25 +66,409 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
                                                      __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
-template <int D>
-struct MfmaShape {
+// ---- 16-bit caches ------------------------------------------------------------------
+template <int DT, int D, int G>
+struct MfmaKv16 {
     static constexpr int KC = D / 32;             // 16x16x32 steps over d for S^T
-    static constexpr int VB = D / 16;             // 16-column blocks of O
+    static constexpr int NACC = D / 16;           // 16-column blocks of O
     static constexpr int NLD = kBlock * D * 2 / 1024;   // coalesced 1 KiB loads per V tile
     static constexpr int RS = D * 2 + 8;          // LDS bytes per staged V token row (padded)
     static constexpr int LDSW = kBlock * RS;      // LDS bytes per wavefront
+    static constexpr int LDS_BYTES = kWavesPerGroup * LDSW;
+    static constexpr size_t TILE = (size_t)kBlock * D * 2;
+    static constexpr int BPT = 1;                 // blocks per tile
+
+    struct Q { u32x4 b[KC]; float f; };
+    struct Tile { u32x4 k[KC], v[NLD]; };
+    struct Extra {};
+
+    // K: lane holds token c16, columns 32 c + 8 q4 .. +8 of each step c.
+    // V: coalesced; load i of lane l reads bytes 1024 i + 16 l of the tile.
+    __device__ static size_t k_lane(int lane) {
+        return (size_t)(lane % 16) * D * 2 + (size_t)(lane / 16) * 16;
+    }
+    __device__ static size_t v_lane(int lane) { return (size_t)lane * 16; }
+
+    // B operand of S^T: query head c16 of the group (zero for c16 >= G), columns
+    // 32 c + 8 q4 .. +8
+    __device__ static void load_q(const void* q, size_t qrow, int c16, int q4, Q& r) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            r.b[c] = c16 < G ? ld16((const char*)q + (qrow + 32 * c + 8 * q4) * 2) : z;
+        r.f = 1.f;
+    }
+    __device__ static void load(const char* kb, const char* vb, const size_t (&offs)[BPT],
+                                Tile& t) {
+        const size_t off = offs[0];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) t.k[c] = ld16_stream(kb + off + c * 64);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) t.v[i] = ld16_stream(vb + off + i * 1024);
+    }
+    // Stage V (rows of masked tokens zeroed) in this wavefront's LDS rows; S^T of the
+    // block: lane holds head c16, tokens 4 q4 .. +3.
+    template <class Ok>
+    __device__ static void scores(const Tile& tl, int h, const Q& q, char* my, int t0, bool edge,
+                                  Ok ok, float (&s)[4]) {
+        const int lane = lane_id();
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int byte = i * 1024 + lane * 16;
+            const int tv = byte / (D * 2), col = byte % (D * 2);
+            u32x4 v = tl.v[i];
+            if (edge) {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                v = ok(h, t0 + tv) ? v : z;
+            }
+            char* dst = my + tv * RS + col;
+            *reinterpret_cast<u32x2*>(dst) = u32x2{v.x, v.y};
+            *reinterpret_cast<u32x2*>(dst + 8) = u32x2{v.z, v.w};
+        }
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) sacc = mfma_16x16x32<DT>(tl.k[c], q.b[c], sacc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] = sacc[r];
+    }
+    // O += P V: B operand = column 16 b + c16 of tokens 4 q4 .. +3, from LDS
+    template <class Ok>
+    __device__ static void pv(f32x4 (&acc)[NACC], const float (&pp)[BPT][4], const Tile&, int,
+                              char* my, const int (&)[BPT], const bool (&)[BPT], Ok, Extra&) {
+        const int lane = lane_id(), c16 = lane % 16, q4 = lane / 16;
+        const float (&p)[4] = pp[0];
+        uint32_t h0, l0, h1, l1;
+        split2<DT>(p[0], p[1], h0, l0);
+        split2<DT>(p[2], p[3], h1, l1);
+        const u32x2 ph = {h0, h1}, pl = {l0, l1};
+        const uint16_t* vr = reinterpret_cast<const uint16_t*>(my + 4 * q4 * RS) + c16;
+#pragma unroll
+        for (int b = 0; b < NACC; ++b) {
+            const uint32_t e0 = vr[16 * b], e1 = vr[RS / 2 + 16 * b];
+            const uint32_t e2 = vr[RS + 16 * b], e3 = vr[3 * RS / 2 + 16 * b];
+            const u32x2 vb = {e0 | (e1 << 16), e2 | (e3 << 16)};
+            acc[b] = mfma_16x16x16<DT>(ph, vb, acc[b]);
+            acc[b] = mfma_16x16x16<DT>(pl, vb, acc[b]);
+        }
+    }
+    __device__ static void init(Extra&) {}
+    __device__ static void rescale(Extra&, float) {}
+    __device__ static void finish(f32x4 (&)[NACC], const Extra&) {}
+    // acc[b] of lane c16 is column 16 b + c16
+    __device__ static void store(const DecodeArgs& a, size_t ob, const f32x4 (&acc)[NACC],
+                                 int r, float inv, int c16) {
+#pragma unroll
+        for (int b = 0; b < NACC; ++b) store_out1(a, ob + 16 * b + c16, acc[b][r] * inv);
+    }
+    __device__ static void store_part(float* dst, const f32x4 (&acc)[NACC], int r, int c16) {
+#pragma unroll
+        for (int b = 0; b < NACC; ++b) dst[16 * b + c16] = acc[b][r];
+    }
 };
 
+// ---- 8-bit caches -------------------------------------------------------------------
+// Tile: 16 rows of D one-byte codes, then the scale row [16][D / 32] fp16.
 template <int DT, int D, int G>
-__global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(DecodeArgs a) {
-    static_assert(DT == DT_F16 || DT == DT_BF16, "16-bit caches");
+struct MfmaKvQ8 {
+    static constexpr int ADT = DT == DT_Q8F16 ? DT_F16 : DT_BF16;   // query type
+    static constexpr int KC = D / 32;             // steps of S^T = scale groups
+    static constexpr int NACC = D / 16;           // 16-column blocks of O, two per group
+    static constexpr int CPL = D / 16;            // V columns a lane loads per token row
+    static constexpr int VW = CPL / 4;            // code dwords per V row and lane
+    static constexpr int SW = KC / 2;             // 16-byte LDS reads of a lane's scales
+    static constexpr int SCALES = kBlock * D;
+    // LDS dwords per staged token pair: column c sits at dword c + 4 (c / 64) (the skew
+    // keeps the 16-byte writes of lanes 8 apart off the same banks), and PS = 8 mod 16
+    // keeps the two-dword reads of the four lane rows on distinct banks
+    static constexpr int PS = (D + D / 16 + 7) / 16 * 16 + 8;
+    static constexpr int SB = D / 32;             // scale-row bytes a lane loads (K or V row)
+    // An 8-bit tile is half the bytes of a 16-bit one: two blocks per tile keep as many
+    // bytes in flight per wavefront (head_dim 256 keeps one: its registers would not fit).
+    static constexpr int BPT = D <= 128 ? 2 : 1;
+    static constexpr int VBLK = kBlock / 2 * PS;  // LDS dwords of one block's staged V
+    static constexpr int LDSV = BPT * VBLK * 4;   // LDS bytes of staged V per wavefront
+    static constexpr int LDSS = LDSV;             // each block's K and V scale rows
+    static constexpr int KS = D + 16;             // LDS bytes per staged K row (padded)
+    static constexpr int LDSK = LDSS + BPT * 2 * D;     // each block's K codes
+    static constexpr int LDSW = LDSK + BPT * kBlock * KS;
+    static constexpr int KN = kBlock * D / 1024;  // coalesced 1 KiB loads of a block's K codes
+    static constexpr int LDS_BYTES = kWavesPerGroup * LDSW;
+    static constexpr size_t TILE = (size_t)(kBlock + 1) * D;
+    static_assert(KC % 2 == 0, "an even number of scale groups");
+
+    struct Q { u32x4 b[KC]; float f; };
+    // k: load i of lane l holds bytes 1024 i + 16 l of the block's codes (whole rows per
+    // load: an MFMA operand's 8-byte pieces are read back from LDS, since loading them
+    // directly would split every row into four small memory requests); v: CPL codes of
+    // token 4 q4 + s; sc: SB bytes of the K scale row (lanes 0-31) or the V scale row
+    // (lanes 32-63).  K, the scale rows and V are staged through LDS when consumed.
+    struct Tile { u32x4 k[BPT][KN]; uint32_t v[BPT][4][VW]; uint32_t sc[BPT][(SB + 3) / 4]; };
+    // sum over this lane's tokens of P x V scale, per group (head c16)
+    struct Extra { float corr[KC]; };
+
+    __device__ static size_t k_lane(int lane) { return (size_t)lane * 16; }
+    __device__ static size_t v_lane(int lane) {
+        return (size_t)(lane / 16) * 4 * D + (size_t)(lane % 16) * CPL;
+    }
+
+    // B operand of S^T in fp16: query head c16 (zero for c16 >= G), columns 32 c + 8 q4 ..
+    // +8, times 2^(15 - e) where 2^e bounds the head's largest |q|: every value then lies
+    // below 2^15 and converts exactly.  f = 2^(e - 15) undoes the scaling.
+    __device__ static void load_q(const void* q, size_t qrow, int c16, int q4, Q& r) {
+        float v[KC][8];
+        float mx = 0.f;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            if (c16 < G) {
+                widen16<ADT>(ld16((const char*)q + (qrow + 32 * c + 8 * q4) * 2), v[c]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[c][e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[c][e]));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));          // over the head's 4 lanes
+        const int ex = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2)
+                w[e / 2] = cvt2<DT_F16>(ldexpf(v[c][e], 15 - ex), ldexpf(v[c][e + 1], 15 - ex));
+            r.b[c] = u32x4{w[0], w[1], w[2], w[3]};
+        }
+        r.f = ldexpf(1.f, ex - 15);
+    }
+    // the scale-row piece of lane l: K row bytes SB l .. (l < 32), V row bytes SB (l - 32) ..
+    __device__ static const char* scale_piece(const char* kb, const char* vb, size_t off,
+                                              int lane) {
+        return lane < 32 ? kb - k_lane(lane) + off + SCALES + SB * lane
+                         : vb - v_lane(lane) + off + SCALES + SB * (lane - 32);
+    }
+    __device__ static void load(const char* kb, const char* vb, const size_t (&offs)[BPT],
+                                Tile& t) {
+        const int lane = lane_id();
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) {
+            const size_t off = offs[h];
+#pragma unroll
+            for (int i = 0; i < KN; ++i) t.k[h][i] = ld16_stream(kb + off + 1024 * i);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const char* p = vb + off + (size_t)s * D;
+                if constexpr (VW == 1) {
+                    t.v[h][s][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+                } else if constexpr (VW == 2) {
+                    const u32x2 x = ld8_stream(p);
+                    t.v[h][s][0] = x.x; t.v[h][s][1] = x.y;
+                } else {
+                    const u32x4 x = ld16_stream(p);
+                    t.v[h][s][0] = x.x; t.v[h][s][1] = x.y; t.v[h][s][2] = x.z; t.v[h][s][3] = x.w;
+                }
+            }
+            const char* sp = scale_piece(kb, vb, off, lane);
+            if constexpr (SB == 2) {
+                t.sc[h][0] = ld2_stream(sp);
+            } else if constexpr (SB == 4) {
+                t.sc[h][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sp));
+            } else {
+                const u32x2 x = ld8_stream(sp);
+                t.sc[h][0] = x.x; t.sc[h][1] = x.y;
+            }
+        }
+    }
+    // fp16 pairs (1152 + c0, 1152 + c1) from code bytes 0, 1 (lo) or 2, 3 (hi) of x, whose
+    // bytes are already flipped by 0x80 (code + 128): the byte goes under 0x64.
+    __device__ static uint32_t pair_lo(uint32_t x) {
+        return __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
+    }
+    __device__ static uint32_t pair_hi(uint32_t x) {
+        return __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
+    }
+    __device__ static int vcol(int c) { return c + 4 * (c / 64); }
+    __device__ static uint32_t minus1152(uint32_t h) {
+        const f16x2 k = {(_Float16)1152.f, (_Float16)1152.f};
+        return __builtin_bit_cast(uint32_t, as_f16x2(h) - k);
+    }
+    // the 4 KC fp16 scales of tokens 4 q4 .. +3 of one scale row, from its staged copy;
+    // (r, group g) is number r KC + g
+    struct Scales { u32x4 w[SW]; };
+    __device__ static void read_scales(const char* row, Scales& sc) {
+        const int q4 = lane_id() / 16;
+#pragma unroll
+        for (int i = 0; i < SW; ++i)
+            sc.w[i] = *reinterpret_cast<const u32x4*>(row + q4 * 8 * KC + 16 * i);
+    }
+    __device__ static float scale(const Scales& sc, int r, int g) {
+        const int i = r * KC + g;
+        const u32x4 w = sc.w[i / 8];
+        const uint32_t d = (i / 2) % 4 == 0 ? w.x : (i / 2) % 4 == 1 ? w.y : (i / 2) % 4 == 2 ? w.z : w.w;
+        return i % 2 ? f16_hi(d) : f16_lo(d);
+    }
+    // S^T of the block, lane: head c16, tokens 4 q4 .. +3.  Step c is scale group c.
+    template <class Ok>
+    __device__ static void scores(const Tile& tl, int h, const Q& q, char* my, int t0, bool,
+                                  Ok ok, float (&s)[4]) {
+        // stage the block's K codes and both scale rows, then read this lane's pieces
+        const int lane = lane_id(), c16 = lane % 16, q4 = lane / 16;
+        char* krow = my + LDSK + h * kBlock * KS;
+#pragma unroll
+        for (int i = 0; i < KN; ++i) {
+            const int byte = 1024 * i + 16 * lane;
+            *reinterpret_cast<u32x4*>(krow + (byte / D) * KS + byte % D) = tl.k[h][i];
+        }
+        char* srow = my + LDSS + h * 2 * D;
+        // a V scale piece (lanes 32-63) belongs to token (lane - 32) / 2: zero for tokens the
+        // row does not see, so that their V values are exact zeros whatever the slot holds
+        const bool keep = lane < 32 || ok(h, t0 + (lane - 32) / 2);
+        if constexpr (SB == 2) {
+            *reinterpret_cast<uint16_t*>(srow + SB * lane) = keep ? (uint16_t)tl.sc[h][0] : 0;
+        } else if constexpr (SB == 4) {
+            *reinterpret_cast<uint32_t*>(srow + SB * lane) = keep ? tl.sc[h][0] : 0u;
+        } else {
+            *reinterpret_cast<u32x2*>(srow + SB * lane) =
+                keep ? u32x2{tl.sc[h][0], tl.sc[h][1]} : u32x2{0u, 0u};
+        }
+        Scales ks;
+        read_scales(srow, ks);
+        u32x2 kp[KC];     // token c16, columns 32 c + 8 q4 .. +8
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            kp[c] = *reinterpret_cast<const u32x2*>(krow + c16 * KS + 32 * c + 8 * q4);
+        f32x4 sc[KC];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const uint32_t x0 = kp[c].x ^ 0x80808080u, x1 = kp[c].y ^ 0x80808080u;
+            const u32x4 a = {minus1152(pair_lo(x0)), minus1152(pair_hi(x0)),
+                             minus1152(pair_lo(x1)), minus1152(pair_hi(x1))};
+            sc[c] = mfma_16x16x32<DT_F16>(a, q.b[c], f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float t = 0.f;
+#pragma unroll
+            for (int c = 0; c < KC; ++c) t = fmaf(scale(ks, r, c), sc[c][r], t);
+            s[r] = t;          // the kernel applies q.f with the softmax scale
+        }
+    }
+    // O += P V on 16x16x16 bf16 MFMAs.  V is staged as bf16 (code + 128) token pairs:
+    // dword (pair p, column c) holds tokens 2 p and 2 p + 1 of column c, so the B operand
+    // of a lane (column 16 b + c16, tokens 4 q4 .. +3) is two dwords.  The A operand of the
+    // two column blocks of group g is P x (V scale of group g), as hi + lo bf16 parts; the
+    // 128 x sum(P x scale) the offset adds is taken off once per segment (finish).  Every
+    // block of the item is staged before any is read back.
+    template <class Ok>
+    __device__ static void pv(f32x4 (&acc)[NACC], const float (&p)[BPT][4], const Tile& tl, int,
+                              char* my, const int (&)[BPT], const bool (&)[BPT], Ok, Extra& x) {
+        const int lane = lane_id(), c16 = lane % 16, q4 = lane / 16;
+        uint32_t* lw = reinterpret_cast<uint32_t*>(my);
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) {
+#pragma unroll
+            for (int pi = 0; pi < 2; ++pi) {
+                uint32_t o[CPL];
+#pragma unroll
+                for (int w = 0; w < VW; ++w) {
+                    const uint32_t y0 = tl.v[h][2 * pi][w] ^ 0x80808080u;
+                    const uint32_t y1 = tl.v[h][2 * pi + 1][w] ^ 0x80808080u;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // the bf16 of an integer below 256 is the high half of its fp32
+                        const float f0 = (float)((y0 >> (8 * e)) & 0xffu);
+                        const float f1 = (float)((y1 >> (8 * e)) & 0xffu);
+                        o[4 * w + e] = __builtin_amdgcn_perm(__float_as_uint(f1),
+                                                             __float_as_uint(f0), 0x07060302u);
+                    }
+                }
+                uint32_t* dst = lw + h * VBLK + (2 * q4 + pi) * PS + vcol(CPL * c16);
+#pragma unroll
+                for (int i = 0; i < CPL; i += 4)
+                    *reinterpret_cast<u32x4*>(dst + i) = u32x4{o[i], o[i + 1], o[i + 2], o[i + 3]};
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) {
+            Scales vs;
+            read_scales(my + LDSS + h * 2 * D + D, vs);
+            const uint32_t* src = lw + h * VBLK + 2 * q4 * PS + c16;
+#pragma unroll
+            for (int g = 0; g < KC; ++g) {
+                float pg[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pg[r] = p[h][r] * scale(vs, r, g);
+                    x.corr[g] += pg[r];
+                }
+                uint32_t h0, l0, h1, l1;
+                split2<DT_BF16>(pg[0], pg[1], h0, l0);
+                split2<DT_BF16>(pg[2], pg[3], h1, l1);
+                const u32x2 ph = {h0, h1}, pl = {l0, l1};
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) {
+                    const int b = 2 * g + bb;
+                    const u32x2 vb = {src[vcol(16 * b)], src[PS + vcol(16 * b)]};
+                    acc[b] = mfma_16x16x16<DT_BF16>(ph, vb, acc[b]);
+                    acc[b] = mfma_16x16x16<DT_BF16>(pl, vb, acc[b]);
+                }
+            }
+        }
+    }
+    __device__ static void init(Extra& x) {
+#pragma unroll
+        for (int g = 0; g < KC; ++g) x.corr[g] = 0.f;
+    }
+    __device__ static void rescale(Extra& x, float alpha) {
+#pragma unroll
+        for (int g = 0; g < KC; ++g) x.corr[g] *= alpha;
+    }
+    // sum_t w_t (c_t + 128) - 128 sum_t w_t: O rows are heads 4 q4 + r, whose sums sit in
+    // lanes 4 q4 + r once summed over the head's 4 lanes
+    __device__ static void finish(f32x4 (&acc)[NACC], const Extra& x) {
+        const int q4 = lane_id() / 16;
+#pragma unroll
+        for (int g = 0; g < KC; ++g) {
+            float t = x.corr[g] + __shfl_xor(x.corr[g], 16);
+            t += __shfl_xor(t, 32);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float cr = __shfl(t, 4 * q4 + r);
+                acc[2 * g][r] = fmaf(-128.f, cr, acc[2 * g][r]);
+                acc[2 * g + 1][r] = fmaf(-128.f, cr, acc[2 * g + 1][r]);
+            }
+        }
+    }
+    // acc[b] of lane c16 is column 16 b + c16
+    __device__ static void store(const DecodeArgs& a, size_t ob, const f32x4 (&acc)[NACC],
+                                 int r, float inv, int c16) {
+#pragma unroll
+        for (int b = 0; b < NACC; ++b) store_out1(a, ob + 16 * b + c16, acc[b][r] * inv);
+    }
+    __device__ static void store_part(float* dst, const f32x4 (&acc)[NACC], int r, int c16) {
+#pragma unroll
+        for (int b = 0; b < NACC; ++b) dst[16 * b + c16] = acc[b][r];
+    }
+};
+
+template <int DT, int D, int G, bool Q8 = (DT == DT_Q8F16 || DT == DT_Q8BF16)>
+struct MfmaKv;
+template <int DT, int D, int G>
+struct MfmaKv<DT, D, G, false> : MfmaKv16<DT, D, G> {};
+template <int DT, int D, int G>
+struct MfmaKv<DT, D, G, true> : MfmaKvQ8<DT, D, G> {};
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(G == 4 || G == 8, "groups of 4 or 8 query heads");
-    using S = MfmaShape<D>;
-    constexpr int KC = S::KC, VB = S::VB, NLD = S::NLD, RS = S::RS;
+    using Ops = MfmaKv<DT, D, G>;
+    using Q = typename Ops::Q;
+    using Tile = typename Ops::Tile;
+    constexpr int NACC = Ops::NACC, BPT = Ops::BPT;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr float kNegBig = -3.402823466e38f;
     constexpr float kLazy = 8.f;
-    __shared__ __align__(16) char lds[kWavesPerGroup * S::LDSW];
+    __shared__ __align__(16) char lds[Ops::LDS_BYTES > 0 ? Ops::LDS_BYTES : 16];
 
     int32_t* hdr = (int32_t*)(a.ws + a.lay.header);
     const uint32_t* cb = (const uint32_t*)(a.ws + a.lay.cb);
@@ -83,14 +487,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
     if (wave >= W) return;
 
     const int c16 = lane % 16, q4 = lane / 16;
-    char* my = lds + (threadIdx.x >> 6) * S::LDSW;
+    char* my = Ops::LDS_BYTES > 0 ? lds + (threadIdx.x >> 6) * (Ops::LDS_BYTES / kWavesPerGroup)
+                                  : lds;
     const float qscale = a.scale * kLog2e;
-    const size_t tile = (size_t)kBlock * D * 2;
-    const size_t block_stride = (size_t)a.num_kv_heads * tile;
-    // K: lane holds token c16, columns 32 c + 8 q4 .. +8 of each step c
-    const char* kbase = (const char*)a.k_cache + (size_t)c16 * D * 2 + (size_t)q4 * 16;
-    // V: coalesced; load i of lane l reads bytes 1024 i + 16 l of the tile
-    const char* vbase = (const char*)a.v_cache + (size_t)lane * 16;
+    const size_t block_stride = (size_t)a.num_kv_heads * Ops::TILE;
+    const char* kbase = (const char*)a.k_cache + Ops::k_lane(lane);
+    const char* vbase = (const char*)a.v_cache + Ops::v_lane(lane);
 
     const uint32_t x_start = wx0[wave];
     const uint32_t x_end = wx0[wave + 1];
@@ -126,37 +528,43 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
         const int n = sg.j1 - c0;
         return lane < n ? a.block_tables[(size_t)sg.seq * a.max_blocks + c0 + lane] : 0;
     };
-    // B operand of S^T: query head c16 of the group (zero for c16 >= G), columns
-    // 32 c + 8 q4 .. +8
-    auto load_q = [&](const Seg& sg, u32x4 (&qb)[KC]) {
+    auto load_q = [&](const Seg& sg, Q& q) {
         const size_t qrow = ((size_t)sg.u * a.num_q_heads + (size_t)sg.g * G + c16) * D;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-            qb[c] = c16 < G ? ld16((const char*)a.q + (qrow + 32 * c + 8 * q4) * 2) : z;
+        Ops::load_q(a.q, qrow, c16, q4, q);
     };
-    struct Tile { u32x4 k[KC], v[NLD]; };
     auto block_id = [&](int ids, int idx, bool& valid) {
         int b = __builtin_amdgcn_readlane(ids, idx);
         valid = (unsigned)b < (unsigned)a.num_blocks;
         return valid ? b : 0;
     };
-    auto load_tile = [&](const Seg& sg, int b, Tile& t) {
-        const size_t off = (size_t)b * block_stride + (size_t)sg.g * tile;
+    // An item: the next BPT blocks of the stream inside one chunk of ids (fewer at the end
+    // of a chunk; cnt = 0 when nothing is left).  A tile always loads BPT blocks: a slot
+    // past cnt re-reads block idx_pad of the same id register and is never consumed.  The
+    // loads are one straight sequence whatever the case, so that the compiler's wait
+    // counts for the tile in use never include the tile being loaded.
+    struct Item { int cnt; bool ok[BPT]; };
+    auto load_item = [&](int g, int ids, int idx0, int cnt, int idx_pad, Tile& t,
+                         Item& it) __attribute__((always_inline)) {
+        size_t off[BPT];
+        it.cnt = cnt;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.k[c] = ld16_stream(kbase + off + c * 64);
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) t.v[i] = ld16_stream(vbase + off + i * 1024);
+        for (int h = 0; h < BPT; ++h) {
+            bool v;
+            const int b = block_id(ids, h < cnt ? idx0 + h : idx_pad, v);
+            it.ok[h] = v;
+            off[h] = (size_t)b * block_stride + (size_t)g * Ops::TILE;
+        }
+        Ops::load(kbase, vbase, off, t);
     };
 
     if (x_start >= x_end) return;
     Seg cur = describe(x_start);
-    u32x4 qb[KC];
-    load_q(cur, qb);
+    Q q;
+    load_q(cur, q);
     int ids = load_ids(cur, cur.j0);
     Tile A, B;
-    bool okA, okB;
-    load_tile(cur, block_id(ids, 0, okA), A);
+    Item iA, iB;
+    load_item(cur.g, ids, 0, min(BPT, cur.j1 - cur.j0), 0, A, iA);
     bool first_segment = true;
     int bad = 0;
 
@@ -164,7 +572,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
         // the next segment's record, queries and first block ids load while this one runs
         const bool more = cur.end < x_end;
         Seg nxt = cur;
-        u32x4 qn[KC];
+        Q qn;
         int nids = 0;
         if (more) {
             nxt = describe(cur.end);
@@ -176,47 +584,49 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
         uint32_t next = cur.pe;
         if (opens_cut && wave + 1 + lane < W) next = wx0[wave + 1 + lane];
 
-        f32x4 acc[VB];     // O: lane holds column 16 b + c16 of heads 4 q4 .. 4 q4 + 3
+        f32x4 acc[NACC];   // O: lane holds heads 4 q4 .. 4 q4 + 3 of its columns
 #pragma unroll
-        for (int b = 0; b < VB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < NACC; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m = kNegBig, lsum = 0.f;   // head c16, this lane's tokens
+        typename Ops::Extra ex;
+        Ops::init(ex);
         const int len = cur.len, lo_tok = cur.lo_tok;
+        const float qs = qscale * q.f;
 
-        auto consume = [&](Tile& tl, int j, bool valid) {
-            const int t0 = j * kBlock;
-            const bool edge = !valid || t0 < lo_tok || t0 + kBlock > len;   // uniform
-            // stage V (rows of masked tokens zeroed) in this wavefront's LDS rows
+        // The blocks of an item are scored first, share one softmax update and then go
+        // through P V together, so their independent work can interleave.
+        auto consume_item = [&](const Tile& tl, const Item& it, int j0) __attribute__((always_inline)) {
+            float sc[BPT][4];
+            bool valid[BPT], edge[BPT];
+            int t0[BPT];
+            auto ok = [&](int h, int t) { return valid[h] && t >= lo_tok && t < len; };
 #pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const int byte = i * 1024 + lane * 16;
-                const int tv = byte / (D * 2), col = byte % (D * 2);
-                u32x4 v = tl.v[i];
-                if (edge) {
-                    const int t = t0 + tv;
-                    const bool ok = valid && t >= lo_tok && t < len;
-                    const u32x4 z = {0u, 0u, 0u, 0u};
-                    v = ok ? v : z;
-                }
-                char* dst = my + tv * RS + col;
-                *reinterpret_cast<u32x2*>(dst) = u32x2{v.x, v.y};
-                *reinterpret_cast<u32x2*>(dst + 8) = u32x2{v.z, v.w};
+            for (int h = 0; h < BPT; ++h) {
+                // a slot past cnt holds a re-read block: scored, then masked entirely
+                t0[h] = (j0 + h) * kBlock;
+                valid[h] = h < it.cnt && it.ok[h];
+                edge[h] = !valid[h] || t0[h] < lo_tok || t0[h] + kBlock > len;   // uniform
+                bad |= h < it.cnt && !it.ok[h];
+                Ops::scores(tl, h, q, my, t0[h], edge[h], ok, sc[h]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[h][r] = c16 < G ? sc[h][r] * qs : -INFINITY;
             }
-            // S^T: lane holds head c16, tokens 4 q4 .. +3
-            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+            bool any_edge = false;
 #pragma unroll
-            for (int c = 0; c < KC; ++c) sacc = mfma_16x16x32<DT>(tl.k[c], qb[c], sacc);
-            float sc[4];
+            for (int h = 0; h < BPT; ++h) any_edge |= edge[h];
+            if (any_edge) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sc[r] = c16 < G ? sacc[r] * qscale : -INFINITY;
-                if (edge) {
-                    const int t = t0 + 4 * q4 + r;
-                    const bool ok = valid && t >= lo_tok && t < len;
-                    sc[r] = ok ? sc[r] : -INFINITY;
-                }
+                for (int h = 0; h < BPT; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sc[h][r] = ok(h, t0[h] + 4 * q4 + r) ? sc[h][r] : -INFINITY;
             }
             // lazy rescaling, as in decode_kernel: m moves only by more than kLazy
-            const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            float mx = sc[0][0];
+#pragma unroll
+            for (int h = 0; h < BPT; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[h][r]);
             if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {
                 float M = fmaxf(mx, __shfl_xor(mx, 16));
                 M = fmaxf(M, __shfl_xor(M, 32));             // max over the head's 4 lanes
@@ -224,77 +634,69 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
                 const float alpha = __builtin_amdgcn_exp2f(m - mn);
                 m = mn;
                 lsum *= alpha;
+                Ops::rescale(ex, alpha);
                 // O rows are heads 4 q4 + r: their factor sits in lane 4 q4 + r
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float ar = __shfl(alpha, 4 * q4 + r);
 #pragma unroll
-                    for (int b = 0; b < VB; ++b) acc[b][r] *= ar;
+                    for (int b = 0; b < NACC; ++b) acc[b][r] *= ar;
                 }
             }
-            float p[4];
+            float p[BPT][4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(sc[r] - m);
-                lsum += p[r];
-            }
-            uint32_t h0, l0, h1, l1;
-            split2<DT>(p[0], p[1], h0, l0);
-            split2<DT>(p[2], p[3], h1, l1);
-            const u32x2 ph = {h0, h1}, pl = {l0, l1};
-            // O += P V: B operand = column 16 b + c16 of tokens 4 q4 .. +3, from LDS
-            const uint16_t* vr = reinterpret_cast<const uint16_t*>(my + 4 * q4 * RS) + c16;
+            for (int h = 0; h < BPT; ++h)
 #pragma unroll
-            for (int b = 0; b < VB; ++b) {
-                const uint32_t e0 = vr[16 * b], e1 = vr[RS / 2 + 16 * b];
-                const uint32_t e2 = vr[RS + 16 * b], e3 = vr[3 * RS / 2 + 16 * b];
-                const u32x2 vb = {e0 | (e1 << 16), e2 | (e3 << 16)};
-                acc[b] = mfma_16x16x16<DT>(ph, vb, acc[b]);
-                acc[b] = mfma_16x16x16<DT>(pl, vb, acc[b]);
-            }
+                for (int r = 0; r < 4; ++r) {
+                    p[h][r] = __builtin_amdgcn_exp2f(sc[h][r] - m);
+                    lsum += p[h][r];
+                }
+            Ops::pv(acc, p, tl, it.cnt, my, t0, edge, ok, ex);
         };
 
-        // blocks of the segment, in chunks of 64 ids; A holds the segment's first block.
-        // The load after each block's is the next block of the stream: in this chunk, the
-        // next chunk, the next segment, or (at the very end) the last block again.
+        // blocks of the segment, in chunks of 64 ids, BPT at a time; A holds the segment's
+        // first item.  The load after each item's is the next item of the stream: in this
+        // chunk, the next chunk or the next segment (nothing at the very end).
+        // plain copies of what the loads need (a select between fields of the two records
+        // would keep both records in memory)
+        const int g_cur = cur.g, g_nxt = nxt.g, j1_cur = cur.j1, nb_nxt = nxt.j1 - nxt.j0;
         int cids = ids;
         for (int c0 = cur.j0;; c0 += kWave) {
             const int n = (cur.j1 - c0) < kWave ? (cur.j1 - c0) : kWave;
             const bool last_chunk = c0 + kWave >= cur.j1;
             const int nc_ids = last_chunk ? 0 : load_ids(cur, c0 + kWave);
-            auto next_block = [&](int k, bool& ok, const Seg*& sg) {
-                sg = &cur;
-                if (k < n) return block_id(cids, k, ok);
-                if (!last_chunk) return block_id(nc_ids, 0, ok);
-                if (more) {
-                    sg = &nxt;
-                    return block_id(nids, 0, ok);
+            const int items = (n + BPT - 1) / BPT;
+            // item k of this chunk, else the first item of the next chunk or of the next
+            // segment; at the very end nothing (the load repeats this chunk's last block).
+            // Every case issues the same loads, so the wait counts stay exact.
+            auto load_next = [&](int k, Tile& t, Item& it) __attribute__((always_inline)) {
+                if (k < items) {
+                    load_item(g_cur, cids, BPT * k, min(BPT, n - BPT * k), BPT * k, t, it);
+                } else if (!last_chunk) {
+                    load_item(g_cur, nc_ids, 0, min(BPT, j1_cur - c0 - kWave), 0, t, it);
+                } else if (more) {
+                    load_item(g_nxt, nids, 0, min(BPT, nb_nxt), 0, t, it);
+                } else {
+                    load_item(g_cur, cids, 0, 0, n - 1, t, it);
                 }
-                return block_id(cids, n - 1, ok);
             };
-            const Seg* sgB;
-            const Seg* sgA;
-            int jj = 0;
-            for (;; jj += 2) {
-                const int bB = next_block(jj + 1, okB, sgB);
-                load_tile(*sgB, bB, B);
-                bad |= !okA;
-                consume(A, c0 + jj, okA);
-                if (jj + 1 >= n) {
+            for (int k = 0;; k += 2) {
+                load_next(k + 1, B, iB);
+                consume_item(A, iA, c0 + BPT * k);
+                if (k + 1 >= items) {
                     A = B;
-                    okA = okB;
+                    iA = iB;
                     break;
                 }
-                const int bA = next_block(jj + 2, okA, sgA);
-                load_tile(*sgA, bA, A);
-                bad |= !okB;
-                consume(B, c0 + jj + 1, okB);
-                if (jj + 2 >= n) break;
+                load_next(k + 2, A, iA);
+                consume_item(B, iB, c0 + BPT * (k + 1));
+                if (k + 2 >= items) break;
             }
             if (last_chunk) break;
             cids = nc_ids;
         }
 
+        Ops::finish(acc, ex);
         // the head's sum over its 4 lanes; O-layout lanes fetch (m, l) of their heads
         float lt = lsum + __shfl_xor(lsum, 16);
         lt += __shfl_xor(lt, 32);
@@ -311,13 +713,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
             if (h < G) {
                 if (complete) {
                     const float inv = lh > 0.f ? 1.f / lh : 0.f;
-                    const size_t ob = ((size_t)cur.u * a.num_q_heads + (size_t)cur.g * G + h) * D + c16;
-#pragma unroll
-                    for (int b = 0; b < VB; ++b) store_out1(a, ob + 16 * b, acc[b][r] * inv);
+                    const size_t ob = ((size_t)cur.u * a.num_q_heads + (size_t)cur.g * G + h) * D;
+                    Ops::store(a, ob, acc, r, inv, c16);
                 } else {
-                    float* dst = pacc + (((size_t)wave * 2 + slot) * G + h) * D + c16;
-#pragma unroll
-                    for (int b = 0; b < VB; ++b) dst[16 * b] = acc[b][r];
+                    Ops::store_part(pacc + (((size_t)wave * 2 + slot) * G + h) * D, acc, r, c16);
                 }
             }
         }
@@ -327,8 +726,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_mfma_kernel(Dec
         }
         if (!more) break;
         cur = nxt;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) qb[c] = qn[c];
+        q = qn;
         ids = nids;
         first_segment = false;
     }

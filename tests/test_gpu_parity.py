@@ -90,6 +90,11 @@ SMALL = [
     ("tiny", dict(dtype="f16", hq=16, hkv=4, d=64)),
     ("tiny", dict(dtype="bf16", hq=16, hkv=2, d=128)),
     ("gqa", dict(batch=9, median=400, lo=16, hi=5000, dtype="f16")),
+    ("tiny", dict(dtype="q8_f16", hq=16, hkv=4, d=64)),
+    ("tiny", dict(dtype="q8_bf16", hq=16, hkv=2, d=128)),
+    ("tiny", dict(dtype="q8_f16", hq=16, hkv=2, d=256)),
+    ("gqa", dict(batch=9, median=400, lo=16, hi=5000, dtype="q8_bf16")),
+    ("swa", dict(batch=5, lo=1500, hi=6000, window=1000, hq=32, hkv=4, d=128, dtype="q8_f16")),
     # 8- and 32-token blocks (16-bit caches)
     ("opt13b", dict(batch=6, lo=64, hi=700, block_size=8)),
     ("opt13b", dict(batch=6, lo=64, hi=700, block_size=32)),
@@ -193,6 +198,34 @@ def test_needle_bit_exact(torch, pa, orc, name, kw, runs):
                 if not np.array_equal(out[s, h], v[h // grp]):
                     raise AssertionError(f"needle seq {s} tau {tau} head {h}: "
                                          f"{out[s, h][:4]} vs {v[h // grp][:4]}")
+    assert pa.device_error_bits(dw.workspace) == 0
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", dict(dtype="bf16", hq=16, hkv=4, d=64)),
+    ("tiny", dict(dtype="q8_f16", hq=16, hkv=4, d=128)),
+    ("tiny", dict(dtype="q8_bf16", hq=16, hkv=2, d=64)),
+    ("gqa", dict(batch=10, median=300, lo=16, hi=3000, dtype="q8_bf16")),
+    ("gqa", dict(batch=10, median=300, lo=16, hi=3000, dtype="q8_f16", hq=32, hkv=4, d=256)),
+])
+def test_matrix_core_and_lane_kernels_agree(torch, pa, orc, monkeypatch, name, kw):
+    """Groups of 4 and 8 query heads run on the matrix-core kernel by default; the per-lane
+    kernel (PA_DECODE_MFMA=0) computes the same rows.  Both meet the oracle and differ from
+    each other only by rounding."""
+    say("mfma-vs-lane", name, kw)
+    w = workloads.make(name, **kw)
+    dw = run(w, torch)
+    ref = orc.Reference(w).attention()
+    mfma = dw.decode().cpu().numpy()
+    check_close(mfma, ref, f"matrix-core {name} {kw}")
+    monkeypatch.setenv("PA_DECODE_MFMA", "0")
+    # the per-lane kernel keeps more wavefronts resident: its workspace is sized for it
+    dw.workspace = pa.alloc_workspace(dw.k_cache, w.num_seqs, w.total_q_rows, w.num_q_heads,
+                                      dw.max_seq_len, dw.q.dtype)
+    lane = dw.decode().cpu().numpy()
+    monkeypatch.delenv("PA_DECODE_MFMA")
+    check_close(lane, ref, f"per-lane {name} {kw}")
+    assert np.abs(mfma - lane).max() <= ATOL
     assert pa.device_error_bits(dw.workspace) == 0
 
 

@@ -320,7 +320,8 @@ def make(name: str, seed: int | None = None, **over) -> Workload:
         sig = over.get("sigma", 1.0)
         x = rng.lognormal(math.log(med), sig, size=B)
         lens = np.clip(np.rint(x), over.get("lo", 16), over.get("hi", 32768)).astype(np.int32)
-        return _plain("gqa", seed, over.get("dtype", "bf16"), 32, 8, 128, lens, 36, rng,
+        return _plain("gqa", seed, over.get("dtype", "bf16"), over.get("hq", 32),
+                      over.get("hkv", 8), over.get("d", 128), lens, 36, rng,
                       bs=over.get("block_size", 16))
 
     if name == "prefix_mixed":
@@ -382,10 +383,11 @@ def make(name: str, seed: int | None = None, **over) -> Workload:
             script.append(Append(s, n, nv, off))
             off += nv
         dt = over.get("dtype", "f16")
-        k, v = _values(seed, off, 4, 256, dt)
-        q = _queries(seed, B, 8, 256, dt)
-        return Workload("swa", seed, dt, 8, 4, 256, bs, nb, lens, np.ones(B, np.int32), W,
-                        np.float32(1.0 / math.sqrt(256)), 29, free_order, script, k, v, q)
+        hq, hkv, d = over.get("hq", 8), over.get("hkv", 4), over.get("d", 256)
+        k, v = _values(seed, off, hkv, d, dt)
+        q = _queries(seed, B, hq, d, dt)
+        return Workload("swa", seed, dt, hq, hkv, d, bs, nb, lens, np.ones(B, np.int32), W,
+                        np.float32(1.0 / math.sqrt(d)), 29, free_order, script, k, v, q)
 
     if name == "parallel_sampling":
         # OPT-13B shape; every prompt is prefilled, then forked into `samples` samples that
