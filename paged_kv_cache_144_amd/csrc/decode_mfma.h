@@ -20,18 +20,21 @@
 //   * P is carried as hi + lo 16-bit parts (two MFMAs), as in the chunk-row kernel.
 //
 // 8-bit caches (MfmaKvQ8; the format of "KV cache by model", sotaaz.com):
-//   * K codes become exact fp16 integers (the flipped code byte under the exponent of 1024
-//     gives 1152 + code; a packed subtract of 1152 leaves the code); the query is held in
-//     fp16 after a power-of-two scaling per head (exact for fp16 and bf16 values), whose
-//     inverse joins the softmax scale;
+//   * a tile of 8-bit codes is half the bytes of a 16-bit one, so a tile holds two blocks
+//     to keep as many bytes in flight per wavefront;
+//   * K rows are loaded whole (each 16-byte piece of a lane lies in one row) and reach the
+//     operand layout through LDS; the codes become exact fp16 integers (the flipped code
+//     byte under the exponent of 1024 gives 1152 + code; a packed subtract of 1152 leaves
+//     the code); the query is held in fp16 after a power-of-two scaling per head (exact for
+//     fp16 and bf16 values), whose inverse joins the softmax scale;
 //   * each 16x16x32 step of S^T covers exactly one 32-column scale group, so every step
 //     keeps its own accumulator and the per-(token, group) scales are applied to the four
 //     partial scores of each lane before they are summed;
-//   * O = P V runs on v_mfma_f32_16x16x4_f32: its A operand for step s is the probability
-//     each lane already holds for token 4 (l / 16) + s, and its B operand is code x scale
-//     in fp32 (exact: 8 x 11 significant bits) of that token and one of the lane's D / 16
-//     consecutive columns.  The lane loads those columns straight from the tile (one
-//     scale group per lane), so nothing is staged in LDS and P needs no hi/lo split.
+//   * O = P V runs on 16x16x16 bf16 MFMAs: V codes are exact in bf16 and are staged in LDS
+//     as token pairs, so a lane's B operand (4 tokens of one column) is two dwords; the 16
+//     columns of an MFMA lie in one scale group, so the V scales go into the A operand:
+//     P x scale of the group, as hi + lo bf16 parts (16 significant bits, as for bf16
+//     caches); the scale rows pass through LDS too, those of unseen tokens zeroed.
 //
 // Masked tokens are removed by selection in both: their scores become -inf and their V
 // values zero (16-bit: rows zeroed before staging; 8-bit: scale zeroed), so NaN in free or
@@ -203,8 +206,7 @@ struct MfmaKvQ8 {
     // token 4 q4 + s; sc: SB bytes of the K scale row (lanes 0-31) or the V scale row
     // (lanes 32-63).  K, the scale rows and V are staged through LDS when consumed.
     struct Tile { u32x4 k[BPT][KN]; uint32_t v[BPT][4][VW]; uint32_t sc[BPT][(SB + 3) / 4]; };
-    // sum over this lane's tokens of P x V scale, per group (head c16)
-    struct Extra { float corr[KC]; };
+    struct Extra {};
 
     __device__ static size_t k_lane(int lane) { return (size_t)lane * 16; }
     __device__ static size_t v_lane(int lane) {
@@ -353,15 +355,14 @@ struct MfmaKvQ8 {
             s[r] = t;          // the kernel applies q.f with the softmax scale
         }
     }
-    // O += P V on 16x16x16 bf16 MFMAs.  V is staged as bf16 (code + 128) token pairs:
-    // dword (pair p, column c) holds tokens 2 p and 2 p + 1 of column c, so the B operand
-    // of a lane (column 16 b + c16, tokens 4 q4 .. +3) is two dwords.  The A operand of the
-    // two column blocks of group g is P x (V scale of group g), as hi + lo bf16 parts; the
-    // 128 x sum(P x scale) the offset adds is taken off once per segment (finish).  Every
+    // O += P V on 16x16x16 bf16 MFMAs.  V is staged as bf16 codes in token pairs: dword
+    // (pair p, column c) holds tokens 2 p and 2 p + 1 of column c, so the B operand of a
+    // lane (column 16 b + c16, tokens 4 q4 .. +3) is two dwords.  The A operand of the two
+    // column blocks of group g is P x (V scale of group g), as hi + lo bf16 parts.  Every
     // block of the item is staged before any is read back.
     template <class Ok>
     __device__ static void pv(f32x4 (&acc)[NACC], const float (&p)[BPT][4], const Tile& tl, int,
-                              char* my, const int (&)[BPT], const bool (&)[BPT], Ok, Extra& x) {
+                              char* my, const int (&)[BPT], const bool (&)[BPT], Ok, Extra&) {
         const int lane = lane_id(), c16 = lane % 16, q4 = lane / 16;
         uint32_t* lw = reinterpret_cast<uint32_t*>(my);
 #pragma unroll
@@ -371,13 +372,13 @@ struct MfmaKvQ8 {
                 uint32_t o[CPL];
 #pragma unroll
                 for (int w = 0; w < VW; ++w) {
-                    const uint32_t y0 = tl.v[h][2 * pi][w] ^ 0x80808080u;
-                    const uint32_t y1 = tl.v[h][2 * pi + 1][w] ^ 0x80808080u;
+                    const uint32_t y0 = tl.v[h][2 * pi][w], y1 = tl.v[h][2 * pi + 1][w];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        // the bf16 of an integer below 256 is the high half of its fp32
-                        const float f0 = (float)((y0 >> (8 * e)) & 0xffu);
-                        const float f1 = (float)((y1 >> (8 * e)) & 0xffu);
+                        // a code is an integer of at most 7 bits: its bf16 is exact, the
+                        // high half of its fp32
+                        const float f0 = (float)(int8_t)((y0 >> (8 * e)) & 0xffu);
+                        const float f1 = (float)(int8_t)((y1 >> (8 * e)) & 0xffu);
                         o[4 * w + e] = __builtin_amdgcn_perm(__float_as_uint(f1),
                                                              __float_as_uint(f0), 0x07060302u);
                     }
@@ -399,7 +400,6 @@ struct MfmaKvQ8 {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     pg[r] = p[h][r] * scale(vs, r, g);
-                    x.corr[g] += pg[r];
                 }
                 uint32_t h0, l0, h1, l1;
                 split2<DT_BF16>(pg[0], pg[1], h0, l0);
@@ -415,30 +415,9 @@ struct MfmaKvQ8 {
             }
         }
     }
-    __device__ static void init(Extra& x) {
-#pragma unroll
-        for (int g = 0; g < KC; ++g) x.corr[g] = 0.f;
-    }
-    __device__ static void rescale(Extra& x, float alpha) {
-#pragma unroll
-        for (int g = 0; g < KC; ++g) x.corr[g] *= alpha;
-    }
-    // sum_t w_t (c_t + 128) - 128 sum_t w_t: O rows are heads 4 q4 + r, whose sums sit in
-    // lanes 4 q4 + r once summed over the head's 4 lanes
-    __device__ static void finish(f32x4 (&acc)[NACC], const Extra& x) {
-        const int q4 = lane_id() / 16;
-#pragma unroll
-        for (int g = 0; g < KC; ++g) {
-            float t = x.corr[g] + __shfl_xor(x.corr[g], 16);
-            t += __shfl_xor(t, 32);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float cr = __shfl(t, 4 * q4 + r);
-                acc[2 * g][r] = fmaf(-128.f, cr, acc[2 * g][r]);
-                acc[2 * g + 1][r] = fmaf(-128.f, cr, acc[2 * g + 1][r]);
-            }
-        }
-    }
+    __device__ static void init(Extra&) {}
+    __device__ static void rescale(Extra&, float) {}
+    __device__ static void finish(f32x4 (&)[NACC], const Extra&) {}
     // acc[b] of lane c16 is column 16 b + c16
     __device__ static void store(const DecodeArgs& a, size_t ob, const f32x4 (&acc)[NACC],
                                  int r, float inv, int c16) {
