@@ -101,6 +101,7 @@ struct MfmaKv16 {
             r.b[c] = c16 < G ? ld16((const char*)q + (qrow + 32 * c + 8 * q4) * 2) : z;
         r.f = 1.f;
     }
+    __device__ static void prep_q(Q&) {}
     __device__ static void load(const char* kb, const char* vb, const size_t (&offs)[BPT],
                                 Tile& t) {
         const size_t off = offs[0];
@@ -215,18 +216,21 @@ struct MfmaKvQ8 {
 
     // B operand of S^T in fp16: query head c16 (zero for c16 >= G), columns 32 c + 8 q4 ..
     // +8, times 2^(15 - e) where 2^e bounds the head's largest |q|: every value then lies
-    // below 2^15 and converts exactly.  f = 2^(e - 15) undoes the scaling.
+    // below 2^15 and converts exactly.  f = 2^(e - 15) undoes the scaling.  load_q only
+    // issues the loads (the next segment's queries load early); prep_q converts them once
+    // the segment is the current one.
     __device__ static void load_q(const void* q, size_t qrow, int c16, int q4, Q& r) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            r.b[c] = c16 < G ? ld16((const char*)q + (qrow + 32 * c + 8 * q4) * 2) : z;
+    }
+    __device__ static void prep_q(Q& r) {
         float v[KC][8];
         float mx = 0.f;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-            if (c16 < G) {
-                widen16<ADT>(ld16((const char*)q + (qrow + 32 * c + 8 * q4) * 2), v[c]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[c][e] = 0.f;
-            }
+            widen16<ADT>(r.b[c], v[c]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[c][e]));
         }
@@ -558,6 +562,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
             load_q(nxt, qn);
             nids = load_ids(nxt, nxt.j0);
         }
+        Ops::prep_q(q);
         // a pair that starts here and continues past the share: the later shares' starts
         const bool opens_cut = cur.starts && cur.end < cur.pe;
         uint32_t next = cur.pe;
