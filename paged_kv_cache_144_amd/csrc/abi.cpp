@@ -74,6 +74,7 @@ struct Plan {
     int chunk_rows = 0;   // query rows per chunk tile; 0 = chunk rows run as decode rows
     int max_tiles = 0;
     int pair_cost = pa::kPairCost;
+    int min_blocks = pa::kMinBlocksPerWave;
     pa::Layout lay{};
 };
 
@@ -97,6 +98,11 @@ pa_status plan_shape(const pa_cache_desc* desc, int32_t num_seqs, int32_t total_
     if (const char* e = std::getenv("PA_PAIR_COST")) {
         const int v = std::atoi(e);
         if (v >= 0 && v <= pa::kMaxPairCost) p.pair_cost = v;
+    }
+    // tuning knob: the smallest share of KV blocks a decode wavefront is given
+    if (const char* e = std::getenv("PA_MIN_BLOCKS")) {
+        const int v = std::atoi(e);
+        if (v >= pa::kMinBlocksFloor && v <= 256) p.min_blocks = v;
     }
     // chunk rows (sequences with several query rows) take the MFMA kernel when one exists
     // for this shape; PA_CHUNK_KERNEL=0 sends them through the decode kernel instead
@@ -299,6 +305,7 @@ pa_status build_args(void* out, pa_dtype out_dtype, const void* q, const void* k
     a.chunk_rows = p.chunk_rows;
     a.max_tiles = p.max_tiles;
     a.pair_cost = p.pair_cost;
+    a.min_blocks = p.min_blocks;
     a.ws = (char*)workspace;
     a.lay = p.lay;
     return PA_OK;

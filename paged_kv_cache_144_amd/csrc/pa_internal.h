@@ -14,7 +14,8 @@ constexpr int kBlock = 16;          // default tokens per KV block (8 and 32 als
                                     // decode kernels for 16-bit caches)
 constexpr int kWave = 64;           // CDNA wavefront width
 constexpr int kWavesPerGroup = 4;   // decode workgroup = 4 independent wavefront workers
-constexpr int kMinBlocksPerWave = 16;  // smallest share of KV blocks worth a wavefront
+constexpr int kMinBlocksPerWave = 16;  // default smallest share of KV blocks per wavefront
+constexpr int kMinBlocksFloor = 4;     // the plan needs shares of at least 4 blocks
 constexpr int kPairCost = 14;       // default fixed cost per pair in quarter blocks: the
                                     // dependent loads that start a segment
 // Consecutive share starts are at least 31 quarter blocks apart (4 T / ceil(T / 16) - 1
@@ -95,6 +96,7 @@ struct DecodeArgs {
     int32_t chunk_rows;               // query rows per chunk tile (0: chunk rows decode)
     int32_t max_tiles;                // chunk tiles the work list holds
     int32_t pair_cost;                // fixed cost of a (row, KV head) pair, quarter blocks
+    int32_t min_blocks;               // smallest share of blocks a wavefront is given
     char* ws;
     Layout lay;
 };

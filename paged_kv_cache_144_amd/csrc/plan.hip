@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     int2* tiles = (int2*)(a.ws + a.lay.tiles);
     int4* tasks = (int4*)(a.ws + a.lay.tasks);
 
-    __shared__ uint32_t s_blk[kPlanThreads], s_til[kPlanThreads], s_wt[kPlanThreads];
+    __shared__ uint32_t s_blk[kPlanThreads], s_til[kPlanThreads], s_pr[kPlanThreads];
     __shared__ int s_err, s_bad, s_empty;
     const int tid = threadIdx.x;
     if (tid == 0) { s_err = 0; s_bad = 0; s_empty = 0; }
@@ -70,10 +70,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     const int per = (B + kPlanThreads - 1) / kPlanThreads;
     const int s0 = min(B, tid * per), s1 = min(B, s0 + per);
     const int QT = a.chunk_rows;
-    const uint32_t C = (uint32_t)a.pair_cost, H = (uint32_t)a.num_kv_heads;
+    const uint32_t H = (uint32_t)a.num_kv_heads;
 
-    // pass 1: validate; count decode blocks (and their weight) and chunk tiles
-    uint32_t my_blk = 0, my_til = 0, my_wt = 0;
+    // pass 1: validate; count decode blocks, (row, KV head) pairs with blocks, chunk tiles
+    uint32_t my_blk = 0, my_til = 0, my_pr = 0;
     int err = 0, bad = 0;
     for (int s = s0; s < s1; ++s) {
         int r0 = s, r1 = s + 1;
@@ -95,17 +95,36 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
             int32_t b_lo, nb;
             unit_range(L - n + r + 1, a.window, a.block_size, b_lo, nb);
             my_blk += (uint32_t)nb * H;                          // one pair per KV head
-            if (nb > 0) my_wt += (4u * (uint32_t)nb + C) * H;
+            if (nb > 0) my_pr += H;
         }
     }
     if (bad) atomicOr(&s_bad, 1);
     if (err) atomicOr(&s_err, err);
     const uint32_t blk_incl = block_scan(s_blk, my_blk);
     const uint32_t til_incl = block_scan(s_til, my_til);
-    const uint32_t wt_incl = block_scan(s_wt, my_wt);
-    const uint32_t TW = s_wt[kPlanThreads - 1];
+    const uint32_t pr_incl = block_scan(s_pr, my_pr);
     const uint32_t T = s_blk[kPlanThreads - 1];
     const uint32_t NT = s_til[kPlanThreads - 1];
+    const uint32_t NP = s_pr[kPlanThreads - 1];
+
+    // W wavefronts, at least min_blocks blocks each (when there are that many), at most
+    // max_waves.  W <= T / min_blocks + 1 makes T / W >= min_blocks / 2 for T >= min_blocks,
+    // so consecutive share starts in the weighted space lie at least 4 T / W - 1 quarter
+    // blocks apart; a pair cost C with C + 4 below that keeps every share non-empty (a
+    // share start at offset o of a pair maps to the pair's first block while o <= C).
+    int W = 0;
+    uint32_t C = 0;
+    if (T > 0) {
+        const uint32_t mb = (uint32_t)a.min_blocks;
+        W = (int)((T + mb - 1) / mb);
+        W = W < 1 ? 1 : (W > a.max_waves ? a.max_waves : W);
+        const uint32_t room = (uint32_t)(4ull * T / (uint32_t)W);
+        C = (uint32_t)a.pair_cost;
+        if (W > 1) C = room >= C + 5 ? C : (room > 5 ? room - 5 : 0);
+    }
+    const uint32_t TW = 4u * T + C * NP;
+    const uint32_t wt_incl = 4u * blk_incl + C * pr_incl;
+    const uint32_t my_wt = 4u * my_blk + C * my_pr;
     if (s_bad || NT > (uint32_t)a.max_tiles) {
         // row ranges cannot be trusted (or would overflow the tile list): no unit, no write
         if (tid == 0) {
@@ -165,11 +184,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
         }
     }
 
-    int W = 0;
-    if (T > 0) {
-        W = (int)((T + kMinBlocksPerWave - 1) / kMinBlocksPerWave);
-        W = W < 1 ? 1 : (W > a.max_waves ? a.max_waves : W);
-    }
     __syncthreads();
 
     // every task slot the merge kernel may look at starts empty

@@ -244,6 +244,14 @@ def test_wave_count_invariance_and_determinism(torch, pa, orc, monkeypatch):
         check_close(out, ref, f"waves={waves}")
         assert np.abs(out - base).max() < 1e-5
     monkeypatch.delenv("PA_DECODE_WAVES")
+    # smaller shares (the plan then lowers the pair cost so that no share is empty)
+    for mb in (4, 5, 9):
+        monkeypatch.setenv("PA_MIN_BLOCKS", str(mb))
+        say("min blocks", mb)
+        out = dw.decode().cpu().numpy()
+        check_close(out, ref, f"min_blocks={mb}")
+        assert np.abs(out - base).max() < 1e-5
+    monkeypatch.delenv("PA_MIN_BLOCKS")
 
 
 def test_out_dtypes(torch, pa):
