@@ -70,7 +70,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
     constexpr float kNegBig = -3.402823466e38f;
     __shared__ __attribute__((aligned(16))) char lds_k[2][S::KREG];
     __shared__ __attribute__((aligned(16))) char lds_v[2][S::VREG];
-    __shared__ int s_ids[4][2];   // block ids of the two blocks of a step, read ahead
 
     const int32_t* hdr = (const int32_t*)(a.ws + a.lay.header);
     const int2* tiles = (const int2*)(a.ws + a.lay.tiles);
@@ -137,65 +136,77 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
     // staging.  K piece c -> token c / (D/8), 16-byte column c % (D/8).  V piece c -> token
     // pair c / (D/8), column group c % (D/8): tokens 2p and 2p+1, 8 columns each, written
     // interleaved as 8 dwords (token 2p in the low half).
-    // two register sets: the loads of the next two steps are in flight during a step
+    // two register sets: the loads of the next two steps are in flight during a step.
+    // Every lane issues the same loads in every case (a position outside the row range or
+    // in a block with an invalid id reads the cache's first bytes instead, and its mask bit
+    // zeroes it when staged), so that the compiler's wait counts for one register set
+    // never include the other set's loads.
     u32x4 sk[2][S::KPT], sv[2][S::VPT][2];
+    uint32_t kmask[2], vmask[2];
     int bad = 0;
-    // the step's two block ids, read from the table two steps ahead into LDS
-    auto fetch_ids = [&](int t0, int& i0, int& i1) {
-        i0 = (t0 < L && t0 + kBlock > lo_first) ? bt[t0 / kBlock] : -1;
-        i1 = (t0 + kBlock < L && t0 + 2 * kBlock > lo_first) ? bt[t0 / kBlock + 1] : -1;
+    // Block ids are uniform over the workgroup: scalar loads, counted apart from the vector
+    // loads.  The table row is read in range only (indices clamped, then selected).
+    typedef const __attribute__((address_space(4))) int32_t* ConstIds;
+    const ConstIds btc = (ConstIds)bt;
+    const int last_b = (L + kBlock - 1) / kBlock - 1;
+    auto step_ids = [&](int t0, int& i0, int& i1) {
+        const int b0 = t0 / kBlock;
+        const int r0 = btc[b0 < last_b ? b0 : (last_b > 0 ? last_b : 0)];
+        const int r1 = btc[b0 + 1 < last_b ? b0 + 1 : (last_b > 0 ? last_b : 0)];
+        i0 = (t0 < L && t0 + kBlock > lo_first) ? r0 : -1;
+        i1 = (t0 + kBlock < L && t0 + 2 * kBlock > lo_first) ? r1 : -1;
     };
-    const int* ids = nullptr;
-    auto kv_off = [&](int t, int t0, bool& ok) -> size_t {
-        ok = false;
-        if (t >= L || t < lo_first) return 0;
-        const int b = ids[(t - t0) / kBlock];
-        if ((unsigned)b >= (unsigned)a.num_blocks) {
-            bad = 1;
-            return 0;
+    auto kv_off = [&](int t, int t0, int i0, int i1, bool& ok) -> size_t {
+        const int b = (t - t0) < kBlock ? i0 : i1;
+        const bool in = t < L && t >= lo_first;
+        const bool valid = (unsigned)b < (unsigned)a.num_blocks;
+        bad |= in && b >= 0 && !valid;
+        ok = in && valid;
+        return ok ? (size_t)b * block_stride + (size_t)g * tile_bytes + (size_t)(t % kBlock) * D * 2
+                  : 0;
+    };
+    auto stage_load = [&](int t0, u32x4* sk, u32x4 (*sv)[2], uint32_t& km, uint32_t& vm) {
+        int i0, i1;
+        step_ids(t0, i0, i1);
+        km = 0;
+        vm = 0;
+#pragma unroll
+        for (int i = 0; i < S::KPT; ++i) {
+            const int c = (tid + i * S::THREADS) % S::KPIECES;
+            bool ok;
+            const size_t off = kv_off(t0 + c / (D / 8), t0, i0, i1, ok);
+            sk[i] = ld16_stream((const char*)a.k_cache + off + (ok ? (c % (D / 8)) * 16 : 0));
+            km |= (uint32_t)ok << i;
         }
-        ok = true;
-        return (size_t)b * block_stride + (size_t)g * tile_bytes + (size_t)(t % kBlock) * D * 2;
+#pragma unroll
+        for (int i = 0; i < S::VPT; ++i) {
+            const int c = (tid + i * S::THREADS) % S::VPIECES;
+            const int t = t0 + 2 * (c / (D / 8)), col = (c % (D / 8)) * 16;
+            bool ok0, ok1;
+            const size_t o0 = kv_off(t, t0, i0, i1, ok0), o1 = kv_off(t + 1, t0, i0, i1, ok1);
+            sv[i][0] = ld16_stream((const char*)a.v_cache + o0 + (ok0 ? col : 0));
+            sv[i][1] = ld16_stream((const char*)a.v_cache + o1 + (ok1 ? col : 0));
+            vm |= ((uint32_t)ok0 | ((uint32_t)ok1 << 1)) << (2 * i);
+        }
     };
-    auto stage_load = [&](int t0, u32x4* sk, u32x4 (*sv)[2]) {
+    auto stage_store = [&](int buf, const u32x4* sk, const u32x4 (*sv)[2], uint32_t km,
+                           uint32_t vm) {
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < S::KPT; ++i) {
             const int c = tid + i * S::THREADS;
-            sk[i] = z;
-            if (c < S::KPIECES) {
-                bool ok;
-                const size_t off = kv_off(t0 + c / (D / 8), t0, ok);
-                if (ok) sk[i] = ld16_stream((const char*)a.k_cache + off + (c % (D / 8)) * 16);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < S::VPT; ++i) {
-            const int c = tid + i * S::THREADS;
-            sv[i][0] = z;
-            sv[i][1] = z;
-            if (c < S::VPIECES) {
-                const int t = t0 + 2 * (c / (D / 8)), col = (c % (D / 8)) * 16;
-                bool ok0, ok1;
-                const size_t o0 = kv_off(t, t0, ok0), o1 = kv_off(t + 1, t0, ok1);
-                if (ok0) sv[i][0] = ld16_stream((const char*)a.v_cache + o0 + col);
-                if (ok1) sv[i][1] = ld16_stream((const char*)a.v_cache + o1 + col);
-            }
-        }
-    };
-    auto stage_store = [&](int buf, const u32x4* sk, const u32x4 (*sv)[2]) {
-#pragma unroll
-        for (int i = 0; i < S::KPT; ++i) {
-            const int c = tid + i * S::THREADS;
             if (c < S::KPIECES)
-                st16(&lds_k[buf][(c / (D / 8)) * S::ROWB + (c % (D / 8)) * 16], sk[i]);
+                st16(&lds_k[buf][(c / (D / 8)) * S::ROWB + (c % (D / 8)) * 16],
+                     (km >> i) & 1u ? sk[i] : z);
         }
 #pragma unroll
         for (int i = 0; i < S::VPT; ++i) {
             const int c = tid + i * S::THREADS;
             if (c < S::VPIECES) {
-                const uint32_t e[4] = {sv[i][0].x, sv[i][0].y, sv[i][0].z, sv[i][0].w};
-                const uint32_t o[4] = {sv[i][1].x, sv[i][1].y, sv[i][1].z, sv[i][1].w};
+                const u32x4 v0 = (vm >> (2 * i)) & 1u ? sv[i][0] : z;
+                const u32x4 v1 = (vm >> (2 * i + 1)) & 1u ? sv[i][1] : z;
+                const uint32_t e[4] = {v0.x, v0.y, v0.z, v0.w};
+                const uint32_t o[4] = {v1.x, v1.y, v1.z, v1.w};
                 uint32_t w8[8];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -210,28 +221,14 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
         }
     };
 
-    if (tid == 0) {
-        for (int k = 0; k < 4; ++k) {
-            int i0, i1;
-            fetch_ids(t_first + k * S::STEP, i0, i1);
-            s_ids[k][0] = i0;
-            s_ids[k][1] = i1;
-        }
-    }
-    __syncthreads();
-    if (nsteps > 0) {
-        ids = s_ids[0];
-        stage_load(t_first, sk[0], sv[0]);
-        stage_store(0, sk[0], sv[0]);
-    }
-    if (nsteps > 1) {
-        ids = s_ids[1];
-        stage_load(t_first + S::STEP, sk[1], sv[1]);
-    }
-    if (nsteps > 2) {
-        ids = s_ids[2];
-        stage_load(t_first + 2 * S::STEP, sk[0], sv[0]);
-    }
+    // loads past the last step repeat the last step (never staged: the same loads in every
+    // case keep the wait counts exact)
+    const int t_last = t_first + (nsteps > 0 ? nsteps - 1 : 0) * S::STEP;
+    auto step_t = [&](int st) { return min(t_first + st * S::STEP, t_last); };
+    stage_load(step_t(0), sk[0], sv[0], kmask[0], vmask[0]);
+    if (nsteps > 0) stage_store(0, sk[0], sv[0], kmask[0], vmask[0]);
+    stage_load(step_t(1), sk[1], sv[1], kmask[1], vmask[1]);
+    stage_load(step_t(2), sk[0], sv[0], kmask[0], vmask[0]);
     __syncthreads();
     // step st computes from LDS buffer st & 1 while steps st+1 (register set (st+1) & 1)
     // and st+2 are loading; then st+1 goes to LDS and step st+3 starts loading into the
@@ -239,8 +236,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
     auto body = [&](auto Pc, int st) {
         constexpr int P = decltype(Pc)::value;
         const int buf = st & 1, t0 = t_first + st * S::STEP;
-        int nid0 = -1, nid1 = -1;
-        if (tid == 0 && st + 4 < nsteps) fetch_ids(t0 + 4 * S::STEP, nid0, nid1);
         if (t0 <= wp_last && t0 + S::STEP > wlo_first) {      // wavefront-uniform
             const char* kl = lds_k[buf];
             const char* vl = lds_v[buf];
@@ -332,15 +327,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
                 }
             }
         }
-        if (st + 1 < nsteps) stage_store(buf ^ 1, sk[P], sv[P]);
-        if (st + 3 < nsteps) {
-            ids = s_ids[(st + 3) % 4];
-            stage_load(t0 + 3 * S::STEP, sk[P], sv[P]);
-        }
-        if (tid == 0 && st + 4 < nsteps) {
-            s_ids[(st + 4) % 4][0] = nid0;
-            s_ids[(st + 4) % 4][1] = nid1;
-        }
+        if (st + 1 < nsteps) stage_store(buf ^ 1, sk[P], sv[P], kmask[P], vmask[P]);
+        stage_load(step_t(st + 3), sk[P], sv[P], kmask[P], vmask[P]);
         __syncthreads();
     };
     for (int st = 0; st < nsteps; st += 2) {
