@@ -156,37 +156,45 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
         i0 = (t0 < L && t0 + kBlock > lo_first) ? r0 : -1;
         i1 = (t0 + kBlock < L && t0 + 2 * kBlock > lo_first) ? r1 : -1;
     };
-    auto kv_off = [&](int t, int t0, int i0, int i1, bool& ok) -> size_t {
-        const int b = (t - t0) < kBlock ? i0 : i1;
-        const bool in = t < L && t >= lo_first;
-        const bool valid = (unsigned)b < (unsigned)a.num_blocks;
-        bad |= in && b >= 0 && !valid;
-        ok = in && valid;
-        return ok ? (size_t)b * block_stride + (size_t)g * tile_bytes + (size_t)(t % kBlock) * D * 2
-                  : 0;
+    // The two blocks of a step: scalar base offsets (the cache's first tile for a missing
+    // or invalid block); each lane's pieces then sit at a fixed offset from one of them.
+    auto step_bases = [&](int t0, size_t (&base)[2], bool (&valid)[2]) {
+        int ids[2];
+        step_ids(t0, ids[0], ids[1]);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            valid[hb] = (unsigned)ids[hb] < (unsigned)a.num_blocks;
+            bad |= ids[hb] >= 0 && !valid[hb];
+            base[hb] = valid[hb] ? (size_t)ids[hb] * block_stride + (size_t)g * tile_bytes : 0;
+        }
     };
     auto stage_load = [&](int t0, u32x4* sk, u32x4 (*sv)[2], uint32_t& km, uint32_t& vm) {
-        int i0, i1;
-        step_ids(t0, i0, i1);
+        size_t base[2];
+        bool valid[2];
+        step_bases(t0, base, valid);
+        auto ok = [&](int tau) {          // token t0 + tau of the step is staged
+            const int t = t0 + tau;
+            return valid[tau / kBlock] && t < L && t >= lo_first;
+        };
         km = 0;
         vm = 0;
 #pragma unroll
         for (int i = 0; i < S::KPT; ++i) {
             const int c = (tid + i * S::THREADS) % S::KPIECES;
-            bool ok;
-            const size_t off = kv_off(t0 + c / (D / 8), t0, i0, i1, ok);
-            sk[i] = ld16_stream((const char*)a.k_cache + off + (ok ? (c % (D / 8)) * 16 : 0));
-            km |= (uint32_t)ok << i;
+            const int tau = c / (D / 8);
+            const uint32_t lane_off = (uint32_t)((tau % kBlock) * D * 2 + (c % (D / 8)) * 16);
+            sk[i] = ld16_stream((const char*)a.k_cache + base[tau / kBlock] + lane_off);
+            km |= (uint32_t)ok(tau) << i;
         }
 #pragma unroll
         for (int i = 0; i < S::VPT; ++i) {
             const int c = (tid + i * S::THREADS) % S::VPIECES;
-            const int t = t0 + 2 * (c / (D / 8)), col = (c % (D / 8)) * 16;
-            bool ok0, ok1;
-            const size_t o0 = kv_off(t, t0, i0, i1, ok0), o1 = kv_off(t + 1, t0, i0, i1, ok1);
-            sv[i][0] = ld16_stream((const char*)a.v_cache + o0 + (ok0 ? col : 0));
-            sv[i][1] = ld16_stream((const char*)a.v_cache + o1 + (ok1 ? col : 0));
-            vm |= ((uint32_t)ok0 | ((uint32_t)ok1 << 1)) << (2 * i);
+            const int tau = 2 * (c / (D / 8));          // tokens tau, tau + 1: one block
+            const uint32_t lane_off = (uint32_t)((tau % kBlock) * D * 2 + (c % (D / 8)) * 16);
+            const char* p = (const char*)a.v_cache + base[tau / kBlock] + lane_off;
+            sv[i][0] = ld16_stream(p);
+            sv[i][1] = ld16_stream(p + D * 2);
+            vm |= ((uint32_t)ok(tau) | ((uint32_t)ok(tau + 1) << 1)) << (2 * i);
         }
     };
     auto stage_store = [&](int buf, const u32x4* sk, const u32x4 (*sv)[2], uint32_t km,
