@@ -73,9 +73,15 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
 
     const int32_t* hdr = (const int32_t*)(a.ws + a.lay.header);
     const int2* tiles = (const int2*)(a.ws + a.lay.tiles);
-    if ((int)blockIdx.x >= hdr[4]) return;                 // whole workgroup leaves together
-    const int2 tl = tiles[blockIdx.x];
-    const int s = tl.x, r0 = tl.y, g = blockIdx.y;
+    // Workgroup i of a.max_tiles * Hkv takes row tile i / Hkv for KV head i % Hkv: the tiles
+    // in use come first, and as workgroups are dispatched round-robin over the XCDs, every
+    // tile of a chunk that reads one KV head's K/V runs on the same XCD and shares its L2
+    // (when Hkv is a multiple of the XCD count).
+    const int tile = (int)blockIdx.x / a.num_kv_heads;
+    const int g = (int)blockIdx.x - tile * a.num_kv_heads;
+    if (tile >= hdr[4]) return;                            // whole workgroup leaves together
+    const int2 tl = tiles[tile];
+    const int s = tl.x, r0 = tl.y;
     const int L = a.seq_lens[s];
     const int rs = a.query_start_loc[s];
     const int n = a.query_start_loc[s + 1] - rs;

@@ -58,7 +58,7 @@ hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream) {
     const void* fn = chunk_kernel_ptr(dtype, a.head_dim, a.group, a.block_size);
     if (!fn) return hipErrorInvalidDeviceFunction;
     void* args[] = {(void*)&a};
-    return hipLaunchKernel(fn, dim3(a.max_tiles, a.num_kv_heads), dim3(kWavesPerGroup * kWave),
+    return hipLaunchKernel(fn, dim3(a.max_tiles * a.num_kv_heads), dim3(kWavesPerGroup * kWave),
                            args, 0, stream);
 }
 
