@@ -47,6 +47,15 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// Lane l's value and lane (l ^ 32)'s (gfx950 v_permlane32_swap: the two halves of the
+// wavefront trade places), one of each per lane in some order: enough for a max or a sum
+// over the two halves without an LDS round trip.
+__device__ __forceinline__ float2 with_partner(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int D>
 struct ChunkShape {
     static constexpr int MW = 32;                 // M-rows per wavefront
@@ -149,6 +158,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
     // never include the other set's loads.
     u32x4 sk[2][S::KPT], sv[2][S::VPT][2];
     uint32_t kmask[2], vmask[2];
+    bool whole[2];                      // every token of the set's step is staged (uniform)
     int bad = 0;
     // Block ids are uniform over the workgroup: scalar loads, counted apart from the vector
     // loads.  The table row is read in range only (indices clamped, then selected).
@@ -174,10 +184,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
             base[hb] = valid[hb] ? (size_t)ids[hb] * block_stride + (size_t)g * tile_bytes : 0;
         }
     };
-    auto stage_load = [&](int t0, u32x4* sk, u32x4 (*sv)[2], uint32_t& km, uint32_t& vm) {
+    auto stage_load = [&](int t0, u32x4* sk, u32x4 (*sv)[2], uint32_t& km, uint32_t& vm,
+                          bool& all) {
         size_t base[2];
         bool valid[2];
         step_bases(t0, base, valid);
+        all = valid[0] && valid[1] && t0 >= lo_first && t0 + S::STEP <= L;
         auto ok = [&](int tau) {          // token t0 + tau of the step is staged
             const int t = t0 + tau;
             return valid[tau / kBlock] && t < L && t >= lo_first;
@@ -203,46 +215,61 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
             vm |= ((uint32_t)ok(tau) | ((uint32_t)ok(tau + 1) << 1)) << (2 * i);
         }
     };
+    // A step whose tokens are all staged (the common case) stores without the per-piece
+    // selects: the store body is instantiated with and without masks, chosen by a scalar
+    // branch.
     auto stage_store = [&](int buf, const u32x4* sk, const u32x4 (*sv)[2], uint32_t km,
-                           uint32_t vm) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
+                           uint32_t vm, bool all) {
+        auto put = [&](auto masked_c) {
+            constexpr bool kMasked = decltype(masked_c)::value;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            auto pick = [&](uint32_t on, const u32x4& x) {
+                if constexpr (kMasked) return on ? x : z;
+                else return x;
+            };
 #pragma unroll
-        for (int i = 0; i < S::KPT; ++i) {
-            const int c = tid + i * S::THREADS;
-            if (c < S::KPIECES)
-                st16(&lds_k[buf][(c / (D / 8)) * S::ROWB + (c % (D / 8)) * 16],
-                     (km >> i) & 1u ? sk[i] : z);
-        }
-#pragma unroll
-        for (int i = 0; i < S::VPT; ++i) {
-            const int c = tid + i * S::THREADS;
-            if (c < S::VPIECES) {
-                const u32x4 v0 = (vm >> (2 * i)) & 1u ? sv[i][0] : z;
-                const u32x4 v1 = (vm >> (2 * i + 1)) & 1u ? sv[i][1] : z;
-                const uint32_t e[4] = {v0.x, v0.y, v0.z, v0.w};
-                const uint32_t o[4] = {v1.x, v1.y, v1.z, v1.w};
-                uint32_t w8[8];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    w8[2 * k] = (e[k] & 0xffffu) | (o[k] << 16);
-                    w8[2 * k + 1] = (e[k] >> 16) | (o[k] & 0xffff0000u);
-                }
-                char* dst = &lds_v[buf][(c / (D / 8)) * S::ROWV + (c % (D / 8)) * 32];
-                const u32x4 w0 = {w8[0], w8[1], w8[2], w8[3]}, w1 = {w8[4], w8[5], w8[6], w8[7]};
-                st16(dst, w0);
-                st16(dst + 16, w1);
+            for (int i = 0; i < S::KPT; ++i) {
+                const int c = tid + i * S::THREADS;
+                if (c < S::KPIECES)
+                    st16(&lds_k[buf][(c / (D / 8)) * S::ROWB + (c % (D / 8)) * 16],
+                         pick((km >> i) & 1u, sk[i]));
             }
-        }
+#pragma unroll
+            for (int i = 0; i < S::VPT; ++i) {
+                const int c = tid + i * S::THREADS;
+                if (c < S::VPIECES) {
+                    const u32x4 v0 = pick((vm >> (2 * i)) & 1u, sv[i][0]);
+                    const u32x4 v1 = pick((vm >> (2 * i + 1)) & 1u, sv[i][1]);
+                    const uint32_t e[4] = {v0.x, v0.y, v0.z, v0.w};
+                    const uint32_t o[4] = {v1.x, v1.y, v1.z, v1.w};
+                    uint32_t w8[8];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        w8[2 * k] = (e[k] & 0xffffu) | (o[k] << 16);
+                        w8[2 * k + 1] = (e[k] >> 16) | (o[k] & 0xffff0000u);
+                    }
+                    char* dst = &lds_v[buf][(c / (D / 8)) * S::ROWV + (c % (D / 8)) * 32];
+                    const u32x4 w0 = {w8[0], w8[1], w8[2], w8[3]};
+                    const u32x4 w1 = {w8[4], w8[5], w8[6], w8[7]};
+                    st16(dst, w0);
+                    st16(dst + 16, w1);
+                }
+            }
+        };
+        if (all)
+            put(std::false_type{});
+        else
+            put(std::true_type{});
     };
 
     // loads past the last step repeat the last step (never staged: the same loads in every
     // case keep the wait counts exact)
     const int t_last = t_first + (nsteps > 0 ? nsteps - 1 : 0) * S::STEP;
     auto step_t = [&](int st) { return min(t_first + st * S::STEP, t_last); };
-    stage_load(step_t(0), sk[0], sv[0], kmask[0], vmask[0]);
-    if (nsteps > 0) stage_store(0, sk[0], sv[0], kmask[0], vmask[0]);
-    stage_load(step_t(1), sk[1], sv[1], kmask[1], vmask[1]);
-    stage_load(step_t(2), sk[0], sv[0], kmask[0], vmask[0]);
+    stage_load(step_t(0), sk[0], sv[0], kmask[0], vmask[0], whole[0]);
+    if (nsteps > 0) stage_store(0, sk[0], sv[0], kmask[0], vmask[0], whole[0]);
+    stage_load(step_t(1), sk[1], sv[1], kmask[1], vmask[1], whole[1]);
+    stage_load(step_t(2), sk[0], sv[0], kmask[0], vmask[0], whole[0]);
     __syncthreads();
     // step st computes from LDS buffer st & 1 while steps st+1 (register set (st+1) & 1)
     // and st+2 are loading; then st+1 goes to LDS and step st+3 starts loading into the
@@ -267,9 +294,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
             float p16[16];
             float mx = -INFINITY;
             // this lane's visible token range of the step, [tlo, thi], as offsets 0..31
-            const int tlo = row_ok ? max(lo - t0, 0) : 32;
-            const int thi = row_ok ? min(pos - t0, 31) : -1;
+            // (computed on masked steps only)
             auto vis = [&](int r) {
+                const int tlo = row_ok ? max(lo - t0, 0) : 32;
+                const int thi = row_ok ? min(pos - t0, 31) : -1;
                 const int tt = 8 * (r / 4) + 4 * h + (r % 4);
                 return tt >= tlo && tt <= thi;
             };
@@ -280,7 +308,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, vis(r) ? sc[r] : -INFINITY);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            {
+                const float2 pm = with_partner(mx);
+                mx = fmaxf(pm.x, pm.y);
+            }
             const float mxs = mx > -INFINITY ? mx * qscale : -INFINITY;
             // raise the running max only when the new one exceeds it by more than 8 (log2)
             if (__ballot(mxs > m_run + 8.f)) {                 // wavefront-uniform
@@ -307,7 +338,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
                     psum += p16[r];
                 }
             }
-            psum += __shfl_xor(psum, 32);
+            {
+                const float2 ps = with_partner(psum);
+                psum = ps.x + ps.y;
+            }
             l_run += psum;
             // P^T operands: K-step k2 covers tokens 16 k2 .. 16 k2 + 15; element kk of lane
             // (j, h) is token 16 k2 + (kk < 4 ? 4 h + kk : 8 + 4 h + kk - 4) = p16[8 k2 + kk]
@@ -341,8 +375,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
                 }
             }
         }
-        if (st + 1 < nsteps) stage_store(buf ^ 1, sk[P], sv[P], kmask[P], vmask[P]);
-        stage_load(step_t(st + 3), sk[P], sv[P], kmask[P], vmask[P]);
+        if (st + 1 < nsteps) stage_store(buf ^ 1, sk[P], sv[P], kmask[P], vmask[P], whole[P]);
+        stage_load(step_t(st + 3), sk[P], sv[P], kmask[P], vmask[P], whole[P]);
         __syncthreads();
     };
     for (int st = 0; st < nsteps; st += 2) {
