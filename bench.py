@@ -234,6 +234,10 @@ def main():
                     help="tokens per KV block (8 and 32: OPT-13B and GQA shapes, 16-bit KV)")
     ap.add_argument("--kv", choices=["native", "q8"], default="native",
                     help="q8: 8-bit KV cache (one fp16 scale per 32 values), same workload")
+    ap.add_argument("--event-every", type=int, default=4, metavar="N",
+                    help="kernel durations come from hipEvents recorded around the launches "
+                         "of every N-th layer of each timed step (each recorded event adds a "
+                         "few microseconds of queue gap, which N = 1 would add to every layer)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--swap-seqs", type=int, default=0, metavar="N",
@@ -307,21 +311,26 @@ def main():
     has_chunks = bool((w.q_rows > 1).any()) and w.dtype in MFMA_PEAK_TFLOPS
     copies = dw.step_copies
 
+    every = max(1, args.event_every)
+    sampled = list(range(0, L, every))            # layers whose launches are timed
+
     def step(events=None, cevents=None, xevents=None):
         pa.decode(dw.q, pools[0][0], pools[0][1], dw.block_tables, dw.seq_lens, float(w.scale),
                   step="plan", **common)
         for li, (kc, vc) in enumerate(pools):
+            timed_layer = li % every == 0
+            si = li // every
             if copies is not None:
-                if xevents is not None:
-                    xevents[li][0].record()
+                if xevents is not None and timed_layer:
+                    xevents[si][0].record()
                 pa.copy_blocks(kc, vc, copies)
-                if xevents is not None:
-                    xevents[li][1].record()
+                if xevents is not None and timed_layer:
+                    xevents[si][1].record()
             pa.write_kv(k_step, v_step, slot_step, kc, vc)
             if events is not None:
-                pa.set_decode_profile_events(*events[li])
+                pa.set_decode_profile_events(*(events[si] if timed_layer else (None, None)))
             if cevents is not None:
-                pa.set_chunk_profile_events(*cevents[li])
+                pa.set_chunk_profile_events(*(cevents[si] if timed_layer else (None, None)))
             pa.decode(dw.q, kc, vc, dw.block_tables, dw.seq_lens, float(w.scale), out=out,
                       step="attend", **common)
         if events is not None:
@@ -332,10 +341,10 @@ def main():
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
-    # one pair of events per decode launch in the timed region
+    # one pair of events per timed launch (every N-th layer) in the timed region
     def event_pairs():
         e = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(L)] for _ in range(args.steps)]
+              for _ in sampled] for _ in range(args.steps)]
         for per in e:
             for a, b in per:
                 a.record()
@@ -379,7 +388,7 @@ def main():
         "traffic": traffic,
         "algorithmic_bytes_per_launch": int(kv_decode),
         "decode_kernel_avg_us": round(dec_avg_ms * 1e3, 2),
-        "launches_timed": args.steps * L,
+        "launches_timed": args.steps * len(sampled),
     }
     chunk_roof = None
     if has_chunks:
@@ -396,7 +405,7 @@ def main():
             "traffic": None,
             "algorithmic_flops_per_launch": int(flops),
             "chunk_kernel_avg_us": round(chunk_avg_ms * 1e3, 2),
-            "launches_timed": args.steps * L,
+            "launches_timed": args.steps * len(sampled),
         }
 
     copy_roof = None
@@ -416,7 +425,7 @@ def main():
             "algorithmic_bytes_per_launch": int(cbytes),
             "copies_per_launch": int(copies.shape[0]),
             "copy_kernel_avg_us": round(copy_avg_ms * 1e3, 2),
-            "launches_timed": args.steps * L,
+            "launches_timed": args.steps * len(sampled),
         }
 
     result = {
