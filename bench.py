@@ -130,6 +130,18 @@ def cpu_baseline(w, n_layers, seconds):
         if el >= seconds:
             break
     frac = passes + i / w.num_seqs
+    # the same oracle on one thread, over a shorter sample
+    ref.threads = 1
+    one_bytes, t1 = 0, time.perf_counter()
+    j = 0
+    while time.perf_counter() - t1 < min(3.0, seconds):
+        chunk = order[j:j + 1]
+        ref.attention(seqs=chunk)
+        one_bytes += pa.kv_bytes_read(w.seq_lens[chunk], w.q_rows[chunk], w.window,
+                                      w.num_kv_heads, w.head_dim, w.elem_bytes)
+        j = (j + 1) % w.num_seqs
+    one_el = time.perf_counter() - t1
+    ref.threads = 0
     return ref, {
         "value": round(done_bytes / el / 1e9, 3),
         "unit": "GB/s",
@@ -139,7 +151,46 @@ def cpu_baseline(w, n_layers, seconds):
                   f"({done_rows} query rows, {done_bytes / 1e9:.3f} GB of KV) in {el:.1f} s",
         "tokens_per_s": round(done_rows / el / n_layers, 3),
         "tokens_per_s_note": f"one layer's rate scaled to {n_layers} layers",
+        "value_one_thread": round(one_bytes / one_el / 1e9, 3),
+        "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def read_ceiling(pa, gib=4, launches=5):
+    """The plain read rate of this device: pa_stream_read over a dedicated buffer of `gib`
+    GiB (far beyond the 256 MB MALL), two untimed launches, then `launches` timed ones."""
+    import torch
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        pa.stream_read(buf, sink)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for a, b in ev:
+        a.record()
+        pa.stream_read(buf, sink)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / launches
+    del buf
+    return {"kernel": "stream_read_kernel", "achieved": round(buf_bytes(gib) / (ms / 1e3) / 1e9, 2),
+            "unit": "GB/s", "bytes_per_launch": buf_bytes(gib), "launches_timed": launches,
+            "note": "one contiguous read of a buffer with 16-byte non-temporal loads, this box"}
+
+
+def buf_bytes(gib):
+    return gib << 30
 
 
 HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction, published
@@ -314,7 +365,7 @@ def main():
     every = max(1, args.event_every)
     sampled = list(range(0, L, every))            # layers whose launches are timed
 
-    def step(events=None, cevents=None, xevents=None):
+    def step(events=None, cevents=None, xevents=None, wevents=None):
         pa.decode(dw.q, pools[0][0], pools[0][1], dw.block_tables, dw.seq_lens, float(w.scale),
                   step="plan", **common)
         for li, (kc, vc) in enumerate(pools):
@@ -326,7 +377,11 @@ def main():
                 pa.copy_blocks(kc, vc, copies)
                 if xevents is not None and timed_layer:
                     xevents[si][1].record()
+            if wevents is not None and timed_layer:
+                wevents[si][0].record()
             pa.write_kv(k_step, v_step, slot_step, kc, vc)
+            if wevents is not None and timed_layer:
+                wevents[si][1].record()
             if events is not None:
                 pa.set_decode_profile_events(*(events[si] if timed_layer else (None, None)))
             if cevents is not None:
@@ -354,11 +409,12 @@ def main():
     evs = event_pairs()
     cevs = event_pairs() if has_chunks else None
     xevs = event_pairs() if copies is not None else None
+    wevs = event_pairs()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for k in range(args.steps):
-        step(evs[k], cevs[k] if cevs else None, xevs[k] if xevs else None)
+        step(evs[k], cevs[k] if cevs else None, xevs[k] if xevs else None, wevs[k])
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -367,6 +423,7 @@ def main():
                     if cevs else 0.0)
     copy_avg_ms = (float(np.mean([a.elapsed_time(b) for per in xevs for a, b in per]))
                    if xevs else 0.0)
+    write_avg_ms = float(np.mean([a.elapsed_time(b) for per in wevs for a, b in per]))
     err_bits = pa.device_error_bits(dw.workspace)
 
     step_s = total_ms / 1e3 / args.steps
@@ -458,8 +515,17 @@ def main():
             "seed": w.seed,
         },
         "roofline": chunk_roof if chunk_roof and chunk_avg_ms > dec_avg_ms else decode_roof,
+        "write_kv": {
+            "avg_us": round(write_avg_ms * 1e3, 2),
+            # each new row of K and of V is read once and written once
+            "bytes_per_launch": int(4 * k_step.numel() * k_step.element_size()),
+            "launches_timed": args.steps * len(sampled),
+        },
         "device_error_bits": err_bits,
     }
+    ceiling = read_ceiling(pa)
+    ceiling["decode_kernel_frac_of_ceiling"] = round(achieved / ceiling["achieved"], 4)
+    result["hbm_read_ceiling"] = ceiling
     if chunk_roof:
         result["roofline_decode"] = decode_roof
         result["roofline_chunk"] = chunk_roof

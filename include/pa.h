@@ -198,6 +198,19 @@ void pa_set_decode_profile_events(void* before, void* after);
  * of several query rows and whose cache dtype is F16 or BF16). */
 void pa_set_chunk_profile_events(void* before, void* after);
 
+/* pa_stream_read - read a device buffer once, contiguously, with the 16-byte non-temporal
+ * loads the attention kernels use, and write (practically) nothing.  It measures the plain
+ * read rate of the device, the ceiling that the paged kernels' KV-read rates are set
+ * against ("PagedAttention deep dive", donmain.dev: decoding is bound by reading the KV
+ * cache).  Not part of the attention path.
+ *
+ *   buf     (device) the buffer, 16-byte aligned; only read.
+ *   bytes   a multiple of 16; 0 launches nothing.
+ *   sink    (device) one uint32; receives a word only if the XOR of all words read equals
+ *           0x9e3779b9 (so that the loads cannot be removed); otherwise untouched.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (misaligned or bytes % 16 != 0), PA_ERR_LAUNCH. */
+pa_status pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* pa_status_string(pa_status s);
 

@@ -32,7 +32,7 @@ BLOCK_SIZE = 16
 # every symbol include/pa.h declares
 EXPORTS = ("pa_write_kv", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode", "pa_decode_plan",
            "pa_decode_attend", "pa_set_decode_profile_events", "pa_set_chunk_profile_events",
-           "pa_status_string",
+           "pa_stream_read", "pa_status_string",
            "pa_pool_create", "pa_pool_destroy", "pa_seq_set_window", "pa_seq_append",
            "pa_seq_share_prefix", "pa_seq_free", "pa_seq_block_table", "pa_pool_block_tables",
            "pa_seq_len", "pa_pool_num_free", "pa_block_refcount", "pa_seq_fork",
@@ -80,6 +80,7 @@ def load():
                                    i32, P, ctypes.c_size_t, P]),
         "pa_set_decode_profile_events": (None, [P, P]),
         "pa_set_chunk_profile_events": (None, [P, P]),
+        "pa_stream_read": (i32, [P, ctypes.c_size_t, P, P]),
         "pa_status_string": (ctypes.c_char_p, [i32]),
         "pa_pool_create": (i32, [i32, i32, P, i32, ctypes.POINTER(P)]),
         "pa_pool_destroy": (None, [P]),
@@ -192,6 +193,21 @@ def write_kv(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
                          _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
                          ctypes.byref(desc), _stream(stream))
     _check(rc, "pa_write_kv")
+
+
+def stream_read(buf, sink, stream=None) -> None:
+    """pa_stream_read: read the whole contiguous device tensor `buf` once (its byte size a
+    multiple of 16); `sink` is a device int32/uint32 word written only in a negligible case."""
+    torch = _torch()
+    lib = load()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink.dtype not in (torch.int32, torch.uint32) or not sink.is_cuda or sink.numel() < 1:
+        raise ValueError("sink must be a device int32 word")
+    rc = lib.pa_stream_read(ctypes.c_void_p(buf.data_ptr()),
+                            buf.numel() * buf.element_size(), ctypes.c_void_p(sink.data_ptr()),
+                            _stream(stream))
+    _check(rc, "pa_stream_read")
 
 
 def copy_blocks(k_cache, v_cache, copies, error_word=None, stream=None) -> None:

@@ -157,6 +157,14 @@ pa_status pa_write_kv(const void* k, const void* v, const int64_t* slot_mapping,
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+pa_status pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (bytes == 0) return PA_OK;
+    if (!buf || !sink) return PA_ERR_NULL;
+    if ((bytes & 15u) || ((uintptr_t)buf & 15u)) return PA_ERR_SHAPE;
+    return pa::launch_stream_read(buf, bytes, sink, (hipStream_t)stream) == hipSuccess
+               ? PA_OK : PA_ERR_LAUNCH;
+}
+
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* desc,
                          const int32_t* copies, int32_t num_copies, int32_t* error_word,
                          void* stream) {

@@ -116,6 +116,7 @@ hipError_t launch_swap_blocks(const void* sk, const void* sv, void* dk, void* dv
                               int32_t hkv, int32_t tile_bytes, int32_t* err,
                               hipStream_t stream);
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream);

@@ -254,6 +254,32 @@ def test_wave_count_invariance_and_determinism(torch, pa, orc, monkeypatch):
     monkeypatch.delenv("PA_MIN_BLOCKS")
 
 
+def test_stream_read_probe(torch, pa):
+    """The read probe reads every word: its sink is written exactly when a thread's fold of
+    the words it read equals the pattern, and a buffer without it leaves the sink alone."""
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    buf = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    pa.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+    # one 16-byte word far into the buffer holds the pattern: some thread must read it
+    pat = int(np.array([0x9e3779b9], dtype=np.uint32).view(np.int32)[0])
+    buf[(1 << 20) - 4] = pat
+    pa.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == pat
+    # a buffer that ends in a partial 32 KiB chunk: the pattern in the last word is still read
+    sink.fill_(7)
+    tail = torch.zeros((1 << 20) + 12, dtype=torch.int32, device="cuda")
+    pa.stream_read(tail, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+    tail[-4] = pat
+    pa.stream_read(tail, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == pat
+
+
 def test_out_dtypes(torch, pa):
     w = workloads.make("gqa", batch=8, median=300)
     dw = run(w, torch)

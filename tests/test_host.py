@@ -58,6 +58,11 @@ def test_host_validation_without_gpu(pa):
     ok = pa.CacheDesc(10, 16, 4, 128, pa.PA_F16)
     assert lib.pa_write_kv(None, None, None, 1, None, None, ctypes.byref(ok), None) == -1
     assert lib.pa_write_kv(None, None, None, 0, None, None, ctypes.byref(ok), None) == 0
+    # the read probe checks its arguments before launching anything
+    assert lib.pa_stream_read(None, 16, None, None) == -1
+    assert lib.pa_stream_read(ctypes.c_void_p(0x1000), 24, ctypes.c_void_p(0x2000), None) == -2
+    assert lib.pa_stream_read(ctypes.c_void_p(0x1008), 16, ctypes.c_void_p(0x2000), None) == -2
+    assert lib.pa_stream_read(None, 0, None, None) == 0
     bdt = pa.CacheDesc(10, 16, 4, 128, 7)
     assert lib.pa_write_kv(None, None, None, 1, None, None, ctypes.byref(bdt), None) == -3
     assert lib.pa_write_kv(None, None, None, 1, None, None, None, None) == -1
