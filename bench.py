@@ -299,8 +299,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the decode path needs no "
-              "collectives); run it with --gpus 1", file=sys.stderr)
+        print("bench.py: the benchmark runs on one GPU only; run it with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
