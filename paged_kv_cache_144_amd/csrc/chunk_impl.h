@@ -82,13 +82,19 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
 
     const int32_t* hdr = (const int32_t*)(a.ws + a.lay.header);
     const int2* tiles = (const int2*)(a.ws + a.lay.tiles);
-    // Workgroup i of a.max_tiles * Hkv takes row tile i / Hkv for KV head i % Hkv: the tiles
-    // in use come first, and as workgroups are dispatched round-robin over the XCDs, every
-    // tile of a chunk that reads one KV head's K/V runs on the same XCD and shares its L2
-    // (when Hkv is a multiple of the XCD count).
-    const int tile = (int)blockIdx.x / a.num_kv_heads;
-    const int g = (int)blockIdx.x - tile * a.num_kv_heads;
-    if (tile >= hdr[4]) return;                            // whole workgroup leaves together
+    // Workgroup i of a.max_tiles * Hkv takes tile position i / Hkv for KV head i % Hkv: the
+    // tiles in use come first, and as workgroups are dispatched round-robin over the XCDs,
+    // every tile of a chunk that reads one KV head's K/V runs on the same XCD and shares its
+    // L2 (when Hkv is a multiple of the XCD count).  The second half of the positions takes
+    // the tiles in reverse order: a chunk's tiles grow longer with their rows, and the two
+    // workgroups that share a CU (positions t and t + NT / 2 when one round holds them all)
+    // then pair a long tile with a short one, which evens the work per CU.
+    const int nt = hdr[4];
+    const int tpos = (int)blockIdx.x / a.num_kv_heads;
+    const int g = (int)blockIdx.x - tpos * a.num_kv_heads;
+    if (tpos >= nt) return;                                // whole workgroup leaves together
+    const int half = (nt + 1) / 2;
+    const int tile = tpos < half ? tpos : nt - 1 - (tpos - half);
     const int2 tl = tiles[tile];
     const int s = tl.x, r0 = tl.y;
     const int L = a.seq_lens[s];
