@@ -525,6 +525,42 @@ def test_chunk_rows_parity(torch, pa, orc, monkeypatch, kw):
     assert np.abs(out - alt).max() < 2e-3
 
 
+WINDOW_CASES = [
+    # (group, head_dim, dtype): the per-lane kernel (G = 1, 2), the matrix-core kernel
+    # (G = 4, 8), 8-bit caches on both
+    (1, 64, "f16"), (2, 128, "bf16"), (4, 128, "bf16"), (8, 64, "f16"), (1, 128, "q8_f16"),
+    (4, 128, "q8_bf16"),
+]
+
+
+@pytest.mark.parametrize("window", [1, 15, 16, 17, 33])
+@pytest.mark.parametrize("g,d,dtype", WINDOW_CASES, ids=[f"g{g}-d{d}-{t}" for g, d, t in WINDOW_CASES])
+def test_small_windows(torch, pa, orc, g, d, dtype, window):
+    """Windows shorter than a block, of exactly one block and just past it, over decode rows
+    and (16-bit caches) chunk rows, with contexts shorter and longer than the window.  A
+    window of one token leaves each row its own token: a decode row's output is its V
+    exactly (weight exp2(0) = 1).  Chunk rows stay within the tolerance only: their weight
+    is exp2 of the rounding error of the scaled score against the separately rounded max,
+    and P enters the matrix cores as two 8-bit-mantissa halves (16 bits in all)."""
+    lens = [1, 5, 16, 17, 40, 300, 33]
+    rows = [1] * len(lens)
+    if not dtype.startswith("q8"):
+        lens += [90, 200]
+        rows += [40, 7]
+    hkv = 2
+    say("window case", g, d, dtype, window)
+    w = workloads.make("rows", lens=lens, rows=rows, hq=g * hkv, hkv=hkv, d=d, dtype=dtype,
+                       window=window)
+    dw = run(w, torch)
+    ref = orc.Reference(w).attention()
+    out = dw.decode().cpu().numpy()
+    assert pa.device_error_bits(dw.workspace) == 0
+    check_close(out, ref, f"window {window} g{g} d{d} {dtype}")
+    if window == 1:
+        dec = w.query_start_loc()[:-1][w.q_rows == 1]
+        assert np.array_equal(out[dec], ref[dec].astype(np.float32)), "one-token window"
+
+
 def test_chunk_rows_before_position_zero(torch, pa):
     w = workloads.make("rows", lens=[5], rows=[9], hq=4, hkv=2, d=64, dtype="bf16")
     dw = run(w, torch)
