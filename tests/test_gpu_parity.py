@@ -561,6 +561,21 @@ def test_small_windows(torch, pa, orc, g, d, dtype, window):
         assert np.array_equal(out[dec], ref[dec].astype(np.float32)), "one-token window"
 
 
+@pytest.mark.parametrize("g,d,dtype", [(1, 64, "f16"), (4, 128, "bf16")], ids=["lane", "mfma"])
+def test_one_long_sequence(torch, pa, orc, g, d, dtype):
+    """A 200,000-token context: its one (row, KV head) pair is cut into hundreds of shares,
+    and the merge combines more partials than a wavefront has lanes (several rounds)."""
+    w = workloads.make("rows", lens=[200_000, 3], rows=[1, 1], hq=g, hkv=1, d=d, dtype=dtype)
+    dw = run(w, torch)
+    ref = orc.Reference(w).attention()
+    out = dw.decode().cpu().numpy()
+    waves = int(dw.workspace[:32].cpu().view(torch.int32)[2])
+    say("long sequence: shares", waves)
+    assert waves > 2 * 64
+    assert pa.device_error_bits(dw.workspace) == 0
+    check_close(out, ref, f"one long sequence {dtype}")
+
+
 def test_chunk_rows_before_position_zero(torch, pa):
     w = workloads.make("rows", lens=[5], rows=[9], hq=4, hkv=2, d=64, dtype="bf16")
     dw = run(w, torch)
