@@ -44,6 +44,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense matrix peak, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = ["decode_impl.h", "decode_mfma.h", "pa_device.h", "pa_internal.h", "plan.hip"]
+CHUNK_SOURCES = ["chunk_impl.h", "pa_device.h", "pa_internal.h", "plan.hip"]
 
 DESCRIPTIONS = {
     "opt13b": "OPT-13B-shaped paged decode: 64 seqs, 40 q heads = 40 KV heads, d=128, fp16 KV, "
@@ -63,24 +64,25 @@ DESCRIPTIONS = {
 }
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "paged_kv_cache_144_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs, or None when
-    there is none for this workload or the kernel sources changed since."""
+def measured_traffic(key: str, files=KERNEL_SOURCES):
+    """HBM bytes per launch of one kernel from the committed rocprofv3 counter runs (entry
+    `key`: the workload, or the workload + "_chunk" for the chunk-row kernel), or None when
+    there is none or that kernel's sources changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(workload)
-    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+    e = t.get(key)
+    if not e or e.get("kernel_source_hash") != kernel_source_hash(files):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -452,6 +454,9 @@ def main():
         flops = pa.chunk_flops(w.seq_lens, w.q_rows, w.window, w.num_q_heads, w.head_dim)
         tflops = flops / (chunk_avg_ms / 1e3) / 1e12
         peak = MFMA_PEAK_TFLOPS[w.dtype]
+        # the chunks' K/V, each (token, KV head) once: what the kernel must read at least
+        chunk_kv = sum(2 * w.num_kv_heads * w.head_dim * w.elem_bytes * int(L)
+                       for L, n in zip(w.seq_lens, w.q_rows) if n > 1)
         chunk_roof = {
             "kernel": "chunk_kernel",
             "bound": "mfma",
@@ -459,7 +464,9 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4),
-            "traffic": None,
+            "traffic": (measured_traffic(args.workload + "_chunk", CHUNK_SOURCES)
+                        if args.block_size == 16 else None),
+            "chunk_kv_bytes_per_launch": int(chunk_kv),
             "algorithmic_flops_per_launch": int(flops),
             "chunk_kernel_avg_us": round(chunk_avg_ms * 1e3, 2),
             "launches_timed": args.steps * len(sampled),
