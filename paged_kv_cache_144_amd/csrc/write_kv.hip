@@ -12,23 +12,29 @@
 
 namespace pa {
 
+// Index type I: 32-bit when the number of 16-byte pieces fits, which avoids emulated 64-bit
+// divisions.  The K and V pieces are loaded before the slot is known (their source is always
+// in range), so the slot load and the data loads are in flight together.  Block sizes are
+// powers of two (8, 16, 32): the slot splits into block and row with a shift and a mask.
+template <typename I>
 __global__ __launch_bounds__(256) void write_kv_kernel(
     const char* __restrict__ k, const char* __restrict__ v, const int64_t* __restrict__ slots,
-    int64_t n_chunks, int chunks_per_row, int hkv, int bs, int64_t pool_slots,
+    I n_chunks, int chunks_per_row, int hkv, int bs_log2, int64_t pool_slots,
     char* __restrict__ kc, char* __restrict__ vc) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_chunks; i += stride) {
-        const int64_t row = i / chunks_per_row;       // (token, head) row
-        const int c = (int)(i - row * chunks_per_row);
-        const int64_t tok = row / hkv;
-        const int h = (int)(row - tok * hkv);
+    const I stride = (I)gridDim.x * blockDim.x;
+    for (I i = (I)blockIdx.x * blockDim.x + threadIdx.x; i < n_chunks; i += stride) {
+        const I row = i / (I)chunks_per_row;          // (token, head) row
+        const int c = (int)(i - row * (I)chunks_per_row);
+        const I tok = row / (I)hkv;
+        const int h = (int)(row - tok * (I)hkv);
+        const size_t src = (size_t)i * 16;
+        const u32x4 kx = ld16(k + src), vx = ld16(v + src);
         const int64_t slot = slots[tok];
         if (slot < 0 || slot >= pool_slots) continue;
-        const int64_t blk = slot / bs, off = slot % bs;
-        const int64_t dst = (((blk * hkv + h) * bs + off) * chunks_per_row + c) * 16;
-        const int64_t src = i * 16;
-        st16(kc + dst, ld16(k + src));
-        st16(vc + dst, ld16(v + src));
+        const int64_t blk = slot >> bs_log2, off = slot & ((1 << bs_log2) - 1);
+        const int64_t dst = (((blk * hkv + h) << bs_log2) + off) * chunks_per_row * 16 + c * 16;
+        st16(kc + dst, kx);
+        st16(vc + dst, vx);
     }
 }
 
@@ -111,9 +117,19 @@ hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, i
     const int64_t n_chunks = (int64_t)n * hkv * chunks_per_row;
     int64_t blocks = (n_chunks + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const char*)k, (const char*)v, slots, n_chunks, chunks_per_row, hkv,
-                       bs, (int64_t)nb * bs, (char*)kc, (char*)vc);
+    int bs_log2 = 0;
+    while ((1 << bs_log2) < bs) ++bs_log2;
+    if ((1 << bs_log2) != bs) return hipErrorInvalidValue;   // 8, 16 or 32 only
+    // 32-bit indices while the grid-stride loop cannot overflow them
+    if (n_chunks + (int64_t)blocks * 256 < ((int64_t)1 << 31)) {
+        hipLaunchKernelGGL(write_kv_kernel<int32_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const char*)k, (const char*)v, slots, (int32_t)n_chunks,
+                           chunks_per_row, hkv, bs_log2, (int64_t)nb * bs, (char*)kc, (char*)vc);
+    } else {
+        hipLaunchKernelGGL(write_kv_kernel<int64_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const char*)k, (const char*)v, slots, n_chunks, chunks_per_row, hkv,
+                           bs_log2, (int64_t)nb * bs, (char*)kc, (char*)vc);
+    }
     return hipGetLastError();
 }
 
