@@ -13,16 +13,15 @@
 // "M-rows" (query row, query head of the group), QT = 4 * 32 / G.  The context is walked in
 // steps of 32 tokens (two blocks).  Each step, the workgroup stages the step's K and V in
 // LDS (16-byte coalesced loads; tokens past the sequence, before the window or in a block
-// with an invalid id are staged as zeros, so no NaN reaches a product): K row-major, V with
-// the two tokens of each even/odd pair interleaved per column, so that one 4-byte LDS read
-// is two consecutive tokens of one column.  Then every wavefront computes
+// with an invalid id are staged as zeros, so no NaN reaches a product), both row-major.
+// Then every wavefront computes
 //     S^T[32 tokens][32 M-rows] = K . Q^T            (D/16 MFMAs, K operand from LDS)
 // applies the causal / window mask by selection (only on steps that straddle a row's edge),
 // runs the online softmax per M-row (each lane owns one M-row column; partner lane l^32
 // holds the other half of the step's tokens), and
 //     O^T[d][M-row] += V^T . P^T                     (4 * D/32 MFMAs: P = hi + lo)
 // where P^T comes straight from the S^T accumulator registers in the MFMA B-operand order
-// and the V^T operand is four 4-byte LDS reads in the matching token order.  The running
+// and the V^T operand is two LDS transpose reads in the matching token order.  The running
 // max is raised only when a row's new maximum exceeds it by more than 2^8 (weights stay
 // <= 256), so the accumulators are rescaled on few steps.  The next step's global loads are
 // in flight while the current step computes (LDS double buffer, one barrier per step).
@@ -56,23 +55,35 @@ __device__ __forceinline__ float2 with_partner(float x) {
     return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// gfx950 LDS transpose read of 4 x 16-bit elements (ds_read_b64_tr_b16)
+__device__ __forceinline__ u32x2 tr_read(const char* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
 template <int D>
 struct ChunkShape {
     static constexpr int MW = 32;                 // M-rows per wavefront
     static constexpr int STEP = 32;               // tokens per step
     static constexpr int ROWB = D * 2 + 16;       // LDS bytes per staged K token row (padded)
-    static constexpr int ROWV = D * 4 + 16;       // LDS bytes per staged V token pair (padded)
+    // LDS bytes per staged V token row: padded so that the row stride is 16 dwords mod 64,
+    // which keeps the transpose reads of the P.V operand (below) off shared banks
+    static constexpr int ROWV = D * 2 + 4 * ((16 - D / 2 % 64 + 64) % 64);
     static constexpr int KREG = STEP * ROWB;
-    static constexpr int VREG = STEP / 2 * ROWV;
+    static constexpr int VREG = STEP * ROWV;
     static constexpr int THREADS = kWavesPerGroup * kWave;
     static constexpr int KPIECES = STEP * D / 8;        // 16-byte pieces of K per step
-    static constexpr int VPIECES = STEP / 2 * D / 8;    // (token pair, 8 columns) pieces of V
+    static constexpr int VPIECES = STEP * D / 8;        // 16-byte pieces of V per step
     static constexpr int KPT = (KPIECES + THREADS - 1) / THREADS;
     static constexpr int VPT = (VPIECES + THREADS - 1) / THREADS;
 };
 
 template <int DT, int D, int G>
-__global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(DecodeArgs a) {
+// d <= 128: two workgroups per CU.  d = 256 needs more than 256 VGPRs: one wavefront per
+// SIMD, so that nothing spills to scratch memory.
+__global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chunk_kernel(DecodeArgs a) {
     using S = ChunkShape<D>;
     constexpr int KS = D / 16, DT32 = D / 32, QR = S::MW / G;
     constexpr float kLog2e = 1.4426950408889634f;
@@ -104,6 +115,9 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 31, h = lane >> 5;
+    // the V row this lane names in the P.V transpose reads (see the product below)
+    const int v_lane = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * S::ROWV +
+                       (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
     // this lane's M-row (column of S^T and O^T)
     const int m = wave * S::MW + j;
@@ -154,15 +168,14 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
     const size_t tile_bytes = (size_t)kBlock * D * 2;
     const size_t block_stride = (size_t)a.num_kv_heads * tile_bytes;
 
-    // staging.  K piece c -> token c / (D/8), 16-byte column c % (D/8).  V piece c -> token
-    // pair c / (D/8), column group c % (D/8): tokens 2p and 2p+1, 8 columns each, written
-    // interleaved as 8 dwords (token 2p in the low half).
+    // staging.  K and V piece c -> token c / (D/8), 16-byte column c % (D/8), both
+    // row-major in LDS.
     // two register sets: the loads of the next two steps are in flight during a step.
     // Every lane issues the same loads in every case (a position outside the row range or
     // in a block with an invalid id reads the cache's first bytes instead, and its mask bit
     // zeroes it when staged), so that the compiler's wait counts for one register set
     // never include the other set's loads.
-    u32x4 sk[2][S::KPT], sv[2][S::VPT][2];
+    u32x4 sk[2][S::KPT], sv[2][S::VPT];
     uint32_t kmask[2], vmask[2];
     bool whole[2];                      // every token of the set's step is staged (uniform)
     int bad = 0;
@@ -190,7 +203,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
             base[hb] = valid[hb] ? (size_t)ids[hb] * block_stride + (size_t)g * tile_bytes : 0;
         }
     };
-    auto stage_load = [&](int t0, u32x4* sk, u32x4 (*sv)[2], uint32_t& km, uint32_t& vm,
+    auto stage_load = [&](int t0, u32x4* sk, u32x4* sv, uint32_t& km, uint32_t& vm,
                           bool& all) {
         size_t base[2];
         bool valid[2];
@@ -213,18 +226,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
 #pragma unroll
         for (int i = 0; i < S::VPT; ++i) {
             const int c = (tid + i * S::THREADS) % S::VPIECES;
-            const int tau = 2 * (c / (D / 8));          // tokens tau, tau + 1: one block
+            const int tau = c / (D / 8);
             const uint32_t lane_off = (uint32_t)((tau % kBlock) * D * 2 + (c % (D / 8)) * 16);
-            const char* p = (const char*)a.v_cache + base[tau / kBlock] + lane_off;
-            sv[i][0] = ld16_stream(p);
-            sv[i][1] = ld16_stream(p + D * 2);
-            vm |= ((uint32_t)ok(tau) | ((uint32_t)ok(tau + 1) << 1)) << (2 * i);
+            sv[i] = ld16_stream((const char*)a.v_cache + base[tau / kBlock] + lane_off);
+            vm |= (uint32_t)ok(tau) << i;
         }
     };
     // A step whose tokens are all staged (the common case) stores without the per-piece
     // selects: the store body is instantiated with and without masks, chosen by a scalar
     // branch.
-    auto stage_store = [&](int buf, const u32x4* sk, const u32x4 (*sv)[2], uint32_t km,
+    auto stage_store = [&](int buf, const u32x4* sk, const u32x4* sv, uint32_t km,
                            uint32_t vm, bool all) {
         auto put = [&](auto masked_c) {
             constexpr bool kMasked = decltype(masked_c)::value;
@@ -243,23 +254,9 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
 #pragma unroll
             for (int i = 0; i < S::VPT; ++i) {
                 const int c = tid + i * S::THREADS;
-                if (c < S::VPIECES) {
-                    const u32x4 v0 = pick((vm >> (2 * i)) & 1u, sv[i][0]);
-                    const u32x4 v1 = pick((vm >> (2 * i + 1)) & 1u, sv[i][1]);
-                    const uint32_t e[4] = {v0.x, v0.y, v0.z, v0.w};
-                    const uint32_t o[4] = {v1.x, v1.y, v1.z, v1.w};
-                    uint32_t w8[8];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        w8[2 * k] = (e[k] & 0xffffu) | (o[k] << 16);
-                        w8[2 * k + 1] = (e[k] >> 16) | (o[k] & 0xffff0000u);
-                    }
-                    char* dst = &lds_v[buf][(c / (D / 8)) * S::ROWV + (c % (D / 8)) * 32];
-                    const u32x4 w0 = {w8[0], w8[1], w8[2], w8[3]};
-                    const u32x4 w1 = {w8[4], w8[5], w8[6], w8[7]};
-                    st16(dst, w0);
-                    st16(dst + 16, w1);
-                }
+                if (c < S::VPIECES)
+                    st16(&lds_v[buf][(c / (D / 8)) * S::ROWV + (c % (D / 8)) * 16],
+                         pick((vm >> i) & 1u, sv[i]));
             }
         };
         if (all)
@@ -364,18 +361,18 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, 2) void chunk_kernel(Decode
                 pb[k2] = th;
                 pl[k2] = tl2;
             }
-            // O^T += V^T . P^T; the V^T operand takes the same token order: dwords of token
-            // pairs (ta, ta+1), (ta+2, ta+3), (tb, tb+1), (tb+2, tb+3)
+            // O^T += V^T . P^T.  Lane (j, h) needs column j of tokens 16 k2 + 4 h .. +3 and
+            // 16 k2 + 8 + 4 h .. +3, in that order: two LDS transpose reads (each lane of a
+            // 16-lane group names one 4-element row; lane 4a+b receives element b of the rows
+            // named by lanes a, a+4, a+8, a+12) over V staged row-major.  Lane s of a group
+            // names token 4 h + s/4 at columns 4 (s%4) of its group's 16-column half.
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-                const int pa_ = 8 * k2 + 2 * h, pb_ = 8 * k2 + 4 + 2 * h;   // token-pair rows
 #pragma unroll
                 for (int dt = 0; dt < DT32; ++dt) {
-                    const char* col = vl + (32 * dt + j) * 4;
-                    const u32x4 va = {*(const uint32_t*)(col + pa_ * S::ROWV),
-                                      *(const uint32_t*)(col + (pa_ + 1) * S::ROWV),
-                                      *(const uint32_t*)(col + pb_ * S::ROWV),
-                                      *(const uint32_t*)(col + (pb_ + 1) * S::ROWV)};
+                    const char* p0 = vl + v_lane + (16 * k2) * S::ROWV + 64 * dt;
+                    const u32x2 t0 = tr_read(p0), t1 = tr_read(p0 + 8 * S::ROWV);
+                    const u32x4 va = {t0.x, t0.y, t1.x, t1.y};
                     acc[dt] = mfma32<DT>(va, pb[k2], acc[dt]);
                     acc[dt] = mfma32<DT>(va, pl[k2], acc[dt]);
                 }
