@@ -74,11 +74,15 @@ struct KvOps<DT, D, G, BS, false> {
         const u32x4 t = ld16(q + elem * QB);
         r.v[gi][0] = t.x; r.v[gi][1] = t.y; r.v[gi][2] = t.z; r.v[gi][3] = t.w;
     }
-    __device__ static void load(const char* kb, const char* vb, size_t off, Tile& t) {
+    // the tile at byte offset off of both caches; bytes = TILE reads it, bytes = 0 issues
+    // the same loads without touching memory (zeros)
+    __device__ static void load_buf(const char* kc, const char* vc, size_t off, uint32_t bytes,
+                                    uint32_t lo, Tile& t) {
+        const rsrc_t rk = buf_rsrc(kc + off, bytes), rv = buf_rsrc(vc + off, bytes);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            t.k[i] = ld16_stream(kb + off + i * 1024);
-            t.v[i] = ld16_stream(vb + off + i * 1024);
+            t.k[i] = ld16_buf(rk, lo + i * 1024);
+            t.v[i] = ld16_buf(rv, lo + i * 1024);
         }
     }
     // this lane's share of q . k for each load and head (summed over the row afterwards)
@@ -136,12 +140,10 @@ struct KvOps<DT, D, G, BS, true> {
     struct Extra { float corr[G]; };   // sum of weight * scale, per head
 
     __device__ static size_t lane_off(int lane) { return (size_t)lane * PE; }
-    __device__ static size_t scale_off(int lane) {
+    // byte offset in the tile of the scale of lane's first load
+    __device__ static uint32_t scale_at(int lane) {
         const int row = lane / LPT, col = lane % LPT;
-        return SCALES + (size_t)(row * GROUPS + col * PE / kQ8Group) * 2 - (size_t)lane * PE;
-    }
-    __device__ static CodeVec ld_codes(const char* p) {
-        return __builtin_nontemporal_load(reinterpret_cast<const CodeVec*>(p));
+        return SCALES + (uint32_t)(row * GROUPS + col * PE / kQ8Group) * 2;
     }
     __device__ static void load_q(const char* q, size_t elem, int gi, Q& r) {
         float f[PE];
@@ -163,15 +165,23 @@ struct KvOps<DT, D, G, BS, true> {
         r.off[gi] = 1152.f * sum;
         r.inv[gi] = ldexpf(1.f, ex - 15);
     }
-    __device__ static void load(const char* kb, const char* vb, size_t off, Tile& t) {
-        const int lane = lane_id();
-        const size_t so = off + scale_off(lane);
+    // as for 16-bit tiles: bytes = TILE reads the tile, bytes = 0 reads nothing
+    __device__ static CodeVec ld_codes(rsrc_t r, uint32_t off) {
+        if constexpr (NW == 2)
+            return __builtin_bit_cast(CodeVec, ld8_buf(r, off));
+        else
+            return __builtin_bit_cast(CodeVec, ld16_buf(r, off));
+    }
+    __device__ static void load_buf(const char* kc, const char* vc, size_t off, uint32_t bytes,
+                                    uint32_t lo, Tile& t) {
+        const rsrc_t rk = buf_rsrc(kc + off, bytes), rv = buf_rsrc(vc + off, bytes);
+        const uint32_t so = scale_at(lane_id());
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            t.k[i] = ld_codes(kb + off + i * (kWave * PE));
-            t.v[i] = ld_codes(vb + off + i * (kWave * PE));
-            t.ks[i] = ld2_stream(kb + so + (size_t)i * TPI * GROUPS * 2);
-            t.vs[i] = ld2_stream(vb + so + (size_t)i * TPI * GROUPS * 2);
+            t.k[i] = ld_codes(rk, lo + i * (kWave * PE));
+            t.v[i] = ld_codes(rv, lo + i * (kWave * PE));
+            t.ks[i] = ld2_buf(rk, so + i * TPI * GROUPS * 2);
+            t.vs[i] = ld2_buf(rv, so + i * TPI * GROUPS * 2);
         }
     }
     // fp16 pair (1152 + c0, 1152 + c1) from two code bytes of w (already flipped by 0x80)
@@ -415,8 +425,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     const float qscale = a.scale * kLog2e;
     const size_t head_stride = S::TILE;
     const size_t block_stride = (size_t)a.num_kv_heads * S::TILE;
-    const char* kbase = (const char*)a.k_cache + S::lane_off(lane);
-    const char* vbase = (const char*)a.v_cache + S::lane_off(lane);
 
     uint32_t x = wx0[wave];
     const uint32_t x_end = wx0[wave + 1];
@@ -465,8 +473,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
             valid = (unsigned)b < (unsigned)a.num_blocks;
             return valid ? b : 0;
         };
-        auto load_tile = [&](int b, typename S::Tile& t) {
-            S::load(kbase, vbase, (size_t)b * block_stride + head_off, t);
+        // live = false: the loads are issued (so every step waits for the same count) but
+        // read nothing where the policy allows it
+        auto load_tile = [&](int b, bool live, typename S::Tile& t) {
+            S::load_buf((const char*)a.k_cache, (const char*)a.v_cache,
+                        (size_t)b * block_stride + head_off, live ? (uint32_t)S::TILE : 0u,
+                        (uint32_t)S::lane_off(lane), t);
         };
         auto consume = [&](typename S::Tile& tl, int j, bool valid) {
             const int t0 = j * BS;
@@ -530,14 +542,15 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
             const int btv = lane < n ? bt[c0 + lane] : 0;
             typename S::Tile A, B;
             bool okA, okB;
-            load_tile(block_id(btv, 0, okA), A);
+            load_tile(block_id(btv, 0, okA), true, A);
             for (int jj = 0; jj < n; jj += 2) {
-                // B <- block jj+1 (or jj again at the end: a cache hit, keeps waits simple)
-                load_tile(block_id(btv, jj + 1 < n ? jj + 1 : jj, okB), B);
+                // B <- block jj+1; past the end the same loads are issued (keeps the waits
+                // simple) but discarded
+                load_tile(block_id(btv, jj + 1 < n ? jj + 1 : jj, okB), jj + 1 < n, B);
                 bad |= !okA;
                 consume(A, c0 + jj, okA);
                 if (jj + 1 >= n) break;
-                load_tile(block_id(btv, jj + 2 < n ? jj + 2 : jj + 1, okA), A);
+                load_tile(block_id(btv, jj + 2 < n ? jj + 2 : jj + 1, okA), jj + 2 < n, A);
                 bad |= !okB;
                 consume(B, c0 + jj + 1, okB);
             }

@@ -45,6 +45,25 @@ __device__ __forceinline__ uint32_t ld2_stream(const void* p) {
 
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Raw buffer resource over `bytes` bytes from p (its address must be wave-uniform).  A lane
+// whose offset lies at or past `bytes` reads zeros and its load touches no memory, so with
+// bytes = 0 a tile load is issued, counted and discarded without any traffic.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+// 16, 8 or 2 bytes at byte offset off of r, non-temporal like ld16_stream
+__device__ __forceinline__ u32x4 ld16_buf(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+__device__ __forceinline__ u32x2 ld8_buf(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2));
+}
+__device__ __forceinline__ uint32_t ld2_buf(rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 2);
+}
+
 // ---- element conversion ----------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
