@@ -66,6 +66,7 @@ struct KvOps<DT, D, G, BS, false> {
 
     struct Tile { u32x4 k[NLD], v[NLD]; };
     struct Q { uint32_t v[G][4]; };
+    typedef Q QRaw;                              // the query as loaded is the query used
     struct Extra {};
 
     __device__ static size_t lane_off(int lane) { return (size_t)lane * 16; }
@@ -74,6 +75,7 @@ struct KvOps<DT, D, G, BS, false> {
         const u32x4 t = ld16(q + elem * QB);
         r.v[gi][0] = t.x; r.v[gi][1] = t.y; r.v[gi][2] = t.z; r.v[gi][3] = t.w;
     }
+    __device__ static void prep_q(const QRaw& r, Q& q) { q = r; }
     // the tile at byte offset off of both caches; bytes = TILE reads it, bytes = 0 issues
     // the same loads without touching memory (zeros)
     __device__ static void load_buf(const char* kc, const char* vc, size_t off, uint32_t bytes,
@@ -137,6 +139,7 @@ struct KvOps<DT, D, G, BS, true> {
     struct Tile { CodeVec k[NLD], v[NLD]; uint32_t ks[NLD], vs[NLD]; };
     // q in fp16 scaled by 2^e per lane and head, 1152 * sum of those values, 2^-e
     struct Q { uint32_t v[G][PE / 2]; float off[G]; float inv[G]; };
+    struct QRaw { u32x4 r[G][PE / 8]; };   // the 16-bit query elements as loaded
     struct Extra { float corr[G]; };   // sum of weight * scale, per head
 
     __device__ static size_t lane_off(int lane) { return (size_t)lane * PE; }
@@ -145,10 +148,18 @@ struct KvOps<DT, D, G, BS, true> {
         const int row = lane / LPT, col = lane % LPT;
         return SCALES + (uint32_t)(row * GROUPS + col * PE / kQ8Group) * 2;
     }
-    __device__ static void load_q(const char* q, size_t elem, int gi, Q& r) {
+    __device__ static void load_q(const char* q, size_t elem, int gi, QRaw& r) {
+#pragma unroll
+        for (int j = 0; j < PE / 8; ++j) r.r[gi][j] = ld16(q + (elem + 8 * j) * QB);
+    }
+    __device__ static void prep_q(const QRaw& raw, Q& r) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) prep_head(raw, gi, r);
+    }
+    __device__ static void prep_head(const QRaw& raw, int gi, Q& r) {
         float f[PE];
 #pragma unroll
-        for (int j = 0; j < PE / 8; ++j) widen16<ADT>(ld16(q + (elem + 8 * j) * QB), f + 8 * j);
+        for (int j = 0; j < PE / 8; ++j) widen16<ADT>(raw.r[gi][j], f + 8 * j);
         float mx = 0.f;
 #pragma unroll
         for (int e = 0; e < PE; ++e) mx = fmaxf(mx, fabsf(f[e]));
@@ -426,34 +437,93 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     const size_t head_stride = S::TILE;
     const size_t block_stride = (size_t)a.num_kv_heads * S::TILE;
 
-    uint32_t x = wx0[wave];
+    const uint32_t x_start = wx0[wave];
     const uint32_t x_end = wx0[wave + 1];
-    int u = wu[wave];
-    bool first_segment = true;
+    int uh = wu[wave];
+    if (x_start >= x_end) return;
 
-    while (x < x_end) {
-        while (cb[u + 1] <= x) ++u;                       // skip finished / empty units
-        const UnitInfo ui = unit[u];
-        const uint32_t base = cb[u];
-        const int g = (int)((x - base) / (uint32_t)ui.nb);
-        const uint32_t ps = base + (uint32_t)g * ui.nb, pe = ps + ui.nb;
-        const uint32_t seg_end = x_end < pe ? x_end : pe;
-        const int j0 = ui.b_lo + (int)(x - ps), j1 = ui.b_lo + (int)(seg_end - ps);
-        const int len = ui.len;
-        const int lo_tok = (a.window > 0 && len > a.window) ? len - a.window : 0;
-        // a pair cut after this segment and starting in it: its later shares' starts,
-        // loaded now and used when the merge record is written
-        const bool opens_cut = x == ps && seg_end < pe;
-        uint32_t next = pe;
-        if (opens_cut && wave + 1 + lane < W) next = wx0[wave + 1 + lane];
-
-        // this lane's slice of the G query rows, kept packed
-        typename S::Q qv;
+    // A segment: the part of pair (u, g) inside this wavefront's share; blocks j0 .. j1-1
+    // of the sequence's table row.
+    struct Seg {
+        int u, g, seq, len, lo_tok, j0, j1;
+        uint32_t ps, pe, end;
+        bool starts;     // the segment starts at the pair's first block
+    };
+    auto describe = [&](uint32_t xs) {
+        while (cb[uh + 1] <= xs) ++uh;                    // skip finished / empty units
+        const UnitInfo ui = unit[uh];
+        const uint32_t base = cb[uh];
+        Seg sg;
+        sg.u = uh;
+        sg.g = (int)((xs - base) / (uint32_t)ui.nb);
+        sg.ps = base + (uint32_t)sg.g * ui.nb;
+        sg.pe = sg.ps + ui.nb;
+        sg.end = x_end < sg.pe ? x_end : sg.pe;
+        sg.starts = xs == sg.ps;
+        sg.j0 = ui.b_lo + (int)(xs - sg.ps);
+        sg.j1 = ui.b_lo + (int)(sg.end - sg.ps);
+        sg.seq = ui.seq;
+        sg.len = ui.len;
+        sg.lo_tok = (a.window > 0 && ui.len > a.window) ? ui.len - a.window : 0;
+        return sg;
+    };
+    // block ids c0 .. c0+63 of the segment, one per lane
+    auto load_ids = [&](const Seg& sg, int c0) {
+        const int n = sg.j1 - c0;
+        return lane < n ? a.block_tables[(size_t)sg.seq * a.max_blocks + c0 + lane] : 0;
+    };
+    // this lane's slice of the segment's G query rows, as loaded
+    auto load_q = [&](const Seg& sg, typename S::QRaw& r) {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
-            const size_t qi = (((size_t)u * a.num_q_heads + (size_t)g * G + gi) * D + col * PE);
-            S::load_q((const char*)a.q, qi, gi, qv);
+            const size_t qi = ((size_t)sg.u * a.num_q_heads + (size_t)sg.g * G + gi) * D + col * PE;
+            S::load_q((const char*)a.q, qi, gi, r);
         }
+    };
+    auto block_id = [&](int ids, int idx, bool& valid) {
+        int b = __builtin_amdgcn_readlane(ids, idx);
+        valid = (unsigned)b < (unsigned)a.num_blocks;
+        return valid ? b : 0;
+    };
+    // live = false: the loads are issued (every step then waits for the same count) but
+    // read nothing
+    auto load_tile = [&](int g, int b, bool live, typename S::Tile& t) {
+        S::load_buf((const char*)a.k_cache, (const char*)a.v_cache,
+                    (size_t)b * block_stride + (size_t)g * head_stride,
+                    live ? (uint32_t)S::TILE : 0u, (uint32_t)S::lane_off(lane), t);
+    };
+
+    // The tiles stream without a break: the load after each block's is the next block of
+    // this 64-id chunk, else the first of the next chunk, else the first of the next
+    // segment, whose record, queries and first ids load while this segment runs.
+    Seg cur = describe(x_start);
+    typename S::QRaw qr;
+    load_q(cur, qr);
+    int ids = load_ids(cur, cur.j0);
+    typename S::Tile A, B;
+    bool okA, okB;
+    load_tile(cur.g, block_id(ids, 0, okA), true, A);
+    bool first_segment = true;
+    int bad = 0;
+
+    for (;;) {
+        const bool more = cur.end < x_end;
+        Seg nxt = cur;
+        typename S::QRaw qn;
+        int nids = 0;
+        if (more) {
+            nxt = describe(cur.end);
+            load_q(nxt, qn);
+            nids = load_ids(nxt, nxt.j0);
+        }
+        typename S::Q qv;
+        S::prep_q(qr, qv);
+        // a pair cut after this segment and starting in it: its later shares' starts,
+        // loaded now and used when the merge record is written
+        const bool opens_cut = cur.starts && cur.end < cur.pe;
+        uint32_t next = cur.pe;
+        if (opens_cut && wave + 1 + lane < W) next = wx0[wave + 1 + lane];
+
         typename S::Extra ex;
         S::init(ex);
         float m[G], l[G], acc[G][PE];
@@ -464,22 +534,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
 #pragma unroll
             for (int e = 0; e < PE; ++e) acc[gi][e] = 0.f;
         }
+        const int len = cur.len, lo_tok = cur.lo_tok;
 
-        const int32_t* bt = a.block_tables + (size_t)ui.seq * a.max_blocks;
-        const size_t head_off = (size_t)g * head_stride;
-
-        auto block_id = [&](int btv, int idx, bool& valid) {
-            int b = __builtin_amdgcn_readlane(btv, idx);
-            valid = (unsigned)b < (unsigned)a.num_blocks;
-            return valid ? b : 0;
-        };
-        // live = false: the loads are issued (so every step waits for the same count) but
-        // read nothing where the policy allows it
-        auto load_tile = [&](int b, bool live, typename S::Tile& t) {
-            S::load_buf((const char*)a.k_cache, (const char*)a.v_cache,
-                        (size_t)b * block_stride + head_off, live ? (uint32_t)S::TILE : 0u,
-                        (uint32_t)S::lane_off(lane), t);
-        };
         auto consume = [&](typename S::Tile& tl, int j, bool valid) {
             const int t0 = j * BS;
             float sc[G][NLD];
@@ -536,31 +592,52 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
             S::accumulate(acc, p, tl, ex);
         };
 
-        int bad = 0;
-        for (int c0 = j0; c0 < j1; c0 += kWave) {
-            const int n = (j1 - c0) < kWave ? (j1 - c0) : kWave;
-            const int btv = lane < n ? bt[c0 + lane] : 0;
-            typename S::Tile A, B;
-            bool okA, okB;
-            load_tile(block_id(btv, 0, okA), true, A);
-            for (int jj = 0; jj < n; jj += 2) {
-                // B <- block jj+1; past the end the same loads are issued (keeps the waits
-                // simple) but discarded
-                load_tile(block_id(btv, jj + 1 < n ? jj + 1 : jj, okB), jj + 1 < n, B);
+        // plain copies of what the loads need (a select between fields of the two records
+        // would keep both records in memory)
+        const int g_cur = cur.g, g_nxt = nxt.g, j1_cur = cur.j1;
+        int cids = ids;
+        for (int c0 = cur.j0;; c0 += kWave) {
+            const int n = (j1_cur - c0) < kWave ? (j1_cur - c0) : kWave;
+            const bool last_chunk = c0 + kWave >= j1_cur;
+            const int nc_ids = last_chunk ? 0 : load_ids(cur, c0 + kWave);
+            // block k of this chunk, else the next chunk's or next segment's first block; at
+            // the very end the same loads read nothing.  Every case issues the same loads,
+            // so the wait counts stay exact.
+            auto load_next = [&](int k, typename S::Tile& t, bool& ok) {
+                if (k < n) {
+                    load_tile(g_cur, block_id(cids, k, ok), true, t);
+                } else if (!last_chunk) {
+                    load_tile(g_cur, block_id(nc_ids, 0, ok), true, t);
+                } else if (more) {
+                    load_tile(g_nxt, block_id(nids, 0, ok), true, t);
+                } else {
+                    ok = false;
+                    load_tile(g_cur, 0, false, t);
+                }
+            };
+            for (int k = 0;; k += 2) {
+                load_next(k + 1, B, okB);
                 bad |= !okA;
-                consume(A, c0 + jj, okA);
-                if (jj + 1 >= n) break;
-                load_tile(block_id(btv, jj + 2 < n ? jj + 2 : jj + 1, okA), jj + 2 < n, A);
+                consume(A, c0 + k, okA);
+                if (k + 1 >= n) {
+                    A = B;
+                    okA = okB;
+                    break;
+                }
+                load_next(k + 2, A, okA);
                 bad |= !okB;
-                consume(B, c0 + jj + 1, okB);
+                consume(B, c0 + k + 1, okB);
+                if (k + 2 >= n) break;
             }
+            if (last_chunk) break;
+            cids = nc_ids;
         }
-        if (bad && lane == 0) atomicOr(hdr, kErrBlockId);
         S::finish(acc, ex);
 
         // combine the TPI rows of the wavefront (log-sum-exp), then write
-        const bool complete = x == ps && seg_end == pe;
+        const bool complete = cur.starts && cur.end == cur.pe;
         const int slot = first_segment ? 0 : 1;
+        const int u = cur.u, g = cur.g;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             float M = m[gi];
@@ -598,12 +675,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
         }
         if (opens_cut) {
             // this wavefront holds the pair's first block: leave its merge task
-            const int nc = pair_waves(wx0, W, wave, pe, next, lane);
+            const int nc = pair_waves(wx0, W, wave, cur.pe, next, lane);
             if (lane == 0) tasks[wave + 1] = make_int4(u, g, nc, first_segment ? 0 : 1);
         }
-        x = seg_end;
+        if (!more) break;
+        cur = nxt;
+        qr = qn;
+        ids = nids;
         first_segment = false;
     }
+    if (bad && lane == 0) atomicOr(hdr, kErrBlockId);
 }
 
 }  // namespace pa
