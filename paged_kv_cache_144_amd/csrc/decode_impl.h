@@ -405,6 +405,35 @@ __device__ void merge_pair(const DecodeArgs& a, int u, int g, int w_first, int n
     }
 }
 
+// A segment: the part of pair (u, g) inside a wavefront's share; blocks j0 .. j1-1 of the
+// sequence's table row.
+struct Seg {
+    int u, g, seq, len, lo_tok, j0, j1;
+    uint32_t ps, pe, end;
+    bool starts;     // the segment starts at the pair's first block
+};
+// the first segment of a share, from the plan's record
+__device__ inline Seg first_segment_of(const WaveStart& st, int window) {
+    Seg sg;
+    sg.u = st.u;
+    sg.g = st.g;
+    sg.seq = st.seq;
+    sg.len = st.len;
+    sg.lo_tok = (window > 0 && st.len > window) ? st.len - window : 0;
+    sg.j0 = st.j0;
+    sg.j1 = st.j1;
+    sg.ps = st.ps;
+    sg.pe = st.pe;
+    sg.end = st.x1 < st.pe ? st.x1 : st.pe;
+    sg.starts = st.x0 == st.ps;
+    return sg;
+}
+// a block id from the table, checked: outside [0, num_blocks) it reads block 0 and is masked
+__device__ inline int checked_block(int b, int num_blocks, bool& valid) {
+    valid = (unsigned)b < (unsigned)num_blocks;
+    return valid ? b : 0;
+}
+
 template <int DT, int D, int G, int BS = kBlock>
 __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeArgs a) {
     using S = KvOps<DT, D, G, BS>;
@@ -417,7 +446,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     const uint32_t* cb = (const uint32_t*)(a.ws + a.lay.cb);
     const UnitInfo* unit = (const UnitInfo*)(a.ws + a.lay.unit);
     const uint32_t* wx0 = (const uint32_t*)(a.ws + a.lay.wave_x0);
-    const int32_t* wu = (const int32_t*)(a.ws + a.lay.wave_u);
     float2* pml = (float2*)(a.ws + a.lay.part_ml);
     float* pacc = (float*)(a.ws + a.lay.part_acc);
 
@@ -427,6 +455,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     const int W = hdr[2], n_empty = hdr[3];
     const int wave = uniform(blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6));
     const int lane = lane_id();
+    // this wavefront's first segment, read with the header (entries from W on are unused)
+    const WaveStart st = ((const WaveStart*)(a.ws + a.lay.wave_st))[wave];
     // rows with nothing to read are zeros (shared out among all launched wavefronts)
     for (int i = wave; i < n_empty; i += gridDim.x * kWavesPerGroup) zero_row(a, empty[i], lane);
     if (wave >= W) return;
@@ -437,18 +467,11 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     const size_t head_stride = S::TILE;
     const size_t block_stride = (size_t)a.num_kv_heads * S::TILE;
 
-    const uint32_t x_start = wx0[wave];
-    const uint32_t x_end = wx0[wave + 1];
-    int uh = wu[wave];
+    const uint32_t x_start = st.x0;
+    const uint32_t x_end = st.x1;
+    int uh = st.u;
     if (x_start >= x_end) return;
 
-    // A segment: the part of pair (u, g) inside this wavefront's share; blocks j0 .. j1-1
-    // of the sequence's table row.
-    struct Seg {
-        int u, g, seq, len, lo_tok, j0, j1;
-        uint32_t ps, pe, end;
-        bool starts;     // the segment starts at the pair's first block
-    };
     auto describe = [&](uint32_t xs) {
         while (cb[uh + 1] <= xs) ++uh;                    // skip finished / empty units
         const UnitInfo ui = unit[uh];
@@ -496,13 +519,13 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     // The tiles stream without a break: the load after each block's is the next block of
     // this 64-id chunk, else the first of the next chunk, else the first of the next
     // segment, whose record, queries and first ids load while this segment runs.
-    Seg cur = describe(x_start);
+    Seg cur = first_segment_of(st, a.window);
     typename S::QRaw qr;
     load_q(cur, qr);
     int ids = load_ids(cur, cur.j0);
     typename S::Tile A, B;
     bool okA, okB;
-    load_tile(cur.g, block_id(ids, 0, okA), true, A);
+    load_tile(cur.g, checked_block(st.b0, a.num_blocks, okA), true, A);
     bool first_segment = true;
     int bad = 0;
 

@@ -457,7 +457,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     const uint32_t* cb = (const uint32_t*)(a.ws + a.lay.cb);
     const UnitInfo* unit = (const UnitInfo*)(a.ws + a.lay.unit);
     const uint32_t* wx0 = (const uint32_t*)(a.ws + a.lay.wave_x0);
-    const int32_t* wu = (const int32_t*)(a.ws + a.lay.wave_u);
     float2* pml = (float2*)(a.ws + a.lay.part_ml);
     float* pacc = (float*)(a.ws + a.lay.part_acc);
     int4* tasks = (int4*)(a.ws + a.lay.tasks);
@@ -466,6 +465,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     const int W = hdr[2], n_empty = hdr[3];
     const int wave = uniform(blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6));
     const int lane = lane_id();
+    // this wavefront's first segment, read with the header (entries from W on are unused)
+    const WaveStart st = ((const WaveStart*)(a.ws + a.lay.wave_st))[wave];
     for (int i = wave; i < n_empty; i += gridDim.x * kWavesPerGroup) zero_row(a, empty[i], lane);
     if (wave >= W) return;
 
@@ -477,17 +478,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     const char* kbase = (const char*)a.k_cache + Ops::k_lane(lane);
     const char* vbase = (const char*)a.v_cache + Ops::v_lane(lane);
 
-    const uint32_t x_start = wx0[wave];
-    const uint32_t x_end = wx0[wave + 1];
-    int uh = wu[wave];
+    const uint32_t x_start = st.x0;
+    const uint32_t x_end = st.x1;
+    int uh = st.u;
 
-    // A segment: the part of pair (u, g) inside this wavefront's share; blocks j0 .. j1-1
-    // of the sequence's table row.
-    struct Seg {
-        int u, g, seq, len, lo_tok, j0, j1;
-        uint32_t ps, pe, end;
-        bool starts;     // the segment starts at the pair's first block
-    };
     auto describe = [&](uint32_t xs) {
         while (cb[uh + 1] <= xs) ++uh;
         const UnitInfo ui = unit[uh];
@@ -541,13 +535,23 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     };
 
     if (x_start >= x_end) return;
-    Seg cur = describe(x_start);
+    Seg cur = first_segment_of(st, a.window);
     Q q;
     load_q(cur, q);
     int ids = load_ids(cur, cur.j0);
     Tile A, B;
     Item iA, iB;
-    load_item(cur.g, ids, 0, min(BPT, cur.j1 - cur.j0), 0, A, iA);
+    {
+        // the first item's blocks come with the plan's record, ahead of the ids
+        size_t off[BPT];
+        iA.cnt = min(BPT, cur.j1 - cur.j0);
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) {
+            const int b = checked_block(h == 0 ? st.b0 : st.b1, a.num_blocks, iA.ok[h]);
+            off[h] = (size_t)b * block_stride + (size_t)cur.g * Ops::TILE;
+        }
+        Ops::load(kbase, vbase, off, A);
+    }
     bool first_segment = true;
     int bad = 0;
 

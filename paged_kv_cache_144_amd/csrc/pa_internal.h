@@ -37,6 +37,19 @@ struct UnitInfo {
     int32_t seq;    // block-table row
 };
 
+// The first segment of a wavefront's share, laid out by the plan so that the wavefront can
+// issue its queries', block ids' and first tile's loads right after reading it (instead of
+// finding its pair through the share start, the unit offsets and the unit record first).
+struct WaveStart {
+    uint32_t x0, x1;   // the share: linear blocks [x0, x1)
+    int32_t u, g;      // its first pair (unit, KV head)
+    uint32_t ps, pe;   // that pair's linear blocks [ps, pe)
+    int32_t j0, j1;    // the first segment's table entries [j0, j1)
+    int32_t seq, len;  // the unit's table row and visible length
+    int32_t b0, b1;    // block ids at j0 and j0 + 1 (b0 again when j1 = j0 + 1)
+};
+static_assert(sizeof(WaveStart) == 48, "three 16-byte loads");
+
 // Workspace layout (all offsets 256-byte aligned); U = query rows, W = wavefront workers:
 //   header   int32[64]: [0] error bits, [1] total blocks T, [2] active waves,
 //                       [3] rows with nothing to read (their output is zeros),
@@ -49,6 +62,8 @@ struct UnitInfo {
 //   empty    int32[U]      the rows with nothing to read
 //   wave_x0  uint32[W+1]   first linear block of each wave's share
 //   wave_u   int32[W]      unit holding that block
+//   wave_st  WaveStart[Wmax+4]  each wavefront's first segment (every launched
+//                          wavefront reads its entry before it checks w < W)
 //   tiles    int2[Tmax]    chunk-row tiles (sequence, first row) for the MFMA kernel
 //   tasks    int4[W+1]     merge task of the cut pair whose first share boundary is w:
 //                          (unit, KV head, contributing wavefronts, slot of the first);
@@ -56,7 +71,8 @@ struct UnitInfo {
 //   part_ml  float2[W*2*G]       partial (max, sum) per wave, slot, head of the group
 //   part_acc float[W*2*G*d]      partial unnormalised output
 struct Layout {
-    size_t header, cb, cw, unit, empty, wave_x0, wave_u, tiles, tasks, part_ml, part_acc, total;
+    size_t header, cb, cw, unit, empty, wave_x0, wave_u, wave_st, tiles, tasks, part_ml, part_acc,
+        total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -71,6 +87,7 @@ inline Layout layout(int num_rows, int max_waves, int max_tiles, int group, int 
     L.empty = o;    o = align256(o + (size_t)num_rows * sizeof(int32_t));
     L.wave_x0 = o;  o = align256(o + (size_t)(max_waves + 1) * sizeof(uint32_t));
     L.wave_u = o;   o = align256(o + (size_t)max_waves * sizeof(int32_t));
+    L.wave_st = o;  o = align256(o + (size_t)(max_waves + 4) * sizeof(WaveStart));
     L.tiles = o;    o = align256(o + (size_t)max_tiles * 2 * sizeof(int32_t));
     L.tasks = o;    o = align256(o + (size_t)(max_waves + 1) * 4 * sizeof(int32_t));
     L.part_ml = o;  o = align256(o + (size_t)max_waves * 2 * group * 2 * sizeof(float));

@@ -59,6 +59,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     int32_t* empty = (int32_t*)(a.ws + a.lay.empty);
     int2* tiles = (int2*)(a.ws + a.lay.tiles);
     int4* tasks = (int4*)(a.ws + a.lay.tasks);
+    WaveStart* wst = (WaveStart*)(a.ws + a.lay.wave_st);
 
     __shared__ uint32_t s_blk[kPlanThreads], s_til[kPlanThreads], s_pr[kPlanThreads];
     __shared__ int s_err, s_bad, s_empty;
@@ -215,8 +216,35 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
+    if (tid == 0) wx0[W] = T;
+    __syncthreads();
+    // each share's first segment, as the decode kernels would find it from wx0 and wu
+    for (int w = tid; w < W; w += kPlanThreads) {
+        const uint32_t x0 = wx0[w], x1 = wx0[w + 1];
+        int u = wu[w];
+        while (cb[u + 1] <= x0) ++u;                 // skip finished / empty units
+        const UnitInfo ui = unit[u];
+        const uint32_t nb = (uint32_t)ui.nb, base = cb[u];
+        const uint32_t g = (x0 - base) / nb;
+        const uint32_t ps = base + g * nb, pe = ps + nb;
+        const uint32_t end = x1 < pe ? x1 : pe;
+        WaveStart st;
+        st.x0 = x0;
+        st.x1 = x1;
+        st.u = u;
+        st.g = (int32_t)g;
+        st.ps = ps;
+        st.pe = pe;
+        st.j0 = ui.b_lo + (int32_t)(x0 - ps);
+        st.j1 = ui.b_lo + (int32_t)(end - ps);
+        st.seq = ui.seq;
+        st.len = ui.len;
+        const int32_t* bt = a.block_tables + (size_t)ui.seq * a.max_blocks;
+        st.b0 = bt[st.j0];
+        st.b1 = st.j0 + 1 < st.j1 ? bt[st.j0 + 1] : st.b0;
+        wst[w] = st;
+    }
     if (tid == 0) {
-        wx0[W] = T;
         hdr[0] = s_err; hdr[1] = (int32_t)T; hdr[2] = W; hdr[3] = s_empty; hdr[4] = (int32_t)NT;
     }
 }
