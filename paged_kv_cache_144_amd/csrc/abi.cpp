@@ -45,6 +45,15 @@ pa_status check_desc(const pa_cache_desc* d) {
     return PA_OK;
 }
 
+// Compute units of the current device (0 on failure).
+int cu_count() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
+
 // Resident decode wavefronts on the current device for one kernel instance.
 int resident_waves(const void* fn) {
     static std::mutex mu;
@@ -71,6 +80,7 @@ struct Plan {
     const void* fn = nullptr;
     int group = 0;
     int max_waves = 0;
+    int wave_round = 0;   // wavefronts of one workgroup on every compute unit
     int chunk_rows = 0;   // query rows per chunk tile; 0 = chunk rows run as decode rows
     int max_tiles = 0;
     int pair_cost = pa::kPairCost;
@@ -89,6 +99,7 @@ pa_status plan_shape(const pa_cache_desc* desc, int32_t num_seqs, int32_t total_
     if (!p.fn) return PA_ERR_UNSUPPORTED;
     p.max_waves = resident_waves(p.fn);
     if (p.max_waves <= 0) return PA_ERR_LAUNCH;
+    p.wave_round = cu_count() * pa::kWavesPerGroup;
     // tuning / testing knob: fewer decode wavefronts than the device keeps resident
     if (const char* e = std::getenv("PA_DECODE_WAVES")) {
         const int v = std::atoi(e);
@@ -310,6 +321,7 @@ pa_status build_args(void* out, pa_dtype out_dtype, const void* q, const void* k
     a.window = window > 0 ? window : 0;
     a.scale = scale;
     a.max_waves = p.max_waves;
+    a.wave_round = p.wave_round;
     a.chunk_rows = p.chunk_rows;
     a.max_tiles = p.max_tiles;
     a.pair_cost = p.pair_cost;

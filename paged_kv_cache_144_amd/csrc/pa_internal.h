@@ -14,12 +14,13 @@ constexpr int kBlock = 16;          // default tokens per KV block (8 and 32 als
                                     // decode kernels for 16-bit caches)
 constexpr int kWave = 64;           // CDNA wavefront width
 constexpr int kWavesPerGroup = 4;   // decode workgroup = 4 independent wavefront workers
-constexpr int kMinBlocksPerWave = 16;  // default smallest share of KV blocks per wavefront
+constexpr int kMinBlocksPerWave = 12;  // default smallest share of KV blocks per wavefront
 constexpr int kMinBlocksFloor = 4;     // the plan needs shares of at least 4 blocks
 constexpr int kPairCost = 14;       // default fixed cost per pair in quarter blocks: the
                                     // dependent loads that start a segment
-// Consecutive share starts are at least 31 quarter blocks apart (4 T / ceil(T / 16) - 1
-// with T >= 16 blocks); a pair cost C with C + 4 <= 31 keeps every share non-empty.
+// The plan lowers the pair cost where shares are short (consecutive share starts lie at
+// least 4 T / W - 1 quarter blocks apart), so any cost up to this bound keeps every share
+// non-empty.
 constexpr int kMaxPairCost = 27;
 constexpr int kQ8Group = 32;        // values per scale in 8-bit caches
 
@@ -110,6 +111,7 @@ struct DecodeArgs {
     int32_t max_blocks, num_seqs, total_q_rows, max_seq_len, window;
     float scale;
     int32_t max_waves;                // decode wavefront workers launched
+    int32_t wave_round;               // wavefronts of one workgroup on every compute unit
     int32_t chunk_rows;               // query rows per chunk tile (0: chunk rows decode)
     int32_t max_tiles;                // chunk tiles the work list holds
     int32_t pair_cost;                // fixed cost of a (row, KV head) pair, quarter blocks

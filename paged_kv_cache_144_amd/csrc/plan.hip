@@ -119,6 +119,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
         const uint32_t mb = (uint32_t)a.min_blocks;
         W = (int)((T + mb - 1) / mb);
         W = W < 1 ? 1 : (W > a.max_waves ? a.max_waves : W);
+        // Whole rounds of one workgroup per compute unit: a partial round would put a
+        // second workgroup on a few units, whose shared bandwidth then sets the kernel's
+        // length (fewer, longer shares keep every property below).
+        if (W < a.max_waves && a.wave_round > 0 && W > a.wave_round)
+            W = W / a.wave_round * a.wave_round;
         const uint32_t room = (uint32_t)(4ull * T / (uint32_t)W);
         C = (uint32_t)a.pair_cost;
         if (W > 1) C = room >= C + 5 ? C : (room > 5 ? room - 5 : 0);

@@ -3,14 +3,16 @@ share sizes and worker counts, the shares it cuts are non-empty, consecutive, co
 block once, and each begins inside the pair its unit record names.  This is the property
 the decode and merge kernels rely on (a cut pair's contributors are the consecutive waves
 whose shares start before its end); the model follows the arithmetic of the plan kernel
-(csrc/plan.hip): weights 4 nb + C per pair, W = ceil(T / min_blocks) capped, the effective
+(csrc/plan.hip): weights 4 nb + C per pair, W = ceil(T / min_blocks) capped at the worker
+count and, below it and above one workgroup per compute unit, rounded down to whole such
+rounds, the effective
 pair cost C' = C while 4 T / W >= C + 5 (else 4 T / W - 5, at least 0), and share w starting
 at weighted position floor(w TW / W)."""
 import numpy as np
 import pytest
 
 
-def plan_split(nbs, heads, min_blocks, max_waves, pair_cost):
+def plan_split(nbs, heads, min_blocks, max_waves, pair_cost, wave_round=0):
     """Share starts wx0[0..W] and the unit of each share, as the plan kernel computes them.
     nbs: blocks per decode unit (row); each unit has `heads` pairs of that size."""
     nbs = np.asarray(nbs, np.int64)
@@ -21,6 +23,8 @@ def plan_split(nbs, heads, min_blocks, max_waves, pair_cost):
         return [0], []
     W = (T + min_blocks - 1) // min_blocks
     W = max(1, min(W, max_waves))
+    if W < max_waves and wave_round > 0 and W > wave_round:
+        W = W // wave_round * wave_round
     room = 4 * T // W
     C = pair_cost
     if W > 1:
@@ -51,8 +55,8 @@ def plan_split(nbs, heads, min_blocks, max_waves, pair_cost):
     return wx0, wu
 
 
-def check(nbs, heads, min_blocks, max_waves, pair_cost):
-    wx0, wu = plan_split(nbs, heads, min_blocks, max_waves, pair_cost)
+def check(nbs, heads, min_blocks, max_waves, pair_cost, wave_round=0):
+    wx0, wu = plan_split(nbs, heads, min_blocks, max_waves, pair_cost, wave_round)
     T = int(np.sum(nbs)) * heads
     assert wx0[0] == 0 and wx0[-1] == T
     # non-empty and consecutive: strictly increasing starts cover [0, T)
@@ -79,7 +83,8 @@ def test_shares_nonempty_random(min_blocks, pair_cost):
             nbs = np.rint(np.exp(rng.normal(3, 1.5, size=n))).astype(int)   # log-normal
         heads = int(rng.choice([1, 2, 4, 8]))
         max_waves = int(rng.choice([1, 3, 17, 64, 1024, 4096]))
-        check(nbs, heads, min_blocks, max_waves, pair_cost)
+        wave_round = int(rng.choice([0, 4, 12, 64]))
+        check(nbs, heads, min_blocks, max_waves, pair_cost, wave_round)
 
 
 def test_shares_edge_cases():
@@ -90,6 +95,17 @@ def test_shares_edge_cases():
     check([5], 1, 4, 4096, 27)             # T / W = 2.5 at the 4-block floor
     check([1] * 50, 8, 4, 4096, 27)        # only one-block pairs
     check([100000], 8, 16, 4096, 27)       # capped by the worker count
+    check([8312], 1, 12, 2048, 14, 1024)   # below one round: 693 shares, unrounded
+    check([8312], 1, 8, 2048, 14, 1024)    # 1039 shares rounded down to 1024
+    check([5000], 1, 4, 2048, 14, 1024)    # 1250 rounded to 1024: shares of 4.9 blocks
+
+
+def test_whole_rounds():
+    # the worker counts the rule gives: capped, unrounded below a round, whole rounds above
+    assert len(plan_split([100000], 8, 12, 4096, 14, 1024)[1]) == 4096
+    assert len(plan_split([8312], 1, 12, 2048, 14, 1024)[1]) == 693
+    assert len(plan_split([8312], 1, 8, 2048, 14, 1024)[1]) == 1024
+    assert len(plan_split([30000], 1, 12, 4096, 14, 1024)[1]) == 2048
 
 
 def test_effective_cost_is_needed():
