@@ -561,19 +561,26 @@ def test_small_windows(torch, pa, orc, g, d, dtype, window):
         assert np.array_equal(out[dec], ref[dec].astype(np.float32)), "one-token window"
 
 
-@pytest.mark.parametrize("g,d,dtype", [(1, 64, "f16"), (4, 128, "bf16")], ids=["lane", "mfma"])
-def test_one_long_sequence(torch, pa, orc, g, d, dtype):
-    """A 200,000-token context: its one (row, KV head) pair is cut into hundreds of shares,
-    and the merge combines more partials than a wavefront has lanes (several rounds)."""
-    w = workloads.make("rows", lens=[200_000, 3], rows=[1, 1], hq=g, hkv=1, d=d, dtype=dtype)
+@pytest.mark.parametrize("g,d,dtype,n", [(1, 64, "f16", 200_000), (4, 128, "bf16", 200_000),
+                                         (1, 64, "f16", 400_000)],
+                         ids=["lane", "mfma", "lane-400k"])
+def test_one_long_sequence(torch, pa, orc, g, d, dtype, n):
+    """A 200,000- or 400,000-token context: its one (row, KV head) pair is cut into more than
+    a thousand shares, and the merge combines more partials than a wavefront has lanes
+    (several rounds).  Above one workgroup per compute unit the share count is a whole
+    number of such rounds (12,500 and 25,000 blocks give 1,042 and 2,084 shares of 12,
+    rounded down)."""
+    w = workloads.make("rows", lens=[n, 3], rows=[1, 1], hq=g, hkv=1, d=d, dtype=dtype)
     dw = run(w, torch)
     ref = orc.Reference(w).attention()
     out = dw.decode().cpu().numpy()
     waves = int(dw.workspace[:32].cpu().view(torch.int32)[2])
     say("long sequence: shares", waves)
     assert waves > 2 * 64
+    per_round = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    assert waves <= per_round or waves % per_round == 0, (waves, per_round)
     assert pa.device_error_bits(dw.workspace) == 0
-    check_close(out, ref, f"one long sequence {dtype}")
+    check_close(out, ref, f"one long sequence {dtype} {n}")
 
 
 def test_chunk_rows_before_position_zero(torch, pa):
