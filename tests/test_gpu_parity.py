@@ -626,3 +626,30 @@ def test_chunk_rows_needle(torch, pa, orc, kw):
             say("needle mismatch seq %d tau %d row %d pos %d head %d maxdiff %.3g got %s want %s"
                 % b)
         assert not bad, f"{len(bad)} mismatches"
+
+
+@pytest.mark.parametrize("hq,dtype,rows", [(1, "f16", [1, 1, 1]), (4, "bf16", [1, 40, 1]),
+                                           (1, "q8_f16", [1, 1, 1])],
+                         ids=["lane-f16", "mfma-bf16-chunk", "lane-q8"])
+def test_blocks_past_4gib_of_the_pool(torch, pa, orc, hq, dtype, rows):
+    """Blocks handed out from the top of a pool of more than 4.5 GiB per cache, so every tile
+    read lies past the first 4 GiB: the output equals, bit for bit, that of the same
+    sequences in a small pool (where blocks sit changes no arithmetic), and the small pool's
+    output matches the oracle."""
+    import dataclasses
+    w = workloads.make("rows", lens=[300, 1000, 17], rows=rows, hq=hq, hkv=1, d=128,
+                       dtype=dtype)
+    small = run(w, torch)
+    ref = orc.Reference(w).attention()
+    out_small = small.decode().cpu().numpy()
+    check_close(out_small, ref, f"small pool {dtype}")
+    del small
+    tile = 16 * 128 * (2 if dtype in ("f16", "bf16") else 1) + (128 if dtype.startswith("q8") else 0)
+    nb = (9 << 29) // tile + 2                       # more than 4.5 GiB of tiles per cache
+    big = dataclasses.replace(w, num_blocks=nb,
+                              free_order=np.arange(nb - 2, -1, -1, dtype=np.int32))
+    dw = run(big, torch)
+    say("pool blocks", nb, "bytes per cache", nb * tile)
+    out_big = dw.decode().cpu().numpy()
+    assert pa.device_error_bits(dw.workspace) == 0
+    assert np.array_equal(out_big, out_small), np.abs(out_big - out_small).max()
