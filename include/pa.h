@@ -69,7 +69,8 @@ typedef enum pa_status {
     PA_ERR_OUT_OF_BLOCKS = -7,  /* ledger: not enough free blocks (nothing was taken)      */
     PA_ERR_SHARED_BLOCK = -8,   /* ledger: a copy-on-write or swap-out would read a block  *
                                  * that has writes pending in the current batch            */
-    PA_ERR_BAD_SEQ = -9         /* ledger: unknown sequence, or one that must be empty     */
+    PA_ERR_BAD_SEQ = -9,        /* ledger: unknown sequence, or one that must be empty     */
+    PA_ERR_ADMISSION = -10      /* ledger: a new request while sequences are swapped out   */
 } pa_status;
 
 /* Describes one layer's KV pool.  block_size must be 16 for the kernels (the pages'
@@ -281,7 +282,8 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* 
 void pa_pool_destroy(pa_pool* p);
 
 /* Keep only the last `window` tokens of `seq` (0 = keep all).  Must precede the first
- * append.  Later appends release blocks that fall wholly before the window (their table
+ * append.  Creates `seq` if it is unknown (PA_ERR_ADMISSION while sequences are swapped
+ * out).  Later appends release blocks that fall wholly before the window (their table
  * entries become -1) and report slot -1 for positions that are not kept. */
 pa_status pa_seq_set_window(pa_pool* p, int64_t seq, int32_t window);
 
@@ -305,7 +307,8 @@ pa_status pa_seq_set_window(pa_pool* p, int64_t seq, int32_t window);
  *
  * All or nothing: PA_ERR_OUT_OF_BLOCKS if the free blocks do not suffice for the copy and
  * the new blocks, PA_ERR_SHARED_BLOCK as above, PA_ERR_BAD_SEQ for a swapped-out
- * sequence; nothing changes on error. */
+ * sequence, PA_ERR_ADMISSION for an unknown `seq` while any sequence is swapped out (see
+ * the swapping section below); nothing changes on error. */
 pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slots_out);
 
 /* `dst` (new or empty) becomes a second sample of `src` (parallel sampling): the same
@@ -353,7 +356,8 @@ int32_t pa_pool_num_pending_copies(const pa_pool* p);
 
 /* `dst` (new or empty) begins with the first n_tokens of `src`, pointing at the same
  * physical blocks (each gets one more reference): a shared system prompt ("PagedAttention
- * deep dive", section on block sharing).  A prefix that ends inside a block shares that
+ * deep dive", section on block sharing).  An unknown dst is a new request:
+ * PA_ERR_ADMISSION while sequences are swapped out.  A prefix that ends inside a block shares that
  * block too; the first append of either sequence into it copies it (see pa_seq_append). */
 pa_status pa_seq_share_prefix(pa_pool* p, int64_t dst, int64_t src, int32_t n_tokens);
 

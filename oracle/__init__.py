@@ -27,7 +27,8 @@ import subprocess
 import numpy as np
 
 from . import q8  # noqa: F401
-from .ledger import Ledger, LedgerError, OutOfBlocks, SharedBlock, run_script  # noqa: F401
+from .ledger import (AdmissionClosed, Ledger, LedgerError, OutOfBlocks, SharedBlock,  # noqa: F401
+                     run_script)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pa_oracle.c")

@@ -22,6 +22,9 @@ What the pages fix, and where:
   * eviction is all-or-nothing per sequence, the victim is the sequence that arrived last,
     and swapping moves an evicted sequence's blocks to CPU memory until GPU memory frees
     up (same notes, scheduling section);
+  * while sequences sit in CPU memory no new request is taken; once finished requests free
+    GPU memory, the swapped sequences come back first (same section, Swapping under the
+    restoring strategies);
   * a sliding-window layer only keeps the most recent W tokens (sotaaz.com, section on
     layer kinds).
 
@@ -46,6 +49,11 @@ Readings where the pages are silent (each listed in the design notes):
     a free device block for each host block, all or nothing;
   * arrival: a sequence arrives when it is first created (append, fork, share or window);
     the victim is the resident sequence holding device blocks that arrived last;
+  * admission: while any sequence is swapped out, a call that would create a sequence for
+    a new request (append, share_prefix or set_window on an unknown id) is refused
+    (AdmissionClosed) and changes nothing; a fork is a further sample of a request already
+    taken, not a new request, and stays allowed; admission reopens as soon as no sequence
+    is swapped out (the last swap-in, or the swapped sequence being dropped);
   * with a window W, after an append of n tokens to a sequence of length c, positions
     before c+n-W are not kept: their slot is -1, a block lying wholly before that point is
     released (table entry -1) and one never allocated stays -1.
@@ -65,6 +73,10 @@ class OutOfBlocks(LedgerError):
 
 class SharedBlock(LedgerError):
     pass
+
+
+class AdmissionClosed(LedgerError):
+    """A new request while sequences are swapped out."""
 
 
 class Ledger:
@@ -134,7 +146,13 @@ class Ledger:
         if seq in self.swapped:
             raise LedgerError(f"seq {seq} is swapped out")
 
+    def _admit(self, seq: int) -> None:
+        """A new request waits while any sequence is swapped out."""
+        if self.swapped and seq not in self.table:
+            raise AdmissionClosed(f"seq {seq}: {len(self.swapped)} sequence(s) swapped out")
+
     def set_window(self, seq: int, window: int) -> None:
+        self._admit(seq)
         self._create(seq)
         self.window[seq] = int(window)
 
@@ -161,6 +179,7 @@ class Ledger:
     def append(self, seq: int, n: int) -> list[int]:
         """Append n tokens; return the slot of each (block * bs + offset, or -1)."""
         self._resident(seq)
+        self._admit(seq)
         self._create(seq)
         tab = self.table[seq]
         cur = self.length[seq]
@@ -222,6 +241,7 @@ class Ledger:
         self._resident(src)
         if self.table.get(dst) or dst in self.swapped:
             raise LedgerError(f"seq {dst} is not empty")
+        self._admit(dst)
         if n_tokens > self.length.get(src, 0):
             raise LedgerError("prefix longer than source")
         nblk = -(-n_tokens // self.bs)

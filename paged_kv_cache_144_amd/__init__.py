@@ -26,7 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_F32, PA_F16, PA_BF16, PA_Q8_F16, PA_Q8_BF16 = 0, 1, 2, 3, 4
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_LAUNCH",
-          -7: "PA_ERR_OUT_OF_BLOCKS", -8: "PA_ERR_SHARED_BLOCK", -9: "PA_ERR_BAD_SEQ"}
+          -7: "PA_ERR_OUT_OF_BLOCKS", -8: "PA_ERR_SHARED_BLOCK", -9: "PA_ERR_BAD_SEQ",
+          -10: "PA_ERR_ADMISSION"}
 BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares

@@ -145,6 +145,7 @@ const char* pa_status_string(pa_status s) {
         case PA_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
         case PA_ERR_SHARED_BLOCK: return "copy-on-write would read a block with pending writes";
         case PA_ERR_BAD_SEQ: return "unknown or non-empty sequence";
+        case PA_ERR_ADMISSION: return "no new request while sequences are swapped out";
     }
     return "unknown status";
 }

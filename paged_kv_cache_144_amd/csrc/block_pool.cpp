@@ -9,8 +9,13 @@
 // sequences referencing a block and copies a shared block when samples write different
 // tokens into it, while earlier blocks stay shared (parallel sampling), and evicts all of
 // a sequence or none of it, the latest arrival first, moving its blocks to CPU memory until
-// there is room again (scheduling).  A sliding-window layer keeps only its last W tokens
-// (sotaaz.com, section on layer kinds).
+// there is room again, and takes no new request while any sequence sits in CPU memory
+// (scheduling, Swapping among the restoring strategies).  A sliding-window layer keeps only
+// its last W tokens (sotaaz.com, section on layer kinds).
+//
+// Admission: a call that would create a sequence for a new request (append, share_prefix,
+// set_window on an unknown id) returns PA_ERR_ADMISSION while a sequence is swapped out.
+// A fork is a further sample of a request already taken and stays allowed.
 //
 // Batches: the caller carries out one batch's work in the order swap-outs, copies,
 // swap-ins, slot writes (each kind all at once) and ends the batch with
@@ -64,7 +69,12 @@ struct pa_pool {
     std::deque<int32_t> host_free;
     std::vector<int32_t> host_quarantine;
     int64_t clock = 0;
+    int64_t num_swapped = 0;           // sequences whose blocks are in host memory
 
+    // a new request waits while any sequence is swapped out
+    bool admission_closed(int64_t seq) const {
+        return num_swapped > 0 && seqs.find(seq) == seqs.end();
+    }
     bool busy(int32_t b) const { return touched[b] || copy_src[b]; }
     void release(int32_t b) {
         if (--ref[b] != 0) return;
@@ -147,6 +157,7 @@ void pa_pool_destroy(pa_pool* p) { delete p; }
 pa_status pa_seq_set_window(pa_pool* p, int64_t seq, int32_t window) {
     if (!p) return PA_ERR_NULL;
     if (window < 0) return PA_ERR_SHAPE;
+    if (p->admission_closed(seq)) return PA_ERR_ADMISSION;
     Seq& s = p->create(seq);
     if (s.len != 0 || s.swapped) return PA_ERR_BAD_SEQ;
     s.window = window;
@@ -160,6 +171,7 @@ pa_status pa_seq_append(pa_pool* p, int64_t seq, int32_t n_tokens, int64_t* slot
         auto it = p->seqs.find(seq);
         if (it != p->seqs.end() && it->second.swapped) return PA_ERR_BAD_SEQ;
     }
+    if (p->admission_closed(seq)) return PA_ERR_ADMISSION;
     Seq& s = p->create(seq);
     const int64_t bs = p->bs;
     const int64_t cur = s.len, end = cur + n_tokens;
@@ -333,6 +345,7 @@ pa_status pa_seq_swap_out(pa_pool* p, int64_t seq, int32_t* pairs, int32_t cap, 
         s.blocks[i] = -1;
     }
     s.swapped = true;
+    ++p->num_swapped;
     return PA_OK;
 }
 
@@ -364,6 +377,7 @@ pa_status pa_seq_swap_in(pa_pool* p, int64_t seq, int32_t* pairs, int32_t cap, i
     }
     s.host.clear();
     s.swapped = false;
+    --p->num_swapped;
     return PA_OK;
 }
 
@@ -377,6 +391,7 @@ pa_status pa_seq_share_prefix(pa_pool* p, int64_t dst, int64_t src, int32_t n_to
     if (dit != p->seqs.end() &&
         (dit->second.len != 0 || !dit->second.blocks.empty() || dit->second.swapped))
         return PA_ERR_BAD_SEQ;
+    if (p->admission_closed(dst)) return PA_ERR_ADMISSION;
     const int64_t nblk = (n_tokens + p->bs - 1) / p->bs;
     const std::vector<int32_t>& sb = it->second.blocks;
     for (int64_t i = 0; i < nblk; ++i)
@@ -397,6 +412,7 @@ pa_status pa_seq_free(pa_pool* p, int64_t seq) {
         if (b >= 0) p->release(b);
     for (int32_t h : it->second.host)
         if (h >= 0) p->host_quarantine.push_back(h);
+    if (it->second.swapped) --p->num_swapped;
     p->seqs.erase(it);
     return PA_OK;
 }

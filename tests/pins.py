@@ -314,19 +314,67 @@ def pin_swap_ledger(orc):
     assert led.latest_resident() == "d" and led.swap_out("d") == []
     assert all(led.refcount(x) == 2 for x in led.block_table("a"))
     assert led.swap_in("d") == []
-    # swap-in needs a free device block per host block, all or nothing
+    # swap-in needs a free device block per host block, all or nothing; a resident
+    # sequence ("c", one full block) takes every free block first
     led.swap_out("b")
     led.take_copies()
-    led.append("e", 4 * led.num_free())
+    led.append("c", 4 * led.num_free())
     try:
         led.swap_in("b")
     except orc.OutOfBlocks:
         pass
     else:
         raise AssertionError("swap-in without free blocks accepted")
-    led.free_seq("e")
+    led.free_seq("c")
     led.take_copies()
     assert len(led.swap_in("b")) == 2
+
+
+def pin_swap_admission(orc):
+    # "vLLM and PagedAttention" notes, scheduling, Swapping: while sequences evicted to CPU
+    # memory are away, no new request is taken; when finished requests free GPU memory the
+    # evicted sequences come back first
+    led = orc.Ledger(range(10), 4, host_blocks=4)
+    led.append("a", 5)                     # blocks 0, 1
+    led.append("b", 3)                     # block 2
+    led.append("c", 6)                     # blocks 3, 4
+    led.take_copies()
+    assert led.swap_out(led.latest_resident()) == [(3, 0), (4, 1)]     # "c" leaves
+    led.take_copies()
+    state = lambda: (led.num_free(), led.num_host_free(), led.block_table("a"),
+                     led.block_table("b"), led.latest_resident())
+    before = state()
+    refused = 0
+    for call in (lambda: led.append("n", 1), lambda: led.append("n", 0),
+                 lambda: led.share_prefix("n", "a", 4), lambda: led.set_window("n", 4)):
+        try:
+            call()
+        except orc.AdmissionClosed:
+            refused += 1
+    assert refused == 4 and state() == before
+    assert led.block_table("n") == [] and led.seq_len("n") == 0
+    # admitted requests go on: a resident appends and a further sample is forked
+    led.append("a", 3)
+    led.fork("a2", "a")
+    led.take_copies()
+    # a resident finishes; the evicted sequence comes back before anyone new
+    led.free_seq("b")
+    led.take_copies()
+    assert len(led.swap_in("c")) == 2
+    led.append("n", 2)                     # admission has reopened
+    assert led.latest_resident() == "n"
+    # dropping the only swapped-out sequence reopens admission as well
+    led.take_copies()
+    led.swap_out("n")
+    try:
+        led.append("m", 1)
+    except orc.AdmissionClosed:
+        pass
+    else:
+        raise AssertionError("new request taken while a sequence is swapped out")
+    led.free_seq("n")
+    led.append("m", 1)
+    assert led.block_table("m") != []
 
 
 def pin_batch_reuse(orc):
@@ -352,8 +400,9 @@ def pin_batch_reuse(orc):
 
 
 def pin_swap_attention(orc):
-    # after evictions, newcomers in the freed blocks and swap-ins, every sequence attends
-    # over exactly its own tokens (unwritten and free slots hold NaN)
+    # after evictions, residents growing into the freed blocks, finished requests leaving
+    # and swap-ins, every sequence attends over exactly its own tokens (unwritten and free
+    # slots hold NaN)
     w = workloads.make("swap", batch=10, victims=3, lo=5, hi=70, hq=4, hkv=2, d=64)
     ref = orc.Reference(w)
     got = ref.attention()
@@ -708,7 +757,7 @@ def pin_nan_isolation(orc):
 ALL = [pin_kv_bytes, pin_kv_totals, pin_kv_q8_bytes, pin_kv_read_bytes, pin_q8_grid,
        pin_q8_rounding, pin_q8_paged, pin_blocks_and_waste, pin_walkthrough,
        pin_parallel_sampling, pin_cow_rules, pin_cow_attention, pin_swap_ledger,
-       pin_batch_reuse, pin_swap_attention, pin_block_sizes, pin_all_or_nothing, pin_window_ledger, pin_widen, pin_write_kv,
+       pin_swap_admission, pin_batch_reuse, pin_swap_attention, pin_block_sizes, pin_all_or_nothing, pin_window_ledger, pin_widen, pin_write_kv,
        pin_one_token, pin_uniform, pin_two_tokens, pin_needle, pin_contiguous, pin_permutation,
        pin_sdpa, pin_brute, pin_window, pin_chunk_rows, pin_shared_prefix, pin_gqa_mapping,
        pin_nan_isolation]

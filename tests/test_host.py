@@ -117,6 +117,8 @@ class PoolAdapter:
                 raise SharedBlock() from None
             if e.code == -9:
                 raise LedgerError() from None
+            if e.code == -10:
+                raise AdmissionClosed() from None
             raise
 
     def append(self, seq, n):
@@ -136,7 +138,7 @@ class PoolAdapter:
         return self._pool.num_host_free()
 
     def share_prefix(self, dst, src, n):
-        self._pool.share_prefix(self._id(dst), self._id(src), n)
+        self._call(self._pool.share_prefix, self._id(dst), self._id(src), n)
 
     def fork(self, dst, src):
         self._call(self._pool.fork, self._id(dst), self._id(src))
@@ -145,10 +147,10 @@ class PoolAdapter:
         return [tuple(int(x) for x in row) for row in self._pool.take_copies()]
 
     def free_seq(self, seq):
-        self._pool.free(self._id(seq))
+        self._call(self._pool.free, self._id(seq))
 
     def set_window(self, seq, w):
-        self._pool.set_window(self._id(seq), w)
+        self._call(self._pool.set_window, self._id(seq), w)
 
     def block_table(self, seq):
         if seq not in self._names or self._pool.seq_len(self._id(seq)) < 0:
@@ -181,18 +183,24 @@ class SharedBlock(LedgerError):
     pass
 
 
+class AdmissionClosed(LedgerError):
+    pass
+
+
 class _PoolAsOracle:
     def __init__(self, pa):
         self.Ledger = lambda free_order, block_size=16, host_blocks=0: PoolAdapter(
             pa, free_order, block_size, host_blocks)
         self.OutOfBlocks = OutOfBlocks
         self.SharedBlock = SharedBlock
+        self.AdmissionClosed = AdmissionClosed
         self.LedgerError = LedgerError
 
 
 @pytest.mark.parametrize("pin", [pins.pin_blocks_and_waste, pins.pin_walkthrough,
                                  pins.pin_parallel_sampling, pins.pin_cow_rules,
-                                 pins.pin_swap_ledger, pins.pin_batch_reuse,
+                                 pins.pin_swap_ledger, pins.pin_swap_admission,
+                                 pins.pin_batch_reuse,
                                  pins.pin_all_or_nothing,
                                  pins.pin_window_ledger], ids=lambda f: f.__name__)
 def test_pool_pins(pa, pin):
@@ -268,7 +276,7 @@ def test_pool_random_scripts_match_oracle(pa, orc, seed):
     led = orc.Ledger(order, 4, nh)
     pool = pa.Pool(nb, 4, order)
     pool.set_host_blocks(nh)
-    codes = {-7: "OutOfBlocks", -8: "SharedBlock", -9: "LedgerError"}
+    codes = {-7: "OutOfBlocks", -8: "SharedBlock", -9: "LedgerError", -10: "AdmissionClosed"}
 
     def both(f_led, f_pool, conv=lambda x: x):
         try:
@@ -303,10 +311,10 @@ def test_pool_random_scripts_match_oracle(pa, orc, seed):
             src = int(rng.choice(live))
             n = int(rng.integers(0, led.seq_len(src) + 1))
             if all(b >= 0 for b in led.block_table(src)[:-(-n // 4)]):
-                led.share_prefix(next_id, src, n)
-                pool.share_prefix(next_id, src, n)
-                live.append(next_id)
-                next_id += 1
+                if both(lambda: led.share_prefix(next_id, src, n),
+                        lambda: pool.share_prefix(next_id, src, n)):
+                    live.append(next_id)
+                    next_id += 1
         elif r < 0.63:
             pick = live + swapped
             seq = pick[int(rng.integers(0, len(pick)))]
@@ -314,10 +322,10 @@ def test_pool_random_scripts_match_oracle(pa, orc, seed):
             led.free_seq(seq)
             pool.free(seq)
         elif r < 0.65:
-            led.set_window(next_id, int(rng.integers(1, 12)))
-            pool.set_window(next_id, led.window[next_id])
-            live.append(next_id)
-            next_id += 1
+            win = int(rng.integers(1, 12))
+            if both(lambda: led.set_window(next_id, win), lambda: pool.set_window(next_id, win)):
+                live.append(next_id)
+                next_id += 1
         elif r < 0.73:
             assert pool.latest_resident() == led.latest_resident()
             seq = led.latest_resident() if rng.random() < 0.5 else int(rng.choice(live))

@@ -58,6 +58,7 @@ PY_MUTANTS = {
     "no_quarantine": ("(self.quarantine if self._busy(block) else self.free)", "self.free"),
     "host_reuse_now": ("                self.host_quarantine.append(h)\n        del self.swapped[seq]",
                        "                self.host_free.append(h)\n        del self.swapped[seq]"),
+    "admit_while_swapped": ("if self.swapped and seq not in self.table:", "if False:"),
     "fork_no_ref": ("                self.ref[b] += 1\n        self._create(dst)\n        self.table[dst] = tab",
                     "                pass\n        self._create(dst)\n        self.table[dst] = tab"),
 }
@@ -110,7 +111,8 @@ def test_ledger_mutant_caught(orc, tmp_path, monkeypatch, name):
     spec = importlib.util.spec_from_file_location("ledger_mut", path)
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
-    for attr in ("Ledger", "SharedBlock", "OutOfBlocks", "LedgerError", "run_script"):
+    for attr in ("Ledger", "SharedBlock", "OutOfBlocks", "LedgerError", "AdmissionClosed",
+                 "run_script"):
         monkeypatch.setattr(orc, attr, getattr(mod, attr))
     failed = _fails_some_pin(orc)
     assert failed, f"planted mistake {name} passed every pin"

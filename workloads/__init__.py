@@ -289,8 +289,8 @@ def make(name: str, seed: int | None = None, **over) -> Workload:
 
     Keyword overrides shrink a workload for fast parity runs while keeping its structure:
       batch=, lo=, hi= (length range), median= / sigma= (log-normal), prefix=, chunks=,
-      chunk_rows=, chunk_lo=, chunk_hi=, window=, prompts= / samples= / plens=, victims=,
-      dtype= (including the 8-bit cache names "q8_f16" and "q8_bf16").
+      chunk_rows=, chunk_lo=, chunk_hi=, window=, prompts= / samples= / plens=, victims= /
+      finishers= / grow_hi=, dtype= (including the 8-bit cache names "q8_f16" and "q8_bf16").
     """
     if name == "tiny":
         seed = 1 if seed is None else seed
@@ -430,34 +430,51 @@ def make(name: str, seed: int | None = None, **over) -> Workload:
         return w
 
     if name == "swap":
-        # OPT-13B shape under memory pressure: every sequence is prefilled; the `victims`
-        # that arrived last are swapped out, the same number of newcomers run in the freed
-        # blocks and leave, the victims are swapped back in (earliest arrival first) and
-        # every sequence appends its next token
+        # OPT-13B shape under memory pressure ("vLLM and PagedAttention" notes, scheduling):
+        # `batch` sequences and `finishers` short-lived requests are prefilled, the
+        # short-lived ones spread among the first arrivals.  The `victims` batch sequences
+        # that arrived last are swapped out.  While they are away no new request is taken:
+        # the residents go on decoding (U{1..grow_hi} tokens each) into the freed blocks and
+        # the short-lived requests finish and leave.  Then the victims come back (earliest
+        # arrival first) and every batch sequence appends its next token.
         seed = 8 if seed is None else seed
         rng = np.random.default_rng(np.random.SeedSequence(entropy=seed, spawn_key=(0,)))
         bs = 16
         B = over.get("batch", 64)
         V = over.get("victims", 8)
+        F = over.get("finishers", V)
         hq, hkv, d = over.get("hq", 40), over.get("hkv", 40), over.get("d", 128)
-        lens = rng.integers(over.get("lo", 64), over.get("hi", 2048) + 1, size=B)
-        need = int(sum(-(-int(L) // bs) for L in lens)) + B
+        lo, hi = over.get("lo", 64), over.get("hi", 2048)
+        lens = rng.integers(lo, hi + 1, size=B)
+        flens = rng.integers(lo, hi + 1, size=F)
+        # creation order: residents with the short-lived requests spread among them, then
+        # the victims
+        order = list(range(B - V))
+        for k in range(F):
+            order.insert((k + 1) * (B - V) // (F + 1) + k, B + k)
+        order += list(range(B - V, B))
+        plen = {s_: int(lens[s_]) for s_ in range(B)}
+        plen.update({B + k: int(flens[k]) for k in range(F)})
+        residents = [s_ for s_ in order if not B - V <= s_ < B]
+        grow = dict(zip(residents, rng.integers(1, over.get("grow_hi", 32) + 1,
+                                                size=len(residents)).tolist()))
+        need = (sum(-(-n // bs) for n in plen.values())
+                + sum(-(-g // bs) + 1 for g in grow.values()) + B)
         nb = _pool_size(need)
         free_order = rng.permutation(nb - 1).astype(np.int32)
         script, off = [], 0
-        for s_ in range(B):
-            script.append(Append(s_, int(lens[s_]), int(lens[s_]), off))
-            off += int(lens[s_])
+        for s_ in order:
+            script.append(Append(s_, plen[s_], plen[s_], off))
+            off += plen[s_]
         script.append(Flush())
         for _ in range(V):
             script.append(SwapOut(None))
         script.append(Flush())
-        for k in range(V):                     # newcomers as long as the victims
-            n = int(lens[B - 1 - k])
-            script.append(Append(B + k, n, n, off))
-            off += n
+        for s_ in residents:
+            script.append(Append(s_, grow[s_], grow[s_], off))
+            off += grow[s_]
         script.append(Flush())
-        for k in range(V):
+        for k in range(F):
             script.append(Free(B + k))
         script.append(Flush())
         for k in range(V):
@@ -470,11 +487,12 @@ def make(name: str, seed: int | None = None, **over) -> Workload:
         dt = over.get("dtype", "f16")
         k_, v_ = _values(seed, off, hkv, d, dt)
         q = _queries(seed, B, hq, d, dt)
+        final = np.array([plen[s_] + grow.get(s_, 0) + 1 for s_ in range(B)], np.int32)
         host = int(sum(-(-int(L) // bs) for L in lens[B - V:]))
-        w = Workload("swap", seed, dt, hq, hkv, d, bs, nb, (lens + 1).astype(np.int32),
+        w = Workload("swap", seed, dt, hq, hkv, d, bs, nb, final,
                      np.ones(B, np.int32), 0, np.float32(1.0 / math.sqrt(d)),
                      over.get("layers", 40), free_order, script, k_, v_, q)
-        w.meta.update(host_blocks=host, victims=V)
+        w.meta.update(host_blocks=host, victims=V, finishers=F)
         return w
 
     if name == "rows":
