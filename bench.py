@@ -87,6 +87,36 @@ def measured_traffic(key: str, files=KERNEL_SOURCES):
     return e.get("hbm_bytes_per_launch")
 
 
+# ------------------------------------------------------------------ work accounting
+def kv_bytes_read(seq_lens, q_rows, window, num_kv_heads, head_dim, elem_bytes) -> int:
+    """Algorithmic KV bytes one attention layer reads: every attended position once, K and V,
+    per KV head (a sliding window caps the positions a row can see).  elem_bytes is the
+    cache's bytes per element: 4, 2, or 17/16 for an 8-bit cache (a 2-byte scale per 32
+    one-byte codes)."""
+    import numpy as np
+    total = 0
+    for L, n in zip(np.asarray(seq_lens).tolist(), np.asarray(q_rows).tolist()):
+        first = L - n                       # position of the first query row
+        lo = max(0, first - window + 1) if window > 0 else 0
+        total += max(0, L - lo)
+    return int(round(2 * num_kv_heads * head_dim * elem_bytes * total))
+
+
+def chunk_flops(seq_lens, q_rows, window, num_q_heads, head_dim) -> int:
+    """Algorithmic FLOPs of the chunk rows (sequences with more than one query row): per row,
+    per query head, per attended token, 2 * head_dim for q.K and 2 * head_dim for p.V."""
+    import numpy as np
+    total = 0
+    for L, n in zip(np.asarray(seq_lens).tolist(), np.asarray(q_rows).tolist()):
+        if n < 2:
+            continue
+        for r in range(n):
+            p = L - n + r
+            lo = max(0, p - window + 1) if window > 0 else 0
+            total += max(0, p - lo + 1)
+    return 4 * head_dim * num_q_heads * total
+
+
 def step_rows(w):
     """Value rows of each sequence's newest q_rows tokens (this step's writes)."""
     import numpy as np
@@ -110,7 +140,6 @@ def cpu_baseline(w, n_layers, seconds):
     import numpy as np
 
     import oracle
-    import paged_kv_cache_144_amd as pa
     ref = oracle.Reference(w, poison=False)
     threads = len(os.sched_getaffinity(0))
     order = np.random.default_rng(0).permutation(w.num_seqs)
@@ -121,8 +150,8 @@ def cpu_baseline(w, n_layers, seconds):
     while True:
         chunk = order[i:i + 8]
         ref.attention(seqs=chunk)
-        done_bytes += pa.kv_bytes_read(w.seq_lens[chunk], w.q_rows[chunk], w.window,
-                                       w.num_kv_heads, w.head_dim, w.elem_bytes)
+        done_bytes += kv_bytes_read(w.seq_lens[chunk], w.q_rows[chunk], w.window,
+                                    w.num_kv_heads, w.head_dim, w.elem_bytes)
         done_rows += int(w.q_rows[chunk].sum())
         i += 8
         if i >= w.num_seqs:
@@ -139,8 +168,8 @@ def cpu_baseline(w, n_layers, seconds):
     while time.perf_counter() - t1 < min(3.0, seconds):
         chunk = order[j:j + 1]
         ref.attention(seqs=chunk)
-        one_bytes += pa.kv_bytes_read(w.seq_lens[chunk], w.q_rows[chunk], w.window,
-                                      w.num_kv_heads, w.head_dim, w.elem_bytes)
+        one_bytes += kv_bytes_read(w.seq_lens[chunk], w.q_rows[chunk], w.window,
+                                   w.num_kv_heads, w.head_dim, w.elem_bytes)
         j = (j + 1) % w.num_seqs
     one_el = time.perf_counter() - t1
     ref.threads = 0
@@ -353,8 +382,8 @@ def main():
     slot_step = dw.slot_mapping.index_select(0, rows).contiguous()
     out = torch.empty((w.total_q_rows, w.num_q_heads, w.head_dim), dtype=torch.float32,
                       device="cuda")
-    kv_layer = pa.kv_bytes_read(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim,
-                                w.elem_bytes)
+    kv_layer = kv_bytes_read(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim,
+                             w.elem_bytes)
     held = sum(len([b for b in dw.pool.block_table(s) if b >= 0]) for s in range(w.num_seqs))
     waste = 1.0 - min(int(w.seq_lens.sum()), held * w.block_size) / max(1, held * w.block_size)
     qsl = dw.qsl if dw.uses_rows else None
@@ -432,8 +461,8 @@ def main():
     value = kv_layer * L / step_s / 1e9
     tokens_per_s = w.total_q_rows / step_s
     dec = w.q_rows == 1
-    kv_decode = pa.kv_bytes_read(w.seq_lens[dec], w.q_rows[dec], w.window, w.num_kv_heads,
-                                 w.head_dim, w.elem_bytes)
+    kv_decode = kv_bytes_read(w.seq_lens[dec], w.q_rows[dec], w.window, w.num_kv_heads,
+                              w.head_dim, w.elem_bytes)
     achieved = kv_decode / (dec_avg_ms / 1e3) / 1e9
     traffic = (measured_traffic(args.workload + ("_q8" if args.kv == "q8" else ""))
                if args.block_size == 16 else None)
@@ -451,7 +480,7 @@ def main():
     }
     chunk_roof = None
     if has_chunks:
-        flops = pa.chunk_flops(w.seq_lens, w.q_rows, w.window, w.num_q_heads, w.head_dim)
+        flops = chunk_flops(w.seq_lens, w.q_rows, w.window, w.num_q_heads, w.head_dim)
         tflops = flops / (chunk_avg_ms / 1e3) / 1e12
         peak = MFMA_PEAK_TFLOPS[w.dtype]
         # the chunks' K/V, each (token, KV head) once: what the kernel must read at least

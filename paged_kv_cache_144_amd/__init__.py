@@ -281,13 +281,32 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, *, max_seq_len,
     plan in `workspace`), step="both" pa_decode."""
     torch = _torch()
     lib = load()
+    if q.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2:
+        raise ValueError("q is [R][Hq][d], the caches [NB][Hkv][rows][d], block_tables [B][MB]")
     R, hq, d = q.shape
     B, mb = block_tables.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache in shape and dtype")
+    if d != k_cache.shape[3]:
+        raise ValueError(f"q has head_dim {d}, the cache {k_cache.shape[3]}")
+    if hq % k_cache.shape[1]:
+        raise ValueError(f"{hq} query heads are not a multiple of {k_cache.shape[1]} KV heads")
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
+                    (seq_lens, "seq_lens"), (query_start_loc, "query_start_loc"),
+                    (workspace, "workspace"), (out, "out")):
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
     if seq_lens.numel() != B:
         raise ValueError("seq_lens length")
     if query_start_loc is not None and query_start_loc.numel() != B + 1:
         raise ValueError("query_start_loc length")
     _check_act(q, k_cache, "q")
+    if out is not None:
+        if tuple(out.shape) != (R, hq, d):
+            raise ValueError(f"out must be [{R}][{hq}][{d}], got {list(out.shape)}")
+        _dtype_code(out)
+        if out_dtype is not None and out.dtype != out_dtype:
+            raise TypeError(f"out is {out.dtype}, out_dtype {out_dtype}")
     if out is None:
         out = torch.empty((R, hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if workspace is None:
@@ -450,31 +469,3 @@ class Pool:
 
     def refcount(self, block) -> int:
         return int(self._lib.pa_block_refcount(self._h, block))
-
-
-# ------------------------------------------------------------------ work accounting
-def kv_bytes_read(seq_lens, q_rows, window, num_kv_heads, head_dim, elem_bytes) -> int:
-    """Algorithmic KV bytes one attention layer reads: every attended position once, K and V,
-    per KV head (a sliding window caps the positions a row can see).  elem_bytes is the
-    cache's bytes per element: 4, 2, or 17/16 for an 8-bit cache (a 2-byte scale per 32
-    one-byte codes)."""
-    total = 0
-    for L, n in zip(np.asarray(seq_lens).tolist(), np.asarray(q_rows).tolist()):
-        first = L - n                       # position of the first query row
-        lo = max(0, first - window + 1) if window > 0 else 0
-        total += max(0, L - lo)
-    return int(round(2 * num_kv_heads * head_dim * elem_bytes * total))
-
-
-def chunk_flops(seq_lens, q_rows, window, num_q_heads, head_dim) -> int:
-    """Algorithmic FLOPs of the chunk rows (sequences with more than one query row): per row,
-    per query head, per attended token, 2 * head_dim for q.K and 2 * head_dim for p.V."""
-    total = 0
-    for L, n in zip(np.asarray(seq_lens).tolist(), np.asarray(q_rows).tolist()):
-        if n < 2:
-            continue
-        for r in range(n):
-            p = L - n + r
-            lo = max(0, p - window + 1) if window > 0 else 0
-            total += max(0, p - lo + 1)
-    return 4 * head_dim * num_q_heads * total

@@ -373,9 +373,11 @@ def test_pool_errors(pa):
                                      ("prefix_mixed", dict(batch=4, chunks=2, chunk_rows=7)),
                                      ("swa", dict(batch=4)), ("opt13b", dict(dtype="q8_f16")),
                                      ("swa", dict(batch=4, dtype="q8_f16"))])
-def test_kv_bytes_matches_oracle(pa, orc, name, kw):
+def test_kv_bytes_matches_oracle(orc, name, kw):
+    """The benchmark's byte accounting (its metric's numerator) against the oracle's."""
+    import bench
     w = workloads.make(name, **kw)
-    a = pa.kv_bytes_read(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim,
+    a = bench.kv_bytes_read(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim,
                          w.elem_bytes)
     if w.dtype in workloads.ACT:
         b = orc.kv_read_bytes(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim, 1,
@@ -384,3 +386,51 @@ def test_kv_bytes_matches_oracle(pa, orc, name, kw):
         b = orc.kv_read_bytes(w.seq_lens, w.q_rows, w.window, w.num_kv_heads, w.head_dim,
                               w.elem_bytes)
     assert a == b
+
+
+class _NoCalls:
+    """Stands in for libpa.so: any use of an entry point fails the test."""
+
+    def __getattr__(self, name):
+        raise AssertionError(f"{name} was called although the arguments were inconsistent")
+
+
+@pytest.mark.parametrize("case", ["consistent", "q_head_dim", "v_shape", "v_dtype", "out_shape", "out_dtype",
+                                  "out_dtype_arg", "heads", "q_dtype", "tables_dim"])
+def test_decode_rejects_mismatch_before_any_call(pa, monkeypatch, case):
+    """decode() checks q, the two caches and out against each other before it reaches the
+    library: a q with the wrong head_dim would otherwise be read past its end and an out
+    sized for it written past its end."""
+    import torch
+    monkeypatch.setattr(pa, "_lib", _NoCalls())
+    f16 = torch.float16
+    kc = torch.zeros(8, 2, 16, 128, dtype=f16)
+    args = dict(q=torch.zeros(3, 4, 128, dtype=f16), k_cache=kc, v_cache=torch.zeros_like(kc),
+                block_tables=torch.zeros(3, 2, dtype=torch.int32),
+                seq_lens=torch.ones(3, dtype=torch.int32),
+                workspace=torch.zeros(1024, dtype=torch.uint8))
+    kw = {}
+    if case == "q_head_dim":
+        args["q"] = torch.zeros(3, 4, 64, dtype=f16)
+    elif case == "v_shape":
+        args["v_cache"] = torch.zeros(8, 2, 16, 64, dtype=f16)
+    elif case == "v_dtype":
+        args["v_cache"] = torch.zeros_like(kc, dtype=torch.bfloat16)
+    elif case == "out_shape":
+        kw["out"] = torch.zeros(3, 4, 64)
+    elif case == "out_dtype":
+        kw["out"] = torch.zeros(3, 4, 128, dtype=torch.float64)
+    elif case == "out_dtype_arg":
+        kw["out"] = torch.zeros(3, 4, 128)
+        kw["out_dtype"] = torch.float16
+    elif case == "heads":
+        args["q"] = torch.zeros(3, 3, 128, dtype=f16)
+    elif case == "q_dtype":
+        args["q"] = torch.zeros(3, 4, 128, dtype=torch.bfloat16)
+    elif case == "tables_dim":
+        args["block_tables"] = torch.zeros(6, dtype=torch.int32)
+    ws = args.pop("workspace")
+    with pytest.raises((ValueError, TypeError)) as e:
+        pa.decode(*args.values(), 0.1, max_seq_len=16, workspace=ws, **kw)
+    # consistent host tensors pass every check and stop only at the device-pointer step
+    assert ("device tensor" in str(e.value)) == (case == "consistent")
