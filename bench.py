@@ -15,13 +15,18 @@ bandwidth on the decode rows' KV bytes, or, when chunked-prefill rows dominate, 
 kernel against the dense MFMA peak on its FLOPs.  `cpu_baseline` is the fp64 CPU oracle
 timed on the host cores on a bounded sample of the same workload.
 
+The default run measures two shapes. The OPT-13B shape gives the
+line's `value`, `roofline` and `cpu_baseline`, and the Qwen3-8B / Mistral-7B GQA shape is
+measured after it with the same steps and reported under the key "gqa" with its own value,
+roofline (kernel named as dispatched), counter traffic and CPU baseline.
+
 In the parallel-sampling workload each layer's step also carries out the copy-on-write
 copies of the first decode step after the fork (pa_copy_blocks) before the slot write; the
 copy kernel is reported in `roofline_copy`.
 
   python bench.py [--steps K] [--warmup W]
                   [--workload opt13b|gqa|prefix_mixed|swa|parallel_sampling|tiny]
-                  [--kv native|q8]
+                  [--also W,...|none] [--kv native|q8]
 """
 from __future__ import annotations
 
@@ -305,35 +310,14 @@ def time_swap(pa, dw, pools, n_seqs):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="opt13b", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--layers", type=int, default=None, help="default: the workload's")
-    ap.add_argument("--block-size", type=int, choices=[8, 16, 32], default=16,
-                    help="tokens per KV block (8 and 32: OPT-13B and GQA shapes, 16-bit KV)")
-    ap.add_argument("--kv", choices=["native", "q8"], default="native",
-                    help="q8: 8-bit KV cache (one fp16 scale per 32 values), same workload")
-    ap.add_argument("--event-every", type=int, default=4, metavar="N",
-                    help="kernel durations come from hipEvents recorded around the launches "
-                         "of every N-th layer of each timed step (each recorded event adds a "
-                         "few microseconds of queue gap, which N = 1 would add to every layer)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--swap-seqs", type=int, default=0, metavar="N",
-                    help="after the timed steps, also time evicting the N sequences that "
-                         "arrived last to pinned host memory and bringing them back")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
-                    help="only run a plain device copy of this size (counter calibration)")
-    args = ap.parse_args()
+# keys of the contract line that a secondary workload's record does not repeat
+CONTRACT_KEYS = ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling",
+                 "vs_baseline", "data")
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: the benchmark runs on one GPU only; run it with --gpus 1",
-              file=sys.stderr)
-        sys.exit(2)
 
+def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=None):
+    """Build one workload on the device, time args.steps steps after args.warmup, and return
+    its result record (the contract keys included) and the decode kernel's GB/s."""
     import numpy as np
     import torch
 
@@ -341,36 +325,14 @@ def main():
     import workloads
     from paged_kv_cache_144_amd.runner import DeviceWorkload
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda")
-        src.fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
-        return
-
     over = {}
-    if args.block_size != 16:
-        if args.workload not in ("opt13b", "gqa") or args.kv == "q8":
-            print("bench.py: 8- and 32-token blocks are built for the OPT-13B and GQA "
-                  "shapes with 16-bit KV", file=sys.stderr)
-            sys.exit(2)
-        over["block_size"] = args.block_size
-    if args.kv == "q8":
-        if args.workload not in Q8_DTYPE:
-            print(f"bench.py: no 8-bit variant of {args.workload}", file=sys.stderr)
-            sys.exit(2)
-        over["dtype"] = Q8_DTYPE[args.workload]
-    w = workloads.make(args.workload, **over)
+    if block_size != 16:
+        over["block_size"] = block_size
+    if kv == "q8":
+        over["dtype"] = Q8_DTYPE[name]
+    w = workloads.make(name, **over)
     L = args.layers or w.n_layers
-    print(f"[bench] building {args.workload}: {w.num_seqs} seqs, {w.total_q_rows} rows, "
+    print(f"[bench] building {name}: {w.num_seqs} seqs, {w.total_q_rows} rows, "
           f"{w.num_blocks} blocks/layer, {L} layers", file=sys.stderr, flush=True)
     dw = DeviceWorkload(w, "cuda")
     pools = [(dw.k_cache, dw.v_cache)]
@@ -427,6 +389,7 @@ def main():
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
+
     # one pair of events per timed launch (every N-th layer) in the timed region
     def event_pairs():
         e = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -464,10 +427,10 @@ def main():
     kv_decode = kv_bytes_read(w.seq_lens[dec], w.q_rows[dec], w.window, w.num_kv_heads,
                               w.head_dim, w.elem_bytes)
     achieved = kv_decode / (dec_avg_ms / 1e3) / 1e9
-    traffic = (measured_traffic(args.workload + ("_q8" if args.kv == "q8" else ""))
-               if args.block_size == 16 else None)
+    traffic = (measured_traffic(name + ("_q8" if kv == "q8" else ""))
+               if block_size == 16 else None)
     decode_roof = {
-        "kernel": "decode_kernel",
+        "kernel": pa.decode_kernel_name(dw.k_cache, w.num_q_heads, dw.q.dtype),
         "bound": "hbm",
         "achieved": round(achieved, 2),
         "peak": HBM_PEAK_GBS,
@@ -484,8 +447,8 @@ def main():
         tflops = flops / (chunk_avg_ms / 1e3) / 1e12
         peak = MFMA_PEAK_TFLOPS[w.dtype]
         # the chunks' K/V, each (token, KV head) once: what the kernel must read at least
-        chunk_kv = sum(2 * w.num_kv_heads * w.head_dim * w.elem_bytes * int(L)
-                       for L, n in zip(w.seq_lens, w.q_rows) if n > 1)
+        chunk_kv = sum(2 * w.num_kv_heads * w.head_dim * w.elem_bytes * int(n_)
+                       for n_, r_ in zip(w.seq_lens, w.q_rows) if r_ > 1)
         chunk_roof = {
             "kernel": "chunk_kernel",
             "bound": "mfma",
@@ -493,8 +456,8 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4),
-            "traffic": (measured_traffic(args.workload + "_chunk", CHUNK_SOURCES)
-                        if args.block_size == 16 else None),
+            "traffic": (measured_traffic(name + "_chunk", CHUNK_SOURCES)
+                        if block_size == 16 else None),
             "chunk_kv_bytes_per_launch": int(chunk_kv),
             "algorithmic_flops_per_launch": int(flops),
             "chunk_kernel_avg_us": round(chunk_avg_ms * 1e3, 2),
@@ -537,9 +500,9 @@ def main():
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(tokens_per_s, 1),
         "config": {
-            "workload": DESCRIPTIONS[args.workload] + (
-                "; 8-bit KV cache, one fp16 scale per 32 values" if args.kv == "q8" else "") + (
-                f"; {args.block_size}-token blocks" if args.block_size != 16 else ""),
+            "workload": DESCRIPTIONS[name] + (
+                "; 8-bit KV cache, one fp16 scale per 32 values" if kv == "q8" else "") + (
+                f"; {block_size}-token blocks" if block_size != 16 else ""),
             "block_size": w.block_size,
             # slots allocated but empty (last blocks) over slots allocated
             "internal_waste": round(float(waste), 5),
@@ -559,25 +522,113 @@ def main():
         },
         "device_error_bits": err_bits,
     }
-    ceiling = read_ceiling(pa)
-    ceiling["decode_kernel_frac_of_ceiling"] = round(achieved / ceiling["achieved"], 4)
-    result["hbm_read_ceiling"] = ceiling
     if chunk_roof:
         result["roofline_decode"] = decode_roof
         result["roofline_chunk"] = chunk_roof
     if copy_roof:
         result["roofline_copy"] = copy_roof
-    if args.swap_seqs > 0:
-        result["swap"] = time_swap(pa, dw, pools, args.swap_seqs)
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        ref, cb = cpu_baseline(w, L, args.cpu_seconds)
+    if swap_seqs > 0:
+        result["swap"] = time_swap(pa, dw, pools, swap_seqs)
+    if cpu_seconds:
+        print(f"[bench] cpu baseline (oracle) on {name}", file=sys.stderr, flush=True)
+        ref, cb = cpu_baseline(w, L, cpu_seconds)
         # the GPU output of the last layer (same values in every layer) on a few decode rows
         dec = np.nonzero(w.q_rows == 1)[0][:16]
         if dec.size:
             got = out.cpu().numpy().astype(np.float64)[w.query_start_loc()[dec]]
             cb["gpu_max_abs_err_vs_oracle"] = float(np.abs(got - ref.attention(seqs=dec)).max())
         result["cpu_baseline"] = cb
+    # release this workload's pools before anything else is built
+    del pools, dw, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return result, achieved
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="opt13b", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--also", default=None, metavar="W[,W...]",
+                    help="workloads measured after the main one, each reported under its own "
+                         "key with its own roofline and CPU baseline (default: gqa when the "
+                         "main workload is the default OPT-13B shape with 16-bit KV, else none; "
+                         "'none' for none)")
+    ap.add_argument("--layers", type=int, default=None, help="default: the workload's")
+    ap.add_argument("--block-size", type=int, choices=[8, 16, 32], default=16,
+                    help="tokens per KV block (8 and 32: OPT-13B and GQA shapes, 16-bit KV)")
+    ap.add_argument("--kv", choices=["native", "q8"], default="native",
+                    help="q8: 8-bit KV cache (one fp16 scale per 32 values), same workload")
+    ap.add_argument("--event-every", type=int, default=4, metavar="N",
+                    help="kernel durations come from hipEvents recorded around the launches "
+                         "of every N-th layer of each timed step (each recorded event adds a "
+                         "few microseconds of queue gap, which N = 1 would add to every layer)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--swap-seqs", type=int, default=0, metavar="N",
+                    help="after the timed steps, also time evicting the N sequences that "
+                         "arrived last to pinned host memory and bringing them back")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: the benchmark runs on one GPU only; run it with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_144_amd as pa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+        return
+
+    if args.block_size != 16 and (args.workload not in ("opt13b", "gqa") or args.kv == "q8"):
+        print("bench.py: 8- and 32-token blocks are built for the OPT-13B and GQA "
+              "shapes with 16-bit KV", file=sys.stderr)
+        sys.exit(2)
+    if args.kv == "q8" and args.workload not in Q8_DTYPE:
+        print(f"bench.py: no 8-bit variant of {args.workload}", file=sys.stderr)
+        sys.exit(2)
+    if args.also is None:
+        default = (args.workload == "opt13b" and args.kv == "native" and args.block_size == 16
+                   and not args.layers)
+        also = ["gqa"] if default else []
+    else:
+        also = [a for a in args.also.split(",") if a and a != "none"]
+    for a in also:
+        if a not in DESCRIPTIONS:
+            print(f"bench.py: unknown workload {a!r}", file=sys.stderr)
+            sys.exit(2)
+
+    cpu = None if args.no_cpu_baseline else args.cpu_seconds
+    result, achieved = measure(args, args.workload, args.kv, args.block_size, args.swap_seqs,
+                               cpu)
+    extra = {}
+    for a in also:
+        r, a_achieved = measure(args, a, args.kv if a in Q8_DTYPE else "native", 16, 0, cpu)
+        extra[a] = (r, a_achieved)
+    ceiling = read_ceiling(pa)
+    ceiling["decode_kernel_frac_of_ceiling"] = round(achieved / ceiling["achieved"], 4)
+    result["hbm_read_ceiling"] = ceiling
+    for a, (r, a_achieved) in extra.items():
+        r["decode_kernel_frac_of_ceiling"] = round(a_achieved / ceiling["achieved"], 4)
+        result[a] = {k: v for k, v in r.items() if k not in CONTRACT_KEYS}
     print(json.dumps(result), flush=True)
 
 

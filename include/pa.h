@@ -189,6 +189,13 @@ pa_status pa_decode_attend(void* out, pa_dtype out_dtype, const void* q,
                            float scale, int32_t window, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* pa_decode_kernel_name - the name of the decode kernel pa_decode launches for decode rows
+ * of this pool and query-head count: "decode_mfma_kernel" (the matrix-core kernel, for
+ * groups of 4 or 8 query heads per KV head with 16-token blocks and 16-bit or 8-bit
+ * caches) or "decode_kernel" (the per-lane kernel); NULL for unsupported arguments.  For
+ * reports that name the kernel a profile timed.  Static storage; launches nothing. */
+const char* pa_decode_kernel_name(const pa_cache_desc* desc, int32_t num_q_heads);
+
 /* Profiling hook: when set (non-NULL), every later pa_decode / pa_decode_attend records the
  * hipEvent_t `before` just before its decode-kernel launch and `after` just after it, on
  * the call's stream, so a caller can time that kernel alone.  The events are the caller's;

@@ -31,7 +31,8 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
 BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares
-EXPORTS = ("pa_write_kv", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode", "pa_decode_plan",
+EXPORTS = ("pa_write_kv", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode_kernel_name",
+           "pa_decode", "pa_decode_plan",
            "pa_decode_attend", "pa_set_decode_profile_events", "pa_set_chunk_profile_events",
            "pa_stream_read", "pa_status_string",
            "pa_pool_create", "pa_pool_destroy", "pa_seq_set_window", "pa_seq_append",
@@ -73,6 +74,7 @@ def load():
         "pa_copy_blocks": (i32, [P, P, D, P, i32, P, P]),
         "pa_swap_blocks": (i32, [P, P, P, P, D, i32, i32, P, i32, P, P]),
         "pa_decode_workspace_size": (ctypes.c_size_t, [D, i32, i32, i32, i32]),
+        "pa_decode_kernel_name": (ctypes.c_char_p, [D, i32]),
         "pa_decode": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32, i32, P,
                             ctypes.c_size_t, P]),
         "pa_decode_plan": (i32, [D, P, i32, P, P, i32, i32, i32, i32, i32, P, ctypes.c_size_t,
@@ -262,6 +264,16 @@ def workspace_size(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len,
     if n == 0:
         raise PAError(-4, "pa_decode_workspace_size")
     return int(n)
+
+
+def decode_kernel_name(k_cache, num_q_heads, q_dtype=None) -> str:
+    """pa_decode_kernel_name: the decode kernel pa_decode launches for this pool and head
+    count ("decode_mfma_kernel" or "decode_kernel")."""
+    desc = cache_desc(k_cache, q_dtype)
+    name = load().pa_decode_kernel_name(ctypes.byref(desc), num_q_heads)
+    if name is None:
+        raise PAError(-4, "pa_decode_kernel_name")
+    return name.decode()
 
 
 def alloc_workspace(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len, q_dtype=None):

@@ -251,6 +251,16 @@ pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+const char* pa_decode_kernel_name(const pa_cache_desc* desc, int32_t num_q_heads) {
+    if (check_desc(desc) != PA_OK || num_q_heads <= 0 || num_q_heads % desc->num_kv_heads)
+        return nullptr;
+    const int group = num_q_heads / desc->num_kv_heads;
+    if (!pa::decode_kernel_ptr(desc->dtype, desc->head_dim, group, desc->block_size))
+        return nullptr;
+    return pa::decode_uses_mfma(desc->dtype, group, desc->block_size) ? "decode_mfma_kernel"
+                                                                      : "decode_kernel";
+}
+
 size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
                                 int32_t total_q_rows, int32_t num_q_heads,
                                 int32_t max_seq_len) {

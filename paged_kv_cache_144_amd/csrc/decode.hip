@@ -16,16 +16,19 @@ const void* decode_kernel_ptr_bf16_bs(int head_dim, int group, int block_size);
 const void* chunk_kernel_ptr_f16(int head_dim, int group);
 const void* chunk_kernel_ptr_bf16(int head_dim, int group);
 
+// Groups of 4 or 8 query heads with 16-token blocks take the matrix-core kernel
+// (PA_DECODE_MFMA=0 selects the per-lane kernel instead).
+bool decode_uses_mfma(int dtype, int group, int block_size) {
+    if (block_size != kBlock || dtype == DT_F32 || (group != 4 && group != 8)) return false;
+    const char* e = std::getenv("PA_DECODE_MFMA");
+    return !(e && e[0] == '0');
+}
+
 const void* decode_kernel_ptr(int dtype, int head_dim, int group, int block_size) {
-    // groups of 4 or 8 query heads with 16-token blocks: the matrix-core kernel
-    // (PA_DECODE_MFMA=0 selects the per-lane kernel instead)
-    if (block_size == kBlock && dtype != DT_F32 && (group == 4 || group == 8)) {
-        const char* e = std::getenv("PA_DECODE_MFMA");
-        if (!(e && e[0] == '0')) {
-            if (dtype == DT_Q8F16 || dtype == DT_Q8BF16)
-                return decode_kernel_ptr_mfma_q8(dtype, head_dim, group);
-            return decode_kernel_ptr_mfma(dtype, head_dim, group);
-        }
+    if (decode_uses_mfma(dtype, group, block_size)) {
+        if (dtype == DT_Q8F16 || dtype == DT_Q8BF16)
+            return decode_kernel_ptr_mfma_q8(dtype, head_dim, group);
+        return decode_kernel_ptr_mfma(dtype, head_dim, group);
     }
     if (block_size != kBlock) {
         switch (dtype) {

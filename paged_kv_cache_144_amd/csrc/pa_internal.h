@@ -142,6 +142,8 @@ hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream);
 
 // The decode kernel instance for (dtype, head_dim, group), or null if none is built.
 const void* decode_kernel_ptr(int dtype, int head_dim, int group, int block_size);
+// Whether that instance is the matrix-core decode kernel (decode_mfma_kernel).
+bool decode_uses_mfma(int dtype, int group, int block_size);
 // The chunk-row MFMA kernel instance, or null (then chunk rows run as decode rows).
 const void* chunk_kernel_ptr(int dtype, int head_dim, int group, int block_size);
 // Query rows one chunk tile covers: 4 wavefronts x 32 (row, head) pairs / group.

@@ -53,6 +53,8 @@ def decode_host_paths(lib):
         mx = int(w.seq_lens.max())
         n = lib.pa_decode_workspace_size(ctypes.byref(desc), B, R, w.num_q_heads, mx)
         assert n > 0, name
+        assert lib.pa_decode_kernel_name(ctypes.byref(desc), w.num_q_heads) in (
+            b"decode_kernel", b"decode_mfma_kernel"), name
         qsl = fake if (w.q_rows != 1).any() else None
         mb = -(-mx // w.block_size)
         out_dt = pa.PA_F32

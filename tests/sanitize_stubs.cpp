@@ -50,6 +50,9 @@ namespace pa {
 const void* decode_kernel_ptr(int, int, int group, int) {
     return group_ok(group) ? &g_kernel : nullptr;
 }
+bool decode_uses_mfma(int dtype, int group, int block_size) {
+    return block_size == kBlock && dtype != PA_F32 && (group == 4 || group == 8);
+}
 const void* chunk_kernel_ptr(int dtype, int, int group, int block_size) {
     return (dtype == PA_F16 || dtype == PA_BF16) && block_size == kBlock && group_ok(group)
                ? &g_kernel

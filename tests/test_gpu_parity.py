@@ -101,7 +101,8 @@ SMALL = [
     ("gqa", dict(batch=12, median=300, lo=16, hi=3000, block_size=8)),
     ("gqa", dict(batch=12, median=300, lo=16, hi=3000, block_size=32)),
     ("gqa", dict(batch=5, median=200, dtype="f16", block_size=32)),
-    # swapping: evictions to pinned host memory, newcomers in the freed blocks, swap-ins
+    # swapping: evictions to pinned host memory, residents growing into the freed blocks,
+    # finished requests leaving, swap-ins (no new request while a sequence is away)
     ("swap", dict(batch=10, victims=3, lo=5, hi=70, hq=4, hkv=2, d=64, dtype="f32")),
     ("swap", dict(batch=12, victims=4, lo=64, hi=700)),
     ("swap", dict(batch=8, victims=3, lo=20, hi=300, hq=8, hkv=2, dtype="q8_bf16")),

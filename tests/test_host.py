@@ -38,6 +38,19 @@ def test_header_symbols_exported(pa):
     assert sorted(pa.EXPORTS) == syms
 
 
+def test_decode_kernel_name(pa):
+    lib = pa.load()
+    name = lambda dt, hq, hkv=8, bs=16, d=128: lib.pa_decode_kernel_name(
+        ctypes.byref(pa.CacheDesc(10, bs, hkv, d, dt)), hq)
+    assert name(pa.PA_BF16, 32) == b"decode_mfma_kernel"          # groups of 4
+    assert name(pa.PA_Q8_BF16, 64) == b"decode_mfma_kernel"       # groups of 8, 8-bit
+    assert name(pa.PA_F16, 40, 40) == b"decode_kernel"            # one query head per KV head
+    assert name(pa.PA_F16, 8, 4, d=256) == b"decode_kernel"       # groups of 2
+    assert name(pa.PA_F32, 32) == b"decode_kernel"
+    assert name(pa.PA_BF16, 32, bs=8) == b"decode_kernel"         # 8-token blocks
+    assert name(pa.PA_BF16, 33) is None and name(pa.PA_BF16, 24) is None
+
+
 def test_status_strings(pa):
     lib = pa.load()
     for code in pa.STATUS:
