@@ -166,6 +166,27 @@ pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q,
                     int32_t num_q_heads, float scale, int32_t window,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode_noalloc - pa_decode for callers that cannot allocate device memory: code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc.  It takes the same
+ * arguments as pa_decode minus the workspace: its workspace is a fixed array of
+ * PA_NOALLOC_SCRATCH_BYTES bytes in the library's device memory, one per device the library
+ * runs on, held until the process ends.  The call allocates and frees nothing; on its first
+ * call on a device it looks up that device's array (hipGetSymbolAddress).
+ *   - Shapes whose pa_decode_workspace_size exceeds PA_NOALLOC_SCRATCH_BYTES are refused
+ *     with PA_ERR_WORKSPACE before anything is launched.
+ *   - Every call on one device shares that device's array, which keeps the last call's
+ *     contents (each call's own plan rewrites everything its kernels read).  Calls whose
+ *     work overlaps on one device (other streams, other threads) race: serialize them.
+ *   - The error bits that pa_decode leaves in its workspace are not readable here.
+ * Errors as pa_decode, and PA_ERR_LAUNCH if the array's address cannot be found. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_decode_noalloc(void* out, pa_dtype out_dtype, const void* q,
+                            const void* k_cache, const void* v_cache, const pa_cache_desc* desc,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, const int32_t* query_start_loc,
+                            int32_t num_seqs, int32_t total_q_rows, int32_t max_seq_len,
+                            int32_t num_q_heads, float scale, int32_t window, void* stream);
+
 /* pa_decode_plan + pa_decode_attend = pa_decode, split so that one plan serves every layer
  * of a step: the plan depends only on block_tables, seq_lens, query_start_loc, the shapes
  * and the window, which all layers of a step share (the CPU ships one set of tables per

@@ -32,7 +32,7 @@ BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_write_kv", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode_kernel_name",
-           "pa_decode", "pa_decode_plan",
+           "pa_decode", "pa_decode_noalloc", "pa_decode_plan",
            "pa_decode_attend", "pa_set_decode_profile_events", "pa_set_chunk_profile_events",
            "pa_stream_read", "pa_status_string",
            "pa_pool_create", "pa_pool_destroy", "pa_seq_set_window", "pa_seq_append",
@@ -77,6 +77,8 @@ def load():
         "pa_decode_kernel_name": (ctypes.c_char_p, [D, i32]),
         "pa_decode": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32, i32, P,
                             ctypes.c_size_t, P]),
+        "pa_decode_noalloc": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32,
+                                    i32, P]),
         "pa_decode_plan": (i32, [D, P, i32, P, P, i32, i32, i32, i32, i32, P, ctypes.c_size_t,
                                  P]),
         "pa_decode_attend": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32,
@@ -340,6 +342,40 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, *, max_seq_len,
             mb, sl, qs, B, R, int(max_seq_len), hq, float(scale), int(window), ws,
             workspace.numel(), st)
     _check(rc, "pa_decode" if step == "both" else "pa_decode_attend")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20      # PA_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, seq_lens, scale, *, max_seq_len, out,
+                   query_start_loc=None, window=0, stream=None):
+    """pa_decode_noalloc: pa_decode with the library's fixed device workspace; `out` is the
+    caller's [R][Hq][d] tensor (nothing is allocated on this path).  Calls that overlap on
+    one device race on that workspace."""
+    torch = _torch()
+    lib = load()
+    if q.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2 or out is None:
+        raise ValueError("q [R][Hq][d], caches [NB][Hkv][rows][d], block_tables [B][MB], out")
+    R, hq, d = q.shape
+    B, mb = block_tables.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache in shape and dtype")
+    if d != k_cache.shape[3] or tuple(out.shape) != (R, hq, d):
+        raise ValueError("q, the cache and out disagree on their shapes")
+    if seq_lens.numel() != B or (query_start_loc is not None
+                                 and query_start_loc.numel() != B + 1):
+        raise ValueError("seq_lens / query_start_loc length")
+    _check_act(q, k_cache, "q")
+    desc = cache_desc(k_cache, q.dtype)
+    rc = lib.pa_decode_noalloc(
+        _dev_ptr(out, "out"), _dtype_code(out), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
+        _dev_ptr(v_cache, "v_cache"), ctypes.byref(desc),
+        _dev_ptr(block_tables, "block_tables", torch.int32), mb,
+        _dev_ptr(seq_lens, "seq_lens", torch.int32),
+        _dev_ptr(query_start_loc, "query_start_loc", torch.int32), B, R, int(max_seq_len), hq,
+        float(scale), int(window), _stream(stream))
+    _check(rc, "pa_decode_noalloc")
     return out
 
 
