@@ -3,8 +3,10 @@
 
 One step = one decode step of the whole batch through every layer: the plan (block tables and
 lengths -> wavefront shares, once per step since all layers share them), then per layer the
-new tokens' slot write (pa_write_kv) and the paged attention (pa_decode_attend: decode kernel
-+ log-sum-exp merge).  Every layer has its own KV pool in HBM, so no layer's reads are served
+new tokens' slot write and the paged attention (decode kernel + log-sum-exp merge).  Where
+the batch allows it (one query row per sequence, 16- or 32-bit cache) the slot write runs
+inside the decode launch (pa_decode_write_attend); otherwise it is its own launch
+(pa_write_kv, then pa_decode_attend).  Every layer has its own KV pool in HBM, so no layer's reads are served
 from cache.  Inputs are synthetic, seeded, already resident in HBM when timing starts.
 
 Prints one JSON line.  `value` is the KV bytes the attention reads per step (each attended
@@ -354,6 +356,10 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
 
     has_chunks = bool((w.q_rows > 1).any()) and w.dtype in MFMA_PEAK_TFLOPS
     copies = dw.step_copies
+    # the one-launch step (slot write inside the decode launch) where it applies: one query
+    # row per sequence and a cache that takes new rows as they are (not 8-bit)
+    fused = (args.step == "fused" and bool((w.q_rows == 1).all())
+             and w.dtype in ("f32", "f16", "bf16"))
 
     every = max(1, args.event_every)
     sampled = list(range(0, L, every))            # layers whose launches are timed
@@ -370,17 +376,23 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
                 pa.copy_blocks(kc, vc, copies)
                 if xevents is not None and timed_layer:
                     xevents[si][1].record()
-            if wevents is not None and timed_layer:
-                wevents[si][0].record()
-            pa.write_kv(k_step, v_step, slot_step, kc, vc)
-            if wevents is not None and timed_layer:
-                wevents[si][1].record()
+            if not fused:
+                if wevents is not None and timed_layer:
+                    wevents[si][0].record()
+                pa.write_kv(k_step, v_step, slot_step, kc, vc)
+                if wevents is not None and timed_layer:
+                    wevents[si][1].record()
             if events is not None:
                 pa.set_decode_profile_events(*(events[si] if timed_layer else (None, None)))
             if cevents is not None:
                 pa.set_chunk_profile_events(*(cevents[si] if timed_layer else (None, None)))
-            pa.decode(dw.q, kc, vc, dw.block_tables, dw.seq_lens, float(w.scale), out=out,
-                      step="attend", **common)
+            if fused:
+                pa.decode_write_attend(dw.q, k_step, v_step, kc, vc, dw.block_tables,
+                                       dw.seq_lens, float(w.scale), max_seq_len=dw.max_seq_len,
+                                       window=w.window, workspace=dw.workspace, out=out)
+            else:
+                pa.decode(dw.q, kc, vc, dw.block_tables, dw.seq_lens, float(w.scale), out=out,
+                          step="attend", **common)
         if events is not None:
             pa.set_decode_profile_events(None, None)
         if cevents is not None:
@@ -403,12 +415,13 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
     evs = event_pairs()
     cevs = event_pairs() if has_chunks else None
     xevs = event_pairs() if copies is not None else None
-    wevs = event_pairs()
+    wevs = None if fused else event_pairs()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for k in range(args.steps):
-        step(evs[k], cevs[k] if cevs else None, xevs[k] if xevs else None, wevs[k])
+        step(evs[k], cevs[k] if cevs else None, xevs[k] if xevs else None,
+             wevs[k] if wevs else None)
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -417,7 +430,8 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
                     if cevs else 0.0)
     copy_avg_ms = (float(np.mean([a.elapsed_time(b) for per in xevs for a, b in per]))
                    if xevs else 0.0)
-    write_avg_ms = float(np.mean([a.elapsed_time(b) for per in wevs for a, b in per]))
+    write_avg_ms = (float(np.mean([a.elapsed_time(b) for per in wevs for a, b in per]))
+                    if wevs else 0.0)
     err_bits = pa.device_error_bits(dw.workspace)
 
     step_s = total_ms / 1e3 / args.steps
@@ -512,14 +526,21 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
             "seq_len_total": int(w.seq_lens.sum()),
             "kv_bytes_per_layer": int(kv_layer),
             "seed": w.seed,
+            "slot_write": "inside the decode launch" if fused else "own launch",
         },
         "roofline": chunk_roof if chunk_roof and chunk_avg_ms > dec_avg_ms else decode_roof,
-        "write_kv": {
-            "avg_us": round(write_avg_ms * 1e3, 2),
+        "write_kv": ({
+            "fused": True,
+            "note": "each new row is read and written inside the decode launch "
+                    "(pa_decode_write_attend): no launch of its own",
             # each new row of K and of V is read once and written once
+            "bytes_per_layer": int(4 * k_step.numel() * k_step.element_size()),
+        } if fused else {
+            "fused": False,
+            "avg_us": round(write_avg_ms * 1e3, 2),
             "bytes_per_launch": int(4 * k_step.numel() * k_step.element_size()),
             "launches_timed": args.steps * len(sampled),
-        },
+        }),
         "device_error_bits": err_bits,
     }
     if chunk_roof:
@@ -565,6 +586,11 @@ def main():
                     help="kernel durations come from hipEvents recorded around the launches "
                          "of every N-th layer of each timed step (each recorded event adds a "
                          "few microseconds of queue gap, which N = 1 would add to every layer)")
+    ap.add_argument("--step", choices=["fused", "separate"], default="fused",
+                    help="fused: each layer's slot write runs inside its decode launch "
+                         "(pa_decode_write_attend) where the batch allows it (one query row "
+                         "per sequence, 16- or 32-bit cache); separate: pa_write_kv, then "
+                         "pa_decode_attend")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--swap-seqs", type=int, default=0, metavar="N",

@@ -166,6 +166,35 @@ pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q,
                     int32_t num_q_heads, float scale, int32_t window,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode_write_attend - one decode step of one layer in one launch: the slot write of
+ * each sequence's new token and the attention, for batches of one query row per sequence.
+ * Source: "vLLM and PagedAttention" notes (ghkdgus29.github.io), section on basic decoding
+ * (the new token's KV goes into the slot after the existing ones, in the block the manager
+ * mapped), and "PagedAttention deep dive" (donmain.dev), section on splitting the KV cache
+ * into blocks (attention gathers the blocks through the table).
+ *
+ * The result equals pa_write_kv of row s of k_new / v_new into the slot
+ * block_tables[s][(L - 1) / bs] * bs + (L - 1) % bs, L = seq_lens[s] (nothing for L = 0),
+ * followed by pa_decode_attend.  The newest token is taken from k_new / v_new directly and
+ * the wavefront that reads its block writes it into the cache, so the slot write costs no
+ * launch of its own.
+ *
+ *   k_new, v_new  (device) [num_seqs][num_kv_heads][head_dim], cache dtype.
+ *   k_cache, v_cache  (device) the pool; the new tokens' slots are written.
+ *   The other arguments are pa_decode_attend's with query_start_loc = NULL and
+ *   total_q_rows = num_seqs; the workspace must hold a plan from pa_decode_plan with those
+ *   values.  A sequence's newest slot must lie in a block no other sequence of the batch
+ *   reads (the ledger's copy-on-write guarantees it).
+ * Errors: as pa_decode_attend; PA_ERR_UNSUPPORTED for 8-bit caches (their new rows are
+ * quantized by pa_write_kv first). */
+pa_status pa_decode_write_attend(void* out, pa_dtype out_dtype, const void* q, const void* k_new,
+                                 const void* v_new, void* k_cache, void* v_cache,
+                                 const pa_cache_desc* desc, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+                                 float scale, int32_t window, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* pa_decode_noalloc - pa_decode for callers that cannot allocate device memory: code under
  * stream capture, tight serving loops, harnesses that forbid hipMalloc.  It takes the same
  * arguments as pa_decode minus the workspace: its workspace is a fixed array of

@@ -32,7 +32,7 @@ BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_write_kv", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode_kernel_name",
-           "pa_decode", "pa_decode_noalloc", "pa_decode_plan",
+           "pa_decode", "pa_decode_write_attend", "pa_decode_noalloc", "pa_decode_plan",
            "pa_decode_attend", "pa_set_decode_profile_events", "pa_set_chunk_profile_events",
            "pa_stream_read", "pa_status_string",
            "pa_pool_create", "pa_pool_destroy", "pa_seq_set_window", "pa_seq_append",
@@ -77,6 +77,8 @@ def load():
         "pa_decode_kernel_name": (ctypes.c_char_p, [D, i32]),
         "pa_decode": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32, i32, P,
                             ctypes.c_size_t, P]),
+        "pa_decode_write_attend": (i32, [P, i32, P, P, P, P, P, D, P, i32, P, i32, i32, i32, f32,
+                                         i32, P, ctypes.c_size_t, P]),
         "pa_decode_noalloc": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32,
                                     i32, P]),
         "pa_decode_plan": (i32, [D, P, i32, P, P, i32, i32, i32, i32, i32, P, ctypes.c_size_t,
@@ -342,6 +344,46 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, *, max_seq_len,
             mb, sl, qs, B, R, int(max_seq_len), hq, float(scale), int(window), ws,
             workspace.numel(), st)
     _check(rc, "pa_decode" if step == "both" else "pa_decode_attend")
+    return out
+
+
+def decode_write_attend(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, scale, *,
+                        max_seq_len, workspace, window=0, out=None, out_dtype=None,
+                        stream=None):
+    """pa_decode_write_attend: write each sequence's new token (k_new / v_new row s, into
+    the slot of position seq_lens[s] - 1) and attend, in one launch.  One query row per
+    sequence; `workspace` must hold the plan (decode(..., step="plan") with the same tables,
+    lengths and window).  Returns out [B][Hq][d]."""
+    torch = _torch()
+    lib = load()
+    if q.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2:
+        raise ValueError("q [B][Hq][d], caches [NB][Hkv][bs][d], block_tables [B][MB]")
+    B, hq, d = q.shape
+    if block_tables.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("one query row per sequence")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache in shape and dtype")
+    if d != k_cache.shape[3]:
+        raise ValueError(f"q has head_dim {d}, the cache {k_cache.shape[3]}")
+    want = (B, k_cache.shape[1], d)
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} must be {list(want)}")
+        _check_act(t, k_cache, name)
+    _check_act(q, k_cache, "q")
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=out_dtype or torch.float32, device=q.device)
+    elif tuple(out.shape) != (B, hq, d):
+        raise ValueError(f"out must be [{B}][{hq}][{d}]")
+    desc = cache_desc(k_cache, q.dtype)
+    rc = lib.pa_decode_write_attend(
+        _dev_ptr(out, "out"), _dtype_code(out), _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"),
+        _dev_ptr(v_new, "v_new"), _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+        ctypes.byref(desc), _dev_ptr(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev_ptr(seq_lens, "seq_lens", torch.int32), B,
+        int(max_seq_len), hq, float(scale), int(window),
+        _dev_ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check(rc, "pa_decode_write_attend")
     return out
 
 

@@ -392,6 +392,28 @@ pa_status pa_decode_attend(void* out, pa_dtype out_dtype, const void* q, const v
     return run_attend(a, desc->dtype, (hipStream_t)stream);
 }
 
+pa_status pa_decode_write_attend(void* out, pa_dtype out_dtype, const void* q, const void* k_new,
+                                 const void* v_new, void* k_cache, void* v_cache,
+                                 const pa_cache_desc* desc, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+                                 float scale, int32_t window, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    if (!desc) return PA_ERR_NULL;
+    if (is_q8(desc->dtype)) return PA_ERR_UNSUPPORTED;   // new rows are quantized first
+    DecodeArgs a;
+    bool nothing;
+    pa_status st = build_args(out, out_dtype, q, k_cache, v_cache, desc, block_tables,
+                              max_blocks_per_seq, seq_lens, nullptr, num_seqs, num_seqs,
+                              max_seq_len, num_q_heads, scale, window, workspace,
+                              workspace_bytes, true, a, nothing);
+    if (st != PA_OK || nothing) return st;
+    if (!k_new || !v_new) return PA_ERR_NULL;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    return run_attend(a, desc->dtype, (hipStream_t)stream);
+}
+
 pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
                     const void* v_cache, const pa_cache_desc* desc,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -54,6 +54,7 @@ struct KvOps;
 // BS tokens (the block size).
 template <int DT, int D, int G, int BS>
 struct KvOps<DT, D, G, BS, false> {
+    static constexpr bool kNewRows = true;       // can take a step's new rows directly
     static constexpr int EB = Elem<DT>::bytes;
     static constexpr int QB = EB;                // bytes per query element
     static constexpr int PE = Elem<DT>::per16;   // elements per 16-byte lane load
@@ -122,6 +123,9 @@ struct KvOps<DT, D, G, BS, false> {
 template <int DT, int D, int G, int BS>
 struct KvOps<DT, D, G, BS, true> {
     static_assert(BS == kBlock, "8-bit tiles hold 16 tokens");
+    // new rows must be quantized into the cache first (pa_write_kv)
+    static constexpr bool kNewRows = false;
+    static constexpr int EB = 1;
     static constexpr int ADT = DT == DT_Q8F16 ? DT_F16 : DT_BF16;   // query / new-row type
     static constexpr int QB = 2;
     static constexpr int PE = G <= 4 ? 16 : 8;
@@ -552,6 +556,19 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
                     (size_t)b * block_stride + (size_t)g * head_stride,
                     live ? (uint32_t)S::TILE : 0u, (uint32_t)S::lane_off(lane), t);
     };
+    // With the step's new rows given, a row's newest token (position len - 1) is not in the
+    // cache yet: the tiles are read with it masked out, and the segment that reaches the
+    // pair's last block adds it from new row u, KV head g, then writes it into its slot.
+    // Lane (row, col) holds bytes 16 col .. +16 of that row.  The loads are issued after the
+    // segment's tiles (registers stay free during the tile loop); waiting for them waits for
+    // the stream's next tile too, once per pair.
+    constexpr int RB = D * S::EB;                  // bytes of one token row
+    const bool fused = S::kNewRows && a.k_new != nullptr;
+    auto load_new = [&](const Seg& sg, u32x4& kn, u32x4& vn) {
+        const size_t off = ((size_t)sg.u * a.num_kv_heads + (size_t)sg.g) * RB + col * 16;
+        kn = ld16((const char*)a.k_new + off);
+        vn = ld16((const char*)a.v_new + off);
+    };
 
     // The tiles stream without a break: the load after each block's is the next block of
     // this 64-id chunk, else the first of the next chunk, else the first of the next
@@ -578,6 +595,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
         }
         typename S::Q qv;
         S::prep_q(qr, qv);
+        const bool takes_new = fused && cur.end == cur.pe && cur.len > 0;
         // a pair cut after this segment and starting in it: its later shares' starts,
         // loaded now and used when the merge record is written
         const bool opens_cut = cur.starts && cur.end < cur.pe;
@@ -594,21 +612,23 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
 #pragma unroll
             for (int e = 0; e < PE; ++e) acc[gi][e] = 0.f;
         }
-        const int len = cur.len, lo_tok = cur.lo_tok;
+        const int lo_tok = cur.lo_tok;
+        // positions at or past lim are masked; with new rows the newest is not in the tiles
+        const int lim_tiles = fused ? cur.len - 1 : cur.len;
 
-        auto consume = [&](typename S::Tile& tl, int j, bool valid) {
-            const int t0 = j * BS;
+        // the tokens t0 + i * TPI + row of tile tl, those in [lo_tok, lim) taken
+        auto consume = [&](typename S::Tile& tl, int t0, int lim, bool valid) {
             float sc[G][NLD];
             S::partial_scores(qv, tl, sc);
 #pragma unroll
             for (int i = 0; i < NLD; ++i)
 #pragma unroll
                 for (int gi = 0; gi < G; ++gi) sc[gi][i] = group_sum<LPT>(sc[gi][i]) * qscale;
-            if (!valid || t0 < lo_tok || t0 + BS > len) {   // wavefront-uniform
+            if (!valid || t0 < lo_tok || t0 + BS > lim) {   // wavefront-uniform
 #pragma unroll
                 for (int i = 0; i < NLD; ++i) {
                     const int t = t0 + i * TPI + row;
-                    const bool ok = valid && t >= lo_tok && t < len;
+                    const bool ok = valid && t >= lo_tok && t < lim;
 #pragma unroll
                     for (int gi = 0; gi < G; ++gi) sc[gi][i] = ok ? sc[gi][i] : -INFINITY;
                     S::mask_v(tl, i, ok);
@@ -656,9 +676,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
         // would keep both records in memory)
         const int g_cur = cur.g, g_nxt = nxt.g, j1_cur = cur.j1;
         int cids = ids;
+        int b_last = 0;          // id of the segment's last block, and whether it is valid
+        bool ok_last = false;
         for (int c0 = cur.j0;; c0 += kWave) {
             const int n = (j1_cur - c0) < kWave ? (j1_cur - c0) : kWave;
             const bool last_chunk = c0 + kWave >= j1_cur;
+            if (last_chunk) b_last = block_id(cids, n - 1, ok_last);
             const int nc_ids = last_chunk ? 0 : load_ids(cur, c0 + kWave);
             // block k of this chunk, else the next chunk's or next segment's first block; at
             // the very end the same loads read nothing.  Every case issues the same loads,
@@ -678,7 +701,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
             for (int k = 0;; k += 2) {
                 load_next(k + 1, B, okB);
                 bad |= !okA;
-                consume(A, c0 + k, okA);
+                consume(A, (c0 + k) * BS, lim_tiles, okA);
                 if (k + 1 >= n) {
                     A = B;
                     okA = okB;
@@ -686,12 +709,17 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
                 }
                 load_next(k + 2, A, okA);
                 bad |= !okB;
-                consume(B, c0 + k + 1, okB);
+                consume(B, (c0 + k + 1) * BS, lim_tiles, okB);
                 if (k + 2 >= n) break;
             }
             if (last_chunk) break;
             cids = nc_ids;
         }
+        // the newest token's K and V row pieces, if this segment takes it; the loads go out
+        // now and arrive while the rows of the wavefront are combined
+        u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
+        if constexpr (S::kNewRows)
+            if (takes_new) load_new(cur, kn, vn);   // wavefront-uniform
         S::finish(acc, ex);
 
         // combine the TPI rows of the wavefront (log-sum-exp), then write
@@ -713,6 +741,20 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
 #pragma unroll
                 for (int e = 0; e < PE; ++e) acc[gi][e] += __shfl_xor(acc[gi][e], msk);
             }
+            if constexpr (S::kNewRows) {
+                if (takes_new) {   // wavefront-uniform: the newest token, one more term
+                    const float sn = group_sum<LPT>(dot16<DT>(qv.v[gi], kn)) * qscale;
+                    const float mn = fmaxf(M, sn);
+                    const float fo = __builtin_amdgcn_exp2f(M - mn);
+                    const float fn = __builtin_amdgcn_exp2f(sn - mn);
+                    float vf[PE];
+                    widen16<DT>(vn, vf);
+                    lt = fmaf(lt, fo, fn);
+#pragma unroll
+                    for (int e = 0; e < PE; ++e) acc[gi][e] = fmaf(acc[gi][e], fo, fn * vf[e]);
+                    M = mn;
+                }
+            }
             if (row == 0) {
                 if (complete) {
                     const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -732,6 +774,13 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
                     }
                 }
             }
+        }
+        if (takes_new && ok_last && row == 0) {
+            // the newest token into its slot: row (len - 1) % BS of the pair's last block
+            const size_t at = (size_t)b_last * block_stride + (size_t)cur.g * head_stride +
+                              (size_t)((cur.len - 1) % BS) * RB + (size_t)col * 16;
+            st16((char*)a.k_cache + at, kn);
+            st16((char*)a.v_cache + at, vn);
         }
         if (opens_cut) {
             // this wavefront holds the pair's first block: leave its merge task

@@ -80,6 +80,7 @@ struct MfmaKv16 {
     static constexpr int LDS_BYTES = kWavesPerGroup * LDSW;
     static constexpr size_t TILE = (size_t)kBlock * D * 2;
     static constexpr int BPT = 1;                 // blocks per tile
+    static constexpr bool kNewRows = true;        // can take a step's new rows directly
 
     struct Q { u32x4 b[KC]; float f; };
     struct Tile { u32x4 k[KC], v[NLD]; };
@@ -109,6 +110,32 @@ struct MfmaKv16 {
         for (int c = 0; c < KC; ++c) t.k[c] = ld16_stream(kb + off + c * 64);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) t.v[i] = ld16_stream(vb + off + i * 1024);
+    }
+    // The tile of the block holding a row's newest token (row r of the tile), with the
+    // step's new rows given: the lanes that hold token row r read it from the new K and V
+    // rows (kn, vn) instead of the cache, whose slot is not written yet.
+    __device__ static void load_new(const char* kb, const char* vb, size_t off, const char* kn,
+                                    const char* vn, int r, Tile& t) {
+        const int lane = lane_id();
+        const char* kp = lane % 16 == r ? kn + (lane / 16) * 16 : kb + off;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) t.k[c] = ld16_stream(kp + c * 64);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int byte = i * 1024 + lane * 16;
+            t.v[i] = ld16_stream(byte / (D * 2) == r ? vn + byte % (D * 2) : vb + off + i * 1024);
+        }
+    }
+    // The same lanes then write that row into its slot (bit copy).
+    __device__ static void store_new(char* kb, char* vb, size_t off, int r, const Tile& t) {
+        const int lane = lane_id();
+        if (lane % 16 == r) {
+#pragma unroll
+            for (int c = 0; c < KC; ++c) st16(kb + off + c * 64, t.k[c]);
+        }
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            if ((i * 1024 + lane * 16) / (D * 2) == r) st16(vb + off + i * 1024, t.v[i]);
     }
     // Stage V (rows of masked tokens zeroed) in this wavefront's LDS rows; S^T of the
     // block: lane holds head c16, tokens 4 q4 .. +3.
@@ -199,6 +226,8 @@ struct MfmaKvQ8 {
     static constexpr int LDS_BYTES = kWavesPerGroup * LDSW;
     static constexpr size_t TILE = (size_t)(kBlock + 1) * D;
     static_assert(KC % 2 == 0, "an even number of scale groups");
+    // new rows must be quantized into the cache first (pa_write_kv)
+    static constexpr bool kNewRows = false;
 
     struct Q { u32x4 b[KC]; float f; };
     // k: load i of lane l holds bytes 1024 i + 16 l of the block's codes (whole rows per
@@ -253,6 +282,15 @@ struct MfmaKvQ8 {
         return lane < 32 ? kb - k_lane(lane) + off + SCALES + SB * lane
                          : vb - v_lane(lane) + off + SCALES + SB * (lane - 32);
     }
+    // never called (kNewRows is false); present so that the shared kernel body compiles
+    __device__ static void load_new(const char* kb, const char* vb, size_t off, const char*,
+                                    const char*, int, Tile& t) {
+        size_t offs[BPT];
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) offs[h] = off;
+        load(kb, vb, offs, t);
+    }
+    __device__ static void store_new(char*, char*, size_t, int, const Tile&) {}
     __device__ static void load(const char* kb, const char* vb, const size_t (&offs)[BPT],
                                 Tile& t) {
         const int lane = lane_id();
@@ -519,9 +557,17 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     // past cnt re-reads block idx_pad of the same id register and is never consumed.  The
     // loads are one straight sequence whatever the case, so that the compiler's wait
     // counts for the tile in use never include the tile being loaded.
-    struct Item { int cnt; bool ok[BPT]; };
-    auto load_item = [&](int g, int ids, int idx0, int cnt, int idx_pad, Tile& t,
-                         Item& it) __attribute__((always_inline)) {
+    // With the step's new rows given (16-bit caches, one block per tile), a row's newest
+    // token (position len - 1) is not in the cache yet: the tile of the block holding it
+    // (table index jl) takes that token row from new row u, KV head g (Ops::load_new), and
+    // the consumer of that tile writes the row into its slot (Ops::store_new).
+    // nl: the segment's length when new rows are given, else 0 (then no index matches)
+    const bool fused = Ops::kNewRows && a.k_new != nullptr;
+    auto new_len = [&](const Seg& sg) { return fused ? sg.len : 0; };
+    struct Item { int cnt; bool ok[BPT]; int b; };
+    // j: the table index of the item's first block; u, nl: its segment's unit and new_len
+    auto load_item = [&](int g, int ids, int idx0, int cnt, int idx_pad, int j, int u, int nl,
+                         Tile& t, Item& it) __attribute__((always_inline)) {
         size_t off[BPT];
         it.cnt = cnt;
 #pragma unroll
@@ -529,9 +575,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
             bool v;
             const int b = block_id(ids, h < cnt ? idx0 + h : idx_pad, v);
             it.ok[h] = v;
+            if (h == 0) it.b = b;
             off[h] = (size_t)b * block_stride + (size_t)g * Ops::TILE;
         }
-        Ops::load(kbase, vbase, off, t);
+        if (cnt > 0 && j == (nl - 1) / kBlock && nl > 0) {   // wavefront-uniform
+            const size_t noff = ((size_t)u * a.num_kv_heads + (size_t)g) * (size_t)(D * 2);
+            Ops::load_new(kbase, vbase, off[0], (const char*)a.k_new + noff,
+                          (const char*)a.v_new + noff, (nl - 1) % kBlock, t);
+        } else {
+            Ops::load(kbase, vbase, off, t);
+        }
     };
 
     if (x_start >= x_end) return;
@@ -548,9 +601,17 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
 #pragma unroll
         for (int h = 0; h < BPT; ++h) {
             const int b = checked_block(h == 0 ? st.b0 : st.b1, a.num_blocks, iA.ok[h]);
+            if (h == 0) iA.b = b;
             off[h] = (size_t)b * block_stride + (size_t)cur.g * Ops::TILE;
         }
-        Ops::load(kbase, vbase, off, A);
+        const int nl = new_len(cur);
+        if (nl > 0 && cur.j0 == (nl - 1) / kBlock) {
+            const size_t noff = ((size_t)cur.u * a.num_kv_heads + (size_t)cur.g) * (size_t)(D * 2);
+            Ops::load_new(kbase, vbase, off[0], (const char*)a.k_new + noff,
+                          (const char*)a.v_new + noff, (nl - 1) % kBlock, A);
+        } else {
+            Ops::load(kbase, vbase, off, A);
+        }
     }
     bool first_segment = true;
     int bad = 0;
@@ -583,7 +644,13 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
 
         // The blocks of an item are scored first, share one softmax update and then go
         // through P V together, so their independent work can interleave.
+        const int nl_cur = new_len(cur);
         auto consume_item = [&](const Tile& tl, const Item& it, int j0) __attribute__((always_inline)) {
+            if (nl_cur > 0 && j0 == (nl_cur - 1) / kBlock && it.ok[0])   // uniform
+                Ops::store_new((char*)a.k_cache + Ops::k_lane(lane),
+                               (char*)a.v_cache + Ops::v_lane(lane),
+                               (size_t)it.b * block_stride + (size_t)cur.g * Ops::TILE,
+                               (nl_cur - 1) % kBlock, tl);   // the new row into its slot
             float sc[BPT][4];
             bool valid[BPT], edge[BPT];
             int t0[BPT];
@@ -648,6 +715,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
         // plain copies of what the loads need (a select between fields of the two records
         // would keep both records in memory)
         const int g_cur = cur.g, g_nxt = nxt.g, j1_cur = cur.j1, nb_nxt = nxt.j1 - nxt.j0;
+        const int j0_nxt = nxt.j0, u_cur = cur.u, u_nxt = nxt.u, nl_nxt = more ? new_len(nxt) : 0;
         int cids = ids;
         for (int c0 = cur.j0;; c0 += kWave) {
             const int n = (cur.j1 - c0) < kWave ? (cur.j1 - c0) : kWave;
@@ -659,13 +727,15 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
             // Every case issues the same loads, so the wait counts stay exact.
             auto load_next = [&](int k, Tile& t, Item& it) __attribute__((always_inline)) {
                 if (k < items) {
-                    load_item(g_cur, cids, BPT * k, min(BPT, n - BPT * k), BPT * k, t, it);
+                    load_item(g_cur, cids, BPT * k, min(BPT, n - BPT * k), BPT * k,
+                              c0 + BPT * k, u_cur, nl_cur, t, it);
                 } else if (!last_chunk) {
-                    load_item(g_cur, nc_ids, 0, min(BPT, j1_cur - c0 - kWave), 0, t, it);
+                    load_item(g_cur, nc_ids, 0, min(BPT, j1_cur - c0 - kWave), 0, c0 + kWave,
+                              u_cur, nl_cur, t, it);
                 } else if (more) {
-                    load_item(g_nxt, nids, 0, min(BPT, nb_nxt), 0, t, it);
+                    load_item(g_nxt, nids, 0, min(BPT, nb_nxt), 0, j0_nxt, u_nxt, nl_nxt, t, it);
                 } else {
-                    load_item(g_cur, cids, 0, 0, n - 1, t, it);
+                    load_item(g_cur, cids, 0, 0, n - 1, -1, 0, 0, t, it);
                 }
             };
             for (int k = 0;; k += 2) {

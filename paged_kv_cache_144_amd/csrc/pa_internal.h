@@ -107,6 +107,13 @@ struct DecodeArgs {
     const int32_t* block_tables;
     const int32_t* seq_lens;
     const int32_t* query_start_loc;   // may be null
+    // This step's new K / V rows, [rows][num_kv_heads][head_dim] in the cache dtype, or null.
+    // When set (decode rows only: one row per sequence), the token at position len - 1 of
+    // row u is taken from row u here instead of the cache, and the wavefront that reads
+    // that position's block also writes the row into its slot: the slot write and the
+    // attention of a decode step in one launch.
+    const void* k_new;
+    const void* v_new;
     int32_t num_blocks, block_size, num_kv_heads, head_dim, num_q_heads, group;
     int32_t max_blocks, num_seqs, total_q_rows, max_seq_len, window;
     float scale;

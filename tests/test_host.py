@@ -101,6 +101,15 @@ def test_host_validation_without_gpu(pa):
     assert lib.pa_swap_blocks(None, None, None, None, None, 4, 4, None, 1, None, None) == -1
     assert lib.pa_swap_blocks(None, None, None, None, ctypes.byref(ok), -1, 4, None, 1, None,
                               None) == -2
+    # the one-launch decode step: 8-bit caches are refused before anything else
+    q8d = pa.CacheDesc(10, 16, 4, 128, pa.PA_Q8_BF16)
+    args = (None, 0, None, None, None, None, None, None, None, 4, None, 1, 16, 4,
+            ctypes.c_float(0.1), 0, None, 0, None)
+    wa = list(args)
+    wa[7] = ctypes.byref(q8d)
+    assert lib.pa_decode_write_attend(*wa) == -4
+    wa[7] = None
+    assert lib.pa_decode_write_attend(*wa) == -1
     odd8 = pa.CacheDesc(10, 16, 4, 4, pa.PA_F16)            # 8-byte rows
     assert lib.pa_copy_blocks(None, None, ctypes.byref(odd8), None, 1, None, None) == -4
 
