@@ -411,6 +411,7 @@ pa_status pa_decode_write_attend(void* out, pa_dtype out_dtype, const void* q, c
     if (!k_new || !v_new) return PA_ERR_NULL;
     a.k_new = k_new;
     a.v_new = v_new;
+    a.row_bytes = (int32_t)row_bytes(desc);
     return run_attend(a, desc->dtype, (hipStream_t)stream);
 }
 

@@ -13,6 +13,12 @@ const void* decode_kernel_ptr_mfma(int dtype, int head_dim, int group);
 const void* decode_kernel_ptr_mfma_q8(int dtype, int head_dim, int group);
 const void* decode_kernel_ptr_f16_bs(int head_dim, int group, int block_size);
 const void* decode_kernel_ptr_bf16_bs(int head_dim, int group, int block_size);
+const void* decode_kernel_ptr_f32_new(int head_dim, int group);
+const void* decode_kernel_ptr_f16_new(int head_dim, int group);
+const void* decode_kernel_ptr_bf16_new(int head_dim, int group);
+const void* decode_kernel_ptr_f16_bs_new(int head_dim, int group, int block_size);
+const void* decode_kernel_ptr_bf16_bs_new(int head_dim, int group, int block_size);
+const void* decode_kernel_ptr_mfma_new(int dtype, int head_dim, int group);
 const void* chunk_kernel_ptr_f16(int head_dim, int group);
 const void* chunk_kernel_ptr_bf16(int head_dim, int group);
 
@@ -24,17 +30,32 @@ bool decode_uses_mfma(int dtype, int group, int block_size) {
     return !(e && e[0] == '0');
 }
 
-const void* decode_kernel_ptr(int dtype, int head_dim, int group, int block_size) {
+const void* decode_kernel_ptr(int dtype, int head_dim, int group, int block_size,
+                              bool new_rows) {
+    const bool q8 = dtype == DT_Q8F16 || dtype == DT_Q8BF16;
+    if (new_rows && q8) return nullptr;   // 8-bit rows are quantized by pa_write_kv first
     if (decode_uses_mfma(dtype, group, block_size)) {
-        if (dtype == DT_Q8F16 || dtype == DT_Q8BF16)
-            return decode_kernel_ptr_mfma_q8(dtype, head_dim, group);
-        return decode_kernel_ptr_mfma(dtype, head_dim, group);
+        if (q8) return decode_kernel_ptr_mfma_q8(dtype, head_dim, group);
+        return new_rows ? decode_kernel_ptr_mfma_new(dtype, head_dim, group)
+                        : decode_kernel_ptr_mfma(dtype, head_dim, group);
     }
     if (block_size != kBlock) {
         switch (dtype) {
-            case DT_F16: return decode_kernel_ptr_f16_bs(head_dim, group, block_size);
-            case DT_BF16: return decode_kernel_ptr_bf16_bs(head_dim, group, block_size);
+            case DT_F16:
+                return new_rows ? decode_kernel_ptr_f16_bs_new(head_dim, group, block_size)
+                                : decode_kernel_ptr_f16_bs(head_dim, group, block_size);
+            case DT_BF16:
+                return new_rows ? decode_kernel_ptr_bf16_bs_new(head_dim, group, block_size)
+                                : decode_kernel_ptr_bf16_bs(head_dim, group, block_size);
             default: return nullptr;   // fp32 and 8-bit caches: 16-token blocks only
+        }
+    }
+    if (new_rows) {
+        switch (dtype) {
+            case DT_F32: return decode_kernel_ptr_f32_new(head_dim, group);
+            case DT_F16: return decode_kernel_ptr_f16_new(head_dim, group);
+            case DT_BF16: return decode_kernel_ptr_bf16_new(head_dim, group);
+            default: return nullptr;
         }
     }
     switch (dtype) {
@@ -66,7 +87,7 @@ hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
-    const void* fn = decode_kernel_ptr(dtype, a.head_dim, a.group, a.block_size);
+    const void* fn = decode_kernel_ptr(dtype, a.head_dim, a.group, a.block_size, a.k_new);
     if (!fn) return hipErrorInvalidDeviceFunction;
     int groups = (a.max_waves + kWavesPerGroup - 1) / kWavesPerGroup;
     if (groups < 1) groups = 1;   // at least one group: it also zeroes rows with nothing to read
@@ -74,12 +95,45 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
     return hipLaunchKernel(fn, dim3(groups), dim3(kWavesPerGroup * kWave), args, 0, stream);
 }
 
+// With a step's new rows given (pa_decode_write_attend): thread t of the slot-write groups
+// copies 16 bytes of one new K or V row into the slot of position len - 1 of its sequence
+// ("vLLM and PagedAttention" notes, basic decoding: the new token goes after the existing
+// ones, in the block the manager mapped).  The decode kernel of the same call took those
+// rows from the new rows directly, so nothing reads the slots before they are written.
+// An id outside the pool is skipped (the decode kernel sets the error bit for it).
+__device__ void write_new_rows(const DecodeArgs& a, long t) {
+    const int pieces = a.row_bytes / 16;
+    const long per_seq = 2L * a.num_kv_heads * pieces;
+    if (t >= per_seq * a.num_seqs) return;
+    const int s = (int)(t / per_seq);
+    const int r = (int)(t % per_seq);
+    const int kv = r / (a.num_kv_heads * pieces);          // 0: K, 1: V
+    const int g = (r / pieces) % a.num_kv_heads, c = r % pieces;
+    const int L = a.seq_lens[s];
+    if (L <= 0 || L > a.max_seq_len || (long)L > (long)a.max_blocks * a.block_size) return;
+    const int j = (L - 1) / a.block_size;
+    const int b = a.block_tables[(size_t)s * a.max_blocks + j];
+    if ((unsigned)b >= (unsigned)a.num_blocks) return;
+    const size_t tile = (size_t)a.block_size * a.row_bytes;
+    const size_t dst = ((size_t)b * a.num_kv_heads + g) * tile +
+                       (size_t)((L - 1) % a.block_size) * a.row_bytes + (size_t)c * 16;
+    const size_t src = ((size_t)s * a.num_kv_heads + g) * a.row_bytes + (size_t)c * 16;
+    const char* from = (const char*)(kv ? a.v_new : a.k_new);
+    char* to = (char*)(kv ? a.v_cache : a.k_cache);
+    st16(to + dst, ld16(from + src));
+}
+
 // Merge kernel: one wavefront per (share boundary w >= 1, head of the group).  It reads
 // the task of boundary w, if any, and combines that pair's partials for its head.  The
 // decode kernel rewrites the same tasks on every call with the same plan and the plan
-// zeroes every task slot, so tasks are read-only here.
+// zeroes every task slot, so tasks are read-only here.  With new rows given, the groups
+// after the merge groups write them into their slots.
 template <int D, int G>
-__global__ __launch_bounds__(kWavesPerGroup * kWave) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWavesPerGroup * kWave) void merge_kernel(DecodeArgs a, int merge_groups) {
+    if ((int)blockIdx.x >= merge_groups) {
+        write_new_rows(a, (long)(blockIdx.x - merge_groups) * blockDim.x + threadIdx.x);
+        return;
+    }
     const int4* tasks = (const int4*)(a.ws + a.lay.tasks);
     const float2* pml = (const float2*)(a.ws + a.lay.part_ml);
     const float* pacc = (const float*)(a.ws + a.lay.part_acc);
@@ -101,9 +155,16 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
 #undef PA_CASES
 #undef PA_CASE
     if (!fn) return hipErrorInvalidDeviceFunction;
-    if (a.max_waves <= 1) return hipSuccess;
-    const int groups = ((a.max_waves - 1) * a.group + kWavesPerGroup - 1) / kWavesPerGroup;
-    void* args[] = {(void*)&a};
+    int groups = a.max_waves > 1
+                     ? ((a.max_waves - 1) * a.group + kWavesPerGroup - 1) / kWavesPerGroup
+                     : 0;
+    const int merge_groups = groups;
+    if (a.k_new) {   // the slot-write groups: 16 bytes per thread, K and V
+        const long threads = 2L * a.num_seqs * a.num_kv_heads * (a.row_bytes / 16);
+        groups += (int)((threads + kWavesPerGroup * kWave - 1) / (kWavesPerGroup * kWave));
+    }
+    if (groups == 0) return hipSuccess;
+    void* args[] = {(void*)&a, (void*)&merge_groups};
     return hipLaunchKernel(fn, dim3(groups), dim3(kWavesPerGroup * kWave), args, 0, stream);
 }
 

@@ -475,7 +475,9 @@ __device__ inline int checked_block(int b, int num_blocks, bool& valid) {
     return valid ? b : 0;
 }
 
-template <int DT, int D, int G, int BS = kBlock>
+// NEW: the instance that takes the step's new rows (pa_decode_write_attend); the other
+// instances compile without any of that code.
+template <int DT, int D, int G, int BS = kBlock, bool NEW = false>
 __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeArgs a) {
     using S = KvOps<DT, D, G, BS>;
     constexpr int PE = S::PE, LPT = S::LPT, TPI = S::TPI, NLD = S::NLD;
@@ -558,12 +560,11 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     };
     // With the step's new rows given, a row's newest token (position len - 1) is not in the
     // cache yet: the tiles are read with it masked out, and the segment that reaches the
-    // pair's last block adds it from new row u, KV head g, then writes it into its slot.
-    // Lane (row, col) holds bytes 16 col .. +16 of that row.  The loads are issued after the
-    // segment's tiles (registers stay free during the tile loop); waiting for them waits for
-    // the stream's next tile too, once per pair.
+    // pair's last block adds it from new row u, KV head g (its slot is written by the merge
+    // launch that follows).  Lane (row, col) holds bytes 16 col .. +16 of that row.  The
+    // loads go out when the segment starts, ahead of its tiles.
     constexpr int RB = D * S::EB;                  // bytes of one token row
-    const bool fused = S::kNewRows && a.k_new != nullptr;
+    constexpr bool fused = NEW && S::kNewRows;
     auto load_new = [&](const Seg& sg, u32x4& kn, u32x4& vn) {
         const size_t off = ((size_t)sg.u * a.num_kv_heads + (size_t)sg.g) * RB + col * 16;
         kn = ld16((const char*)a.k_new + off);
@@ -596,6 +597,9 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
         typename S::Q qv;
         S::prep_q(qr, qv);
         const bool takes_new = fused && cur.end == cur.pe && cur.len > 0;
+        u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
+        if constexpr (fused)
+            if (takes_new) load_new(cur, kn, vn);   // wavefront-uniform
         // a pair cut after this segment and starting in it: its later shares' starts,
         // loaded now and used when the merge record is written
         const bool opens_cut = cur.starts && cur.end < cur.pe;
@@ -676,12 +680,9 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
         // would keep both records in memory)
         const int g_cur = cur.g, g_nxt = nxt.g, j1_cur = cur.j1;
         int cids = ids;
-        int b_last = 0;          // id of the segment's last block, and whether it is valid
-        bool ok_last = false;
         for (int c0 = cur.j0;; c0 += kWave) {
             const int n = (j1_cur - c0) < kWave ? (j1_cur - c0) : kWave;
             const bool last_chunk = c0 + kWave >= j1_cur;
-            if (last_chunk) b_last = block_id(cids, n - 1, ok_last);
             const int nc_ids = last_chunk ? 0 : load_ids(cur, c0 + kWave);
             // block k of this chunk, else the next chunk's or next segment's first block; at
             // the very end the same loads read nothing.  Every case issues the same loads,
@@ -715,11 +716,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
             if (last_chunk) break;
             cids = nc_ids;
         }
-        // the newest token's K and V row pieces, if this segment takes it; the loads go out
-        // now and arrive while the rows of the wavefront are combined
-        u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
-        if constexpr (S::kNewRows)
-            if (takes_new) load_new(cur, kn, vn);   // wavefront-uniform
         S::finish(acc, ex);
 
         // combine the TPI rows of the wavefront (log-sum-exp), then write
@@ -741,7 +737,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
 #pragma unroll
                 for (int e = 0; e < PE; ++e) acc[gi][e] += __shfl_xor(acc[gi][e], msk);
             }
-            if constexpr (S::kNewRows) {
+            if constexpr (fused) {
                 if (takes_new) {   // wavefront-uniform: the newest token, one more term
                     const float sn = group_sum<LPT>(dot16<DT>(qv.v[gi], kn)) * qscale;
                     const float mn = fmaxf(M, sn);
@@ -774,13 +770,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
                     }
                 }
             }
-        }
-        if (takes_new && ok_last && row == 0) {
-            // the newest token into its slot: row (len - 1) % BS of the pair's last block
-            const size_t at = (size_t)b_last * block_stride + (size_t)cur.g * head_stride +
-                              (size_t)((cur.len - 1) % BS) * RB + (size_t)col * 16;
-            st16((char*)a.k_cache + at, kn);
-            st16((char*)a.v_cache + at, vn);
         }
         if (opens_cut) {
             // this wavefront holds the pair's first block: leave its merge task

@@ -116,26 +116,17 @@ struct MfmaKv16 {
     // rows (kn, vn) instead of the cache, whose slot is not written yet.
     __device__ static void load_new(const char* kb, const char* vb, size_t off, const char* kn,
                                     const char* vn, int r, Tile& t) {
+        constexpr int LPR = D * 2 / 16;           // lanes per token row in a V load
+        constexpr int RPL = kWave / LPR;          // token rows per V load
         const int lane = lane_id();
         const char* kp = lane % 16 == r ? kn + (lane / 16) * 16 : kb + off;
 #pragma unroll
         for (int c = 0; c < KC; ++c) t.k[c] = ld16_stream(kp + c * 64);
+        // token row r lies in V load r / RPL, lanes LPR (r % RPL) .. +LPR
+        const int ir = r / RPL;
+        const char* vr = lane / LPR == r % RPL ? vn + (lane % LPR) * 16 : vb + off + ir * 1024;
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int byte = i * 1024 + lane * 16;
-            t.v[i] = ld16_stream(byte / (D * 2) == r ? vn + byte % (D * 2) : vb + off + i * 1024);
-        }
-    }
-    // The same lanes then write that row into its slot (bit copy).
-    __device__ static void store_new(char* kb, char* vb, size_t off, int r, const Tile& t) {
-        const int lane = lane_id();
-        if (lane % 16 == r) {
-#pragma unroll
-            for (int c = 0; c < KC; ++c) st16(kb + off + c * 64, t.k[c]);
-        }
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-            if ((i * 1024 + lane * 16) / (D * 2) == r) st16(vb + off + i * 1024, t.v[i]);
+        for (int i = 0; i < NLD; ++i) t.v[i] = ld16_stream(i == ir ? vr : vb + off + i * 1024);
     }
     // Stage V (rows of masked tokens zeroed) in this wavefront's LDS rows; S^T of the
     // block: lane holds head c16, tokens 4 q4 .. +3.
@@ -290,7 +281,6 @@ struct MfmaKvQ8 {
         for (int h = 0; h < BPT; ++h) offs[h] = off;
         load(kb, vb, offs, t);
     }
-    __device__ static void store_new(char*, char*, size_t, int, const Tile&) {}
     __device__ static void load(const char* kb, const char* vb, const size_t (&offs)[BPT],
                                 Tile& t) {
         const int lane = lane_id();
@@ -479,7 +469,9 @@ struct MfmaKv<DT, D, G, false> : MfmaKv16<DT, D, G> {};
 template <int DT, int D, int G>
 struct MfmaKv<DT, D, G, true> : MfmaKvQ8<DT, D, G> {};
 
-template <int DT, int D, int G>
+// NEW: the instance that takes the step's new rows (pa_decode_write_attend); the other
+// instances compile without any of that code.
+template <int DT, int D, int G, bool NEW = false>
 __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(G == 4 || G == 8, "groups of 4 or 8 query heads");
     using Ops = MfmaKv<DT, D, G>;
@@ -559,12 +551,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     // counts for the tile in use never include the tile being loaded.
     // With the step's new rows given (16-bit caches, one block per tile), a row's newest
     // token (position len - 1) is not in the cache yet: the tile of the block holding it
-    // (table index jl) takes that token row from new row u, KV head g (Ops::load_new), and
-    // the consumer of that tile writes the row into its slot (Ops::store_new).
+    // (table index jl) takes that token row from new row u, KV head g (Ops::load_new).  Its
+    // slot is written by the merge launch that follows.
     // nl: the segment's length when new rows are given, else 0 (then no index matches)
-    const bool fused = Ops::kNewRows && a.k_new != nullptr;
+    constexpr bool fused = NEW && Ops::kNewRows;
     auto new_len = [&](const Seg& sg) { return fused ? sg.len : 0; };
-    struct Item { int cnt; bool ok[BPT]; int b; };
+    struct Item { int cnt; bool ok[BPT]; };
     // j: the table index of the item's first block; u, nl: its segment's unit and new_len
     auto load_item = [&](int g, int ids, int idx0, int cnt, int idx_pad, int j, int u, int nl,
                          Tile& t, Item& it) __attribute__((always_inline)) {
@@ -575,10 +567,9 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
             bool v;
             const int b = block_id(ids, h < cnt ? idx0 + h : idx_pad, v);
             it.ok[h] = v;
-            if (h == 0) it.b = b;
             off[h] = (size_t)b * block_stride + (size_t)g * Ops::TILE;
         }
-        if (cnt > 0 && j == (nl - 1) / kBlock && nl > 0) {   // wavefront-uniform
+        if (fused && cnt > 0 && j == (nl - 1) / kBlock && nl > 0) {   // wavefront-uniform
             const size_t noff = ((size_t)u * a.num_kv_heads + (size_t)g) * (size_t)(D * 2);
             Ops::load_new(kbase, vbase, off[0], (const char*)a.k_new + noff,
                           (const char*)a.v_new + noff, (nl - 1) % kBlock, t);
@@ -601,11 +592,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
 #pragma unroll
         for (int h = 0; h < BPT; ++h) {
             const int b = checked_block(h == 0 ? st.b0 : st.b1, a.num_blocks, iA.ok[h]);
-            if (h == 0) iA.b = b;
             off[h] = (size_t)b * block_stride + (size_t)cur.g * Ops::TILE;
         }
         const int nl = new_len(cur);
-        if (nl > 0 && cur.j0 == (nl - 1) / kBlock) {
+        if (fused && nl > 0 && cur.j0 == (nl - 1) / kBlock) {
             const size_t noff = ((size_t)cur.u * a.num_kv_heads + (size_t)cur.g) * (size_t)(D * 2);
             Ops::load_new(kbase, vbase, off[0], (const char*)a.k_new + noff,
                           (const char*)a.v_new + noff, (nl - 1) % kBlock, A);
@@ -646,11 +636,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
         // through P V together, so their independent work can interleave.
         const int nl_cur = new_len(cur);
         auto consume_item = [&](const Tile& tl, const Item& it, int j0) __attribute__((always_inline)) {
-            if (nl_cur > 0 && j0 == (nl_cur - 1) / kBlock && it.ok[0])   // uniform
-                Ops::store_new((char*)a.k_cache + Ops::k_lane(lane),
-                               (char*)a.v_cache + Ops::v_lane(lane),
-                               (size_t)it.b * block_stride + (size_t)cur.g * Ops::TILE,
-                               (nl_cur - 1) % kBlock, tl);   // the new row into its slot
             float sc[BPT][4];
             bool valid[BPT], edge[BPT];
             int t0[BPT];

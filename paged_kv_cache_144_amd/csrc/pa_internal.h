@@ -108,12 +108,13 @@ struct DecodeArgs {
     const int32_t* seq_lens;
     const int32_t* query_start_loc;   // may be null
     // This step's new K / V rows, [rows][num_kv_heads][head_dim] in the cache dtype, or null.
-    // When set (decode rows only: one row per sequence), the token at position len - 1 of
-    // row u is taken from row u here instead of the cache, and the wavefront that reads
-    // that position's block also writes the row into its slot: the slot write and the
-    // attention of a decode step in one launch.
+    // When set (decode rows only: one row per sequence), the decode kernels take the token
+    // at position len - 1 of row u from row u here instead of the cache, and the merge
+    // launch that follows writes each row into its slot: a decode step's slot write costs
+    // no launch of its own.  row_bytes: bytes of one K or V row (head_dim x element size).
     const void* k_new;
     const void* v_new;
+    int32_t row_bytes;
     int32_t num_blocks, block_size, num_kv_heads, head_dim, num_q_heads, group;
     int32_t max_blocks, num_seqs, total_q_rows, max_seq_len, window;
     float scale;
@@ -147,8 +148,10 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream);
 
-// The decode kernel instance for (dtype, head_dim, group), or null if none is built.
-const void* decode_kernel_ptr(int dtype, int head_dim, int group, int block_size);
+// The decode kernel instance for (dtype, head_dim, group), or null if none is built;
+// new_rows: the instance that takes the step's new rows (pa_decode_write_attend).
+const void* decode_kernel_ptr(int dtype, int head_dim, int group, int block_size,
+                              bool new_rows = false);
 // Whether that instance is the matrix-core decode kernel (decode_mfma_kernel).
 bool decode_uses_mfma(int dtype, int group, int block_size);
 // The chunk-row MFMA kernel instance, or null (then chunk rows run as decode rows).

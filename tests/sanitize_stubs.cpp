@@ -47,7 +47,7 @@ hipError_t hipPointerGetAttributes(hipPointerAttribute_t* attr, const void* p) {
 
 namespace pa {
 
-const void* decode_kernel_ptr(int, int, int group, int) {
+const void* decode_kernel_ptr(int, int, int group, int, bool) {
     return group_ok(group) ? &g_kernel : nullptr;
 }
 bool decode_uses_mfma(int dtype, int group, int block_size) {
