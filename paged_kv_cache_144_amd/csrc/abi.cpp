@@ -415,6 +415,28 @@ pa_status pa_decode_write_attend(void* out, pa_dtype out_dtype, const void* q, c
     return run_attend(a, desc->dtype, (hipStream_t)stream);
 }
 
+pa_status pa_decode_noalloc(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                            const void* v_cache, const pa_cache_desc* desc,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, const int32_t* query_start_loc,
+                            int32_t num_seqs, int32_t total_q_rows, int32_t max_seq_len,
+                            int32_t num_q_heads, float scale, int32_t window, void* stream) {
+    // shapes whose workspace exceeds the array are refused before anything is touched
+    const size_t need =
+        pa_decode_workspace_size(desc, num_seqs, total_q_rows, num_q_heads, max_seq_len);
+    if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    size_t bytes = 0;
+    const pa_status st = pa::noalloc_scratch(&ws, &bytes);
+    if (st != PA_OK) return st;
+    // pa_decode validates the remaining arguments; its plan kernel writes every part of the
+    // workspace the attention reads (headers, shares, zeroed merge records), so what an
+    // earlier call left in the array never matters
+    return pa_decode(out, out_dtype, q, k_cache, v_cache, desc, block_tables,
+                     max_blocks_per_seq, seq_lens, query_start_loc, num_seqs, total_q_rows,
+                     max_seq_len, num_q_heads, scale, window, ws, bytes, stream);
+}
+
 pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
                     const void* v_cache, const pa_cache_desc* desc,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -128,6 +128,10 @@ struct DecodeArgs {
     Layout lay;
 };
 
+// The fixed workspace of pa_decode_noalloc on the current device (noalloc.hip): its device
+// address and size, looked up on the first call on each device.
+pa_status noalloc_scratch(void** out, size_t* bytes);
+
 // launchers (each enqueues on `stream`, returns hipSuccess or the launch error)
 hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, int32_t n,
                            void* kc, void* vc, int32_t nb, int32_t bs, int32_t hkv, int32_t d,

@@ -77,6 +77,13 @@ def decode_host_paths(lib):
                              fake, qsl, B, R, mx, w.num_q_heads + 1, ctypes.c_float(w.scale),
                              w.window, fake, n, None) in (-2, -4)
         assert launches() == before, name
+        # the entry point without a workspace argument: same launches, or a refusal
+        # when the shape needs more than its fixed workspace
+        before = launches()
+        rc = lib.pa_decode_noalloc(fake, out_dt, fake, fake, fake, ctypes.byref(desc), fake, mb,
+                                   fake, qsl, B, R, mx, w.num_q_heads, ctypes.c_float(w.scale),
+                                   w.window, None)
+        assert (rc == 0 and launches() > before) or (rc == -5 and launches() == before), name
         say("decode host path", name, kw, "workspace", n)
 
 

@@ -47,6 +47,14 @@ hipError_t hipPointerGetAttributes(hipPointerAttribute_t* attr, const void* p) {
 
 namespace pa {
 
+// the pretend device's fixed workspace of pa_decode_noalloc: an address the stubbed
+// launches never dereference
+pa_status noalloc_scratch(void** out, size_t* bytes) {
+    *out = reinterpret_cast<void*>(uintptr_t(1) << 40);
+    *bytes = PA_NOALLOC_SCRATCH_BYTES;
+    return PA_OK;
+}
+
 const void* decode_kernel_ptr(int, int, int group, int, bool) {
     return group_ok(group) ? &g_kernel : nullptr;
 }
