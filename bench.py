@@ -50,7 +50,8 @@ Q8_DTYPE = {"opt13b": "q8_f16", "gqa": "q8_bf16", "swa": "q8_f16", "prefix_mixed
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense matrix peak, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SOURCES = ["decode_impl.h", "decode_mfma.h", "pa_device.h", "pa_internal.h", "plan.hip"]
+KERNEL_SOURCES = ["decode_impl.h", "decode_mfma.h", "decode_group.h", "pa_device.h", "pa_internal.h",
+                  "plan.hip"]
 CHUNK_SOURCES = ["chunk_impl.h", "pa_device.h", "pa_internal.h", "plan.hip"]
 
 DESCRIPTIONS = {
@@ -444,7 +445,8 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
     traffic = (measured_traffic(name + ("_q8" if kv == "q8" else ""))
                if block_size == 16 else None)
     decode_roof = {
-        "kernel": pa.decode_kernel_name(dw.k_cache, w.num_q_heads, dw.q.dtype),
+        "kernel": pa.decode_kernel_name(dw.k_cache, w.num_q_heads, dw.q.dtype, w.num_seqs,
+                                        w.window if dec.all() else 0),
         "bound": "hbm",
         "achieved": round(achieved, 2),
         "peak": HBM_PEAK_GBS,

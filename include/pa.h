@@ -151,7 +151,9 @@ size_t pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
  *   workspace     (device) at least pa_decode_workspace_size(...) bytes, 256-byte aligned.
  *                 Its first 4 bytes receive the call's device error bits: 1 = a block id
  *                 outside [0, num_blocks) was met, 2 = a sequence length or row count was
- *                 out of range.  Concurrent calls must not share a workspace.
+ *                 out of range, 4 = pa_decode_attend was given a plan made for the other
+ *                 decode mode (a different window; nothing computed).  Concurrent calls
+ *                 must not share a workspace.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE,
  * PA_ERR_LAUNCH.
  */
@@ -176,8 +178,9 @@ pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q,
  * The result equals pa_write_kv of row s of k_new / v_new into the slot
  * block_tables[s][(L - 1) / bs] * bs + (L - 1) % bs, L = seq_lens[s] (nothing for L = 0),
  * followed by pa_decode_attend.  The newest token is taken from k_new / v_new directly and
- * the wavefront that reads its block writes it into the cache, so the slot write costs no
- * launch of its own.
+ * the attention's own launches write it into the cache (the launch that combines cut
+ * pairs, or in group mode the wavefront that holds the pair's last block), so the slot
+ * write costs no launch of its own.
  *
  *   k_new, v_new  (device) [num_seqs][num_kv_heads][head_dim], cache dtype.
  *   k_cache, v_cache  (device) the pool; the new tokens' slots are written.
@@ -239,12 +242,21 @@ pa_status pa_decode_attend(void* out, pa_dtype out_dtype, const void* q,
                            float scale, int32_t window, void* workspace,
                            size_t workspace_bytes, void* stream);
 
-/* pa_decode_kernel_name - the name of the decode kernel pa_decode launches for decode rows
- * of this pool and query-head count: "decode_mfma_kernel" (the matrix-core kernel, for
- * groups of 4 or 8 query heads per KV head with 16-token blocks and 16-bit or 8-bit
- * caches) or "decode_kernel" (the per-lane kernel); NULL for unsupported arguments.  For
- * reports that name the kernel a profile timed.  Static storage; launches nothing. */
-const char* pa_decode_kernel_name(const pa_cache_desc* desc, int32_t num_q_heads);
+/* pa_decode_kernel_name - the name of the decode kernel pa_decode launches for a batch of
+ * num_seqs decode rows (one query row per sequence, query_start_loc NULL) of this pool and
+ * query-head count under `window` (0: none):
+ *   "decode_mfma_kernel"  the matrix-core kernel, for groups of 4 or 8 query heads per KV
+ *                         head with 16-token blocks and 16-bit or 8-bit caches;
+ *   "decode_group_kernel" the per-lane kernel in group mode, one workgroup per (row, KV
+ *                         head) pair, for sliding-window batches on the per-lane kernel
+ *                         with 16-token blocks whose windows span at most 256 or 512
+ *                         blocks (sotaaz.com, "KV cache by model", layer kinds);
+ *   "decode_kernel"       the per-lane kernel otherwise;
+ * NULL for unsupported arguments.  For reports that name the kernel a profile timed.
+ * Static storage; launches nothing (with window > 0 it queries the device's occupancy, so
+ * a device must be present). */
+const char* pa_decode_kernel_name(const pa_cache_desc* desc, int32_t num_q_heads,
+                                  int32_t num_seqs, int32_t window);
 
 /* Profiling hook: when set (non-NULL), every later pa_decode / pa_decode_attend records the
  * hipEvent_t `before` just before its decode-kernel launch and `after` just after it, on

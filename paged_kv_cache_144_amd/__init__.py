@@ -74,7 +74,7 @@ def load():
         "pa_copy_blocks": (i32, [P, P, D, P, i32, P, P]),
         "pa_swap_blocks": (i32, [P, P, P, P, D, i32, i32, P, i32, P, P]),
         "pa_decode_workspace_size": (ctypes.c_size_t, [D, i32, i32, i32, i32]),
-        "pa_decode_kernel_name": (ctypes.c_char_p, [D, i32]),
+        "pa_decode_kernel_name": (ctypes.c_char_p, [D, i32, i32, i32]),
         "pa_decode": (i32, [P, i32, P, P, P, D, P, i32, P, P, i32, i32, i32, i32, f32, i32, P,
                             ctypes.c_size_t, P]),
         "pa_decode_write_attend": (i32, [P, i32, P, P, P, P, P, D, P, i32, P, i32, i32, i32, f32,
@@ -270,11 +270,12 @@ def workspace_size(k_cache, num_seqs, total_q_rows, num_q_heads, max_seq_len,
     return int(n)
 
 
-def decode_kernel_name(k_cache, num_q_heads, q_dtype=None) -> str:
-    """pa_decode_kernel_name: the decode kernel pa_decode launches for this pool and head
-    count ("decode_mfma_kernel" or "decode_kernel")."""
+def decode_kernel_name(k_cache, num_q_heads, q_dtype=None, num_seqs=0, window=0) -> str:
+    """pa_decode_kernel_name: the decode kernel pa_decode launches for a batch of num_seqs
+    decode rows of this pool and head count under `window` ("decode_mfma_kernel",
+    "decode_group_kernel" or "decode_kernel")."""
     desc = cache_desc(k_cache, q_dtype)
-    name = load().pa_decode_kernel_name(ctypes.byref(desc), num_q_heads)
+    name = load().pa_decode_kernel_name(ctypes.byref(desc), num_q_heads, num_seqs, window)
     if name is None:
         raise PAError(-4, "pa_decode_kernel_name")
     return name.decode()

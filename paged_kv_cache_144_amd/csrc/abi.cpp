@@ -129,6 +129,42 @@ pa_status plan_shape(const pa_cache_desc* desc, int32_t num_seqs, int32_t total_
     return PA_OK;
 }
 
+// Group mode for a batch of num_seqs decode rows (one query row each) under a sliding window
+// of `window` tokens: the workgroups per (row, KV head) pair, or 0 for the wave split.
+// A sliding-window layer bounds every pair by its window (sotaaz.com, "KV cache by model",
+// section on layer kinds: such a layer only needs the last W tokens), so a fixed number of
+// wavefronts per pair is balanced; they combine in LDS and through a per-pair arrival
+// counter, with no merge launch.  Small batches split each pair among S = CUs / pairs
+// workgroups, so that every compute unit streams one; below 4 the split's cross-workgroup
+// handoff (an L2 write-back and invalidate at agent scope) costs more than it saves and S
+// is 1.  S is raised where a wavefront's share would pass one 64-entry chunk of block ids
+// and lowered where shares would fall under two blocks.  The per-lane kernel with 16-token blocks only; the
+// workspace must hold one record per wavefront.  PA_GROUP_MODE=0 keeps the wave split (for
+// A/Bs); PA_GROUP_SPLIT=S fixes the split (for sweeps).
+int group_split(const pa_cache_desc* desc, const Plan& p, int32_t num_seqs, int32_t window) {
+    const char* gm = std::getenv("PA_GROUP_MODE");
+    if ((gm && gm[0] == '0') || window <= 0 || desc->block_size != pa::kBlock) return 0;
+    if (num_seqs <= 0 || pa::decode_uses_mfma(desc->dtype, p.group, desc->block_size)) return 0;
+    if (!pa::decode_group_ptr(desc->dtype, desc->head_dim, p.group, false)) return 0;
+    constexpr int WB = pa::kWavesPerGroup;
+    const int64_t win_blocks = ((int64_t)window + desc->block_size - 1) / desc->block_size + 1;
+    const int64_t pairs = (int64_t)num_seqs * desc->num_kv_heads;
+    int64_t s = cu_count() / pairs;
+    if (s < 4) s = 1;
+    if (s > win_blocks / (2 * WB)) s = win_blocks / (2 * WB);
+    const int64_t need = (win_blocks + 64 * WB - 1) / (64 * WB);
+    if (s < need) s = need;
+    if (s < 1) s = 1;
+    if (s > pa::kGroupMaxSplit) s = pa::kGroupMaxSplit;
+    if (const char* e = std::getenv("PA_GROUP_SPLIT")) {
+        const int v = std::atoi(e);
+        if (v >= 1 && v <= pa::kGroupMaxSplit && v >= need) s = v;
+    }
+    if (win_blocks > 64 * WB * s) return 0;
+    if (WB * s * pairs > p.max_waves) return 0;
+    return (int)s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,12 +287,19 @@ pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-const char* pa_decode_kernel_name(const pa_cache_desc* desc, int32_t num_q_heads) {
-    if (check_desc(desc) != PA_OK || num_q_heads <= 0 || num_q_heads % desc->num_kv_heads)
+const char* pa_decode_kernel_name(const pa_cache_desc* desc, int32_t num_q_heads,
+                                  int32_t num_seqs, int32_t window) {
+    if (check_desc(desc) != PA_OK || num_q_heads <= 0 || num_q_heads % desc->num_kv_heads ||
+        num_seqs < 0)
         return nullptr;
     const int group = num_q_heads / desc->num_kv_heads;
     if (!pa::decode_kernel_ptr(desc->dtype, desc->head_dim, group, desc->block_size))
         return nullptr;
+    if (window > 0) {
+        Plan p;
+        if (plan_shape(desc, num_seqs, num_seqs, num_q_heads, true, p) != PA_OK) return nullptr;
+        if (group_split(desc, p, num_seqs, window) > 0) return "decode_group_kernel";
+    }
     return pa::decode_uses_mfma(desc->dtype, group, desc->block_size) ? "decode_mfma_kernel"
                                                                       : "decode_kernel";
 }
@@ -339,6 +382,12 @@ pa_status build_args(void* out, pa_dtype out_dtype, const void* q, const void* k
     a.min_blocks = p.min_blocks;
     a.ws = (char*)workspace;
     a.lay = p.lay;
+    // sliding-window decode batches: one workgroup per (row, KV head) pair
+    const int split = query_start_loc ? 0 : group_split(desc, p, num_seqs, window);
+    if (split > 0) {
+        a.group_mode = split;
+        a.max_waves = pa::kWavesPerGroup * split * num_seqs * desc->num_kv_heads;
+    }
     return PA_OK;
 }
 

@@ -19,6 +19,10 @@ const void* decode_kernel_ptr_bf16_new(int head_dim, int group);
 const void* decode_kernel_ptr_f16_bs_new(int head_dim, int group, int block_size);
 const void* decode_kernel_ptr_bf16_bs_new(int head_dim, int group, int block_size);
 const void* decode_kernel_ptr_mfma_new(int dtype, int head_dim, int group);
+const void* decode_group_ptr_f32(int head_dim, int group, bool new_rows);
+const void* decode_group_ptr_f16(int head_dim, int group, bool new_rows);
+const void* decode_group_ptr_bf16(int head_dim, int group, bool new_rows);
+const void* decode_group_ptr_q8(int dtype, int head_dim, int group);
 const void* chunk_kernel_ptr_f16(int head_dim, int group);
 const void* chunk_kernel_ptr_bf16(int head_dim, int group);
 
@@ -68,6 +72,17 @@ const void* decode_kernel_ptr(int dtype, int head_dim, int group, int block_size
     }
 }
 
+const void* decode_group_ptr(int dtype, int head_dim, int group, bool new_rows) {
+    switch (dtype) {
+        case DT_F32: return decode_group_ptr_f32(head_dim, group, new_rows);
+        case DT_F16: return decode_group_ptr_f16(head_dim, group, new_rows);
+        case DT_BF16: return decode_group_ptr_bf16(head_dim, group, new_rows);
+        case DT_Q8F16:
+        case DT_Q8BF16: return new_rows ? nullptr : decode_group_ptr_q8(dtype, head_dim, group);
+        default: return nullptr;
+    }
+}
+
 const void* chunk_kernel_ptr(int dtype, int head_dim, int group, int block_size) {
     if (block_size != kBlock) return nullptr;   // other block sizes: chunk rows decode
     switch (dtype) {
@@ -87,11 +102,18 @@ hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
-    const void* fn = decode_kernel_ptr(dtype, a.head_dim, a.group, a.block_size, a.k_new);
+    const void* fn = a.group_mode ? decode_group_ptr(dtype, a.head_dim, a.group, a.k_new)
+                                  : decode_kernel_ptr(dtype, a.head_dim, a.group, a.block_size,
+                                                      a.k_new);
     if (!fn) return hipErrorInvalidDeviceFunction;
+    void* args[] = {(void*)&a};
+    if (a.group_mode) {
+        // group_mode workgroups per pair, one wave record each wavefront
+        const int groups = a.max_waves / kWavesPerGroup > 0 ? a.max_waves / kWavesPerGroup : 1;
+        return hipLaunchKernel(fn, dim3(groups), dim3(kWavesPerGroup * kWave), args, 0, stream);
+    }
     int groups = (a.max_waves + kWavesPerGroup - 1) / kWavesPerGroup;
     if (groups < 1) groups = 1;   // at least one group: it also zeroes rows with nothing to read
-    void* args[] = {(void*)&a};
     return hipLaunchKernel(fn, dim3(groups), dim3(kWavesPerGroup * kWave), args, 0, stream);
 }
 
@@ -139,14 +161,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void merge_kernel(DecodeArg
     const float* pacc = (const float*)(a.ws + a.lay.part_acc);
     const int q = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
     const int w = q / G + 1, gi = q % G;
-    const int W = ((const int32_t*)(a.ws + a.lay.header))[2];
-    if (w >= W) return;
+    const int32_t* hdr = (const int32_t*)(a.ws + a.lay.header);
+    const int W = hdr[2];
+    if (w >= W || hdr[5] != 0) return;   // (a group-mode plan holds no merge tasks)
     const int4 t = tasks[w];
     if (t.z <= 0) return;
     merge_pair<D, G>(a, t.x, t.y, w - 1, t.z, t.w, gi, pml, pacc, lane_id());
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
+    if (a.group_mode) return hipSuccess;   // combined inside the decode launch
     const void* fn = nullptr;
 #define PA_CASE(D, G) \
     if (a.head_dim == D && a.group == G) fn = (const void*)&merge_kernel<D, G>;

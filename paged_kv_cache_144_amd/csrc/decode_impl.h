@@ -503,6 +503,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     // rows with nothing to read are zeros (shared out among all launched wavefronts)
     for (int i = wave; i < n_empty; i += gridDim.x * kWavesPerGroup) zero_row(a, empty[i], lane);
     if (wave >= W) return;
+    if (hdr[5] != 0) {   // a group-mode plan: its records are not wave shares
+        if (wave == 0 && lane == 0) atomicOr(hdr, kErrPlanMode);
+        return;
+    }
 
     const int row = lane / LPT;        // which token of each load this lane holds
     const int col = lane % LPT;        // which PE-element column

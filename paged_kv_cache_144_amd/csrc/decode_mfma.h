@@ -499,6 +499,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     const WaveStart st = ((const WaveStart*)(a.ws + a.lay.wave_st))[wave];
     for (int i = wave; i < n_empty; i += gridDim.x * kWavesPerGroup) zero_row(a, empty[i], lane);
     if (wave >= W) return;
+    if (hdr[5] != 0) {   // a group-mode plan: its records are not wave shares
+        if (wave == 0 && lane == 0) atomicOr(hdr, kErrPlanMode);
+        return;
+    }
 
     const int c16 = lane % 16, q4 = lane / 16;
     char* my = Ops::LDS_BYTES > 0 ? lds + (threadIdx.x >> 6) * (Ops::LDS_BYTES / kWavesPerGroup)

@@ -24,9 +24,15 @@ constexpr int kPairCost = 14;       // default fixed cost per pair in quarter bl
 constexpr int kMaxPairCost = 27;
 constexpr int kQ8Group = 32;        // values per scale in 8-bit caches
 
+// Group mode: each (row, KV head) pair is split among at most kGroupMaxSplit workgroups of
+// kWavesPerGroup wavefronts; a wavefront takes at most 64 blocks (one chunk of block ids),
+// so a window may span at most 64 kWavesPerGroup kGroupMaxSplit blocks.
+constexpr int kGroupMaxSplit = 8;
+
 // Error bits written to the first word of the workspace.
 constexpr int kErrBlockId = 1;
 constexpr int kErrSeqLen = 2;
+constexpr int kErrPlanMode = 4;   // the plan was made for the other decode mode
 
 // One decode unit per query row: what the row reads, derived once per call by the plan
 // kernel.  A chunk row r of a sequence with n rows and length L is the decode row of
@@ -54,7 +60,7 @@ static_assert(sizeof(WaveStart) == 48, "three 16-byte loads");
 // Workspace layout (all offsets 256-byte aligned); U = query rows, W = wavefront workers:
 //   header   int32[64]: [0] error bits, [1] total blocks T, [2] active waves,
 //                       [3] rows with nothing to read (their output is zeros),
-//                       [4] chunk-row tiles
+//                       [4] chunk-row tiles, [5] the plan's group_mode
 //   cb       uint32[U+1]   linear offset of pair (u, kv head 0); pair (u, g) starts at
 //                          cb[u] + g * nb(u) and spans nb(u) blocks
 //   cw       uint32[U+1]   the same in the weighted space the wave shares cut evenly: a
@@ -68,8 +74,11 @@ static_assert(sizeof(WaveStart) == 48, "three 16-byte loads");
 //   tiles    int2[Tmax]    chunk-row tiles (sequence, first row) for the MFMA kernel
 //   tasks    int4[W+1]     merge task of the cut pair whose first share boundary is w:
 //                          (unit, KV head, contributing wavefronts, slot of the first);
-//                          zeroed by the plan, written by the pair's first wavefront
+//                          zeroed by the plan, written by the pair's first wavefront;
+//                          in group mode int32 per pair: the arrival counter of its
+//                          workgroups (zeroed by the plan, reset by the last arrival)
 //   part_ml  float2[W*2*G]       partial (max, sum) per wave, slot, head of the group
+//                                (group mode: per workgroup and head)
 //   part_acc float[W*2*G*d]      partial unnormalised output
 struct Layout {
     size_t header, cb, cw, unit, empty, wave_x0, wave_u, wave_st, tiles, tasks, part_ml, part_acc,
@@ -124,6 +133,12 @@ struct DecodeArgs {
     int32_t max_tiles;                // chunk tiles the work list holds
     int32_t pair_cost;                // fixed cost of a (row, KV head) pair, quarter blocks
     int32_t min_blocks;               // smallest share of blocks a wavefront is given
+    // Group mode (sliding-window decode batches on the per-lane kernel): one workgroup of
+    // group_mode workgroups per (row, KV head) pair (0: off), wavefront i of the pair's
+    // 4 group_mode taking the i-th part of its blocks; they combine in LDS and through the
+    // pair's arrival counter, so no merge launch follows.  max_waves is then
+    // kWavesPerGroup x group_mode x rows x KV heads.
+    int32_t group_mode;
     char* ws;
     Layout lay;
 };
@@ -156,6 +171,8 @@ hipError_t launch_chunk(const DecodeArgs& a, int dtype, hipStream_t stream);
 // new_rows: the instance that takes the step's new rows (pa_decode_write_attend).
 const void* decode_kernel_ptr(int dtype, int head_dim, int group, int block_size,
                               bool new_rows = false);
+// The group-mode decode kernel instance (16-token blocks), or null.
+const void* decode_group_ptr(int dtype, int head_dim, int group, bool new_rows);
 // Whether that instance is the matrix-core decode kernel (decode_mfma_kernel).
 bool decode_uses_mfma(int dtype, int group, int block_size);
 // The chunk-row MFMA kernel instance, or null (then chunk rows run as decode rows).

@@ -115,7 +115,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     // share start at offset o of a pair maps to the pair's first block while o <= C).
     int W = 0;
     uint32_t C = 0;
-    if (T > 0) {
+    if (a.group_mode) {
+        W = a.max_waves;   // 4 group_mode wavefronts per (row, KV head), empty or not
+    } else if (T > 0) {
         const uint32_t mb = (uint32_t)a.min_blocks;
         W = (int)((T + mb - 1) / mb);
         W = W < 1 ? 1 : (W > a.max_waves ? a.max_waves : W);
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
         // row ranges cannot be trusted (or would overflow the tile list): no unit, no write
         if (tid == 0) {
             hdr[0] = s_err | kErrSeqLen;
-            hdr[1] = 0; hdr[2] = 0; hdr[3] = 0; hdr[4] = 0;
+            hdr[1] = 0; hdr[2] = 0; hdr[3] = 0; hdr[4] = 0; hdr[5] = a.group_mode;
         }
         return;
     }
@@ -192,7 +194,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
 
     __syncthreads();
 
-    // every task slot the merge kernel may look at starts empty
+    // every task slot the merge kernel may look at starts empty (in group mode: every
+    // pair's arrival counter starts at zero)
     for (int w = tid; w <= a.max_waves; w += kPlanThreads) tasks[w] = make_int4(0, 0, 0, 0);
     // rows with nothing to read (empty context, or rejected lengths) get zeros later
     for (int u = tid; u < U; u += kPlanThreads)
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     // position in a pair's first C quarters maps to the pair's first block, one further on
     // to the next whole block.  Consecutive y differ by at least 31 >= C + 4, so every share
     // holds at least one block and the shares are consecutive.
-    for (int u = tid; u < U && W > 0; u += kPlanThreads) {
+    for (int u = tid; u < U && W > 0 && !a.group_mode; u += kPlanThreads) {
         const uint64_t c0 = cw[u], c1 = cw[u + 1];
         if (c1 == c0) continue;
         const uint64_t w0 = (c0 * (uint64_t)W + TW - 1) / TW;
@@ -220,11 +223,40 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
             wu[w] = u;
         }
     }
+    // group mode: wavefront i of the N = 4 group_mode wavefronts of pair (u, g) takes blocks
+    // [i nb / N, (i + 1) nb / N) of the pair (an empty share when the pair has fewer blocks);
+    // the pairs' arrival counters live in the task slots zeroed above
+    for (int w = tid; w < W && a.group_mode; w += kPlanThreads) {
+        const int N = kWavesPerGroup * a.group_mode, pr = w / N, i = w % N;
+        const int u = pr / (int)H, g = pr % (int)H;
+        const UnitInfo ui = unit[u];
+        const uint32_t nb = ui.nb > 0 ? (uint32_t)ui.nb : 0u;
+        const uint32_t ps = cb[u] + (uint32_t)g * nb;
+        WaveStart st{};
+        st.x0 = ps + (uint32_t)i * nb / N;
+        st.x1 = ps + (uint32_t)(i + 1) * nb / N;
+        st.u = u;
+        st.g = g;
+        st.ps = ps;
+        st.pe = ps + nb;
+        st.j0 = ui.b_lo + (int32_t)(st.x0 - ps);
+        st.j1 = ui.b_lo + (int32_t)(st.x1 - ps);
+        st.seq = ui.seq;
+        st.len = ui.len;
+        if (st.x1 > st.x0) {
+            const int32_t* bt = a.block_tables + (size_t)ui.seq * a.max_blocks;
+            st.b0 = bt[st.j0];
+            st.b1 = st.j0 + 1 < st.j1 ? bt[st.j0 + 1] : st.b0;
+        }
+        wst[w] = st;
+        wx0[w] = st.x0;
+        wu[w] = u;
+    }
     __syncthreads();
     if (tid == 0) wx0[W] = T;
     __syncthreads();
     // each share's first segment, as the decode kernels would find it from wx0 and wu
-    for (int w = tid; w < W; w += kPlanThreads) {
+    for (int w = tid; w < W && !a.group_mode; w += kPlanThreads) {
         const uint32_t x0 = wx0[w], x1 = wx0[w + 1];
         int u = wu[w];
         while (cb[u + 1] <= x0) ++u;                 // skip finished / empty units
@@ -251,6 +283,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     }
     if (tid == 0) {
         hdr[0] = s_err; hdr[1] = (int32_t)T; hdr[2] = W; hdr[3] = s_empty; hdr[4] = (int32_t)NT;
+        hdr[5] = a.group_mode;
     }
 }
 

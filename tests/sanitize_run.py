@@ -53,8 +53,9 @@ def decode_host_paths(lib):
         mx = int(w.seq_lens.max())
         n = lib.pa_decode_workspace_size(ctypes.byref(desc), B, R, w.num_q_heads, mx)
         assert n > 0, name
-        assert lib.pa_decode_kernel_name(ctypes.byref(desc), w.num_q_heads) in (
-            b"decode_kernel", b"decode_mfma_kernel"), name
+        kname = lib.pa_decode_kernel_name(ctypes.byref(desc), w.num_q_heads, B, w.window)
+        assert kname in (b"decode_kernel", b"decode_mfma_kernel", b"decode_group_kernel"), name
+        assert (kname == b"decode_group_kernel") == (name == "swa"), (name, kname)
         qsl = fake if (w.q_rows != 1).any() else None
         mb = -(-mx // w.block_size)
         out_dt = pa.PA_F32

@@ -58,6 +58,9 @@ pa_status noalloc_scratch(void** out, size_t* bytes) {
 const void* decode_kernel_ptr(int, int, int group, int, bool) {
     return group_ok(group) ? &g_kernel : nullptr;
 }
+const void* decode_group_ptr(int, int, int group, bool) {
+    return group_ok(group) ? &g_kernel : nullptr;
+}
 bool decode_uses_mfma(int dtype, int group, int block_size) {
     return block_size == kBlock && dtype != PA_F32 && (group == 4 || group == 8);
 }

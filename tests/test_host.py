@@ -41,7 +41,7 @@ def test_header_symbols_exported(pa):
 def test_decode_kernel_name(pa):
     lib = pa.load()
     name = lambda dt, hq, hkv=8, bs=16, d=128: lib.pa_decode_kernel_name(
-        ctypes.byref(pa.CacheDesc(10, bs, hkv, d, dt)), hq)
+        ctypes.byref(pa.CacheDesc(10, bs, hkv, d, dt)), hq, 4, 0)
     assert name(pa.PA_BF16, 32) == b"decode_mfma_kernel"          # groups of 4
     assert name(pa.PA_Q8_BF16, 64) == b"decode_mfma_kernel"       # groups of 8, 8-bit
     assert name(pa.PA_F16, 40, 40) == b"decode_kernel"            # one query head per KV head
