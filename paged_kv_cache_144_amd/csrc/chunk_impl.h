@@ -19,9 +19,13 @@
 // applies the causal / window mask by selection (only on steps that straddle a row's edge),
 // runs the online softmax per M-row (each lane owns one M-row column; partner lane l^32
 // holds the other half of the step's tokens), and
-//     O^T[d][M-row] += V^T . P^T                     (4 * D/32 MFMAs: P = hi + lo)
+//     O^T[d][M-row] += V^T . P^T                     (2 * D/32 fp16 MFMAs)
 // where P^T comes straight from the S^T accumulator registers in the MFMA B-operand order
-// and the V^T operand is two LDS transpose reads in the matching token order.  The running
+// and the V^T operand is two LDS transpose reads in the matching token order.  P and V
+// enter that product in fp16 for both cache types: bf16 V is converted as it is staged,
+// exactly wherever |v| lies in fp16's range.  A bf16 value beyond that range sets a flag,
+// and the workgroup then computes its tile again in a second pass that stages V as bf16 and
+// carries P as hi + lo bf16 parts (two MFMAs per product).  The running
 // max is raised only when a row's new maximum exceeds it by more than 2^8 (weights stay
 // <= 256), so the accumulators are rescaled on few steps.  The next step's global loads are
 // in flight while the current step computes (LDS double buffer, one barrier per step).
@@ -90,6 +94,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     constexpr float kNegBig = -3.402823466e38f;
     __shared__ __attribute__((aligned(16))) char lds_k[2][S::KREG];
     __shared__ __attribute__((aligned(16))) char lds_v[2][S::VREG];
+    __shared__ int lds_vover;                  // a staged bf16 V value is beyond fp16's range
+    constexpr bool kConvV = DT == DT_BF16;
 
     const int32_t* hdr = (const int32_t*)(a.ws + a.lay.header);
     const int2* tiles = (const int2*)(a.ws + a.lay.tiles);
@@ -157,11 +163,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     }
 
     f32x16 acc[DT32];
-#pragma unroll
-    for (int dt = 0; dt < DT32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-    float m_run = kNegBig, l_run = 0.f;
+    float m_run, l_run;
     const float qscale = fabsf(a.scale) * kLog2e;
 
     const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks;
@@ -232,11 +234,28 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             vm |= (uint32_t)ok(tau) << i;
         }
     };
+    // bf16 V -> fp16, rounded to nearest: exact for |v| in fp16's normal range, within
+    // 2^-25 below it.  vmax collects the largest |v| bit patterns (two 16-bit halves; for
+    // bf16, a larger magnitude is a larger pattern), so that values past the range are
+    // caught: |v| >= 65520 is a bf16 pattern of at least 0x4780 (65536).
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    auto v_to_f16 = [&](const u32x4& x, u16x2& vmax) {
+        u32x4 y;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float lo = __uint_as_float(x[w] << 16);
+            const float hi = __uint_as_float(x[w] & 0xffff0000u);
+            vmax = __builtin_elementwise_max(vmax, __builtin_bit_cast(u16x2, x[w] & 0x7fff7fffu));
+            y[w] = cvt2<DT_F16>(lo, hi);
+        }
+        return y;
+    };
     // A step whose tokens are all staged (the common case) stores without the per-piece
     // selects: the store body is instantiated with and without masks, chosen by a scalar
-    // branch.
-    auto stage_store = [&](int buf, const u32x4* sk, const u32x4* sv, uint32_t km,
+    // branch.  Cc: the fp16 pass (bf16 V converted) or the bf16 pass.
+    auto stage_store = [&](auto Cc, int buf, const u32x4* sk, const u32x4* sv, uint32_t km,
                            uint32_t vm, bool all) {
+        constexpr bool kConv = decltype(Cc)::value && kConvV;
         auto put = [&](auto masked_c) {
             constexpr bool kMasked = decltype(masked_c)::value;
             const u32x4 z = {0u, 0u, 0u, 0u};
@@ -251,13 +270,19 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
                     st16(&lds_k[buf][(c / (D / 8)) * S::ROWB + (c % (D / 8)) * 16],
                          pick((km >> i) & 1u, sk[i]));
             }
+            u16x2 vmax = {0, 0};
 #pragma unroll
             for (int i = 0; i < S::VPT; ++i) {
                 const int c = tid + i * S::THREADS;
-                if (c < S::VPIECES)
-                    st16(&lds_v[buf][(c / (D / 8)) * S::ROWV + (c % (D / 8)) * 16],
-                         pick((vm >> i) & 1u, sv[i]));
+                if (c < S::VPIECES) {
+                    u32x4 x = pick((vm >> i) & 1u, sv[i]);
+                    if constexpr (kConv) x = v_to_f16(x, vmax);
+                    st16(&lds_v[buf][(c / (D / 8)) * S::ROWV + (c % (D / 8)) * 16], x);
+                }
             }
+            // 65520 and above round to infinity in fp16; NaN (a larger pattern still)
+            // would pass through unchanged but takes the bf16 pass too
+            if (kConv && (vmax.x >= 0x4780 || vmax.y >= 0x4780)) lds_vover = 1;
         };
         if (all)
             put(std::false_type{});
@@ -269,16 +294,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     // case keep the wait counts exact)
     const int t_last = t_first + (nsteps > 0 ? nsteps - 1 : 0) * S::STEP;
     auto step_t = [&](int st) { return min(t_first + st * S::STEP, t_last); };
-    stage_load(step_t(0), sk[0], sv[0], kmask[0], vmask[0], whole[0]);
-    if (nsteps > 0) stage_store(0, sk[0], sv[0], kmask[0], vmask[0], whole[0]);
-    stage_load(step_t(1), sk[1], sv[1], kmask[1], vmask[1], whole[1]);
-    stage_load(step_t(2), sk[0], sv[0], kmask[0], vmask[0], whole[0]);
-    __syncthreads();
     // step st computes from LDS buffer st & 1 while steps st+1 (register set (st+1) & 1)
     // and st+2 are loading; then st+1 goes to LDS and step st+3 starts loading into the
     // set st+1 used.  P = (st + 1) & 1 is a compile-time constant.
-    auto body = [&](auto Pc, int st) {
+    auto body = [&](auto Cc, auto Pc, int st) {
         constexpr int P = decltype(Pc)::value;
+        constexpr bool kF16PV = DT == DT_F16 || decltype(Cc)::value;
         const int buf = st & 1, t0 = t_first + st * S::STEP;
         if (t0 <= wp_last && t0 + S::STEP > wlo_first) {      // wavefront-uniform
             const char* kl = lds_k[buf];
@@ -347,19 +368,27 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             }
             l_run += psum;
             // P^T operands: K-step k2 covers tokens 16 k2 .. 16 k2 + 15; element kk of lane
-            // (j, h) is token 16 k2 + (kk < 4 ? 4 h + kk : 8 + 4 h + kk - 4) = p16[8 k2 + kk]
+            // (j, h) is token 16 k2 + (kk < 4 ? 4 h + kk : 8 + 4 h + kk - 4) = p16[8 k2 + kk].
+            // fp16 pass: P rounded to nearest fp16 (2^-11 relative; p <= 2^8 here).  bf16
+            // pass: P = hi + lo bf16 parts (about 16 significant bits).
             u32x4 pb[2], pl[2];
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const float* pp = p16 + 8 * k2;
-                uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-                split2<DT>(pp[0], pp[1], h0, l0);
-                split2<DT>(pp[2], pp[3], h1, l1);
-                split2<DT>(pp[4], pp[5], h2, l2);
-                split2<DT>(pp[6], pp[7], h3, l3);
-                const u32x4 th = {h0, h1, h2, h3}, tl2 = {l0, l1, l2, l3};
-                pb[k2] = th;
-                pl[k2] = tl2;
+                if constexpr (kF16PV) {
+                    const u32x4 th = {cvt2<DT_F16>(pp[0], pp[1]), cvt2<DT_F16>(pp[2], pp[3]),
+                                      cvt2<DT_F16>(pp[4], pp[5]), cvt2<DT_F16>(pp[6], pp[7])};
+                    pb[k2] = th;
+                } else {
+                    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+                    split2<DT>(pp[0], pp[1], h0, l0);
+                    split2<DT>(pp[2], pp[3], h1, l1);
+                    split2<DT>(pp[4], pp[5], h2, l2);
+                    split2<DT>(pp[6], pp[7], h3, l3);
+                    const u32x4 th = {h0, h1, h2, h3}, tl2 = {l0, l1, l2, l3};
+                    pb[k2] = th;
+                    pl[k2] = tl2;
+                }
             }
             // O^T += V^T . P^T.  Lane (j, h) needs column j of tokens 16 k2 + 4 h .. +3 and
             // 16 k2 + 8 + 4 h .. +3, in that order: two LDS transpose reads (each lane of a
@@ -373,18 +402,44 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
                     const char* p0 = vl + v_lane + (16 * k2) * S::ROWV + 64 * dt;
                     const u32x2 t0 = tr_read(p0), t1 = tr_read(p0 + 8 * S::ROWV);
                     const u32x4 va = {t0.x, t0.y, t1.x, t1.y};
-                    acc[dt] = mfma32<DT>(va, pb[k2], acc[dt]);
-                    acc[dt] = mfma32<DT>(va, pl[k2], acc[dt]);
+                    if constexpr (kF16PV) {
+                        acc[dt] = mfma32<DT_F16>(va, pb[k2], acc[dt]);
+                    } else {
+                        acc[dt] = mfma32<DT>(va, pb[k2], acc[dt]);
+                        acc[dt] = mfma32<DT>(va, pl[k2], acc[dt]);
+                    }
                 }
             }
         }
-        if (st + 1 < nsteps) stage_store(buf ^ 1, sk[P], sv[P], kmask[P], vmask[P], whole[P]);
+        if (st + 1 < nsteps)
+            stage_store(Cc, buf ^ 1, sk[P], sv[P], kmask[P], vmask[P], whole[P]);
         stage_load(step_t(st + 3), sk[P], sv[P], kmask[P], vmask[P], whole[P]);
         __syncthreads();
     };
-    for (int st = 0; st < nsteps; st += 2) {
-        body(std::integral_constant<int, 1>{}, st);
-        if (st + 1 < nsteps) body(std::integral_constant<int, 0>{}, st + 1);
+    // one pass over the tile's steps
+    auto pass = [&](auto Cc) {
+#pragma unroll
+        for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+        m_run = kNegBig;
+        l_run = 0.f;
+        stage_load(step_t(0), sk[0], sv[0], kmask[0], vmask[0], whole[0]);
+        if (nsteps > 0) stage_store(Cc, 0, sk[0], sv[0], kmask[0], vmask[0], whole[0]);
+        stage_load(step_t(1), sk[1], sv[1], kmask[1], vmask[1], whole[1]);
+        stage_load(step_t(2), sk[0], sv[0], kmask[0], vmask[0], whole[0]);
+        __syncthreads();
+        for (int st = 0; st < nsteps; st += 2) {
+            body(Cc, std::integral_constant<int, 1>{}, st);
+            if (st + 1 < nsteps) body(Cc, std::integral_constant<int, 0>{}, st + 1);
+        }
+    };
+    if (tid == 0) lds_vover = 0;
+    __syncthreads();
+    pass(std::true_type{});
+    if constexpr (kConvV) {
+        // every pass ends on a barrier, so the flag is settled and the same for the group
+        if (__builtin_amdgcn_readfirstlane(lds_vover) != 0) pass(std::false_type{});
     }
     if (bad) atomicOr((int32_t*)(a.ws + a.lay.header), kErrBlockId);
 

@@ -526,6 +526,41 @@ def test_chunk_rows_parity(torch, pa, orc, monkeypatch, kw):
     assert np.abs(out - alt).max() < 2e-3
 
 
+def test_chunk_rows_bf16_values_past_fp16_range(torch, pa, orc, monkeypatch):
+    """The chunk kernel multiplies P and V in fp16, converting bf16 V as it stages it; a bf16
+    value beyond fp16's range (|v| >= 65520) sends its workgroup through a second pass that
+    keeps V in bf16.  With such values planted in the context of two chunks, the output stays
+    finite and meets the oracle and the decode route within 2e-3 + 2^-14 max|v| (P as hi + lo
+    bf16 parts there), and the rows of the other sequences stay within the usual bound."""
+    kw = dict(lens=[300, 64, 100, 40], rows=[37, 1, 100, 2], hq=8, hkv=2, d=128, dtype="bf16")
+    w = workloads.make("rows", **kw)
+    lr = logical_rows(w)
+    big = workloads.to_storage(np.array([1.0e5, -3.0e5, 7.0e4, 65520.0], np.float32), "bf16")
+    for s, taus in ((0, (5, 250)), (2, (0, 61, 99))):
+        for i, tau in enumerate(taus):
+            w.v[lr[s][tau], i % w.num_kv_heads, 3:7] = big
+    vmax = 3.0e5
+    dw = run(w, torch)
+    ref = orc.Reference(w).attention()
+    out = dw.decode().cpu().numpy()
+    assert pa.device_error_bits(dw.workspace) == 0
+    assert np.isfinite(out).all(), "non-finite output: the bf16 pass did not run"
+    qsl = w.query_start_loc()
+    hit = np.zeros(out.shape[0], bool)
+    for s in (0, 2):
+        hit[qsl[s]:qsl[s + 1]] = True
+    bound = 2e-3 + vmax * 2.0 ** -14
+    d = np.abs(out[hit] - ref[hit])
+    say(f"rows with large V: max|d|={d.max():.3e} (bound {bound:.3e}), "
+        f"max|ref|={np.abs(ref[hit]).max():.3e}")
+    assert d.max() <= bound
+    check_close(out[~hit], ref[~hit], "other rows")
+    monkeypatch.setenv("PA_CHUNK_KERNEL", "0")
+    alt = dw.decode().cpu().numpy()
+    monkeypatch.delenv("PA_CHUNK_KERNEL")
+    assert np.abs(out - alt).max() <= bound
+
+
 WINDOW_CASES = [
     # (group, head_dim, dtype): the per-lane kernel (G = 1, 2), the matrix-core kernel
     # (G = 4, 8), 8-bit caches on both
