@@ -362,15 +362,19 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
     fused = (args.step == "fused" and bool((w.q_rows == 1).all())
              and w.dtype in ("f32", "f16", "bf16"))
 
-    every = max(1, args.event_every)
-    sampled = list(range(0, L, every))            # layers whose launches are timed
+    # layers whose launches are timed: about three per step, in the middle of each group of
+    # `every` layers (an event pair costs the GPU a few microseconds, about a tenth of a
+    # sliding-window layer, so fewer pairs keep the step close to an untimed one)
+    every = max(1, args.event_every or -(-L // 3))
+    sampled = list(range(every // 2, L, every))
+    slot = {li: si for si, li in enumerate(sampled)}
 
     def step(events=None, cevents=None, xevents=None, wevents=None):
         pa.decode(dw.q, pools[0][0], pools[0][1], dw.block_tables, dw.seq_lens, float(w.scale),
                   step="plan", **common)
         for li, (kc, vc) in enumerate(pools):
-            timed_layer = li % every == 0
-            si = li // every
+            timed_layer = li in slot
+            si = slot.get(li, 0)
             if copies is not None:
                 if xevents is not None and timed_layer:
                     xevents[si][0].record()
@@ -584,10 +588,11 @@ def main():
                     help="tokens per KV block (8 and 32: OPT-13B and GQA shapes, 16-bit KV)")
     ap.add_argument("--kv", choices=["native", "q8"], default="native",
                     help="q8: 8-bit KV cache (one fp16 scale per 32 values), same workload")
-    ap.add_argument("--event-every", type=int, default=4, metavar="N",
+    ap.add_argument("--event-every", type=int, default=None, metavar="N",
                     help="kernel durations come from hipEvents recorded around the launches "
                          "of every N-th layer of each timed step (each recorded event adds a "
-                         "few microseconds of queue gap, which N = 1 would add to every layer)")
+                         "few microseconds of queue gap, which N = 1 would add to every layer); "
+                         "default: about three layers per step")
     ap.add_argument("--step", choices=["fused", "separate"], default="fused",
                     help="fused: each layer's slot write runs inside its decode launch "
                          "(pa_decode_write_attend) where the batch allows it (one query row "
