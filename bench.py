@@ -50,9 +50,15 @@ Q8_DTYPE = {"opt13b": "q8_f16", "gqa": "q8_bf16", "swa": "q8_f16", "prefix_mixed
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense matrix peak, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SOURCES = ["decode_impl.h", "decode_mfma.h", "decode_group.h", "pa_device.h", "pa_internal.h",
-                  "plan.hip"]
-CHUNK_SOURCES = ["chunk_impl.h", "pa_device.h", "pa_internal.h", "plan.hip"]
+# The sources each kernel is built from (the launch code in decode.hip and the plan
+# included): a committed counter record stays valid while they are unchanged.
+COMMON_SOURCES = ["pa_device.h", "pa_internal.h", "plan.hip", "decode.hip"]
+KERNEL_SOURCES = {
+    "decode_kernel": ["decode_impl.h", *COMMON_SOURCES],
+    "decode_mfma_kernel": ["decode_impl.h", "decode_mfma.h", *COMMON_SOURCES],
+    "decode_group_kernel": ["decode_impl.h", "decode_group.h", *COMMON_SOURCES],
+}
+CHUNK_SOURCES = ["chunk_impl.h", *COMMON_SOURCES]
 
 DESCRIPTIONS = {
     "opt13b": "OPT-13B-shaped paged decode: 64 seqs, 40 q heads = 40 KV heads, d=128, fp16 KV, "
@@ -72,7 +78,7 @@ DESCRIPTIONS = {
 }
 
 
-def kernel_source_hash(files=KERNEL_SOURCES) -> str:
+def kernel_source_hash(files) -> str:
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "paged_kv_cache_144_amd", "csrc", f), "rb") as fh:
@@ -80,7 +86,7 @@ def kernel_source_hash(files=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(key: str, files=KERNEL_SOURCES):
+def measured_traffic(key: str, files):
     """HBM bytes per launch of one kernel from the committed rocprofv3 counter runs (entry
     `key`: the workload, or the workload + "_chunk" for the chunk-row kernel), or None when
     there is none or that kernel's sources changed since."""
@@ -368,6 +374,19 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
     every = max(1, args.event_every or -(-L // 3))
     sampled = list(range(every // 2, L, every))
     slot = {li: si for si, li in enumerate(sampled)}
+    # Where a layer is exactly one launch (the one-launch step in group mode: no merge, no
+    # copy, no chunk rows), one event pair brackets a run of consecutive layers instead, so
+    # that the pair's own cost (a few microseconds, a sixth of a sliding-window kernel) is
+    # shared by the run; the per-launch time then includes the short gaps between launches.
+    kernel = pa.decode_kernel_name(dw.k_cache, w.num_q_heads, dw.q.dtype, w.num_seqs,
+                                   w.window if bool((w.q_rows == 1).all()) else 0)
+    run = 1
+    if (fused and kernel == "decode_group_kernel" and copies is None and not has_chunks
+            and args.event_every is None and every >= 4):
+        run = every - 2
+        sampled = list(range(1, L - run + 1, every))
+        slot = {li: si for si, li in enumerate(sampled)}
+    run_end = {li + run - 1: si for si, li in enumerate(sampled)}
 
     def step(events=None, cevents=None, xevents=None, wevents=None):
         pa.decode(dw.q, pools[0][0], pools[0][1], dw.block_tables, dw.seq_lens, float(w.scale),
@@ -387,8 +406,10 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
                 pa.write_kv(k_step, v_step, slot_step, kc, vc)
                 if wevents is not None and timed_layer:
                     wevents[si][1].record()
-            if events is not None:
+            if events is not None and run == 1:
                 pa.set_decode_profile_events(*(events[si] if timed_layer else (None, None)))
+            elif events is not None and timed_layer:
+                events[si][0].record()
             if cevents is not None:
                 pa.set_chunk_profile_events(*(cevents[si] if timed_layer else (None, None)))
             if fused:
@@ -398,6 +419,8 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
             else:
                 pa.decode(dw.q, kc, vc, dw.block_tables, dw.seq_lens, float(w.scale), out=out,
                           step="attend", **common)
+            if events is not None and run > 1 and li in run_end:
+                events[run_end[li]][1].record()
         if events is not None:
             pa.set_decode_profile_events(None, None)
         if cevents is not None:
@@ -430,7 +453,7 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    dec_avg_ms = float(np.mean([a.elapsed_time(b) for per in evs for a, b in per]))
+    dec_avg_ms = float(np.mean([a.elapsed_time(b) for per in evs for a, b in per])) / run
     chunk_avg_ms = (float(np.mean([a.elapsed_time(b) for per in cevs for a, b in per]))
                     if cevs else 0.0)
     copy_avg_ms = (float(np.mean([a.elapsed_time(b) for per in xevs for a, b in per]))
@@ -446,11 +469,10 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
     kv_decode = kv_bytes_read(w.seq_lens[dec], w.q_rows[dec], w.window, w.num_kv_heads,
                               w.head_dim, w.elem_bytes)
     achieved = kv_decode / (dec_avg_ms / 1e3) / 1e9
-    traffic = (measured_traffic(name + ("_q8" if kv == "q8" else ""))
+    traffic = (measured_traffic(name + ("_q8" if kv == "q8" else ""), KERNEL_SOURCES[kernel])
                if block_size == 16 else None)
     decode_roof = {
-        "kernel": pa.decode_kernel_name(dw.k_cache, w.num_q_heads, dw.q.dtype, w.num_seqs,
-                                        w.window if dec.all() else 0),
+        "kernel": kernel,
         "bound": "hbm",
         "achieved": round(achieved, 2),
         "peak": HBM_PEAK_GBS,
@@ -459,7 +481,9 @@ def measure(args, name, kv="native", block_size=16, swap_seqs=0, cpu_seconds=Non
         "traffic": traffic,
         "algorithmic_bytes_per_launch": int(kv_decode),
         "decode_kernel_avg_us": round(dec_avg_ms * 1e3, 2),
-        "launches_timed": args.steps * len(sampled),
+        "launches_timed": args.steps * len(sampled) * run,
+        "timing": ("hipEvents around each timed launch" if run == 1 else
+                   f"hipEvents around runs of {run} consecutive one-launch layers"),
     }
     chunk_roof = None
     if has_chunks:
