@@ -81,6 +81,13 @@ struct MfmaKv16 {
     static constexpr size_t TILE = (size_t)kBlock * D * 2;
     static constexpr int BPT = 1;                 // blocks per tile
     static constexpr bool kNewRows = true;        // can take a step's new rows directly
+    // column c16 of S^T is query head c16 (none past G); output row 4 q4 + r is head
+    // 4 q4 + r, for every column block
+    __device__ static int q_head(int c16) { return c16; }
+    __device__ static bool q_valid(int c16) { return c16 < G; }
+    __device__ static int row_head(int q4, int r) { return 4 * q4 + r; }
+    __device__ static bool row_valid(int q4, int r) { return 4 * q4 + r < G; }
+    __device__ static bool row_has_block(int, int, int) { return true; }
 
     struct Q { u32x4 b[KC]; float f; };
     struct Tile { u32x4 k[KC], v[NLD]; };
@@ -177,14 +184,18 @@ struct MfmaKv16 {
     __device__ static void rescale(Extra&, float) {}
     __device__ static void finish(f32x4 (&)[NACC], const Extra&) {}
     // acc[b] of lane c16 is column 16 b + c16
+    // row r of lane quad q4, column blocks row_has_block(q4, r, b)
     __device__ static void store(const DecodeArgs& a, size_t ob, const f32x4 (&acc)[NACC],
-                                 int r, float inv, int c16) {
+                                 int r, float inv, int c16, int q4) {
 #pragma unroll
-        for (int b = 0; b < NACC; ++b) store_out1(a, ob + 16 * b + c16, acc[b][r] * inv);
+        for (int b = 0; b < NACC; ++b)
+            if (row_has_block(q4, r, b)) store_out1(a, ob + 16 * b + c16, acc[b][r] * inv);
     }
-    __device__ static void store_part(float* dst, const f32x4 (&acc)[NACC], int r, int c16) {
+    __device__ static void store_part(float* dst, const f32x4 (&acc)[NACC], int r, int c16,
+                                      int q4) {
 #pragma unroll
-        for (int b = 0; b < NACC; ++b) dst[16 * b + c16] = acc[b][r];
+        for (int b = 0; b < NACC; ++b)
+            if (row_has_block(q4, r, b)) dst[16 * b + c16] = acc[b][r];
     }
 };
 
@@ -219,6 +230,22 @@ struct MfmaKvQ8 {
     static_assert(KC % 2 == 0, "an even number of scale groups");
     // new rows must be quantized into the cache first (pa_write_kv)
     static constexpr bool kNewRows = false;
+    // Stacked P.V, where the scale groups and heads fit the MFMA's 16 rows: A row m is
+    // (scale group m / G, head m % G), so one A operand (P x the row's own V scale) serves
+    // every 16-column block, and output row m is meaningful in its own group's two column
+    // blocks only.  The query's columns then repeat the heads (column m holds head m % G),
+    // so that S^T, the softmax and P arrive in that row order with no lane exchange.
+    static constexpr bool kStacked = KC * G <= 16;
+    __device__ static int q_head(int c16) { return kStacked ? c16 % G : c16; }
+    __device__ static bool q_valid(int c16) { return kStacked ? c16 / G < KC : c16 < G; }
+    __device__ static int row_head(int q4, int r) { return kStacked ? (4 * q4 + r) % G : 4 * q4 + r; }
+    __device__ static bool row_valid(int q4, int r) {
+        return kStacked ? (4 * q4 + r) / G < KC : 4 * q4 + r < G;
+    }
+    // column block b (scale group b / 2) of output row 4 q4 + r
+    __device__ static bool row_has_block(int q4, int r, int b) {
+        return !kStacked || (4 * q4 + r) / G == b / 2;
+    }
 
     struct Q { u32x4 b[KC]; float f; };
     // k: load i of lane l holds bytes 1024 i + 16 l of the block's codes (whole rows per
@@ -243,7 +270,7 @@ struct MfmaKvQ8 {
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int c = 0; c < KC; ++c)
-            r.b[c] = c16 < G ? ld16((const char*)q + (qrow + 32 * c + 8 * q4) * 2) : z;
+            r.b[c] = q_valid(c16) ? ld16((const char*)q + (qrow + 32 * c + 8 * q4) * 2) : z;
     }
     __device__ static void prep_q(Q& r) {
         float v[KC][8];
@@ -357,7 +384,26 @@ struct MfmaKvQ8 {
         // a V scale piece (lanes 32-63) belongs to token (lane - 32) / 2: zero for tokens the
         // row does not see, so that their V values are exact zeros whatever the slot holds
         const bool keep = lane < 32 || ok(h, t0 + (lane - 32) / 2);
-        if constexpr (SB == 2) {
+        if constexpr (kStacked) {
+            // K row as below; the V row group-major, [group][token], so that a lane's four
+            // tokens of its own group are one 8-byte read.  Lane 32 + i holds the SB / 2
+            // scales of token i / 2, groups (i % 2) SB / 2 ..
+            if (lane < 32) {
+                if constexpr (SB == 2)
+                    *reinterpret_cast<uint16_t*>(srow + SB * lane) = (uint16_t)tl.sc[h][0];
+                else
+                    *reinterpret_cast<uint32_t*>(srow + SB * lane) = tl.sc[h][0];
+            } else {
+                const int i = lane - 32, t = i / 2;
+                uint16_t* vrow = reinterpret_cast<uint16_t*>(srow + D);
+#pragma unroll
+                for (int e = 0; e < SB / 2; ++e) {
+                    const int g = (i % 2) * (SB / 2) + e;
+                    const uint32_t w = tl.sc[h][e / 2];
+                    vrow[g * kBlock + t] = keep ? (uint16_t)(e % 2 ? w >> 16 : w & 0xffffu) : 0;
+                }
+            }
+        } else if constexpr (SB == 2) {
             *reinterpret_cast<uint16_t*>(srow + SB * lane) = keep ? (uint16_t)tl.sc[h][0] : 0;
         } else if constexpr (SB == 4) {
             *reinterpret_cast<uint32_t*>(srow + SB * lane) = keep ? tl.sc[h][0] : 0u;
@@ -421,6 +467,30 @@ struct MfmaKvQ8 {
                     *reinterpret_cast<u32x4*>(dst + i) = u32x4{o[i], o[i + 1], o[i + 2], o[i + 3]};
             }
         }
+        if constexpr (kStacked) {
+            // A row c16 = (group c16 / G, head c16 % G): this lane's p (its column's head)
+            // times the V scales of its group, tokens 4 q4 .. +3; one A for every block b
+            const int gq = c16 / G < KC ? c16 / G : KC - 1;
+#pragma unroll
+            for (int h = 0; h < BPT; ++h) {
+                const u32x2 sw = *reinterpret_cast<const u32x2*>(
+                    my + LDSS + h * 2 * D + D + (gq * kBlock + 4 * q4) * 2);
+                const float pg0 = p[h][0] * f16_lo(sw.x), pg1 = p[h][1] * f16_hi(sw.x);
+                const float pg2 = p[h][2] * f16_lo(sw.y), pg3 = p[h][3] * f16_hi(sw.y);
+                uint32_t h0, l0, h1, l1;
+                split2<DT_BF16>(pg0, pg1, h0, l0);
+                split2<DT_BF16>(pg2, pg3, h1, l1);
+                const u32x2 ph = {h0, h1}, pl = {l0, l1};
+                const uint32_t* src = lw + h * VBLK + 2 * q4 * PS + c16;
+#pragma unroll
+                for (int b = 0; b < NACC; ++b) {
+                    const u32x2 vb = {src[vcol(16 * b)], src[PS + vcol(16 * b)]};
+                    acc[b] = mfma_16x16x16<DT_BF16>(ph, vb, acc[b]);
+                    acc[b] = mfma_16x16x16<DT_BF16>(pl, vb, acc[b]);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int h = 0; h < BPT; ++h) {
             Scales vs;
@@ -451,14 +521,18 @@ struct MfmaKvQ8 {
     __device__ static void rescale(Extra&, float) {}
     __device__ static void finish(f32x4 (&)[NACC], const Extra&) {}
     // acc[b] of lane c16 is column 16 b + c16
+    // row r of lane quad q4, column blocks row_has_block(q4, r, b)
     __device__ static void store(const DecodeArgs& a, size_t ob, const f32x4 (&acc)[NACC],
-                                 int r, float inv, int c16) {
+                                 int r, float inv, int c16, int q4) {
 #pragma unroll
-        for (int b = 0; b < NACC; ++b) store_out1(a, ob + 16 * b + c16, acc[b][r] * inv);
+        for (int b = 0; b < NACC; ++b)
+            if (row_has_block(q4, r, b)) store_out1(a, ob + 16 * b + c16, acc[b][r] * inv);
     }
-    __device__ static void store_part(float* dst, const f32x4 (&acc)[NACC], int r, int c16) {
+    __device__ static void store_part(float* dst, const f32x4 (&acc)[NACC], int r, int c16,
+                                      int q4) {
 #pragma unroll
-        for (int b = 0; b < NACC; ++b) dst[16 * b + c16] = acc[b][r];
+        for (int b = 0; b < NACC; ++b)
+            if (row_has_block(q4, r, b)) dst[16 * b + c16] = acc[b][r];
     }
 };
 
@@ -540,7 +614,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
         return lane < n ? a.block_tables[(size_t)sg.seq * a.max_blocks + c0 + lane] : 0;
     };
     auto load_q = [&](const Seg& sg, Q& q) {
-        const size_t qrow = ((size_t)sg.u * a.num_q_heads + (size_t)sg.g * G + c16) * D;
+        const size_t qrow =
+            ((size_t)sg.u * a.num_q_heads + (size_t)sg.g * G + Ops::q_head(c16)) * D;
         Ops::load_q(a.q, qrow, c16, q4, q);
     };
     auto block_id = [&](int ids, int idx, bool& valid) {
@@ -653,7 +728,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
                 bad |= h < it.cnt && !it.ok[h];
                 Ops::scores(tl, h, q, my, t0[h], edge[h], ok, sc[h]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sc[h][r] = c16 < G ? sc[h][r] * qs : -INFINITY;
+                for (int r = 0; r < 4; ++r) sc[h][r] = Ops::q_valid(c16) ? sc[h][r] * qs : -INFINITY;
             }
             bool any_edge = false;
 #pragma unroll
@@ -679,10 +754,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
                 m = mn;
                 lsum *= alpha;
                 Ops::rescale(ex, alpha);
-                // O rows are heads 4 q4 + r: their factor sits in lane 4 q4 + r
+                // O row 4 q4 + r belongs to head row_head: its factor sits in that lane
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float ar = __shfl(alpha, 4 * q4 + r);
+                    const float ar = __shfl(alpha, Ops::row_head(q4, r));
 #pragma unroll
                     for (int b = 0; b < NACC; ++b) acc[b][r] *= ar;
                 }
@@ -755,15 +830,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int h = 4 * q4 + r;
+            const int h = Ops::row_head(q4, r);
             const float lh = __shfl(lt, h);
-            if (h < G) {
+            if (Ops::row_valid(q4, r)) {
                 if (complete) {
                     const float inv = lh > 0.f ? 1.f / lh : 0.f;
                     const size_t ob = ((size_t)cur.u * a.num_q_heads + (size_t)cur.g * G + h) * D;
-                    Ops::store(a, ob, acc, r, inv, c16);
+                    Ops::store(a, ob, acc, r, inv, c16, q4);
                 } else {
-                    Ops::store_part(pacc + (((size_t)wave * 2 + slot) * G + h) * D, acc, r, c16);
+                    Ops::store_part(pacc + (((size_t)wave * 2 + slot) * G + h) * D, acc, r, c16,
+                                    q4);
                 }
             }
         }
