@@ -210,10 +210,11 @@ struct MfmaKvQ8 {
     static constexpr int VW = CPL / 4;            // code dwords per V row and lane
     static constexpr int SW = KC / 2;             // 16-byte LDS reads of a lane's scales
     static constexpr int SCALES = kBlock * D;
-    // LDS dwords per staged token pair: column c sits at dword c + 4 (c / 64) (the skew
-    // keeps the 16-byte writes of lanes 8 apart off the same banks), and PS = 8 mod 16
-    // keeps the two-dword reads of the four lane rows on distinct banks
-    static constexpr int PS = (D + D / 16 + 7) / 16 * 16 + 8;
+    // LDS dwords per staged token pair: column c sits at dword c + 4 (c / 32) (the skew puts
+    // the 16-byte writes of the 8 lanes of one pass, CPL columns apart, on distinct groups
+    // of 4 of the 32 banks), and PS = 8 mod 16 keeps the one-dword reads of two lane rows
+    // on distinct banks
+    static constexpr int PS = (D + D / 8 + 15) / 16 * 16 + 8;
     static constexpr int SB = D / 32;             // scale-row bytes a lane loads (K or V row)
     // An 8-bit tile is half the bytes of a 16-bit one: two blocks per tile keep as many
     // bytes in flight per wavefront (head_dim 256 keeps one: its registers would not fit).
@@ -348,7 +349,11 @@ struct MfmaKvQ8 {
     __device__ static uint32_t pair_hi(uint32_t x) {
         return __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
     }
-    __device__ static int vcol(int c) { return c + 4 * (c / 64); }
+    __device__ static int vcol(int c) { return c + 4 * (c / 32); }
+    // K rows 8 .. 15 hold each 16-byte piece with its 8-byte halves swapped (byte offset
+    // XOR 8), so that the 8-byte operand reads of tokens c16 and c16 + 8, whose padded rows
+    // otherwise meet on the same banks, use different bank pairs
+    __device__ static int kswz(int row) { return (row & 8) ? 8 : 0; }
     __device__ static uint32_t minus1152(uint32_t h) {
         const f16x2 k = {(_Float16)1152.f, (_Float16)1152.f};
         return __builtin_bit_cast(uint32_t, as_f16x2(h) - k);
@@ -377,8 +382,10 @@ struct MfmaKvQ8 {
         char* krow = my + LDSK + h * kBlock * KS;
 #pragma unroll
         for (int i = 0; i < KN; ++i) {
-            const int byte = 1024 * i + 16 * lane;
-            *reinterpret_cast<u32x4*>(krow + (byte / D) * KS + byte % D) = tl.k[h][i];
+            const int byte = 1024 * i + 16 * lane, row = byte / D;
+            const u32x4 x = tl.k[h][i];
+            *reinterpret_cast<u32x4*>(krow + row * KS + byte % D) =
+                kswz(row) ? u32x4{x.z, x.w, x.x, x.y} : x;
         }
         char* srow = my + LDSS + h * 2 * D;
         // a V scale piece (lanes 32-63) belongs to token (lane - 32) / 2: zero for tokens the
@@ -414,9 +421,9 @@ struct MfmaKvQ8 {
         Scales ks;
         read_scales(srow, ks);
         u32x2 kp[KC];     // token c16, columns 32 c + 8 q4 .. +8
+        const char* kr = krow + c16 * KS + ((8 * q4) ^ kswz(c16));
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-            kp[c] = *reinterpret_cast<const u32x2*>(krow + c16 * KS + 32 * c + 8 * q4);
+        for (int c = 0; c < KC; ++c) kp[c] = *reinterpret_cast<const u32x2*>(kr + 32 * c);
         f32x4 sc[KC];
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
