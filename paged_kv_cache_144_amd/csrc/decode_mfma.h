@@ -24,9 +24,10 @@
 //     to keep as many bytes in flight per wavefront;
 //   * K rows are loaded whole (each 16-byte piece of a lane lies in one row) and reach the
 //     operand layout through LDS; the codes become exact fp16 integers (the flipped code
-//     byte under the exponent of 1024 gives 1152 + code; a packed subtract of 1152 leaves
-//     the code); the query is held in fp16 after a power-of-two scaling per head (exact for
-//     fp16 and bf16 values), whose inverse joins the softmax scale;
+//     byte under the exponent of 1024 gives 1152 + code; the score MFMA's accumulator
+//     starts at -1152 x the group's query sum, which removes the offset); the query is held
+//     in fp16 after a power-of-two scaling per head (exact for fp16 and bf16 values), whose
+//     inverse joins the softmax scale;
 //   * each 16x16x32 step of S^T covers exactly one 32-column scale group, so every step
 //     keeps its own accumulator and the per-(token, group) scales are applied to the four
 //     partial scores of each lane before they are summed;
@@ -248,7 +249,9 @@ struct MfmaKvQ8 {
         return !kStacked || (4 * q4 + r) / G == b / 2;
     }
 
-    struct Q { u32x4 b[KC]; float f; };
+    // bias[c]: -1152 x the sum of the head's 32 (scaled) query values of scale group c,
+    // the accumulator start that cancels the +1152 carried by every K code (below)
+    struct Q { u32x4 b[KC]; float f; float bias[KC]; };
     // k: load i of lane l holds bytes 1024 i + 16 l of the block's codes (whole rows per
     // load: an MFMA operand's 8-byte pieces are read back from LDS, since loading them
     // directly would split every row into four small memory requests); v: CPL codes of
@@ -288,10 +291,17 @@ struct MfmaKvQ8 {
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
             uint32_t w[4];
+            float sum = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; e += 2)
-                w[e / 2] = cvt2<DT_F16>(ldexpf(v[c][e], 15 - ex), ldexpf(v[c][e + 1], 15 - ex));
+            for (int e = 0; e < 8; e += 2) {
+                const float a = ldexpf(v[c][e], 15 - ex), b = ldexpf(v[c][e + 1], 15 - ex);
+                w[e / 2] = cvt2<DT_F16>(a, b);
+                sum += a + b;
+            }
             r.b[c] = u32x4{w[0], w[1], w[2], w[3]};
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);               // the group's 32 columns
+            r.bias[c] = -1152.f * sum;
         }
         r.f = ldexpf(1.f, ex - 15);
     }
@@ -354,10 +364,6 @@ struct MfmaKvQ8 {
     // XOR 8), so that the 8-byte operand reads of tokens c16 and c16 + 8, whose padded rows
     // otherwise meet on the same banks, use different bank pairs
     __device__ static int kswz(int row) { return (row & 8) ? 8 : 0; }
-    __device__ static uint32_t minus1152(uint32_t h) {
-        const f16x2 k = {(_Float16)1152.f, (_Float16)1152.f};
-        return __builtin_bit_cast(uint32_t, as_f16x2(h) - k);
-    }
     // the 4 KC fp16 scales of tokens 4 q4 .. +3 of one scale row, from its staged copy;
     // (r, group g) is number r KC + g
     struct Scales { u32x4 w[SW]; };
@@ -424,13 +430,17 @@ struct MfmaKvQ8 {
         const char* kr = krow + c16 * KS + ((8 * q4) ^ kswz(c16));
 #pragma unroll
         for (int c = 0; c < KC; ++c) kp[c] = *reinterpret_cast<const u32x2*>(kr + 32 * c);
+        // The A operand carries 1152 + code (exact fp16 integers, no subtraction); the
+        // accumulator starts at -1152 x the group's query sum, which takes the offset out.
+        // The products are exact; the offset adds at most a few fp32 roundings of the
+        // group's sum of |1152 q| (about 1e-5 of the raw score's scale).
         f32x4 sc[KC];
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
             const uint32_t x0 = kp[c].x ^ 0x80808080u, x1 = kp[c].y ^ 0x80808080u;
-            const u32x4 a = {minus1152(pair_lo(x0)), minus1152(pair_hi(x0)),
-                             minus1152(pair_lo(x1)), minus1152(pair_hi(x1))};
-            sc[c] = mfma_16x16x32<DT_F16>(a, q.b[c], f32x4{0.f, 0.f, 0.f, 0.f});
+            const u32x4 a = {pair_lo(x0), pair_hi(x0), pair_lo(x1), pair_hi(x1)};
+            const float bc = q.bias[c];
+            sc[c] = mfma_16x16x32<DT_F16>(a, q.b[c], f32x4{bc, bc, bc, bc});
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
