@@ -25,7 +25,8 @@
 //   * K rows are loaded whole (each 16-byte piece of a lane lies in one row) and reach the
 //     operand layout through LDS; the codes become exact fp16 integers (the flipped code
 //     byte under the exponent of 1024 gives 1152 + code; the score MFMA's accumulator
-//     starts at -1152 x the group's query sum, which removes the offset); the query is held
+//     starts at -1152 x the group's query sum, which removes the offset, or a packed
+//     subtraction does where registers are short); the query is held
 //     in fp16 after a power-of-two scaling per head (exact for fp16 and bf16 values), whose
 //     inverse joins the softmax scale;
 //   * each 16x16x32 step of S^T covers exactly one 32-column scale group, so every step
@@ -249,9 +250,12 @@ struct MfmaKvQ8 {
         return !kStacked || (4 * q4 + r) / G == b / 2;
     }
 
-    // bias[c]: -1152 x the sum of the head's 32 (scaled) query values of scale group c,
-    // the accumulator start that cancels the +1152 carried by every K code (below)
-    struct Q { u32x4 b[KC]; float f; float bias[KC]; };
+    // The K code offset (+1152, below) is cancelled by the score accumulator's start where
+    // the instance has registers for it (4 per scale group: the stacked instances with
+    // d >= 128), else by a packed subtraction per code pair.
+    static constexpr bool kBiasK = kStacked && D >= 128;
+    // bias[c]: -1152 x the sum of the head's 32 (scaled) query values of scale group c
+    struct Q { u32x4 b[KC]; float f; float bias[kBiasK ? KC : 1]; };
     // k: load i of lane l holds bytes 1024 i + 16 l of the block's codes (whole rows per
     // load: an MFMA operand's 8-byte pieces are read back from LDS, since loading them
     // directly would split every row into four small memory requests); v: CPL codes of
@@ -299,9 +303,11 @@ struct MfmaKvQ8 {
                 sum += a + b;
             }
             r.b[c] = u32x4{w[0], w[1], w[2], w[3]};
-            sum += __shfl_xor(sum, 16);
-            sum += __shfl_xor(sum, 32);               // the group's 32 columns
-            r.bias[c] = -1152.f * sum;
+            if constexpr (kBiasK) {
+                sum += __shfl_xor(sum, 16);
+                sum += __shfl_xor(sum, 32);           // the group's 32 columns
+                r.bias[c] = -1152.f * sum;
+            }
         }
         r.f = ldexpf(1.f, ex - 15);
     }
@@ -360,6 +366,10 @@ struct MfmaKvQ8 {
         return __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
     }
     __device__ static int vcol(int c) { return c + 4 * (c / 32); }
+    __device__ static uint32_t minus1152(uint32_t h) {
+        const f16x2 k = {(_Float16)1152.f, (_Float16)1152.f};
+        return __builtin_bit_cast(uint32_t, as_f16x2(h) - k);
+    }
     // K rows 8 .. 15 hold each 16-byte piece with its 8-byte halves swapped (byte offset
     // XOR 8), so that the 8-byte operand reads of tokens c16 and c16 + 8, whose padded rows
     // otherwise meet on the same banks, use different bank pairs
@@ -430,17 +440,23 @@ struct MfmaKvQ8 {
         const char* kr = krow + c16 * KS + ((8 * q4) ^ kswz(c16));
 #pragma unroll
         for (int c = 0; c < KC; ++c) kp[c] = *reinterpret_cast<const u32x2*>(kr + 32 * c);
-        // The A operand carries 1152 + code (exact fp16 integers, no subtraction); the
-        // accumulator starts at -1152 x the group's query sum, which takes the offset out.
-        // The products are exact; the offset adds at most a few fp32 roundings of the
+        // kBiasK: the A operand carries 1152 + code (exact fp16 integers, no subtraction);
+        // the accumulator starts at -1152 x the group's query sum, which takes the offset
+        // out.  The products are exact; the offset adds at most a few fp32 roundings of the
         // group's sum of |1152 q| (about 1e-5 of the raw score's scale).
         f32x4 sc[KC];
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
             const uint32_t x0 = kp[c].x ^ 0x80808080u, x1 = kp[c].y ^ 0x80808080u;
-            const u32x4 a = {pair_lo(x0), pair_hi(x0), pair_lo(x1), pair_hi(x1)};
-            const float bc = q.bias[c];
-            sc[c] = mfma_16x16x32<DT_F16>(a, q.b[c], f32x4{bc, bc, bc, bc});
+            if constexpr (kBiasK) {
+                const u32x4 a = {pair_lo(x0), pair_hi(x0), pair_lo(x1), pair_hi(x1)};
+                const float bc = q.bias[c];
+                sc[c] = mfma_16x16x32<DT_F16>(a, q.b[c], f32x4{bc, bc, bc, bc});
+            } else {
+                const u32x4 a = {minus1152(pair_lo(x0)), minus1152(pair_hi(x0)),
+                                 minus1152(pair_lo(x1)), minus1152(pair_hi(x1))};
+                sc[c] = mfma_16x16x32<DT_F16>(a, q.b[c], f32x4{0.f, 0.f, 0.f, 0.f});
+            }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
