@@ -414,8 +414,10 @@ struct MfmaKvQ8 {
             if (lane < 32) {
                 if constexpr (SB == 2)
                     *reinterpret_cast<uint16_t*>(srow + SB * lane) = (uint16_t)tl.sc[h][0];
-                else
+                else if constexpr (SB == 4)
                     *reinterpret_cast<uint32_t*>(srow + SB * lane) = tl.sc[h][0];
+                else
+                    *reinterpret_cast<u32x2*>(srow + SB * lane) = u32x2{tl.sc[h][0], tl.sc[h][1]};
             } else {
                 const int i = lane - 32, t = i / 2;
                 uint16_t* vrow = reinterpret_cast<uint16_t*>(srow + D);
