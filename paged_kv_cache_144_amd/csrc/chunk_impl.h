@@ -119,7 +119,11 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     const int n = a.query_start_loc[s + 1] - rs;
     const int QT = kWavesPerGroup * QR;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    __builtin_assume(tid < S::THREADS);
+    // the wavefront index as a scalar, so that its row and token bounds below are scalars
+    // and the steps it skips or masks branch on the scalar unit
+    const int wave = uniform(tid >> 6);
     const int j = lane & 31, h = lane >> 5;
     // the V row this lane names in the P.V transpose reads (see the product below)
     const int v_lane = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * S::ROWV +
@@ -174,64 +178,54 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     // row-major in LDS.
     // two register sets: the loads of the next two steps are in flight during a step.
     // Every lane issues the same loads in every case (a position outside the row range or
-    // in a block with an invalid id reads the cache's first bytes instead, and its mask bit
-    // zeroes it when staged), so that the compiler's wait counts for one register set
-    // never include the other set's loads.
-    u32x4 sk[2][S::KPT], sv[2][S::VPT];
-    uint32_t kmask[2], vmask[2];
-    bool whole[2];                      // every token of the set's step is staged (uniform)
-    int bad = 0;
+    // in a block with an invalid id reads the cache's first bytes instead, and the masked
+    // store zeroes it), so that the compiler's wait counts for one register set never
+    // include the other set's loads.  What the store needs to know of the set's step is
+    // scalar: its first token, which of its two blocks are staged, and whether all of its
+    // tokens are.
+    // flags: bit 0 / 1 the step's first / second block is staged, bit 2 all its tokens are
+    struct Stage {
+        u32x4 k[S::KPT], v[S::VPT];
+        int t0, flags;
+    };
+    Stage sg[2];
     // Block ids are uniform over the workgroup: scalar loads, counted apart from the vector
-    // loads.  The table row is read in range only (indices clamped, then selected).
+    // loads.  The table row is read in range only: a step's first token lies before L (the
+    // steps past the last repeat it), and its second block is read only when it starts
+    // before L (else the first block's entry is read again, and not used).
     typedef const __attribute__((address_space(4))) int32_t* ConstIds;
     const ConstIds btc = (ConstIds)bt;
-    const int last_b = (L + kBlock - 1) / kBlock - 1;
-    auto step_ids = [&](int t0, int& i0, int& i1) {
-        const int b0 = t0 / kBlock;
-        const int r0 = btc[b0 < last_b ? b0 : (last_b > 0 ? last_b : 0)];
-        const int r1 = btc[b0 + 1 < last_b ? b0 + 1 : (last_b > 0 ? last_b : 0)];
-        i0 = (t0 < L && t0 + kBlock > lo_first) ? r0 : -1;
-        i1 = (t0 + kBlock < L && t0 + 2 * kBlock > lo_first) ? r1 : -1;
-    };
-    // The two blocks of a step: scalar base offsets (the cache's first tile for a missing
-    // or invalid block); each lane's pieces then sit at a fixed offset from one of them.
-    auto step_bases = [&](int t0, size_t (&base)[2], bool (&valid)[2]) {
-        int ids[2];
-        step_ids(t0, ids[0], ids[1]);
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            valid[hb] = (unsigned)ids[hb] < (unsigned)a.num_blocks;
-            bad |= ids[hb] >= 0 && !valid[hb];
-            base[hb] = valid[hb] ? (size_t)ids[hb] * block_stride + (size_t)g * tile_bytes : 0;
-        }
-    };
-    auto stage_load = [&](int t0, u32x4* sk, u32x4* sv, uint32_t& km, uint32_t& vm,
-                          bool& all) {
-        size_t base[2];
-        bool valid[2];
-        step_bases(t0, base, valid);
-        all = valid[0] && valid[1] && t0 >= lo_first && t0 + S::STEP <= L;
-        auto ok = [&](int tau) {          // token t0 + tau of the step is staged
-            const int t = t0 + tau;
-            return valid[tau / kBlock] && t < L && t >= lo_first;
-        };
-        km = 0;
-        vm = 0;
+    const uint64_t goff = (uint64_t)g * tile_bytes;
+    // A step's two blocks: scalar base offsets (the cache's first tile for a block outside
+    // the row's range or with an invalid id); each lane's pieces sit at a fixed 32-bit
+    // offset from one of them.
+    auto stage_load = [&](int t0, Stage& st) {
+        const uint32_t b0 = (uint32_t)t0 / kBlock;
+        const bool two = t0 + kBlock < L;
+        const int r0 = btc[b0], r1 = btc[two ? b0 + 1 : b0];
+        const int id0 = t0 + kBlock > lo_first ? r0 : -1;
+        const int id1 = two && t0 + 2 * kBlock > lo_first ? r1 : -1;
+        const bool ok0 = (uint32_t)id0 < (uint32_t)a.num_blocks;
+        const bool ok1 = (uint32_t)id1 < (uint32_t)a.num_blocks;
+        st.t0 = t0;
+        st.flags = (int)ok0 | (int)ok1 << 1 |
+                   (int)(ok0 && ok1 && t0 >= lo_first && t0 + S::STEP <= L) << 2;
+        const uint64_t base[2] = {
+            ok0 ? (uint64_t)(uint32_t)id0 * (uint32_t)block_stride + goff : 0,
+            ok1 ? (uint64_t)(uint32_t)id1 * (uint32_t)block_stride + goff : 0};
 #pragma unroll
         for (int i = 0; i < S::KPT; ++i) {
             const int c = (tid + i * S::THREADS) % S::KPIECES;
             const int tau = c / (D / 8);
             const uint32_t lane_off = (uint32_t)((tau % kBlock) * D * 2 + (c % (D / 8)) * 16);
-            sk[i] = ld16_stream((const char*)a.k_cache + base[tau / kBlock] + lane_off);
-            km |= (uint32_t)ok(tau) << i;
+            st.k[i] = ld16_stream((const char*)a.k_cache + base[tau / kBlock] + lane_off);
         }
 #pragma unroll
         for (int i = 0; i < S::VPT; ++i) {
             const int c = (tid + i * S::THREADS) % S::VPIECES;
             const int tau = c / (D / 8);
             const uint32_t lane_off = (uint32_t)((tau % kBlock) * D * 2 + (c % (D / 8)) * 16);
-            sv[i] = ld16_stream((const char*)a.v_cache + base[tau / kBlock] + lane_off);
-            vm |= (uint32_t)ok(tau) << i;
+            st.v[i] = ld16_stream((const char*)a.v_cache + base[tau / kBlock] + lane_off);
         }
     };
     // bf16 V -> fp16, rounded to nearest: exact for |v| in fp16's normal range, within
@@ -253,29 +247,34 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     // A step whose tokens are all staged (the common case) stores without the per-piece
     // selects: the store body is instantiated with and without masks, chosen by a scalar
     // branch.  Cc: the fp16 pass (bf16 V converted) or the bf16 pass.
-    auto stage_store = [&](auto Cc, int buf, const u32x4* sk, const u32x4* sv, uint32_t km,
-                           uint32_t vm, bool all) {
+    auto stage_store = [&](auto Cc, int buf, const Stage& st) {
         constexpr bool kConv = decltype(Cc)::value && kConvV;
         auto put = [&](auto masked_c) {
             constexpr bool kMasked = decltype(masked_c)::value;
             const u32x4 z = {0u, 0u, 0u, 0u};
-            auto pick = [&](uint32_t on, const u32x4& x) {
-                if constexpr (kMasked) return on ? x : z;
-                else return x;
+            // token tau of the step is staged: its block is, and it lies in [lo_first, L)
+            auto pick = [&](int tau, const u32x4& x) {
+                if constexpr (kMasked) {
+                    const int t = st.t0 + tau;
+                    const bool on = (st.flags >> (tau / kBlock) & 1) && t < L && t >= lo_first;
+                    return on ? x : z;
+                } else {
+                    return x;
+                }
             };
 #pragma unroll
             for (int i = 0; i < S::KPT; ++i) {
                 const int c = tid + i * S::THREADS;
                 if (c < S::KPIECES)
                     st16(&lds_k[buf][(c / (D / 8)) * S::ROWB + (c % (D / 8)) * 16],
-                         pick((km >> i) & 1u, sk[i]));
+                         pick(c / (D / 8), st.k[i]));
             }
             u16x2 vmax = {0, 0};
 #pragma unroll
             for (int i = 0; i < S::VPT; ++i) {
                 const int c = tid + i * S::THREADS;
                 if (c < S::VPIECES) {
-                    u32x4 x = pick((vm >> i) & 1u, sv[i]);
+                    u32x4 x = pick(c / (D / 8), st.v[i]);
                     if constexpr (kConv) x = v_to_f16(x, vmax);
                     st16(&lds_v[buf][(c / (D / 8)) * S::ROWV + (c % (D / 8)) * 16], x);
                 }
@@ -284,7 +283,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             // would pass through unchanged but takes the bf16 pass too
             if (kConv && (vmax.x >= 0x4780 || vmax.y >= 0x4780)) lds_vover = 1;
         };
-        if (all)
+        if (st.flags & 4)
             put(std::false_type{});
         else
             put(std::true_type{});
@@ -293,6 +292,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     // loads past the last step repeat the last step (never staged: the same loads in every
     // case keep the wait counts exact)
     const int t_last = t_first + (nsteps > 0 ? nsteps - 1 : 0) * S::STEP;
+    // A block id outside the pool sets the error bit (its tokens are staged as zeros).  The
+    // ids the steps read, blocks t_first / 16 .. t_last / 16 + 1 that start before L and
+    // end after lo_first, are checked once here, spread over the workgroup's threads.
+    {
+        bool bad = false;
+        for (int b = t_first / kBlock + tid; b <= t_last / kBlock + 1; b += S::THREADS)
+            if (kBlock * b < L && kBlock * b + kBlock > lo_first)
+                bad |= (uint32_t)bt[b] >= (uint32_t)a.num_blocks;
+        if (bad) atomicOr((int32_t*)(a.ws + a.lay.header), kErrBlockId);
+    }
     auto step_t = [&](int st) { return min(t_first + st * S::STEP, t_last); };
     // step st computes from LDS buffer st & 1 while steps st+1 (register set (st+1) & 1)
     // and st+2 are loading; then st+1 goes to LDS and step st+3 starts loading into the
@@ -308,10 +317,23 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             f32x16 sc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+            if constexpr (KS <= 8) {
+                // the step's K operands are all read before the first product (the
+                // scheduling barrier keeps them there), so that the chain waits for one
+                // LDS latency, not one per product.  d = 256 has no registers to spare.
+                u32x4 ka[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 ka = ld16(kl + j * S::ROWB + (16 * ks + 8 * h) * 2);
-                sc = mfma32<DT>(ka, qb[ks], sc);
+                for (int ks = 0; ks < KS; ++ks)
+                    ka[ks] = ld16(kl + j * S::ROWB + (16 * ks + 8 * h) * 2);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) sc = mfma32<DT>(ka[ks], qb[ks], sc);
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u32x4 ka = ld16(kl + j * S::ROWB + (16 * ks + 8 * h) * 2);
+                    sc = mfma32<DT>(ka, qb[ks], sc);
+                }
             }
             // element r of this lane is token t0 + 8 (r/4) + 4 h + r%4 of its M-row
             const bool full = w_rows_full && t0 + S::STEP - 1 <= wp_first && t0 >= wlo_last;
@@ -319,11 +341,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             float mx = -INFINITY;
             // this lane's visible token range of the step, [tlo, thi], as offsets 0..31
             // (computed on masked steps only)
+            // (as offsets from 4 h, so that element r compares a constant)
+            const int tlo_h = (row_ok ? max(lo - t0, 0) : 32) - 4 * h;
+            const int thi_h = (row_ok ? min(pos - t0, 31) : -1) - 4 * h;
             auto vis = [&](int r) {
-                const int tlo = row_ok ? max(lo - t0, 0) : 32;
-                const int thi = row_ok ? min(pos - t0, 31) : -1;
-                const int tt = 8 * (r / 4) + 4 * h + (r % 4);
-                return tt >= tlo && tt <= thi;
+                const int tt = 8 * (r / 4) + (r % 4);
+                return tt >= tlo_h && tt <= thi_h;
             };
             if (full) {
 #pragma unroll
@@ -411,9 +434,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
                 }
             }
         }
-        if (st + 1 < nsteps)
-            stage_store(Cc, buf ^ 1, sk[P], sv[P], kmask[P], vmask[P], whole[P]);
-        stage_load(step_t(st + 3), sk[P], sv[P], kmask[P], vmask[P], whole[P]);
+        if (st + 1 < nsteps) stage_store(Cc, buf ^ 1, sg[P]);
+        stage_load(step_t(st + 3), sg[P]);
         __syncthreads();
     };
     // one pass over the tile's steps
@@ -424,10 +446,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
         m_run = kNegBig;
         l_run = 0.f;
-        stage_load(step_t(0), sk[0], sv[0], kmask[0], vmask[0], whole[0]);
-        if (nsteps > 0) stage_store(Cc, 0, sk[0], sv[0], kmask[0], vmask[0], whole[0]);
-        stage_load(step_t(1), sk[1], sv[1], kmask[1], vmask[1], whole[1]);
-        stage_load(step_t(2), sk[0], sv[0], kmask[0], vmask[0], whole[0]);
+        stage_load(step_t(0), sg[0]);
+        if (nsteps > 0) stage_store(Cc, 0, sg[0]);
+        stage_load(step_t(1), sg[1]);
+        stage_load(step_t(2), sg[0]);
         __syncthreads();
         for (int st = 0; st < nsteps; st += 2) {
             body(Cc, std::integral_constant<int, 1>{}, st);
@@ -441,7 +463,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
         // every pass ends on a barrier, so the flag is settled and the same for the group
         if (__builtin_amdgcn_readfirstlane(lds_vover) != 0) pass(std::false_type{});
     }
-    if (bad) atomicOr((int32_t*)(a.ws + a.lay.header), kErrBlockId);
 
     // out[row][head][d]: lane holds O^T[d = 32 dt + 8 (r/4) + 4 h + r%4][its M-row]
     if (row_ok) {

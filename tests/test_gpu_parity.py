@@ -627,6 +627,39 @@ def test_chunk_rows_before_position_zero(torch, pa):
     assert np.isfinite(out).all() and np.abs(out[4:]).max() > 0
 
 
+def test_chunk_rows_bad_block_id(torch, pa, orc):
+    """A block id outside the pool that a chunk tile reads sets error bit 1 without a fault:
+    the output stays finite and the other sequences meet the oracle.  An id in a block that
+    lies before every chunk row's window is never read: no error bit, the output meets the
+    oracle."""
+    w = workloads.make("rows", **CHUNK_CASES[0])      # sequences 0 and 2 take chunk tiles
+    dw = run(w, torch)
+    ref = orc.Reference(w).attention()
+    qsl = w.query_start_loc()
+    bt = dw.block_tables.clone()
+    for s, j, bad_id in ((2, 1, w.num_blocks + 5), (0, 0, -3)):
+        dw.block_tables[s, j] = bad_id
+        out = dw.decode().cpu().numpy()
+        assert pa.device_error_bits(dw.workspace) & 1, (s, j, bad_id)
+        assert np.isfinite(out).all()
+        for o in range(w.num_seqs):
+            if o != s:
+                check_close(out[qsl[o]:qsl[o + 1]], ref[qsl[o]:qsl[o + 1]], f"seq {o}")
+        dw.block_tables.copy_(bt)
+    out = dw.decode().cpu().numpy()
+    assert pa.device_error_bits(dw.workspace) == 0
+    check_close(out, ref, "restored")
+
+    w = workloads.make("rows", **CHUNK_CASES[4])      # window 128: rows at 636.. and 304..
+    dw = run(w, torch)
+    ref = orc.Reference(w).attention()
+    dw.block_tables[0, 2] = w.num_blocks + 5
+    dw.block_tables[1, 2] = -1
+    out = dw.decode().cpu().numpy()
+    assert pa.device_error_bits(dw.workspace) == 0
+    check_close(out, ref, "ids before the window")
+
+
 @pytest.mark.parametrize("kw", [CHUNK_CASES[0], CHUNK_CASES[3], CHUNK_CASES[4]],
                          ids=["bf16-g4", "f16-d256", "bf16-window"])
 def test_chunk_rows_needle(torch, pa, orc, kw):
