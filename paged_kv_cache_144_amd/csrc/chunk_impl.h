@@ -338,51 +338,71 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             // element r of this lane is token t0 + 8 (r/4) + 4 h + r%4 of its M-row
             const bool full = w_rows_full && t0 + S::STEP - 1 <= wp_first && t0 >= wlo_last;
             float p16[16];
-            float mx = -INFINITY;
-            // this lane's visible token range of the step, [tlo, thi], as offsets 0..31
-            // (computed on masked steps only)
-            // (as offsets from 4 h, so that element r compares a constant)
-            const int tlo_h = (row_ok ? max(lo - t0, 0) : 32) - 4 * h;
-            const int thi_h = (row_ok ? min(pos - t0, 31) : -1) - 4 * h;
+            // element r is visible: it lies in this lane's visible token range of the step,
+            // [tlo, thi] as offsets 0..31 (both less 4 h, so that element r compares a
+            // constant).  Where registers allow (d <= 128), only masked steps compute the
+            // range; at d = 256 every step does, which keeps that instance from spilling.
+            auto range = [&](int& tlo_h, int& thi_h) {
+                tlo_h = (row_ok ? max(lo - t0, 0) : 32) - 4 * h;
+                thi_h = (row_ok ? min(pos - t0, 31) : -1) - 4 * h;
+            };
+            int tlo_e = 0, thi_e = 0;
+            if constexpr (KS > 8) range(tlo_e, thi_e);
             auto vis = [&](int r) {
+                int tlo_h = tlo_e, thi_h = thi_e;
+                if constexpr (KS <= 8) range(tlo_h, thi_h);
                 const int tt = 8 * (r / 4) + (r % 4);
                 return tt >= tlo_h && tt <= thi_h;
             };
-            if (full) {
+            // the weights p = 2^(s qscale - m_run) with the running max as it stands, and
+            // this lane's sum of them
+            auto weights = [&]() {
+                float ps = 0.f;
+                if (full) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-            } else {
+                    for (int r = 0; r < 16; ++r) {
+                        p16[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], qscale, -m_run));
+                        ps += p16[r];
+                    }
+                } else {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, vis(r) ? sc[r] : -INFINITY);
-            }
-            {
-                const float2 pm = with_partner(mx);
-                mx = fmaxf(pm.x, pm.y);
-            }
-            const float mxs = mx > -INFINITY ? mx * qscale : -INFINITY;
-            // raise the running max only when the new one exceeds it by more than 8 (log2)
-            if (__ballot(mxs > m_run + 8.f)) {                 // wavefront-uniform
-                const float mn = fmaxf(m_run, mxs);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-                m_run = mn;
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT32; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-            }
-            float psum = 0.f;
-            if (full) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    p16[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], qscale, -m_run));
-                    psum += p16[r];
+                    for (int r = 0; r < 16; ++r) {
+                        p16[r] = vis(r) ? __builtin_amdgcn_exp2f(fmaf(sc[r], qscale, -m_run))
+                                        : 0.f;
+                        ps += p16[r];
+                    }
                 }
-            } else {
+                return ps;
+            };
+            float psum = weights();
+            // The running max is raised only when the step's maximum exceeds it by more than
+            // 8 (log2), and then some weight exceeds 2^8: steps where no lane's sum reaches
+            // 2^8 (the common case, and the first step always does: m_run starts at the
+            // lowest float) need neither the maximum nor the exchange with the partner lane.
+            if (__ballot(psum >= 256.f)) {                     // wavefront-uniform
+                float mx = -INFINITY;
+                if (full) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    p16[r] = vis(r) ? __builtin_amdgcn_exp2f(fmaf(sc[r], qscale, -m_run)) : 0.f;
-                    psum += p16[r];
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, vis(r) ? sc[r] : -INFINITY);
+                }
+                {
+                    const float2 pm = with_partner(mx);
+                    mx = fmaxf(pm.x, pm.y);
+                }
+                const float mxs = mx > -INFINITY ? mx * qscale : -INFINITY;
+                if (__ballot(mxs > m_run + 8.f)) {             // wavefront-uniform
+                    const float mn = fmaxf(m_run, mxs);
+                    const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+                    m_run = mn;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+                    psum = weights();
                 }
             }
             {
