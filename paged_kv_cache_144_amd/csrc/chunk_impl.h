@@ -167,6 +167,9 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     }
 
     f32x16 acc[DT32];
+    // m_run: the running max (log2 units), the same in the two lanes of an M-row;
+    // l_run: this lane's part of the weight sum (its half of each step's tokens), the two
+    // parts added once at the end
     float m_run, l_run;
     const float qscale = fabsf(a.scale) * kLog2e;
 
@@ -196,15 +199,24 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     typedef const __attribute__((address_space(4))) int32_t* ConstIds;
     const ConstIds btc = (ConstIds)bt;
     const uint64_t goff = (uint64_t)g * tile_bytes;
-    // A step's two blocks: scalar base offsets (the cache's first tile for a block outside
-    // the row's range or with an invalid id); each lane's pieces sit at a fixed 32-bit
-    // offset from one of them.
-    auto stage_load = [&](int t0, Stage& st) {
+    // A step's two block ids (-1: the block is outside the row's range).  (Fetching them a
+    // step early measured slower: scalar loads share the LDS wait counter, so the next
+    // step's first products then wait for them too.)
+    struct StepIds {
+        int t0, id0, id1;
+    };
+    auto step_ids = [&](int t0) {
         const uint32_t b0 = (uint32_t)t0 / kBlock;
         const bool two = t0 + kBlock < L;
         const int r0 = btc[b0], r1 = btc[two ? b0 + 1 : b0];
-        const int id0 = t0 + kBlock > lo_first ? r0 : -1;
-        const int id1 = two && t0 + 2 * kBlock > lo_first ? r1 : -1;
+        return StepIds{t0, t0 + kBlock > lo_first ? r0 : -1,
+                       two && t0 + 2 * kBlock > lo_first ? r1 : -1};
+    };
+    // The step's loads: scalar base offsets of its two blocks (the cache's first tile for a
+    // block outside the row's range or with an invalid id); each lane's pieces sit at a
+    // fixed 32-bit offset from one of them.
+    auto stage_load = [&](const StepIds& ids, Stage& st) {
+        const int t0 = ids.t0, id0 = ids.id0, id1 = ids.id1;
         const bool ok0 = (uint32_t)id0 < (uint32_t)a.num_blocks;
         const bool ok1 = (uint32_t)id1 < (uint32_t)a.num_blocks;
         st.t0 = t0;
@@ -357,21 +369,19 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             // the weights p = 2^(s qscale - m_run) with the running max as it stands, and
             // this lane's sum of them
             auto weights = [&]() {
-                float ps = 0.f;
                 if (full) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
+                    for (int r = 0; r < 16; ++r)
                         p16[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], qscale, -m_run));
-                        ps += p16[r];
-                    }
                 } else {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
+                    for (int r = 0; r < 16; ++r)
                         p16[r] = vis(r) ? __builtin_amdgcn_exp2f(fmaf(sc[r], qscale, -m_run))
                                         : 0.f;
-                        ps += p16[r];
-                    }
                 }
+                float ps = p16[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) ps += p16[r];
                 return ps;
             };
             float psum = weights();
@@ -404,10 +414,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
                         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
                     psum = weights();
                 }
-            }
-            {
-                const float2 ps = with_partner(psum);
-                psum = ps.x + ps.y;
             }
             l_run += psum;
             // P^T operands: K-step k2 covers tokens 16 k2 .. 16 k2 + 15; element kk of lane
@@ -455,7 +461,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             }
         }
         if (st + 1 < nsteps) stage_store(Cc, buf ^ 1, sg[P]);
-        stage_load(step_t(st + 3), sg[P]);
+        stage_load(step_ids(step_t(st + 3)), sg[P]);
         __syncthreads();
     };
     // one pass over the tile's steps
@@ -466,10 +472,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
         m_run = kNegBig;
         l_run = 0.f;
-        stage_load(step_t(0), sg[0]);
+        stage_load(step_ids(step_t(0)), sg[0]);
         if (nsteps > 0) stage_store(Cc, 0, sg[0]);
-        stage_load(step_t(1), sg[1]);
-        stage_load(step_t(2), sg[0]);
+        stage_load(step_ids(step_t(1)), sg[1]);
+        stage_load(step_ids(step_t(2)), sg[0]);
         __syncthreads();
         for (int st = 0; st < nsteps; st += 2) {
             body(Cc, std::integral_constant<int, 1>{}, st);
@@ -485,8 +491,11 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     }
 
     // out[row][head][d]: lane holds O^T[d = 32 dt + 8 (r/4) + 4 h + r%4][its M-row]
+    // the row's weight sum: this lane's part and its partner's (taken by every lane)
+    const float2 lp = with_partner(l_run);
+    const float l_row = lp.x + lp.y;
     if (row_ok) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
         const size_t obase = ((size_t)(rs + qrow) * a.num_q_heads + (size_t)g * G + gi) * D;
 #pragma unroll
         for (int dt = 0; dt < DT32; ++dt)
