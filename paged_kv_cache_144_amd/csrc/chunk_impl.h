@@ -347,6 +347,21 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
                     sc = mfma32<DT>(ka, qb[ks], sc);
                 }
             }
+            // The V^T operand of the P.V product for tokens 16 k2 .. 16 k2 + 15 and columns
+            // 32 dt .. 32 dt + 31 (the transpose reads are described at the product below).
+            // Where registers allow (d <= 128), the first half is read before the softmax,
+            // so that its LDS latency passes during the exponentials.
+            auto v_operand = [&](int k2, int dt) {
+                const char* p0 = vl + v_lane + (16 * k2) * S::ROWV + 64 * dt;
+                const u32x2 t0 = tr_read(p0), t1 = tr_read(p0 + 8 * S::ROWV);
+                return u32x4{t0.x, t0.y, t1.x, t1.y};
+            };
+            constexpr bool kEarlyV = KS <= 8;
+            u32x4 va0[DT32];
+            if constexpr (kEarlyV) {
+#pragma unroll
+                for (int dt = 0; dt < DT32; ++dt) va0[dt] = v_operand(0, dt);
+            }
             // element r of this lane is token t0 + 8 (r/4) + 4 h + r%4 of its M-row
             const bool full = w_rows_full && t0 + S::STEP - 1 <= wp_first && t0 >= wlo_last;
             float p16[16];
@@ -448,9 +463,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
                 for (int dt = 0; dt < DT32; ++dt) {
-                    const char* p0 = vl + v_lane + (16 * k2) * S::ROWV + 64 * dt;
-                    const u32x2 t0 = tr_read(p0), t1 = tr_read(p0 + 8 * S::ROWV);
-                    const u32x4 va = {t0.x, t0.y, t1.x, t1.y};
+                    const u32x4 va = k2 == 0 && kEarlyV ? va0[dt] : v_operand(k2, dt);
                     if constexpr (kF16PV) {
                         acc[dt] = mfma32<DT_F16>(va, pb[k2], acc[dt]);
                     } else {
