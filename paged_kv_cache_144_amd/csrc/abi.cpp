@@ -99,6 +99,9 @@ pa_status plan_shape(const pa_cache_desc* desc, int32_t num_seqs, int32_t total_
     if (!p.fn) return PA_ERR_UNSUPPORTED;
     p.max_waves = resident_waves(p.fn);
     if (p.max_waves <= 0) return PA_ERR_LAUNCH;
+    if ((desc->dtype == PA_Q8_F16 || desc->dtype == PA_Q8_BF16) &&
+        pa::decode_uses_mfma(desc->dtype, p.group, desc->block_size))
+        p.pair_cost = pa::kPairCostQ8Mfma;
     p.wave_round = cu_count() * pa::kWavesPerGroup;
     // tuning / testing knob: fewer decode wavefronts than the device keeps resident
     if (const char* e = std::getenv("PA_DECODE_WAVES")) {

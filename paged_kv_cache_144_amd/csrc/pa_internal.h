@@ -18,6 +18,9 @@ constexpr int kMinBlocksPerWave = 12;  // default smallest share of KV blocks pe
 constexpr int kMinBlocksFloor = 4;     // the plan needs shares of at least 4 blocks
 constexpr int kPairCost = 14;       // default fixed cost per pair in quarter blocks: the
                                     // dependent loads that start a segment
+// The 8-bit matrix-core decode kernel reads half the bytes per block, so a pair's fixed
+// cost weighs more against its blocks there.
+constexpr int kPairCostQ8Mfma = 22;
 // The plan lowers the pair cost where shares are short (consecutive share starts lie at
 // least 4 T / W - 1 quarter blocks apart), so any cost up to this bound keeps every share
 // non-empty.

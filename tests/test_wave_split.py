@@ -69,7 +69,7 @@ def check(nbs, heads, min_blocks, max_waves, pair_cost, wave_round=0):
 
 
 @pytest.mark.parametrize("min_blocks", [4, 5, 8, 16, 33])
-@pytest.mark.parametrize("pair_cost", [0, 14, 27])
+@pytest.mark.parametrize("pair_cost", [0, 14, 22, 27])
 def test_shares_nonempty_random(min_blocks, pair_cost):
     rng = np.random.default_rng(1000 * min_blocks + pair_cost)
     for _ in range(60):
