@@ -23,9 +23,10 @@
 // where P^T comes straight from the S^T accumulator registers in the MFMA B-operand order
 // and the V^T operand is two LDS transpose reads in the matching token order.  P and V
 // enter that product in fp16 for both cache types: bf16 V is converted as it is staged,
-// exactly wherever |v| lies in fp16's range.  A bf16 value beyond that range sets a flag,
-// and the workgroup then computes its tile again in a second pass that stages V as bf16 and
-// carries P as hi + lo bf16 parts (two MFMAs per product).  The running
+// exactly wherever |v| lies in fp16's range.  A bf16 value beyond that range becomes an
+// infinity, which leaves non-finite accumulators; the workgroup then computes its tile
+// again in a second pass that stages V as bf16 and carries P as hi + lo bf16 parts (two
+// MFMAs per product).  The running
 // max is raised only when a row's new maximum exceeds it by more than 2^8 (weights stay
 // <= 256), so the accumulators are rescaled on few steps.  The next step's global loads are
 // in flight while the current step computes (LDS double buffer, one barrier per step).
@@ -241,17 +242,13 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
         }
     };
     // bf16 V -> fp16, rounded to nearest: exact for |v| in fp16's normal range, within
-    // 2^-25 below it.  vmax collects the largest |v| bit patterns (two 16-bit halves; for
-    // bf16, a larger magnitude is a larger pattern), so that values past the range are
-    // caught: |v| >= 65520 is a bf16 pattern of at least 0x4780 (65536).
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    auto v_to_f16 = [&](const u32x4& x, u16x2& vmax) {
+    // 2^-25 below it; |v| >= 65520 becomes an infinity (caught after the pass, below).
+    auto v_to_f16 = [&](const u32x4& x) {
         u32x4 y;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const float lo = __uint_as_float(x[w] << 16);
             const float hi = __uint_as_float(x[w] & 0xffff0000u);
-            vmax = __builtin_elementwise_max(vmax, __builtin_bit_cast(u16x2, x[w] & 0x7fff7fffu));
             y[w] = cvt2<DT_F16>(lo, hi);
         }
         return y;
@@ -281,19 +278,15 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
                     st16(&lds_k[buf][(c / (D / 8)) * S::ROWB + (c % (D / 8)) * 16],
                          pick(c / (D / 8), st.k[i]));
             }
-            u16x2 vmax = {0, 0};
 #pragma unroll
             for (int i = 0; i < S::VPT; ++i) {
                 const int c = tid + i * S::THREADS;
                 if (c < S::VPIECES) {
                     u32x4 x = pick(c / (D / 8), st.v[i]);
-                    if constexpr (kConv) x = v_to_f16(x, vmax);
+                    if constexpr (kConv) x = v_to_f16(x);
                     st16(&lds_v[buf][(c / (D / 8)) * S::ROWV + (c % (D / 8)) * 16], x);
                 }
             }
-            // 65520 and above round to infinity in fp16; NaN (a larger pattern still)
-            // would pass through unchanged but takes the bf16 pass too
-            if (kConv && (vmax.x >= 0x4780 || vmax.y >= 0x4780)) lds_vover = 1;
         };
         if (st.flags & 4)
             put(std::false_type{});
@@ -499,7 +492,18 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     __syncthreads();
     pass(std::true_type{});
     if constexpr (kConvV) {
-        // every pass ends on a barrier, so the flag is settled and the same for the group
+        // A staged bf16 value beyond fp16's range became an infinity, and every product it
+        // entered left an infinite or NaN (0 x inf) accumulator in each wavefront that
+        // computed its step; finite accumulators stay far below the float range, so the
+        // sum of |acc| is finite exactly when none is.  Such a tile is computed again with
+        // V kept in bf16.  (A NaN in V also takes that pass; its output is NaN either way.)
+        float sa = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sa += fabsf(acc[dt][r]);
+        if (!(sa < INFINITY)) lds_vover = 1;
+        __syncthreads();
         if (__builtin_amdgcn_readfirstlane(lds_vover) != 0) pass(std::false_type{});
     }
 
