@@ -120,6 +120,23 @@ CASES = [
 
 @pytest.mark.parametrize("name,kw", CASES, ids=[f"{n}-{i}" for i, (n, _) in enumerate(CASES)])
 def test_write_attend_parity(torch, pa, orc, name, kw):
+    check_write_attend(torch, pa, orc, name, kw)
+
+
+# The workloads the benchmark times with the one-launch step (one query row per sequence),
+# at their full sizes.
+FULL = [("opt13b", {}), ("gqa", {}), ("swa", {}), ("parallel_sampling", {})]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,kw", FULL, ids=[n for n, _ in FULL])
+def test_write_attend_full_size(torch, pa, orc, name, kw):
+    """The one-launch step at the workloads' full sizes, in the launch configuration the
+    benchmark times: the same requirements as the smaller cases above."""
+    check_write_attend(torch, pa, orc, name, kw)
+
+
+def check_write_attend(torch, pa, orc, name, kw):
     say("case", name, kw)
     w = workloads.make(name, **kw)
     st = Step(torch, pa, w)

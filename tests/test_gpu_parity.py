@@ -358,7 +358,7 @@ def test_write_kv_skips(torch, pa):
 FULL = [("tiny", {}), ("opt13b", {}), ("gqa", {}), ("prefix_mixed", {}), ("swa", {}),
         ("parallel_sampling", {}), ("swap", {}), ("opt13b", dict(block_size=32)),
         ("gqa", dict(block_size=8)), ("opt13b", dict(dtype="q8_f16")),
-        ("gqa", dict(dtype="q8_bf16"))]
+        ("gqa", dict(dtype="q8_bf16")), ("swa", dict(dtype="q8_f16"))]
 
 
 @pytest.mark.slow
