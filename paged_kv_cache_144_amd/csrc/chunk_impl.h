@@ -26,10 +26,10 @@
 // exactly wherever |v| lies in fp16's range.  A bf16 value beyond that range becomes an
 // infinity, which leaves non-finite accumulators; the workgroup then computes its tile
 // again in a second pass that stages V as bf16 and carries P as hi + lo bf16 parts (two
-// MFMAs per product).  The running
-// max is raised only when a row's new maximum exceeds it by more than 2^8 (weights stay
-// <= 256), so the accumulators are rescaled on few steps.  The next step's global loads are
-// in flight while the current step computes (LDS double buffer, one barrier per step).
+// MFMAs per product).  The running max is raised only when a row's new maximum exceeds it
+// by more than 2^8 (weights stay <= 256), so the accumulators are rescaled on few steps.
+// The next steps' global loads are in flight while the current step computes (LDS double
+// buffer, one barrier per step).
 #pragma once
 
 #include <type_traits>
