@@ -348,50 +348,67 @@ __device__ __forceinline__ void store_out1(const DecodeArgs& a, size_t idx, floa
     }
 }
 
+// One round of loads for at most R contributors: every contributor's (max, sum) and output
+// slice load together (lane c < nc holds contributor c's (max, sum), every lane its columns
+// of each output), so the task, that round and the store are the only dependent steps.
+// Indices past nc re-read contributor 0 and get weight 0: no branches, so every load goes
+// out before the first wait.
+template <int D, int G, int R>
+__device__ void merge_round(const DecodeArgs& a, int u, int g, int w_first, int nc,
+                            int first_slot, int gi, const float2* pml, const float* pacc,
+                            int lane) {
+    constexpr int KD = (D + kWave - 1) / kWave;
+    auto part = [&](int c) {
+        return ((size_t)(w_first + c) * 2 + (c == 0 ? first_slot : 0)) * G + gi;
+    };
+    const float2 mine = pml[part(lane < nc ? lane : 0)];
+    float val[R][KD];
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const float* src = pacc + part(t < nc ? t : 0) * D;
+#pragma unroll
+        for (int k = 0; k < KD; ++k)
+            val[t][k] = (D % 64 == 0 || lane + 64 * k < D) ? src[lane + 64 * k] : 0.f;
+    }
+    const float M = wave_max(lane < nc ? mine.x : -3.402823466e38f);
+    const float f = lane < nc ? __builtin_amdgcn_exp2f(mine.x - M) : 0.f;
+    const float den = wave_sum(f * mine.y);
+    float num[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) num[k] = 0.f;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const float ft = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), t));
+#pragma unroll
+        for (int k = 0; k < KD; ++k) num[k] += ft * val[t][k];
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const size_t obase = ((size_t)u * a.num_q_heads + (size_t)g * G + gi) * D;
+#pragma unroll
+    for (int k = 0; k < KD; ++k)
+        if (D % 64 == 0 || lane + 64 * k < D) store_out1(a, obase + lane + 64 * k, num[k] * inv);
+}
+
 // Combine the partials of head gi of pair (u, g) left by wavefronts w_first ..
 // w_first + nc - 1 (slot first_slot for the first, slot 0 for the others):
 //   out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c,   M = max_c m_c   (m in log2 units)
+// Up to 8 contributors (every cut pair of evenly long sequences) take one round of 8 loads;
+// up to 32 (the long pairs of a skewed length mix, cut over many wavefronts) one round of
+// 32 (d <= 128); more take rounds of four.
 template <int D, int G>
 __device__ void merge_pair(const DecodeArgs& a, int u, int g, int w_first, int nc,
                            int first_slot, int gi, const float2* pml, const float* pacc,
                            int lane) {
     constexpr int KD = (D + kWave - 1) / kWave;
-    constexpr int R = 8;   // contributors merged from one round of loads
-    if (nc <= R) {
-        // every contributor's (max, sum) and output slice load together: lane c < nc holds
-        // contributor c's (max, sum), and every lane its columns of each output
-        auto part = [&](int c) {
-            return ((size_t)(w_first + c) * 2 + (c == 0 ? first_slot : 0)) * G + gi;
-        };
-        // (indices past nc re-read contributor 0 and get weight 0: no branches, so every
-        // load goes out before the first wait)
-        const float2 mine = pml[part(lane < nc ? lane : 0)];
-        float val[R][KD];
-#pragma unroll
-        for (int t = 0; t < R; ++t) {
-            const float* src = pacc + part(t < nc ? t : 0) * D;
-#pragma unroll
-            for (int k = 0; k < KD; ++k)
-                val[t][k] = (D % 64 == 0 || lane + 64 * k < D) ? src[lane + 64 * k] : 0.f;
-        }
-        const float M = wave_max(lane < nc ? mine.x : -3.402823466e38f);
-        const float f = lane < nc ? __builtin_amdgcn_exp2f(mine.x - M) : 0.f;
-        const float den = wave_sum(f * mine.y);
-        float num[KD];
-#pragma unroll
-        for (int k = 0; k < KD; ++k) num[k] = 0.f;
-#pragma unroll
-        for (int t = 0; t < R; ++t) {
-            const float ft = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), t));
-#pragma unroll
-            for (int k = 0; k < KD; ++k) num[k] += ft * val[t][k];
-        }
-        const float inv = den > 0.f ? 1.f / den : 0.f;
-        const size_t obase = ((size_t)u * a.num_q_heads + (size_t)g * G + gi) * D;
-#pragma unroll
-        for (int k = 0; k < KD; ++k)
-            if (D % 64 == 0 || lane + 64 * k < D) store_out1(a, obase + lane + 64 * k, num[k] * inv);
+    if (nc <= 8) {
+        merge_round<D, G, 8>(a, u, g, w_first, nc, first_slot, gi, pml, pacc, lane);
         return;
+    }
+    if constexpr (D <= 128) {
+        if (nc <= 32) {
+            merge_round<D, G, 32>(a, u, g, w_first, nc, first_slot, gi, pml, pacc, lane);
+            return;
+        }
     }
     {
         float M = -3.402823466e38f;
