@@ -187,17 +187,23 @@ struct MfmaKv16 {
     __device__ static void finish(f32x4 (&)[NACC], const Extra&) {}
     // acc[b] of lane c16 is column 16 b + c16
     // row r of lane quad q4, column blocks row_has_block(q4, r, b)
-    __device__ static void store(const DecodeArgs& a, size_t ob, const f32x4 (&acc)[NACC],
-                                 int r, float inv, int c16, int q4) {
+    // the head's row of the staged output: column 16 b + c16 = acc[b][r] x inv, as fp32 or
+    // converted to the 16-bit output type
+    __device__ static void stage_out(float* dst, const f32x4 (&acc)[NACC], int r, float inv,
+                                     int c16, int q4) {
 #pragma unroll
         for (int b = 0; b < NACC; ++b)
-            if (row_has_block(q4, r, b)) store_out1(a, ob + 16 * b + c16, acc[b][r] * inv);
+            if (row_has_block(q4, r, b)) dst[16 * b + c16] = acc[b][r] * inv;
     }
-    __device__ static void store_part(float* dst, const f32x4 (&acc)[NACC], int r, int c16,
-                                      int q4) {
+    __device__ static void stage_out16(int out_dtype, uint16_t* dst, const f32x4 (&acc)[NACC],
+                                       int r, float inv, int c16, int q4) {
 #pragma unroll
         for (int b = 0; b < NACC; ++b)
-            if (row_has_block(q4, r, b)) dst[16 * b + c16] = acc[b][r];
+            if (row_has_block(q4, r, b)) {
+                const float v = acc[b][r] * inv;
+                dst[16 * b + c16] = (uint16_t)(out_dtype == PA_F16 ? f32_to_f16_bits(v)
+                                                                   : f32_to_bf16_bits(v));
+            }
     }
 };
 
@@ -557,17 +563,23 @@ struct MfmaKvQ8 {
     __device__ static void finish(f32x4 (&)[NACC], const Extra&) {}
     // acc[b] of lane c16 is column 16 b + c16
     // row r of lane quad q4, column blocks row_has_block(q4, r, b)
-    __device__ static void store(const DecodeArgs& a, size_t ob, const f32x4 (&acc)[NACC],
-                                 int r, float inv, int c16, int q4) {
+    // the head's row of the staged output: column 16 b + c16 = acc[b][r] x inv, as fp32 or
+    // converted to the 16-bit output type
+    __device__ static void stage_out(float* dst, const f32x4 (&acc)[NACC], int r, float inv,
+                                     int c16, int q4) {
 #pragma unroll
         for (int b = 0; b < NACC; ++b)
-            if (row_has_block(q4, r, b)) store_out1(a, ob + 16 * b + c16, acc[b][r] * inv);
+            if (row_has_block(q4, r, b)) dst[16 * b + c16] = acc[b][r] * inv;
     }
-    __device__ static void store_part(float* dst, const f32x4 (&acc)[NACC], int r, int c16,
-                                      int q4) {
+    __device__ static void stage_out16(int out_dtype, uint16_t* dst, const f32x4 (&acc)[NACC],
+                                       int r, float inv, int c16, int q4) {
 #pragma unroll
         for (int b = 0; b < NACC; ++b)
-            if (row_has_block(q4, r, b)) dst[16 * b + c16] = acc[b][r];
+            if (row_has_block(q4, r, b)) {
+                const float v = acc[b][r] * inv;
+                dst[16 * b + c16] = (uint16_t)(out_dtype == PA_F16 ? f32_to_f16_bits(v)
+                                                                   : f32_to_bf16_bits(v));
+            }
     }
 };
 
@@ -616,6 +628,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     const int c16 = lane % 16, q4 = lane / 16;
     char* my = Ops::LDS_BYTES > 0 ? lds + (threadIdx.x >> 6) * (Ops::LDS_BYTES / kWavesPerGroup)
                                   : lds;
+    // A finished segment's output (16-bit values, or fp32 values and partials) is staged in
+    // this wavefront's rows of lds_out as [G heads][D] and leaves as whole 16-byte lane
+    // stores: one or two store instructions instead of one per (row, column block) of the
+    // MFMA layout, each of which wrote 32-byte pieces.
+    __shared__ __align__(16) float lds_out[kWavesPerGroup][G * D];
+    float* mo = lds_out[threadIdx.x >> 6];
     const float qscale = a.scale * kLog2e;
     const size_t block_stride = (size_t)a.num_kv_heads * Ops::TILE;
     const char* kbase = (const char*)a.k_cache + Ops::k_lane(lane);
@@ -859,6 +877,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
         lt += __shfl_xor(lt, 32);
         const bool complete = cur.starts && cur.end == cur.pe;
         const int slot = first_segment ? 0 : 1;
+        const bool out16 = complete && a.out_dtype != PA_F32;
         if (!complete && q4 == 0 && c16 < G) {
             const size_t pi = ((size_t)wave * 2 + slot) * G + c16;
             pml[pi] = make_float2(m, lt);
@@ -868,13 +887,35 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
             const int h = Ops::row_head(q4, r);
             const float lh = __shfl(lt, h);
             if (Ops::row_valid(q4, r)) {
-                if (complete) {
-                    const float inv = lh > 0.f ? 1.f / lh : 0.f;
-                    const size_t ob = ((size_t)cur.u * a.num_q_heads + (size_t)cur.g * G + h) * D;
-                    Ops::store(a, ob, acc, r, inv, c16, q4);
-                } else {
-                    Ops::store_part(pacc + (((size_t)wave * 2 + slot) * G + h) * D, acc, r, c16,
-                                    q4);
+                const float inv = !complete ? 1.f : lh > 0.f ? 1.f / lh : 0.f;
+                if (out16)
+                    Ops::stage_out16(a.out_dtype, reinterpret_cast<uint16_t*>(mo) + h * D, acc,
+                                     r, inv, c16, q4);
+                else
+                    Ops::stage_out(mo + h * D, acc, r, inv, c16, q4);
+            }
+        }
+        {
+            // the wavefront's own LDS rows, written and read back in order: no barrier
+            constexpr int N = G * D;
+            if (out16) {
+                const size_t ob = ((size_t)cur.u * a.num_q_heads + (size_t)cur.g * G) * D;
+                const uint16_t* m16 = reinterpret_cast<const uint16_t*>(mo);
+#pragma unroll
+                for (int i0 = 0; i0 < N; i0 += kWave * 8) {
+                    const int i = i0 + lane * 8;
+                    if (N % (kWave * 8) == 0 || i < N)
+                        st16((uint16_t*)a.out + ob + i, *reinterpret_cast<const u32x4*>(m16 + i));
+                }
+            } else {
+                float* dst = complete
+                    ? (float*)a.out + ((size_t)cur.u * a.num_q_heads + (size_t)cur.g * G) * D
+                    : pacc + ((size_t)wave * 2 + slot) * G * D;
+#pragma unroll
+                for (int i0 = 0; i0 < N; i0 += kWave * 4) {
+                    const int i = i0 + lane * 4;
+                    if (N % (kWave * 4) == 0 || i < N)
+                        st16(dst + i, *reinterpret_cast<const u32x4*>(mo + i));
                 }
             }
         }
