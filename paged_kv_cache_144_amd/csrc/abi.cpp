@@ -3,6 +3,7 @@
 // freed here and no call synchronizes.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <map>
@@ -99,6 +100,13 @@ pa_status plan_shape(const pa_cache_desc* desc, int32_t num_seqs, int32_t total_
     if (!p.fn) return PA_ERR_UNSUPPORTED;
     p.max_waves = resident_waves(p.fn);
     if (p.max_waves <= 0) return PA_ERR_LAUNCH;
+    // The per-lane kernel with 16- and 32-bit caches keeps one workgroup per compute unit:
+    // its light work per byte needs no second workgroup to keep the memory busy, and fewer,
+    // longer shares cut fewer pairs.  8-bit caches, which decode their codes on the vector
+    // ALU, and the matrix-core kernel keep every resident wavefront.
+    const bool q8 = desc->dtype == PA_Q8_F16 || desc->dtype == PA_Q8_BF16;
+    if (!q8 && !pa::decode_uses_mfma(desc->dtype, p.group, desc->block_size))
+        p.max_waves = std::min(p.max_waves, cu_count() * pa::kWavesPerGroup);
     if ((desc->dtype == PA_Q8_F16 || desc->dtype == PA_Q8_BF16) &&
         pa::decode_uses_mfma(desc->dtype, p.group, desc->block_size))
         p.pair_cost = pa::kPairCostQ8Mfma;

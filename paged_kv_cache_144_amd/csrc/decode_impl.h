@@ -486,6 +486,34 @@ __device__ inline Seg first_segment_of(const WaveStart& st, int window) {
     sg.starts = st.x0 == st.ps;
     return sg;
 }
+// a wavefront's first-segment record with every field wave-uniform (the record is read by
+// vector loads; as uniform values its fields, and the branches on them, stay scalar)
+__device__ inline WaveStart uniform_start(const WaveStart& r) {
+    WaveStart st;
+    st.x0 = (uint32_t)uniform((int)r.x0);
+    st.x1 = (uint32_t)uniform((int)r.x1);
+    st.u = uniform(r.u);
+    st.g = uniform(r.g);
+    st.ps = (uint32_t)uniform((int)r.ps);
+    st.pe = (uint32_t)uniform((int)r.pe);
+    st.j0 = uniform(r.j0);
+    st.j1 = uniform(r.j1);
+    st.seq = uniform(r.seq);
+    st.len = uniform(r.len);
+    st.b0 = uniform(r.b0);
+    st.b1 = uniform(r.b1);
+    return st;
+}
+// a unit record by scalar loads, one field at a time
+__device__ inline UnitInfo ld_unit(const UnitInfo* p) {
+    const int32_t* f = reinterpret_cast<const int32_t*>(p);
+    UnitInfo ui;
+    ui.b_lo = ld_scalar(f);
+    ui.nb = ld_scalar(f + 1);
+    ui.len = ld_scalar(f + 2);
+    ui.seq = ld_scalar(f + 3);
+    return ui;
+}
 // a block id from the table, checked: outside [0, num_blocks) it reads block 0 and is masked
 __device__ inline int checked_block(int b, int num_blocks, bool& valid) {
     valid = (unsigned)b < (unsigned)num_blocks;
@@ -506,6 +534,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     const uint32_t* cb = (const uint32_t*)(a.ws + a.lay.cb);
     const UnitInfo* unit = (const UnitInfo*)(a.ws + a.lay.unit);
     const uint32_t* wx0 = (const uint32_t*)(a.ws + a.lay.wave_x0);
+    const int32_t* wcut = (const int32_t*)(a.ws + a.lay.wave_u);
     float2* pml = (float2*)(a.ws + a.lay.part_ml);
     float* pacc = (float*)(a.ws + a.lay.part_acc);
 
@@ -516,7 +545,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     const int wave = uniform(blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6));
     const int lane = lane_id();
     // this wavefront's first segment, read with the header (entries from W on are unused)
-    const WaveStart st = ((const WaveStart*)(a.ws + a.lay.wave_st))[wave];
+    const WaveStart st = uniform_start(((const WaveStart*)(a.ws + a.lay.wave_st))[wave]);
     // rows with nothing to read are zeros (shared out among all launched wavefronts)
     for (int i = wave; i < n_empty; i += gridDim.x * kWavesPerGroup) zero_row(a, empty[i], lane);
     if (wave >= W) return;
@@ -533,13 +562,15 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
 
     const uint32_t x_start = st.x0;
     const uint32_t x_end = st.x1;
-    int uh = st.u;
+    int uh = uniform(st.u);
     if (x_start >= x_end) return;
 
+    // the unit offsets and records are read by scalar loads (uh is wave-uniform), so that
+    // describing the next segment does not wait for the tiles in flight
     auto describe = [&](uint32_t xs) {
-        while (cb[uh + 1] <= xs) ++uh;                    // skip finished / empty units
-        const UnitInfo ui = unit[uh];
-        const uint32_t base = cb[uh];
+        while (ld_scalar(cb + uh + 1) <= xs) ++uh;       // skip finished / empty units
+        const UnitInfo ui = ld_unit(unit + uh);
+        const uint32_t base = ld_scalar(cb + uh);
         Seg sg;
         sg.u = uh;
         sg.g = (int)((xs - base) / (uint32_t)ui.nb);
@@ -621,11 +652,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
         u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
         if constexpr (fused)
             if (takes_new) load_new(cur, kn, vn);   // wavefront-uniform
-        // a pair cut after this segment and starting in it: its later shares' starts,
-        // loaded now and used when the merge record is written
+        // a pair cut after this segment and starting in it (only a share's last segment)
         const bool opens_cut = cur.starts && cur.end < cur.pe;
-        uint32_t next = cur.pe;
-        if (opens_cut && wave + 1 + lane < W) next = wx0[wave + 1 + lane];
 
         typename S::Extra ex;
         S::init(ex);
@@ -700,21 +728,35 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
         // plain copies of what the loads need (a select between fields of the two records
         // would keep both records in memory)
         const int g_cur = cur.g, g_nxt = nxt.g, j1_cur = cur.j1;
+        // The first block id of the next chunk and of the next segment come by scalar loads:
+        // reading them out of a vector-loaded id register at the chunk's end would make the
+        // wavefront wait for the tile in flight before issuing the next one.
+        const int32_t* bt_cur = a.block_tables + (size_t)cur.seq * a.max_blocks;
+        const int nxt_b =
+            more ? ld_scalar_at(a.block_tables + (size_t)nxt.seq * a.max_blocks + nxt.j0) : 0;
         int cids = ids;
         for (int c0 = cur.j0;; c0 += kWave) {
             const int n = (j1_cur - c0) < kWave ? (j1_cur - c0) : kWave;
             const bool last_chunk = c0 + kWave >= j1_cur;
             const int nc_ids = last_chunk ? 0 : load_ids(cur, c0 + kWave);
-            // block k of this chunk, else the next chunk's or next segment's first block; at
-            // the very end the same loads read nothing.  Every case issues the same loads,
-            // so the wait counts stay exact.
+            const int nc_b = last_chunk ? 0 : ld_scalar_at(bt_cur + c0 + kWave);
+            // An odd chunk is padded with an empty block (loads of 0 bytes, never consumed),
+            // so that the block after the chunk always lands in A: moving a tile from B to A
+            // would wait for all loads in flight.
+            const int n2 = (n + 1) & ~1;
+            // block k of this chunk, the padding, else the next chunk's or next segment's
+            // first block; at the very end the same loads read nothing.  Every case issues
+            // the same loads, so the wait counts stay exact.
             auto load_next = [&](int k, typename S::Tile& t, bool& ok) {
                 if (k < n) {
                     load_tile(g_cur, block_id(cids, k, ok), true, t);
+                } else if (k < n2) {
+                    ok = false;
+                    load_tile(g_cur, 0, false, t);
                 } else if (!last_chunk) {
-                    load_tile(g_cur, block_id(nc_ids, 0, ok), true, t);
+                    load_tile(g_cur, checked_block(nc_b, a.num_blocks, ok), true, t);
                 } else if (more) {
-                    load_tile(g_nxt, block_id(nids, 0, ok), true, t);
+                    load_tile(g_nxt, checked_block(nxt_b, a.num_blocks, ok), true, t);
                 } else {
                     ok = false;
                     load_tile(g_cur, 0, false, t);
@@ -724,14 +766,11 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
                 load_next(k + 1, B, okB);
                 bad |= !okA;
                 consume(A, (c0 + k) * BS, lim_tiles, okA);
-                if (k + 1 >= n) {
-                    A = B;
-                    okA = okB;
-                    break;
-                }
                 load_next(k + 2, A, okA);
-                bad |= !okB;
-                consume(B, (c0 + k + 1) * BS, lim_tiles, okB);
+                if (k + 1 < n) {   // wavefront-uniform: the padding is not consumed
+                    bad |= !okB;
+                    consume(B, (c0 + k + 1) * BS, lim_tiles, okB);
+                }
                 if (k + 2 >= n) break;
             }
             if (last_chunk) break;
@@ -793,8 +832,9 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
             }
         }
         if (opens_cut) {
-            // this wavefront holds the pair's first block: leave its merge task
-            const int nc = pair_waves(wx0, W, wave, cur.pe, next, lane);
+            // this wavefront holds the pair's first block: leave its merge task (the plan
+            // counted the shares the pair spans)
+            const int nc = ld_scalar(wcut + wave);
             if (lane == 0) tasks[wave + 1] = make_int4(u, g, nc, first_segment ? 0 : 1);
         }
         if (!more) break;

@@ -208,4 +208,22 @@ __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// A read through the constant address space: with a wave-uniform address it becomes a
+// scalar load, counted apart from the vector memory operations.  (Vector loads and stores
+// share one in-order counter: waiting for a vector load whose value is needed at once means
+// waiting for every vector load and store issued before it, tiles in flight included.)
+// Only for data that no launch in flight writes.
+template <class T>
+__device__ __forceinline__ T ld_scalar(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+// the same, for an address the compiler may hold in vector registers (made uniform first)
+template <class T>
+__device__ __forceinline__ T ld_scalar_at(const T* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return ld_scalar((const T*)(lo | hi << 32));
+}
+
 }  // namespace pa

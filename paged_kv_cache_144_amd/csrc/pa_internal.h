@@ -71,7 +71,9 @@ static_assert(sizeof(WaveStart) == 48, "three 16-byte loads");
 //   unit     UnitInfo[U]
 //   empty    int32[U]      the rows with nothing to read
 //   wave_x0  uint32[W+1]   first linear block of each wave's share
-//   wave_u   int32[W]      unit holding that block
+//   wave_u   int32[W]      unit holding that block, while the plan runs; then the number of
+//                          shares of the cut pair that the share's last segment opens (0:
+//                          none), which the decode kernels read for the pair's merge task
 //   wave_st  WaveStart[Wmax+4]  each wavefront's first segment (every launched
 //                          wavefront reads its entry before it checks w < W)
 //   tiles    int2[Tmax]    chunk-row tiles (sequence, first row) for the MFMA kernel

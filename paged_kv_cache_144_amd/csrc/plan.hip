@@ -280,6 +280,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
         st.b0 = bt[st.j0];
         st.b1 = st.j0 + 1 < st.j1 ? bt[st.j0 + 1] : st.b0;
         wst[w] = st;
+        // A pair that starts inside this share and runs past its end is cut: its first
+        // wavefront writes its merge task, whose contributor count is the number of shares
+        // that start before the pair's end.  Only the share's last segment can open such a
+        // pair.  The count replaces the unit index in wu (read above, by this thread only).
+        int nc = 0;
+        {
+            int ul = u;
+            while (cb[ul + 1] <= x1 - 1) ++ul;       // the unit of the share's last block
+            const uint32_t nbl = (uint32_t)unit[ul].nb, bl = cb[ul];
+            const uint32_t psl = bl + (x1 - 1 - bl) / nbl * nbl, pel = psl + nbl;
+            if (psl >= x0 && pel > x1) {
+                // first share index past w that starts at or after pel (wx0[W] = T >= pel)
+                int lo = w + 1, hi = W;
+                while (lo < hi) {
+                    const int mid = (lo + hi) / 2;
+                    if (wx0[mid] < pel) lo = mid + 1; else hi = mid;
+                }
+                nc = lo - w;
+            }
+        }
+        wu[w] = nc;
     }
     if (tid == 0) {
         hdr[0] = s_err; hdr[1] = (int32_t)T; hdr[2] = W; hdr[3] = s_empty; hdr[4] = (int32_t)NT;
