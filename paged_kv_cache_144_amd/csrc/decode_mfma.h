@@ -83,6 +83,8 @@ struct MfmaKv16 {
     static constexpr size_t TILE = (size_t)kBlock * D * 2;
     static constexpr int BPT = 1;                 // blocks per tile
     static constexpr bool kNewRows = true;        // can take a step's new rows directly
+    static constexpr bool kStageOut = true;       // outputs leave through LDS (see the kernel)
+    static constexpr bool kLeanStream = true;     // the item stream without full waits (kernel)
     // column c16 of S^T is query head c16 (none past G); output row 4 q4 + r is head
     // 4 q4 + r, for every column block
     __device__ static int q_head(int c16) { return c16; }
@@ -112,6 +114,16 @@ struct MfmaKv16 {
         r.f = 1.f;
     }
     __device__ static void prep_q(Q&) {}
+    // the loads of a tile, issued over a resource of 0 bytes: zeros, no memory access (for
+    // a slot nothing will consume; the same loads as load(), so the wait counts match)
+    __device__ static void load_null(const char* base, Tile& t) {
+        const rsrc_t r = buf_rsrc(base, 0u);
+        const uint32_t o = (uint32_t)lane_id() * 16u;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) t.k[c] = ld16_buf(r, o);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) t.v[i] = ld16_buf(r, o);
+    }
     __device__ static void load(const char* kb, const char* vb, const size_t (&offs)[BPT],
                                 Tile& t) {
         const size_t off = offs[0];
@@ -239,6 +251,12 @@ struct MfmaKvQ8 {
     static_assert(KC % 2 == 0, "an even number of scale groups");
     // new rows must be quantized into the cache first (pa_write_kv)
     static constexpr bool kNewRows = false;
+    // Outputs are stored straight from the MFMA layout: the staging through LDS that the
+    // 16-bit kernel uses needs registers this kernel does not have.
+    static constexpr bool kStageOut = false;
+    // The item stream keeps its register-held block ids and its copy of a tile between the
+    // register sets: the scalar ids and the padding item of the 16-bit kernel spill here.
+    static constexpr bool kLeanStream = false;
     // Stacked P.V, where the scale groups and heads fit the MFMA's 16 rows: A row m is
     // (scale group m / G, head m % G), so one A operand (P x the row's own V scale) serves
     // every 16-column block, and output row m is meaningful in its own group's two column
@@ -330,6 +348,37 @@ struct MfmaKvQ8 {
 #pragma unroll
         for (int h = 0; h < BPT; ++h) offs[h] = off;
         load(kb, vb, offs, t);
+    }
+    // the loads of a tile, issued over a resource of 0 bytes: zeros, no memory access (for
+    // a slot nothing will consume; the same loads as load(), so the wait counts match)
+    __device__ static void load_null(const char* base, Tile& t) {
+        const rsrc_t r = buf_rsrc(base, 0u);
+        const uint32_t o = (uint32_t)lane_id() * 16u;
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) {
+#pragma unroll
+            for (int i = 0; i < KN; ++i) t.k[h][i] = ld16_buf(r, o);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if constexpr (VW == 1) {
+                    t.v[h][s][0] = ld4_buf(r, o);
+                } else if constexpr (VW == 2) {
+                    const u32x2 x = ld8_buf(r, o);
+                    t.v[h][s][0] = x.x; t.v[h][s][1] = x.y;
+                } else {
+                    const u32x4 x = ld16_buf(r, o);
+                    t.v[h][s][0] = x.x; t.v[h][s][1] = x.y; t.v[h][s][2] = x.z; t.v[h][s][3] = x.w;
+                }
+            }
+            if constexpr (SB == 2) {
+                t.sc[h][0] = ld2_buf(r, o);
+            } else if constexpr (SB == 4) {
+                t.sc[h][0] = ld4_buf(r, o);
+            } else {
+                const u32x2 x = ld8_buf(r, o);
+                t.sc[h][0] = x.x; t.sc[h][1] = x.y;
+            }
+        }
     }
     __device__ static void load(const char* kb, const char* vb, const size_t (&offs)[BPT],
                                 Tile& t) {
@@ -563,23 +612,19 @@ struct MfmaKvQ8 {
     __device__ static void finish(f32x4 (&)[NACC], const Extra&) {}
     // acc[b] of lane c16 is column 16 b + c16
     // row r of lane quad q4, column blocks row_has_block(q4, r, b)
-    // the head's row of the staged output: column 16 b + c16 = acc[b][r] x inv, as fp32 or
-    // converted to the 16-bit output type
-    __device__ static void stage_out(float* dst, const f32x4 (&acc)[NACC], int r, float inv,
-                                     int c16, int q4) {
+    // acc[b] of lane c16 is column 16 b + c16; row r of lane quad q4, column blocks
+    // row_has_block(q4, r, b)
+    __device__ static void store(const DecodeArgs& a, size_t ob, const f32x4 (&acc)[NACC],
+                                 int r, float inv, int c16, int q4) {
 #pragma unroll
         for (int b = 0; b < NACC; ++b)
-            if (row_has_block(q4, r, b)) dst[16 * b + c16] = acc[b][r] * inv;
+            if (row_has_block(q4, r, b)) store_out1(a, ob + 16 * b + c16, acc[b][r] * inv);
     }
-    __device__ static void stage_out16(int out_dtype, uint16_t* dst, const f32x4 (&acc)[NACC],
-                                       int r, float inv, int c16, int q4) {
+    __device__ static void store_part(float* dst, const f32x4 (&acc)[NACC], int r, int c16,
+                                      int q4) {
 #pragma unroll
         for (int b = 0; b < NACC; ++b)
-            if (row_has_block(q4, r, b)) {
-                const float v = acc[b][r] * inv;
-                dst[16 * b + c16] = (uint16_t)(out_dtype == PA_F16 ? f32_to_f16_bits(v)
-                                                                   : f32_to_bf16_bits(v));
-            }
+            if (row_has_block(q4, r, b)) dst[16 * b + c16] = acc[b][r];
     }
 };
 
@@ -607,7 +652,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     int32_t* hdr = (int32_t*)(a.ws + a.lay.header);
     const uint32_t* cb = (const uint32_t*)(a.ws + a.lay.cb);
     const UnitInfo* unit = (const UnitInfo*)(a.ws + a.lay.unit);
-    const uint32_t* wx0 = (const uint32_t*)(a.ws + a.lay.wave_x0);
+    const int32_t* wcut = (const int32_t*)(a.ws + a.lay.wave_u);
     float2* pml = (float2*)(a.ws + a.lay.part_ml);
     float* pacc = (float*)(a.ws + a.lay.part_acc);
     int4* tasks = (int4*)(a.ws + a.lay.tasks);
@@ -632,7 +677,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     // this wavefront's rows of lds_out as [G heads][D] and leaves as whole 16-byte lane
     // stores: one or two store instructions instead of one per (row, column block) of the
     // MFMA layout, each of which wrote 32-byte pieces.
-    __shared__ __align__(16) float lds_out[kWavesPerGroup][G * D];
+    __shared__ __align__(16) float lds_out[kWavesPerGroup][Ops::kStageOut ? G * D : 4];
     float* mo = lds_out[threadIdx.x >> 6];
     const float qscale = a.scale * kLog2e;
     const size_t block_stride = (size_t)a.num_kv_heads * Ops::TILE;
@@ -643,10 +688,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     const uint32_t x_end = st.x1;
     int uh = st.u;
 
+    // the unit offsets and records are read by scalar loads (uh is wave-uniform), so that
+    // describing the next segment does not wait for the tiles in flight
     auto describe = [&](uint32_t xs) {
-        while (cb[uh + 1] <= xs) ++uh;
-        const UnitInfo ui = unit[uh];
-        const uint32_t base = cb[uh];
+        while (ld_scalar(cb + uh + 1) <= xs) ++uh;
+        const UnitInfo ui = ld_unit(unit + uh);
+        const uint32_t base = ld_scalar(cb + uh);
         Seg sg;
         sg.u = uh;
         sg.g = (int)((xs - base) / (uint32_t)ui.nb);
@@ -671,16 +718,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
             ((size_t)sg.u * a.num_q_heads + (size_t)sg.g * G + Ops::q_head(c16)) * D;
         Ops::load_q(a.q, qrow, c16, q4, q);
     };
-    auto block_id = [&](int ids, int idx, bool& valid) {
-        int b = __builtin_amdgcn_readlane(ids, idx);
-        valid = (unsigned)b < (unsigned)a.num_blocks;
-        return valid ? b : 0;
-    };
     // An item: the next BPT blocks of the stream inside one chunk of ids (fewer at the end
-    // of a chunk; cnt = 0 when nothing is left).  A tile always loads BPT blocks: a slot
-    // past cnt re-reads block idx_pad of the same id register and is never consumed.  The
-    // loads are one straight sequence whatever the case, so that the compiler's wait
-    // counts for the tile in use never include the tile being loaded.
+    // of a chunk).  A tile always loads BPT blocks: a slot past cnt re-reads another block
+    // of the item and is never consumed.  The loads are one straight sequence whatever the
+    // case, so that the compiler's wait counts for the tile in use never include the tile
+    // being loaded.  An empty item (cnt = 0: padding, or the end of the share) issues the
+    // same loads over a resource of 0 bytes.
     // With the step's new rows given (16-bit caches, one block per tile), a row's newest
     // token (position len - 1) is not in the cache yet: the tile of the block holding it
     // (table index jl) takes that token row from new row u, KV head g (Ops::load_new).  Its
@@ -689,15 +732,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
     constexpr bool fused = NEW && Ops::kNewRows;
     auto new_len = [&](const Seg& sg) { return fused ? sg.len : 0; };
     struct Item { int cnt; bool ok[BPT]; };
-    // j: the table index of the item's first block; u, nl: its segment's unit and new_len
-    auto load_item = [&](int g, int ids, int idx0, int cnt, int idx_pad, int j, int u, int nl,
+    // bid: the item's block ids (slots past cnt repeat one of them); j: the table index of
+    // its first block; u, nl: its segment's unit and new_len
+    auto load_item = [&](int g, const int (&bid)[BPT], int cnt, int j, int u, int nl,
                          Tile& t, Item& it) __attribute__((always_inline)) {
         size_t off[BPT];
         it.cnt = cnt;
 #pragma unroll
         for (int h = 0; h < BPT; ++h) {
             bool v;
-            const int b = block_id(ids, h < cnt ? idx0 + h : idx_pad, v);
+            const int b = checked_block(bid[h], a.num_blocks, v);
             it.ok[h] = v;
             off[h] = (size_t)b * block_stride + (size_t)g * Ops::TILE;
         }
@@ -708,6 +752,34 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
         } else {
             Ops::load(kbase, vbase, off, t);
         }
+    };
+    // block ids idx0 .. of a vector-loaded id register (slots past cnt repeat idx_pad)
+    auto ids_of = [&](int ids, int idx0, int cnt, int idx_pad, int (&bid)[BPT])
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < BPT; ++h)
+            bid[h] = __builtin_amdgcn_readlane(ids, h < cnt ? idx0 + h : idx_pad);
+    };
+    // the first BPT block ids of table entries [j, j1), by scalar loads (entries past j1
+    // repeat the last): reading them out of a vector-loaded id register would make the
+    // wavefront wait for the tile in flight before it could issue the next one
+    auto ids_ahead = [&](int seq, int j, int j1, int (&bid)[BPT]) __attribute__((always_inline)) {
+        const int32_t* row = a.block_tables + (size_t)seq * a.max_blocks;
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) bid[h] = ld_scalar_at(row + (j + h < j1 ? j + h : j1 - 1));
+    };
+    // the same from an id register: ids idx0 .. for cnt slots, the rest repeat idx_pad
+    auto load_item_reg = [&](int g, int ids, int idx0, int cnt, int idx_pad, int j, int u,
+                             int nl, Tile& t, Item& it) __attribute__((always_inline)) {
+        int bid[BPT];
+        ids_of(ids, idx0, cnt, idx_pad, bid);
+        load_item(g, bid, cnt, j, u, nl, t, it);
+    };
+    auto load_empty = [&](Tile& t, Item& it) __attribute__((always_inline)) {
+        it.cnt = 0;
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) it.ok[h] = false;
+        Ops::load_null((const char*)a.k_cache, t);
     };
 
     if (x_start >= x_end) return;
@@ -744,16 +816,18 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
         Seg nxt = cur;
         Q qn;
         int nids = 0;
+        int nxt_bid[BPT];
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) nxt_bid[h] = 0;
         if (more) {
             nxt = describe(cur.end);
             load_q(nxt, qn);
             nids = load_ids(nxt, nxt.j0);
+            if constexpr (Ops::kLeanStream) ids_ahead(nxt.seq, nxt.j0, nxt.j1, nxt_bid);
         }
         Ops::prep_q(q);
-        // a pair that starts here and continues past the share: the later shares' starts
+        // a pair that starts here and continues past the share (only a share's last segment)
         const bool opens_cut = cur.starts && cur.end < cur.pe;
-        uint32_t next = cur.pe;
-        if (opens_cut && wave + 1 + lane < W) next = wx0[wave + 1 + lane];
 
         f32x4 acc[NACC];   // O: lane holds heads 4 q4 .. 4 q4 + 3 of its columns
 #pragma unroll
@@ -834,41 +908,89 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
         const int g_cur = cur.g, g_nxt = nxt.g, j1_cur = cur.j1, nb_nxt = nxt.j1 - nxt.j0;
         const int j0_nxt = nxt.j0, u_cur = cur.u, u_nxt = nxt.u, nl_nxt = more ? new_len(nxt) : 0;
         int cids = ids;
-        for (int c0 = cur.j0;; c0 += kWave) {
-            const int n = (cur.j1 - c0) < kWave ? (cur.j1 - c0) : kWave;
-            const bool last_chunk = c0 + kWave >= cur.j1;
-            const int nc_ids = last_chunk ? 0 : load_ids(cur, c0 + kWave);
-            const int items = (n + BPT - 1) / BPT;
-            // item k of this chunk, else the first item of the next chunk or of the next
-            // segment; at the very end nothing (the load repeats this chunk's last block).
-            // Every case issues the same loads, so the wait counts stay exact.
-            auto load_next = [&](int k, Tile& t, Item& it) __attribute__((always_inline)) {
-                if (k < items) {
-                    load_item(g_cur, cids, BPT * k, min(BPT, n - BPT * k), BPT * k,
-                              c0 + BPT * k, u_cur, nl_cur, t, it);
-                } else if (!last_chunk) {
-                    load_item(g_cur, nc_ids, 0, min(BPT, j1_cur - c0 - kWave), 0, c0 + kWave,
-                              u_cur, nl_cur, t, it);
-                } else if (more) {
-                    load_item(g_nxt, nids, 0, min(BPT, nb_nxt), 0, j0_nxt, u_nxt, nl_nxt, t, it);
-                } else {
-                    load_item(g_cur, cids, 0, 0, n - 1, -1, 0, 0, t, it);
+        if constexpr (!Ops::kLeanStream) {
+            for (int c0 = cur.j0;; c0 += kWave) {
+                const int n = (cur.j1 - c0) < kWave ? (cur.j1 - c0) : kWave;
+                const bool last_chunk = c0 + kWave >= cur.j1;
+                const int nc_ids = last_chunk ? 0 : load_ids(cur, c0 + kWave);
+                const int items = (n + BPT - 1) / BPT;
+                // item k of this chunk, else the first item of the next chunk or of the next
+                // segment; at the very end nothing (the load repeats this chunk's last
+                // block).  Every case issues the same loads, so the wait counts stay exact.
+                auto load_next = [&](int k, Tile& t, Item& it) __attribute__((always_inline)) {
+                    if (k < items) {
+                        load_item_reg(g_cur, cids, BPT * k, min(BPT, n - BPT * k), BPT * k,
+                                      c0 + BPT * k, u_cur, nl_cur, t, it);
+                    } else if (!last_chunk) {
+                        load_item_reg(g_cur, nc_ids, 0, min(BPT, j1_cur - c0 - kWave), 0,
+                                      c0 + kWave, u_cur, nl_cur, t, it);
+                    } else if (more) {
+                        load_item_reg(g_nxt, nids, 0, min(BPT, nb_nxt), 0, j0_nxt, u_nxt, nl_nxt,
+                                      t, it);
+                    } else {
+                        load_item_reg(g_cur, cids, 0, 0, n - 1, -1, 0, 0, t, it);
+                    }
+                };
+                for (int k = 0;; k += 2) {
+                    load_next(k + 1, B, iB);
+                    consume_item(A, iA, c0 + BPT * k);
+                    if (k + 1 >= items) {
+                        A = B;
+                        iA = iB;
+                        break;
+                    }
+                    load_next(k + 2, A, iA);
+                    consume_item(B, iB, c0 + BPT * (k + 1));
+                    if (k + 2 >= items) break;
                 }
-            };
-            for (int k = 0;; k += 2) {
-                load_next(k + 1, B, iB);
-                consume_item(A, iA, c0 + BPT * k);
-                if (k + 1 >= items) {
-                    A = B;
-                    iA = iB;
-                    break;
-                }
-                load_next(k + 2, A, iA);
-                consume_item(B, iB, c0 + BPT * (k + 1));
-                if (k + 2 >= items) break;
+                if (last_chunk) break;
+                cids = nc_ids;
             }
-            if (last_chunk) break;
-            cids = nc_ids;
+        } else {
+            for (int c0 = cur.j0;; c0 += kWave) {
+                const int n = (cur.j1 - c0) < kWave ? (cur.j1 - c0) : kWave;
+                const bool last_chunk = c0 + kWave >= cur.j1;
+                const int nc_ids = last_chunk ? 0 : load_ids(cur, c0 + kWave);
+                int nc_bid[BPT];
+#pragma unroll
+                for (int h = 0; h < BPT; ++h) nc_bid[h] = 0;
+                if (!last_chunk) ids_ahead(cur.seq, c0 + kWave, j1_cur, nc_bid);
+                const int items = (n + BPT - 1) / BPT;
+                // An odd number of items is padded with an empty one (never consumed), so that
+                // the item after the chunk always lands in A: moving a tile from B to A would
+                // wait for all loads in flight.
+                const int items2 = (items + 1) & ~1;
+                // item k of this chunk, the padding, else the first item of the next chunk or of
+                // the next segment; at the very end an empty item.  Every case issues the same
+                // loads, so the wait counts stay exact.
+                auto load_next = [&](int k, Tile& t, Item& it) __attribute__((always_inline)) {
+                    if (k < items) {
+                        int bid[BPT];
+                        const int cnt = min(BPT, n - BPT * k);
+                        ids_of(cids, BPT * k, cnt, BPT * k, bid);
+                        load_item(g_cur, bid, cnt, c0 + BPT * k, u_cur, nl_cur, t, it);
+                    } else if (k < items2) {
+                        load_empty(t, it);
+                    } else if (!last_chunk) {
+                        load_item(g_cur, nc_bid, min(BPT, j1_cur - c0 - kWave), c0 + kWave, u_cur,
+                                  nl_cur, t, it);
+                    } else if (more) {
+                        load_item(g_nxt, nxt_bid, min(BPT, nb_nxt), j0_nxt, u_nxt, nl_nxt, t, it);
+                    } else {
+                        load_empty(t, it);
+                    }
+                };
+                for (int k = 0;; k += 2) {
+                    load_next(k + 1, B, iB);
+                    consume_item(A, iA, c0 + BPT * k);
+                    load_next(k + 2, A, iA);
+                    if (k + 1 < items)   // wavefront-uniform: the padding is not consumed
+                        consume_item(B, iB, c0 + BPT * (k + 1));
+                    if (k + 2 >= items) break;
+                }
+                if (last_chunk) break;
+                cids = nc_ids;
+            }
         }
 
         Ops::finish(acc, ex);
@@ -882,20 +1004,20 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
             const size_t pi = ((size_t)wave * 2 + slot) * G + c16;
             pml[pi] = make_float2(m, lt);
         }
+        if constexpr (Ops::kStageOut) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int h = Ops::row_head(q4, r);
-            const float lh = __shfl(lt, h);
-            if (Ops::row_valid(q4, r)) {
-                const float inv = !complete ? 1.f : lh > 0.f ? 1.f / lh : 0.f;
-                if (out16)
-                    Ops::stage_out16(a.out_dtype, reinterpret_cast<uint16_t*>(mo) + h * D, acc,
-                                     r, inv, c16, q4);
-                else
-                    Ops::stage_out(mo + h * D, acc, r, inv, c16, q4);
+            for (int r = 0; r < 4; ++r) {
+                const int h = Ops::row_head(q4, r);
+                const float lh = __shfl(lt, h);
+                if (Ops::row_valid(q4, r)) {
+                    const float inv = !complete ? 1.f : lh > 0.f ? 1.f / lh : 0.f;
+                    if (out16)
+                        Ops::stage_out16(a.out_dtype, reinterpret_cast<uint16_t*>(mo) + h * D,
+                                         acc, r, inv, c16, q4);
+                    else
+                        Ops::stage_out(mo + h * D, acc, r, inv, c16, q4);
+                }
             }
-        }
-        {
             // the wavefront's own LDS rows, written and read back in order: no barrier
             constexpr int N = G * D;
             if (out16) {
@@ -918,9 +1040,26 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void deco
                         st16(dst + i, *reinterpret_cast<const u32x4*>(mo + i));
                 }
             }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = Ops::row_head(q4, r);
+                const float lh = __shfl(lt, h);
+                if (Ops::row_valid(q4, r)) {
+                    if (complete) {
+                        const float inv = lh > 0.f ? 1.f / lh : 0.f;
+                        const size_t ob =
+                            ((size_t)cur.u * a.num_q_heads + (size_t)cur.g * G + h) * D;
+                        Ops::store(a, ob, acc, r, inv, c16, q4);
+                    } else {
+                        Ops::store_part(pacc + (((size_t)wave * 2 + slot) * G + h) * D, acc, r,
+                                        c16, q4);
+                    }
+                }
+            }
         }
-        if (opens_cut) {
-            const int nc = pair_waves(wx0, W, wave, cur.pe, next, lane);
+        if (opens_cut) {   // the plan counted the shares the pair spans
+            const int nc = ld_scalar(wcut + wave);
             if (lane == 0) tasks[wave + 1] = make_int4(cur.u, cur.g, nc, first_segment ? 0 : 1);
         }
         if (!more) break;

@@ -53,12 +53,15 @@ __device__ __forceinline__ rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
                                              0x00020000);
 }
-// 16, 8 or 2 bytes at byte offset off of r, non-temporal like ld16_stream
+// 16, 8, 4 or 2 bytes at byte offset off of r, non-temporal like ld16_stream
 __device__ __forceinline__ u32x4 ld16_buf(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
 }
 __device__ __forceinline__ u32x2 ld8_buf(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2));
+}
+__device__ __forceinline__ uint32_t ld4_buf(rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 2);
 }
 __device__ __forceinline__ uint32_t ld2_buf(rsrc_t r, uint32_t off) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 2);
