@@ -7,7 +7,9 @@ whose shares start before its end); the model follows the arithmetic of the plan
 count and, below it and above one workgroup per compute unit, rounded down to whole such
 rounds, the effective
 pair cost C' = C while 4 T / W >= C + 5 (else 4 T / W - 5, at least 0), and share w starting
-at weighted position floor(w TW / W)."""
+at weighted position floor(w TW / W).  The plan also counts, per share, the shares that the
+cut pair opened by its last segment spans (the merge task's contributors); the model checks
+that count against the shares that meet each pair, found by brute force."""
 import numpy as np
 import pytest
 
@@ -55,8 +57,65 @@ def plan_split(nbs, heads, min_blocks, max_waves, pair_cost, wave_round=0):
     return wx0, wu
 
 
+def plan_cut_counts(nbs, heads, wx0, wu):
+    """Per share, the plan's count of the shares that the cut pair opened by its last
+    segment spans (0: no such pair): the pair holding the share's last block is cut when it
+    starts inside the share and ends past it; its count is the number of shares that start
+    before its end, found by a binary search over the later share starts (csrc/plan.hip)."""
+    nbs = np.asarray(nbs, np.int64)
+    cb = np.concatenate([[0], np.cumsum(nbs * heads)])
+    W = len(wu)
+    out = []
+    for w in range(W):
+        x0, x1 = wx0[w], wx0[w + 1]
+        u = wu[w]
+        while cb[u + 1] <= x0:
+            u += 1
+        ul = u
+        while cb[ul + 1] <= x1 - 1:
+            ul += 1
+        nb = int(nbs[ul])
+        psl = int(cb[ul]) + (x1 - 1 - int(cb[ul])) // nb * nb
+        pel = psl + nb
+        nc = 0
+        if psl >= x0 and pel > x1:
+            lo, hi = w + 1, W
+            while lo < hi:
+                mid = (lo + hi) // 2
+                if wx0[mid] < pel:
+                    lo = mid + 1
+                else:
+                    hi = mid
+            nc = lo - w
+        out.append(nc)
+    return out
+
+
+def brute_cut_counts(nbs, heads, wx0):
+    """The same by definition: every pair, the shares whose block ranges meet it; a pair met
+    by several shares is counted at the share holding its first block."""
+    nbs = np.asarray(nbs, np.int64)
+    W = len(wx0) - 1
+    out = [0] * W
+    pos = 0
+    for nb in nbs.tolist():
+        for _ in range(heads):
+            ps, pe = pos, pos + nb
+            pos = pe
+            if nb == 0:
+                continue
+            meet = [w for w in range(W) if wx0[w] < pe and wx0[w + 1] > ps]
+            if len(meet) > 1:
+                assert wx0[meet[0]] <= ps < wx0[meet[0] + 1]   # the first holds its start
+                out[meet[0]] = len(meet)
+    return out
+
+
 def check(nbs, heads, min_blocks, max_waves, pair_cost, wave_round=0):
     wx0, wu = plan_split(nbs, heads, min_blocks, max_waves, pair_cost, wave_round)
+    if wu:
+        assert plan_cut_counts(nbs, heads, wx0, wu) == brute_cut_counts(nbs, heads, wx0), (
+            nbs, heads, min_blocks, max_waves, pair_cost, wave_round)
     T = int(np.sum(nbs)) * heads
     assert wx0[0] == 0 and wx0[-1] == T
     # non-empty and consecutive: strictly increasing starts cover [0, T)
