@@ -131,7 +131,15 @@ __device__ void write_new_rows(const DecodeArgs& a, long t) {
     const int r = (int)(t % per_seq);
     const int kv = r / (a.num_kv_heads * pieces);          // 0: K, 1: V
     const int g = (r / pieces) % a.num_kv_heads, c = r % pieces;
+    // The row piece loads beside the sequence's length, so that the store waits for two
+    // dependent loads (length, then table entry), not three.  (The empty asm takes the
+    // piece where it is loaded: the compiler would otherwise sink the load past the
+    // checks, next to the store.)
+    const size_t src = ((size_t)s * a.num_kv_heads + g) * a.row_bytes + (size_t)c * 16;
+    const char* from = (const char*)(kv ? a.v_new : a.k_new);
+    u32x4 row = ld16(from + src);
     const int L = a.seq_lens[s];
+    asm volatile("" : "+v"(row));
     if (L <= 0 || L > a.max_seq_len || (long)L > (long)a.max_blocks * a.block_size) return;
     const int j = (L - 1) / a.block_size;
     const int b = a.block_tables[(size_t)s * a.max_blocks + j];
@@ -139,10 +147,8 @@ __device__ void write_new_rows(const DecodeArgs& a, long t) {
     const size_t tile = (size_t)a.block_size * a.row_bytes;
     const size_t dst = ((size_t)b * a.num_kv_heads + g) * tile +
                        (size_t)((L - 1) % a.block_size) * a.row_bytes + (size_t)c * 16;
-    const size_t src = ((size_t)s * a.num_kv_heads + g) * a.row_bytes + (size_t)c * 16;
-    const char* from = (const char*)(kv ? a.v_new : a.k_new);
     char* to = (char*)(kv ? a.v_cache : a.k_cache);
-    st16(to + dst, ld16(from + src));
+    st16(to + dst, row);
 }
 
 // Merge kernel: one wavefront per (share boundary w >= 1, head of the group).  It reads
@@ -159,12 +165,17 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void merge_kernel(DecodeArg
     const int4* tasks = (const int4*)(a.ws + a.lay.tasks);
     const float2* pml = (const float2*)(a.ws + a.lay.part_ml);
     const float* pacc = (const float*)(a.ws + a.lay.part_acc);
-    const int q = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int q = uniform(blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6));
     const int w = q / G + 1, gi = q % G;
     const int32_t* hdr = (const int32_t*)(a.ws + a.lay.header);
-    const int W = hdr[2];
-    if (w >= W || hdr[5] != 0) return;   // (a group-mode plan holds no merge tasks)
-    const int4 t = tasks[w];
+    // The header's fields and the task slot are read together by scalar loads (w is
+    // wave-uniform; the slot index is clamped to the last of the max_waves + 1 slots, as the
+    // grid is rounded up to whole workgroups): one wait before the partials are loaded.
+    const int32_t* slot = (const int32_t*)(tasks + (w < a.max_waves ? w : a.max_waves));
+    const int4 t = make_int4(ld_scalar(slot), ld_scalar(slot + 1), ld_scalar(slot + 2),
+                             ld_scalar(slot + 3));
+    const int W = ld_scalar(hdr + 2), group_mode = ld_scalar(hdr + 5);
+    if (w >= W || group_mode != 0) return;   // (a group-mode plan holds no merge tasks)
     if (t.z <= 0) return;
     merge_pair<D, G>(a, t.x, t.y, w - 1, t.z, t.w, gi, pml, pacc, lane_id());
 }

@@ -274,24 +274,6 @@ struct KvOps<DT, D, G, BS, true> {
     }
 };
 
-// The wavefronts whose shares hold blocks of a pair cut by share boundaries: `wave` holds
-// its first block; the shares are consecutive and non-empty, so the others are the waves
-// after it whose shares start before the pair's end pe.  `next` is wx0[wave + 1 + lane]
-// (or pe where that index is past W), loaded early by the caller.
-__device__ inline int pair_waves(const uint32_t* wx0, int W, int wave, uint32_t pe,
-                                 uint32_t next, int lane) {
-    int n = 1;
-    uint64_t m = __builtin_amdgcn_ballot_w64(next < pe);
-    for (int base = wave + 1;;) {
-        n += __builtin_popcountll(m);
-        if (m != ~0ull) break;
-        base += kWave;
-        const int w = base + lane;
-        m = __builtin_amdgcn_ballot_w64(w < W && wx0[w] < pe);
-    }
-    return n;
-}
-
 template <int PE>
 __device__ __forceinline__ void store_row(const DecodeArgs& a, size_t idx, const float* v) {
     if (a.out_dtype == PA_F32) {
@@ -533,7 +515,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void decode_kernel(DecodeAr
     int32_t* hdr = (int32_t*)(a.ws + a.lay.header);
     const uint32_t* cb = (const uint32_t*)(a.ws + a.lay.cb);
     const UnitInfo* unit = (const UnitInfo*)(a.ws + a.lay.unit);
-    const uint32_t* wx0 = (const uint32_t*)(a.ws + a.lay.wave_x0);
     const int32_t* wcut = (const int32_t*)(a.ws + a.lay.wave_u);
     float2* pml = (float2*)(a.ws + a.lay.part_ml);
     float* pacc = (float*)(a.ws + a.lay.part_acc);
