@@ -152,6 +152,20 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
     const bool w_rows_full = r0 + (wave + 1) * QR <= n;
     const int wp_first = L - n + r0 + wave * QR;
     const int wlo_last = (a.window > 0) ? max(0, wp_last - a.window + 1) : 0;
+    // A range [lo, hi] of step starts, kept as lo and hi - lo so that a test is one unsigned
+    // compare; an empty range (hi < lo, or !ok) holds no step start.
+    struct Span {
+        uint32_t lo, n;
+        __device__ bool has(int t) const { return (uint32_t)t - lo <= n; }
+    };
+    auto make_span = [](int lo, int hi, bool ok) {
+        return ok && hi >= lo ? Span{(uint32_t)lo, (uint32_t)(hi - lo)} : Span{1u << 30, 0u};
+    };
+    // the steps some row of the wavefront sees: t0 <= wp_last and t0 + STEP > wlo_first
+    const Span w_steps = make_span(wlo_first - (S::STEP - 1), wp_last, true);
+    // the steps every row of the wavefront sees whole: all its rows exist,
+    // t0 + STEP - 1 <= wp_first and t0 >= wlo_last
+    const Span w_full = make_span(wlo_last, wp_first - (S::STEP - 1), w_rows_full);
 
     // Q^T operand: 8 elements at d = 16 ks + 8 h of this lane's row and head
     u32x4 qb[KS];
@@ -213,19 +227,33 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
         return StepIds{t0, t0 + kBlock > lo_first ? r0 : -1,
                        two && t0 + 2 * kBlock > lo_first ? r1 : -1};
     };
+    // the steps inside the row range, t0 >= lo_first and t0 + STEP <= L, when every block
+    // id the tile reads is in the pool (set by the check before the loop)
+    Span in_steps = make_span(0, -1, false);
     // The step's loads: scalar base offsets of its two blocks (the cache's first tile for a
     // block outside the row's range or with an invalid id); each lane's pieces sit at a
-    // fixed 32-bit offset from one of them.
-    auto stage_load = [&](const StepIds& ids, Stage& st) {
-        const int t0 = ids.t0, id0 = ids.id0, id1 = ids.id1;
-        const bool ok0 = (uint32_t)id0 < (uint32_t)a.num_blocks;
-        const bool ok1 = (uint32_t)id1 < (uint32_t)a.num_blocks;
+    // fixed 32-bit offset from one of them.  A step inside the row's range, [lo_first, L),
+    // with valid ids (the common case) takes a short scalar path: two table entries, two
+    // products, all its tokens staged.
+    auto stage_load = [&](int t0, Stage& st) {
+        uint64_t base[2];
         st.t0 = t0;
-        st.flags = (int)ok0 | (int)ok1 << 1 |
-                   (int)(ok0 && ok1 && t0 >= lo_first && t0 + S::STEP <= L) << 2;
-        const uint64_t base[2] = {
-            ok0 ? (uint64_t)(uint32_t)id0 * (uint32_t)block_stride + goff : 0,
-            ok1 ? (uint64_t)(uint32_t)id1 * (uint32_t)block_stride + goff : 0};
+        if (in_steps.has(t0)) {
+            const uint32_t b0 = (uint32_t)t0 / kBlock;
+            const int id0 = btc[b0], id1 = btc[b0 + 1];
+            st.flags = 7;
+            base[0] = (uint64_t)(uint32_t)id0 * (uint32_t)block_stride + goff;
+            base[1] = (uint64_t)(uint32_t)id1 * (uint32_t)block_stride + goff;
+        } else {
+            const StepIds ids = step_ids(t0);
+            const int id0 = ids.id0, id1 = ids.id1;
+            const bool ok0 = (uint32_t)id0 < (uint32_t)a.num_blocks;
+            const bool ok1 = (uint32_t)id1 < (uint32_t)a.num_blocks;
+            st.flags = (int)ok0 | (int)ok1 << 1 |
+                       (int)(ok0 && ok1 && t0 >= lo_first && t0 + S::STEP <= L) << 2;
+            base[0] = ok0 ? (uint64_t)(uint32_t)id0 * (uint32_t)block_stride + goff : 0;
+            base[1] = ok1 ? (uint64_t)(uint32_t)id1 * (uint32_t)block_stride + goff : 0;
+        }
 #pragma unroll
         for (int i = 0; i < S::KPT; ++i) {
             const int c = (tid + i * S::THREADS) % S::KPIECES;
@@ -306,6 +334,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             if (kBlock * b < L && kBlock * b + kBlock > lo_first)
                 bad |= (uint32_t)bt[b] >= (uint32_t)a.num_blocks;
         if (bad) atomicOr((int32_t*)(a.ws + a.lay.header), kErrBlockId);
+        const bool ids_ok = __builtin_amdgcn_readfirstlane(__syncthreads_or(bad)) == 0;
+        in_steps = make_span(lo_first, L - S::STEP, ids_ok);
     }
     auto step_t = [&](int st) { return min(t_first + st * S::STEP, t_last); };
     // step st computes from LDS buffer st & 1 while steps st+1 (register set (st+1) & 1)
@@ -315,7 +345,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
         constexpr int P = decltype(Pc)::value;
         constexpr bool kF16PV = DT == DT_F16 || decltype(Cc)::value;
         const int buf = st & 1, t0 = t_first + st * S::STEP;
-        if (t0 <= wp_last && t0 + S::STEP > wlo_first) {      // wavefront-uniform
+        if (w_steps.has(t0)) {                                  // wavefront-uniform
             const char* kl = lds_k[buf];
             const char* vl = lds_v[buf];
             // S^T = K . Q^T (raw dot products)
@@ -356,7 +386,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
                 for (int dt = 0; dt < DT32; ++dt) va0[dt] = v_operand(0, dt);
             }
             // element r of this lane is token t0 + 8 (r/4) + 4 h + r%4 of its M-row
-            const bool full = w_rows_full && t0 + S::STEP - 1 <= wp_first && t0 >= wlo_last;
+            const bool full = w_full.has(t0);
             float p16[16];
             // element r is visible: it lies in this lane's visible token range of the step,
             // [tlo, thi] as offsets 0..31 (both less 4 h, so that element r compares a
@@ -467,7 +497,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             }
         }
         if (st + 1 < nsteps) stage_store(Cc, buf ^ 1, sg[P]);
-        stage_load(step_ids(step_t(st + 3)), sg[P]);
+        stage_load(step_t(st + 3), sg[P]);
         __syncthreads();
     };
     // one pass over the tile's steps
@@ -478,10 +508,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chun
             for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
         m_run = kNegBig;
         l_run = 0.f;
-        stage_load(step_ids(step_t(0)), sg[0]);
+        stage_load(step_t(0), sg[0]);
         if (nsteps > 0) stage_store(Cc, 0, sg[0]);
-        stage_load(step_ids(step_t(1)), sg[1]);
-        stage_load(step_ids(step_t(2)), sg[0]);
+        stage_load(step_t(1), sg[1]);
+        stage_load(step_t(2), sg[0]);
         __syncthreads();
         for (int st = 0; st < nsteps; st += 2) {
             body(Cc, std::integral_constant<int, 1>{}, st);
