@@ -87,7 +87,8 @@ struct ChunkShape {
 
 template <int DT, int D, int G>
 // d <= 128: two workgroups per CU.  d = 256 needs more than 256 VGPRs: one wavefront per
-// SIMD, so that nothing spills to scratch memory.
+// SIMD (512 registers).  Its fp16 instances spill nothing; the bf16 ones, which also hold the
+// second pass, spill 2-4 registers (12-20 bytes of scratch memory per lane).
 __global__ __launch_bounds__(kWavesPerGroup * kWave, D <= 128 ? 2 : 1) void chunk_kernel(DecodeArgs a) {
     using S = ChunkShape<D>;
     constexpr int KS = D / 16, DT32 = D / 32, QR = S::MW / G;
